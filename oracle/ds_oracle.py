@@ -1,0 +1,196 @@
+"""CPU oracle for the Double Sparsity decode step.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only the tests, the smoke check and the benchmark's CPU
+baseline leg use it.  It shares no code with the HIP library.
+
+Plain numpy in float64.  It follows the method step by step, in the order the
+Double Sparsity page describes it (method details: offline calibration of a
+static channel-sparsity pattern, then online selection of the important
+tokens, then self-attention over those tokens only), not a fused or blocked
+reformulation.  Inputs are the already-rounded stored values, widened exactly
+to float64 by the caller.
+
+Where the pages leave a step open, the reading taken is:
+  * calibration score of channel c for KV head g: mean over the calibration
+    queries of the group's query heads of |q_c|, times the mean over the
+    calibration keys of |k_c| (the mean of |q_c|*|k_c| over all query/key
+    pairs, which factorises into this product); keep the r largest, lower
+    channel id first on ties, return ids ascending;
+  * label score: sum over the r label channels and over the group's query
+    heads of q_c * K_c, with no scale (a positive scale cannot change a
+    ranking);
+  * block score: the maximum label score over the tokens of the block that
+    exist;
+  * selection: the k largest scores, lower index first on ties, returned in
+    ascending index order;
+  * attention: softmax of q.K / sqrt(d) over the selected tokens only, no
+    forced sink or recent tokens, no causal mask (a decode query sees all T).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+# -- offline stage ----------------------------------------------------------
+
+def calibrate_channels(q_cal: np.ndarray, k_cal: np.ndarray, Hkv: int, r: int) -> np.ndarray:
+    """Static label channels per KV head, [Hkv, r] int32, ascending.
+
+    Double Sparsity page, method details and abstract: the channel-sparsity
+    pattern is nearly static, so it is fixed offline from a small calibration
+    set and reused at run time.  The page does not give the calibration rule;
+    the rule used is the importance mean|q_c| * mean|k_c|, pooled over the
+    query heads that share KV head g.
+
+    q_cal: [n_q, Hq, d]; k_cal: [Hkv, n_k, d].
+    """
+    q = np.asarray(q_cal, dtype=np.float64)
+    k = np.asarray(k_cal, dtype=np.float64)
+    n_q, Hq, d = q.shape
+    if Hq % Hkv or not (1 <= r <= d):
+        raise ValueError("bad calibration shape")
+    G = Hq // Hkv
+    out = np.empty((Hkv, r), dtype=np.int32)
+    for g in range(Hkv):
+        a = np.abs(q[:, g * G:(g + 1) * G, :]).mean(axis=(0, 1))   # [d]
+        b = np.abs(k[g]).mean(axis=0)                                # [d]
+        importance = a * b
+        order = np.argsort(-importance, kind="stable")                # ties: lower c first
+        out[g] = np.sort(order[:r])
+    return out
+
+
+# -- online stage: identification through label channels --------------------
+
+def label_rows(K: np.ndarray, ch: np.ndarray) -> np.ndarray:
+    """Label cache of one KV head: L[t, j] = K[t, ch[j]]  ([T, r]).
+
+    Double Sparsity page, key points and abstract: only the important feature
+    channels of K are consulted to find the important tokens.
+    """
+    return np.asarray(K)[:, np.asarray(ch)]
+
+
+def label_scores(q_group: np.ndarray, L: np.ndarray, ch: np.ndarray) -> np.ndarray:
+    """Approximate score of every token, u[t] = sum_h sum_j q[h, ch[j]] * L[t, j].
+
+    Double Sparsity page, abstract: channel sparsity identifies the important
+    tokens.  Query heads that share one KV head are summed so the group keeps
+    one token set.  q_group: [G, d]; L: [T, r].  Returns float64 [T].
+    """
+    qs = np.asarray(q_group, dtype=np.float64)[:, np.asarray(ch)]    # [G, r]
+    per_head = np.asarray(L, dtype=np.float64) @ qs.T                 # [T, G]
+    return per_head.sum(axis=1)
+
+
+def block_scores(u: np.ndarray, block: int) -> np.ndarray:
+    """Block informativeness = max of the token scores in the block.
+
+    Jenga page, core method item 1: token scores are aggregated block-wise by
+    taking the maximum (default block of 64 tokens).  A partial last block
+    takes the max over the tokens it has.
+    """
+    u = np.asarray(u, dtype=np.float64)
+    nb = -(-len(u) // block)
+    return np.array([u[i * block:min((i + 1) * block, len(u))].max() for i in range(nb)])
+
+
+def select_topk(u: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest scores, ties to the lower index, ascending.
+
+    Double Sparsity page, method details: the tokens with the higher
+    (approximate) activations are the ones kept.  HiP page, abstract: the top-k
+    keys for the query.
+    """
+    u = np.asarray(u, dtype=np.float64)
+    if not (1 <= k <= len(u)):
+        raise ValueError("k out of range")
+    order = np.argsort(-u, kind="stable")
+    return np.sort(order[:k]).astype(np.int64)
+
+
+def blocks_to_tokens(blocks: np.ndarray, block: int, T: int) -> np.ndarray:
+    """Token ids covered by the kept blocks, ascending, clipped to the T valid tokens."""
+    blocks = np.sort(np.asarray(blocks, dtype=np.int64))
+    toks = (blocks[:, None] * block + np.arange(block)[None, :]).reshape(-1)
+    return toks[toks < T]
+
+
+# -- online stage: exact attention over the kept tokens ---------------------
+
+def attention_weights(q_group: np.ndarray, K: np.ndarray, S: np.ndarray, scale: float) -> np.ndarray:
+    """Softmax weights [G, |S|] of each query head over the kept tokens S."""
+    z = np.asarray(q_group, dtype=np.float64) @ np.asarray(K, dtype=np.float64)[S].T * scale
+    z = z - z.max(axis=1, keepdims=True)
+    w = np.exp(z)
+    return w / w.sum(axis=1, keepdims=True)
+
+
+def attend(q_group: np.ndarray, K: np.ndarray, V: np.ndarray, S: np.ndarray, scale: float) -> np.ndarray:
+    """Self-attention restricted to the kept tokens: out[h] = softmax(q_h.K_S * scale) V_S.
+
+    Double Sparsity page, key points and abstract: token sparsity computes
+    self-attention with the important tokens only.  Jenga page, core method
+    item 3: kept rows are read in place from the original cache (no reordered
+    copy), which does not change the result.  Returns float64 [G, d].
+    """
+    w = attention_weights(q_group, K, S, scale)
+    return w @ np.asarray(V, dtype=np.float64)[S]
+
+
+def attend_partial(q_group, K, V, S, scale):
+    """Unnormalised softmax state over a slice S of the kept tokens: (m [G], l [G], acc [G, d])."""
+    z = np.asarray(q_group, dtype=np.float64) @ np.asarray(K, dtype=np.float64)[S].T * scale
+    m = z.max(axis=1)
+    p = np.exp(z - m[:, None])
+    return m, p.sum(axis=1), p @ np.asarray(V, dtype=np.float64)[S]
+
+
+def merge_partials(parts):
+    """Combine per-slice softmax states by log-sum-exp: m = max m_s, l = sum l_s e^(m_s - m),
+    out = sum acc_s e^(m_s - m) / l.  Exact algebra of softmax over a partitioned set."""
+    m = np.max(np.stack([p[0] for p in parts]), axis=0)
+    l = sum(p[1] * np.exp(p[0] - m) for p in parts)
+    acc = sum(p[2] * np.exp(p[0] - m)[:, None] for p in parts)
+    return acc / l[:, None]
+
+
+# -- one decode step of one (sequence, KV head) unit ------------------------
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)
+
+
+def decode_unit(q_group, K, V, ch, k_units, block=1, scale=None, T=None):
+    """Double Sparsity decode for one unit, steps in the page's order.
+
+    q_group [G, d], K and V [>= T, d] (float64 values), ch [r] label channels.
+    Returns (out [G, d], kept unit ids ascending, scores of the units).
+    """
+    K = np.asarray(K, dtype=np.float64)
+    if T is None:
+        T = K.shape[0]
+    K = K[:T]
+    V = np.asarray(V, dtype=np.float64)[:T]
+    if scale is None:
+        scale = default_scale(K.shape[1])
+    L = label_rows(K, ch)
+    u = label_scores(q_group, L, ch)
+    if block == 1:
+        scores = u
+        kept = select_topk(u, k_units)
+        S = kept
+    else:
+        scores = block_scores(u, block)
+        kept = select_topk(scores, k_units)
+        S = blocks_to_tokens(kept, block, T)
+    return attend(q_group, K, V, S, scale), kept, scores
+
+
+def tokens_of(kept, block, T):
+    """Token ids attended for a kept-unit list (identity for block == 1)."""
+    kept = np.asarray(kept, dtype=np.int64)
+    return kept if block == 1 else blocks_to_tokens(kept, block, T)

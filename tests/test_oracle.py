@@ -1,0 +1,445 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each check ties an oracle function to something other than itself: brute force
+with exact (fsum) sums on tiny inputs, a library routine (torch's fp64
+scaled_dot_product_attention), closed forms, invariants, planted structure in
+the synthetic workloads, and a hand-worked fixture.  The mutation tests at the
+end plant plausible mistakes in a copy of the oracle and check that some pin
+catches each one.
+"""
+import json
+import math
+import os
+import types
+
+import numpy as np
+import pytest
+import torch
+
+import dsgen
+import oracle as O
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _ns(**override):
+    ns = types.SimpleNamespace(**{k: getattr(O, k) for k in O.__all__})
+    for k, v in override.items():
+        setattr(ns, k, v)
+    return ns
+
+
+# ---------------------------------------------------------------- brute force helpers
+
+def brute_rank_select(u, k):
+    """Index t is kept iff fewer than k indices beat it (larger, or equal with a lower id)."""
+    n = len(u)
+    keep = []
+    for t in range(n):
+        beat = sum(1 for s in range(n) if u[s] > u[t] or (u[s] == u[t] and s < t))
+        if beat < k:
+            keep.append(t)
+    return keep
+
+
+def brute_importance(q_cal, k_cal, g, G):
+    n_q, Hq, d = q_cal.shape
+    n_k = k_cal.shape[1]
+    out = []
+    for c in range(d):
+        tot = math.fsum(abs(float(q_cal[n, h, c])) * abs(float(k_cal[g, m, c]))
+                        for n in range(n_q) for h in range(g * G, (g + 1) * G) for m in range(n_k))
+        out.append(tot / (n_q * G * n_k))
+    return out
+
+
+def brute_label_score(q_group, K, ch, t):
+    return math.fsum(float(q_group[h, c]) * float(K[t, c]) for h in range(q_group.shape[0]) for c in ch)
+
+
+# ---------------------------------------------------------------- checks (shared with mutation tests)
+
+def check_calibration_brute(ns, seed=0):
+    rng = np.random.default_rng(seed)
+    n_q, n_k, Hq, Hkv, d = 5, 7, 4, 2, 9
+    q = rng.standard_normal((n_q, Hq, d))
+    k = rng.standard_normal((Hkv, n_k, d))
+    G = Hq // Hkv
+    for r in (1, 3, 9):
+        got = ns.calibrate_channels(q, k, Hkv, r)
+        for g in range(Hkv):
+            want = brute_rank_select(brute_importance(q, k, g, G), r)
+            assert list(got[g]) == want, (r, g, list(got[g]), want)
+
+
+def check_calibration_ties(ns):
+    q = np.ones((3, 2, 8))
+    k = np.ones((1, 4, 8))
+    for r in (1, 5, 8):
+        assert list(ns.calibrate_channels(q, k, 1, r)[0]) == list(range(r))
+    # channels 2 and 6 tie for the top; 0 and 4 tie for third
+    k2 = np.ones((1, 4, 8))
+    k2[0, :, 2] = k2[0, :, 6] = 5.0
+    k2[0, :, 0] = k2[0, :, 4] = 3.0
+    assert list(ns.calibrate_channels(q, k2, 1, 3)[0]) == [0, 2, 6]
+
+
+def check_label_gather(ns):
+    K = np.arange(70, dtype=np.float64).reshape(7, 10)
+    ch = np.array([1, 4, 9])
+    L = ns.label_rows(K, ch)
+    for t in range(7):
+        for j, c in enumerate(ch):
+            assert L[t, j] == 10 * t + c
+
+
+def check_scores_brute(ns, seed=1):
+    rng = np.random.default_rng(seed)
+    G, d, T = 3, 16, 20
+    q = rng.standard_normal((G, d))
+    K = rng.standard_normal((T, d))
+    for ch in (np.arange(d), np.array([0, 5, 6, 11]), np.array([15])):
+        u = ns.label_scores(q, ns.label_rows(K, ch), ch)
+        want = [brute_label_score(q, K, ch, t) for t in range(T)]
+        np.testing.assert_allclose(u, want, rtol=0, atol=1e-12)
+
+
+def check_block_max_brute(ns, seed=2):
+    rng = np.random.default_rng(seed)
+    for T, b in ((100, 64), (128, 64), (7, 3), (5, 1)):
+        u = rng.standard_normal(T)
+        got = ns.block_scores(u, b)
+        want = []
+        for s in range(0, T, b):
+            m = -math.inf
+            for t in range(s, min(s + b, T)):
+                m = u[t] if u[t] > m else m
+            want.append(m)
+        assert list(got) == want
+
+
+def check_select_brute(ns, seed=3):
+    rng = np.random.default_rng(seed)
+    for n in (1, 2, 17, 40):
+        u = rng.integers(-3, 4, size=n).astype(np.float64)   # many exact ties
+        for k in sorted({1, n // 3 + 1, n // 2 + 1, n}):
+            assert list(ns.select_topk(u, k)) == brute_rank_select(list(u), k), (n, k)
+
+
+def _sdpa(q_group, K, V, S, scale):
+    """torch's fp64 scaled_dot_product_attention with a boolean mask keeping S."""
+    G, d = q_group.shape
+    T = K.shape[0]
+    mask = torch.zeros((1, 1, 1, T), dtype=torch.bool)
+    mask[..., torch.as_tensor(np.asarray(S))] = True
+    qt = torch.as_tensor(q_group, dtype=torch.float64).reshape(1, G, 1, d)
+    kt = torch.as_tensor(K, dtype=torch.float64).reshape(1, 1, T, d).expand(1, G, T, d).contiguous()
+    vt = torch.as_tensor(V, dtype=torch.float64).reshape(1, 1, T, d).expand(1, G, T, d).contiguous()
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale)
+    return o.reshape(G, d).numpy()
+
+
+def check_attend_sdpa(ns, seed=4):
+    rng = np.random.default_rng(seed)
+    G, d, T = 4, 32, 50
+    q = rng.standard_normal((G, d)) * 2
+    K = rng.standard_normal((T, d))
+    V = rng.standard_normal((T, d))
+    scale = 1 / math.sqrt(d)
+    for S in (np.arange(T), np.array([3]), np.sort(rng.choice(T, 13, replace=False))):
+        np.testing.assert_allclose(ns.attend(q, K, V, S, scale), _sdpa(q, K, V, S, scale),
+                                   rtol=0, atol=1e-12)
+
+
+def check_split_merge(ns, seed=5):
+    rng = np.random.default_rng(seed)
+    G, d, T = 2, 8, 40
+    q = rng.standard_normal((G, d)) * 3
+    K = rng.standard_normal((T, d))
+    V = rng.standard_normal((T, d))
+    S = np.sort(rng.choice(T, 23, replace=False))
+    whole = ns.attend(q, K, V, S, 0.5)
+    for parts in (1, 2, 5, 23):
+        cuts = np.sort(rng.choice(np.arange(1, len(S)), parts - 1, replace=False)) if parts > 1 else []
+        pieces = np.split(S, cuts)
+        merged = ns.merge_partials([ns.attend_partial(q, K, V, p, 0.5) for p in pieces])
+        np.testing.assert_allclose(merged, whole, rtol=0, atol=1e-12)
+
+
+def check_golden(ns):
+    with open(os.path.join(HERE, "golden", "hand_worked.json")) as f:
+        gold = json.load(f)
+    cal = gold["calibration"]
+    qc = np.array(cal["q_cal"], dtype=np.float64)
+    kc = np.array(cal["k_cal"], dtype=np.float64)
+    for r, want in cal["expected"].items():
+        assert list(ns.calibrate_channels(qc, kc, 1, int(r))[0]) == want
+    dec = gold["decode"]
+    K = np.array(dec["K"], dtype=np.float64)
+    V = np.array(dec["V"], dtype=np.float64)
+    ch = np.array(dec["channels"])
+    scale = 1 / math.sqrt(dec["d"])
+    T = K.shape[0]
+    for case in dec["cases"]:
+        q = np.array(case["q"], dtype=np.float64)
+        u = ns.label_scores(q, ns.label_rows(K, ch), ch)
+        if case["block"] == 1:
+            kept = ns.select_topk(u, case["k_units"])
+            S = kept
+        else:
+            kept = ns.select_topk(ns.block_scores(u, case["block"]), case["k_units"])
+            S = ns.blocks_to_tokens(kept, case["block"], T)
+        assert list(kept) == case["kept"], case["why"]
+        np.testing.assert_allclose(ns.attend(q, K, V, S, scale), np.array(case["out"]),
+                                   rtol=0, atol=1e-12, err_msg=case["why"])
+
+
+# ---------------------------------------------------------------- pins
+
+def test_calibration_matches_all_pairs_brute_force():
+    check_calibration_brute(O)
+
+
+def test_calibration_ties_go_to_lower_channel():
+    check_calibration_ties(O)
+
+
+@pytest.mark.parametrize("name", dsgen.WORKLOAD_ORDER)
+def test_calibration_recovers_planted_outliers(name):
+    """The planted x6 channels dominate mean|q_c|*mean|k_c| by a wide margin, so r >= 8
+    label channels must contain them and r == 8 must equal them."""
+    w = dsgen.get(name)
+    qc, kc = dsgen.gen_calib(w)
+    ch = O.calibrate_channels(qc, kc, w.Hkv, w.r)
+    planted = dsgen.outlier_channels(w)
+    for g in range(w.Hkv):
+        assert set(planted[g]) <= set(ch[g])
+        assert list(ch[g]) == sorted(ch[g])
+        if w.r == w.n_outliers:
+            assert list(ch[g]) == list(planted[g])
+
+
+def test_label_is_identity_gather():
+    check_label_gather(O)
+
+
+def test_label_scores_match_exact_brute_force():
+    check_scores_brute(O)
+
+
+def test_label_scores_channel_order_and_head_additivity():
+    rng = np.random.default_rng(6)
+    G, d, T = 4, 24, 33
+    q = rng.standard_normal((G, d))
+    K = rng.standard_normal((T, d))
+    ch = np.array([2, 3, 7, 19, 20])
+    u = O.label_scores(q, O.label_rows(K, ch), ch)
+    perm = ch[[3, 0, 4, 1, 2]]
+    np.testing.assert_allclose(O.label_scores(q, O.label_rows(K, perm), perm), u, rtol=0, atol=1e-12)
+    # GQA: the group's score is the sum of the single-head (MHA, G = 1) scores
+    heads = sum(O.label_scores(q[h:h + 1], O.label_rows(K, ch), ch) for h in range(G))
+    np.testing.assert_allclose(heads, u, rtol=0, atol=1e-12)
+
+
+def test_block_max_matches_brute_force():
+    check_block_max_brute(O)
+
+
+def test_select_matches_rank_counting_with_ties():
+    check_select_brute(O)
+
+
+def test_r_equals_d_selects_exact_topk_of_true_scores():
+    """With every channel as a label channel, identification is exact: the kept set is the
+    top-k of the true q.k (summed over the group), by exact brute force."""
+    rng = np.random.default_rng(7)
+    G, d, T, k = 2, 16, 60, 9
+    q = rng.standard_normal((G, d))
+    K = rng.standard_normal((T, d))
+    V = rng.standard_normal((T, d))
+    _, kept, _ = O.decode_unit(q, K, V, np.arange(d), k)
+    true = [math.fsum(float(q[h, c]) * float(K[t, c]) for h in range(G) for c in range(d)) for t in range(T)]
+    assert list(kept) == brute_rank_select(true, k)
+
+
+def test_k_equals_T_is_dense_attention():
+    rng = np.random.default_rng(8)
+    G, d, T = 3, 32, 64
+    q = rng.standard_normal((G, d)) * 2
+    K = rng.standard_normal((T, d))
+    V = rng.standard_normal((T, d))
+    out, kept, _ = O.decode_unit(q, K, V, np.array([0, 1, 2, 3]), T)
+    assert list(kept) == list(range(T))
+    np.testing.assert_allclose(out, _sdpa(q, K, V, np.arange(T), 1 / math.sqrt(d)), rtol=0, atol=1e-12)
+
+
+def test_attention_matches_torch_sdpa():
+    check_attend_sdpa(O)
+
+
+def test_weights_sum_to_one_and_output_is_convex_combination():
+    rng = np.random.default_rng(9)
+    G, d, T = 4, 16, 80
+    q = rng.standard_normal((G, d)) * 4
+    K = rng.standard_normal((T, d))
+    V = rng.standard_normal((T, d))
+    S = np.sort(rng.choice(T, 20, replace=False))
+    w = O.attention_weights(q, K, S, 0.25)
+    assert np.all(w >= 0)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+    out = O.attend(q, K, V, S, 0.25)
+    lo, hi = V[S].min(axis=0), V[S].max(axis=0)
+    assert np.all(out >= lo - 1e-12) and np.all(out <= hi + 1e-12)
+
+
+def test_block_variant_special_cases():
+    rng = np.random.default_rng(10)
+    G, d, T = 2, 16, 100
+    q = rng.standard_normal((G, d))
+    K = rng.standard_normal((T, d))
+    V = rng.standard_normal((T, d))
+    ch = np.array([1, 5, 9])
+    # block = 1 is the token variant
+    o1, k1, s1 = O.decode_unit(q, K, V, ch, 10, block=1)
+    np.testing.assert_array_equal(O.block_scores(s1, 1), s1)
+    np.testing.assert_array_equal(O.select_topk(O.block_scores(s1, 1), 10), k1)
+    # keeping every block is dense attention, including the partial last block (100 = 64 + 36)
+    od, kd, sd = O.decode_unit(q, K, V, ch, 2, block=64)
+    assert list(kd) == [0, 1] and len(sd) == 2
+    np.testing.assert_allclose(od, _sdpa(q, K, V, np.arange(T), 0.25), rtol=0, atol=1e-12)
+    assert list(O.blocks_to_tokens(np.array([1]), 64, T)) == list(range(64, 100))
+
+
+def test_split_merge_is_partition_invariant():
+    check_split_merge(O)
+
+
+def test_hand_worked_fixture():
+    check_golden(O)
+
+
+def test_decode_unit_on_workload_slice():
+    """One full-length unit of the headline workload: the kept set has k distinct ascending
+    ids, and exact identification (r = d) keeps more of the true top-k than the r = 16 labels,
+    which in turn beat the k/T recall of random pruning by a wide margin."""
+    w = dsgen.get("llama7b_16k")
+    K, V, q = dsgen.gen_unit(w, 0, 3)
+    K, V, q = dsgen.to_f64(K, w.dtype), dsgen.to_f64(V, w.dtype), dsgen.to_f64(q, w.dtype)
+    qc, kc = dsgen.gen_calib(w)
+    ch = O.calibrate_channels(qc, kc, w.Hkv, w.r)[3]
+    out, kept, u = O.decode_unit(q, K, V, ch, w.k_units)
+    assert len(kept) == w.k_units and np.all(np.diff(kept) > 0)
+    _, exact, _ = O.decode_unit(q, K, V, np.arange(w.d), w.k_units)
+    recall = len(set(kept) & set(exact)) / w.k_units
+    assert recall > 4 * w.k_units / w.T
+    assert np.all(np.isfinite(out))
+
+
+# ---------------------------------------------------------------- planted mistakes
+
+def _mut_calib_sum_not_product(q_cal, k_cal, Hkv, r):
+    q = np.asarray(q_cal, np.float64); k = np.asarray(k_cal, np.float64)
+    G = q.shape[1] // Hkv
+    out = np.empty((Hkv, r), np.int32)
+    for g in range(Hkv):
+        s = np.abs(q[:, g * G:(g + 1) * G]).mean(axis=(0, 1)) + np.abs(k[g]).mean(axis=0)
+        out[g] = np.sort(np.argsort(-s, kind="stable")[:r])
+    return out
+
+
+def _mut_calib_ties_high(q_cal, k_cal, Hkv, r):
+    q = np.asarray(q_cal, np.float64); k = np.asarray(k_cal, np.float64)
+    G = q.shape[1] // Hkv
+    out = np.empty((Hkv, r), np.int32)
+    for g in range(Hkv):
+        s = np.abs(q[:, g * G:(g + 1) * G]).mean(axis=(0, 1)) * np.abs(k[g]).mean(axis=0)
+        d = len(s)
+        order = d - 1 - np.argsort(-s[::-1], kind="stable")
+        out[g] = np.sort(order[:r])
+    return out
+
+
+def _mut_label_wrong_index(K, ch):
+    return np.asarray(K)[:, np.asarray(ch) - 1]
+
+
+def _mut_scores_one_head(q_group, L, ch):
+    return np.asarray(L, np.float64) @ np.asarray(q_group, np.float64)[0, np.asarray(ch)]
+
+
+def _mut_scores_dropped_term(q_group, L, ch):
+    qs = np.asarray(q_group, np.float64)[:, np.asarray(ch)]
+    return (np.asarray(L, np.float64)[:, :-1] @ qs[:, :-1].T).sum(axis=1) if len(ch) > 1 else \
+        (np.asarray(L, np.float64) @ qs.T).sum(axis=1) * 0
+
+
+def _mut_block_mean(u, block):
+    u = np.asarray(u, np.float64)
+    nb = -(-len(u) // block)
+    return np.array([u[i * block:(i + 1) * block].mean() for i in range(nb)])
+
+
+def _mut_select_ties_high(u, k):
+    u = np.asarray(u, np.float64)
+    order = len(u) - 1 - np.argsort(-u[::-1], kind="stable")
+    return np.sort(order[:k])
+
+
+def _mut_select_smallest(u, k):
+    return np.sort(np.argsort(np.asarray(u), kind="stable")[:k])
+
+
+def _mut_attend_no_scale(q_group, K, V, S, scale):
+    return O.attend(q_group, K, V, S, 1.0)
+
+
+def _mut_attend_transposed(q_group, K, V, S, scale):
+    z = np.asarray(q_group) @ np.asarray(V)[S].T * scale     # K and V swapped
+    w = np.exp(z - z.max(axis=1, keepdims=True))
+    w /= w.sum(axis=1, keepdims=True)
+    return w @ np.asarray(K)[S]
+
+
+def _mut_merge_no_rescale(parts):
+    l = sum(p[1] for p in parts)
+    return sum(p[2] for p in parts) / l[:, None]
+
+
+MUTANTS = [
+    ("calibrate_channels", _mut_calib_sum_not_product, check_calibration_brute),
+    ("calibrate_channels", _mut_calib_ties_high, check_calibration_ties),
+    ("label_rows", _mut_label_wrong_index, check_label_gather),
+    ("label_scores", _mut_scores_one_head, check_scores_brute),
+    ("label_scores", _mut_scores_dropped_term, check_scores_brute),
+    ("block_scores", _mut_block_mean, check_block_max_brute),
+    ("select_topk", _mut_select_ties_high, check_select_brute),
+    ("select_topk", _mut_select_smallest, check_select_brute),
+    ("attend", _mut_attend_no_scale, check_attend_sdpa),
+    ("attend", _mut_attend_transposed, check_attend_sdpa),
+    ("merge_partials", _mut_merge_no_rescale, check_split_merge),
+]
+
+
+@pytest.mark.parametrize("fn,mutant,check", MUTANTS, ids=[f"{m[0]}:{m[1].__name__}" for m in MUTANTS])
+def test_pins_catch_planted_mistake(fn, mutant, check):
+    with pytest.raises(AssertionError):
+        check(_ns(**{fn: mutant}))
+
+
+GOLDEN_MUTANTS = [
+    ("calibrate_channels", _mut_calib_sum_not_product),
+    ("calibrate_channels", _mut_calib_ties_high),
+    ("label_rows", _mut_label_wrong_index),
+    ("label_scores", _mut_scores_one_head),
+    ("label_scores", _mut_scores_dropped_term),
+    ("block_scores", _mut_block_mean),
+    ("select_topk", _mut_select_ties_high),
+    ("select_topk", _mut_select_smallest),
+    ("attend", _mut_attend_transposed),
+]
+
+
+@pytest.mark.parametrize("fn,mutant", GOLDEN_MUTANTS, ids=[f"{m[0]}:{m[1].__name__}" for m in GOLDEN_MUTANTS])
+def test_hand_worked_fixture_catches_planted_mistake(fn, mutant):
+    with pytest.raises(AssertionError):
+        check_golden(_ns(**{fn: mutant}))
