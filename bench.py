@@ -1,0 +1,333 @@
+"""Benchmark of the Double Sparsity sparse decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama7b_16k]
+
+A step is one pass of the whole per-step path over one decode batch: append
+the newest token's label row (label-cache pack of row T-1), then
+ds_decode_sparse_attn (label scores, top-k select, split-K gather attention,
+cross-split merge).  Offline calibration is outside the step.  Steps rotate
+over N independent copies of the cache ("layers") so the per-step working set
+cannot be served from the 256 MB Infinity Cache.  K steps are captured into
+HIP graphs and replayed; the timed region is bracketed by device
+synchronisation and HIP events on the replay stream.
+
+Per-kernel durations come from the stage entry points (same kernels), each
+replayed from its own graph over the rotating instances; the dominant one
+gives the roofline object.  The CPU baseline times the float64 oracle on a
+bounded sample of the same workload with a process pool.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import dsgen  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "sparse decode attention µs/step + achieved HBM GB/s (T=16K, 32 heads, bf16)"
+MALL_BYTES = 256 * 2 ** 20
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w: dsgen.Workload) -> dict:
+    """Bytes the method must move per step (score workspace, split partials and
+    the label build are excluded)."""
+    e = w.elem_bytes
+    k_tok = min(w.k_units * w.block, w.T)
+    parts = {
+        "label_scan": w.B * w.Hkv * w.T * w.r * e,
+        "kv_gather": 2 * w.B * w.Hkv * k_tok * w.d * e,
+        "q": w.B * w.Hq * w.d * e,
+        "out": 4 * w.B * w.Hq * w.d,
+        "indices": 4 * w.B * w.Hkv * w.k_units,
+        "label_append": 2 * w.B * w.Hkv * w.r * e,   # read r channels of K row T-1, write one label row
+    }
+    parts["step"] = sum(parts.values())
+    return parts
+
+
+def default_instances(w: dsgen.Workload) -> int:
+    per = algorithmic_bytes(w)["step"]
+    n = max(1, math.ceil(2 * MALL_BYTES / per))
+    inst_bytes = 2 * w.B * w.Hkv * w.cap * w.d * w.elem_bytes
+    cap = max(1, int(60e9 // max(inst_bytes, 1)))
+    return int(min(n, 32, cap))
+
+
+# ---------------------------------------------------------------- CPU baseline (oracle)
+
+_ORACLE_UNITS = None
+
+
+def _oracle_init():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+
+
+def _oracle_task(i):
+    import oracle as O
+    qg, Kf, Vf, ch, k, block, T = _ORACLE_UNITS[i]
+    O.decode_unit(qg, Kf, Vf, ch, k, block, None, T)
+    return i
+
+
+def cpu_baseline(w, q, K, V, ch, seconds: float):
+    """Wall time of the oracle's decode step on the host cores, over a bounded sample."""
+    global _ORACLE_UNITS
+    import multiprocessing as mp
+    units = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
+    # A sample of whole units; at most 64 units (about 2 GB of float64 inputs at T=16K).
+    sample = units[:64]
+    G = w.G
+    _ORACLE_UNITS = [(dsgen.to_f64(q[b, g * G:(g + 1) * G], w.dtype), dsgen.to_f64(K[b, g, :w.T], w.dtype),
+                      dsgen.to_f64(V[b, g, :w.T], w.dtype), ch[g], w.k_units, w.block, w.T) for b, g in sample]
+    cores = max(1, min(16, len(os.sched_getaffinity(0)), len(sample)))
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores, initializer=_oracle_init) as pool:
+        pool.map(_oracle_task, range(len(sample)))   # warm
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            pool.map(_oracle_task, range(len(sample)))
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or reps >= 1000:
+                break
+    _ORACLE_UNITS = None
+    per_unit_s = el / (reps * len(sample))
+    step_s = per_unit_s * len(units)
+    return {"step_s": step_s, "cores": cores, "reps": reps, "sample_units": len(sample), "units": len(units),
+            "elapsed_s": el}
+
+
+# ---------------------------------------------------------------- GPU
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=640)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--workload", default=dsgen.HEADLINE, choices=dsgen.WORKLOAD_ORDER)
+    ap.add_argument("--instances", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this single-GPU build has no multi-GPU path "
+              "(each GPU would run the same kernels on its own share of (sequence, KV head) rows).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import long_context_sparse_ds_amd as L
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    L.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = dsgen.get(args.workload)
+    ab = algorithmic_bytes(w)
+    n_inst = args.instances or default_instances(w)
+    log(f"workload {w.name}: {w}")
+    log(f"algorithmic bytes/step {ab['step']}, instances {n_inst}")
+
+    t0 = time.perf_counter()
+    q, K, V = dsgen.gen_cache(w)
+    qc, kc = dsgen.gen_calib(w)
+    ch = L.ds_calibrate_channels(qc, kc, w.r)
+    log(f"generated inputs in {time.perf_counter() - t0:.1f}s")
+
+    def up(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    q0, K0, V0 = up(q), up(K), up(V)
+    chd = torch.from_numpy(ch).to(dev)
+    # full label build, timed on its own (prefill cost, not part of the step)
+    lab0 = L.ds_build_label_cache(K0, chd)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    L.ds_build_label_cache(K0, chd, label=lab0)
+    ev1.record()
+    torch.cuda.synchronize()
+    label_build_us = ev0.elapsed_time(ev1) * 1e3
+
+    inst = []
+    for i in range(n_inst):
+        if i == 0:
+            qi, Ki, Vi, li = q0, K0, V0, lab0
+        else:
+            qi, Ki, Vi, li = q0.clone(), K0.clone(), V0.clone(), lab0.clone()
+        ws = L.alloc_workspace(w.B, w.Hq, w.Hkv, w.d, w.T, w.block, w.k_units, dev)
+        out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
+        idx = torch.empty((w.B, w.Hkv, w.k_units), dtype=torch.int32, device=dev)
+        inst.append(dict(q=qi, K=Ki, V=Vi, label=li, ws=ws, out=out, idx=idx))
+    del q, K, V
+    torch.cuda.synchronize()
+    log(f"{n_inst} instances resident ({torch.cuda.memory_allocated() / 2 ** 30:.1f} GiB)")
+
+    def step(i):
+        it = inst[i % n_inst]
+        L.ds_build_label_cache(it["K"], chd, w.T - 1, w.T, label=it["label"])
+        L.ds_decode_sparse_attn(it["q"], it["K"], it["V"], it["label"], chd, w.T, w.k_units, w.block,
+                                out=it["out"], indices=it["idx"], workspace=it["ws"])
+
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def capture(n_steps, fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            fn(0)   # eager run on the capture stream (lazy init)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(n_steps):
+                    fn(i)
+        torch.cuda.synchronize()
+        return g
+
+    rot = capture(n_inst, step)
+    rem = args.steps % n_inst
+    rem_graph = capture(rem, step) if rem else None
+    warm_graph = capture(args.warmup, step) if args.warmup else None
+
+    with torch.cuda.stream(stream):
+        if warm_graph is not None:
+            warm_graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t_host0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(args.steps // n_inst):
+            rot.replay()
+        if rem_graph is not None:
+            rem_graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_host1 = time.perf_counter()
+    ms_total = e0.elapsed_time(e1)
+    us_step = ms_total * 1e3 / args.steps
+    log(f"graph replay: {us_step:.2f} us/step over {args.steps} steps (host wall {(t_host1 - t_host0) * 1e3:.2f} ms)")
+
+    # eager (host-launched) steps, for reference
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        e0.record(stream)
+        n_eager = min(args.steps, 4 * n_inst)
+        for i in range(n_eager):
+            step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    us_step_eager = e0.elapsed_time(e1) * 1e3 / n_eager
+
+    # ---- per-kernel durations via the stage entry points, graph-replayed over the instances
+    scores_buf = [torch.empty((w.B, w.Hkv, -(-w.n_units // 64) * 64), dtype=torch.float32, device=dev)
+                  for _ in range(n_inst)]
+
+    def st_append(i):
+        it = inst[i % n_inst]
+        L.ds_build_label_cache(it["K"], chd, w.T - 1, w.T, label=it["label"])
+
+    def st_scores(i):
+        it = inst[i % n_inst]
+        L.ds_label_scores(it["q"], it["label"], chd, w.T, w.block, scores=scores_buf[i % n_inst])
+
+    def st_select(i):
+        it = inst[i % n_inst]
+        L.ds_topk_select(scores_buf[i % n_inst], w.n_units, w.k_units, idx=it["idx"])
+
+    def st_attn(i):
+        it = inst[i % n_inst]
+        L.ds_sparse_attn_from_indices(it["q"], it["K"], it["V"], it["idx"], w.T, w.block, out=it["out"],
+                                      workspace=it["ws"])
+
+    kernel_us = {}
+    for name, fn in (("label_append", st_append), ("scores", st_scores), ("select", st_select),
+                     ("attention", st_attn)):
+        g = capture(n_inst, fn)
+        with torch.cuda.stream(stream):
+            g.replay()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(args.kernel_reps):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+        kernel_us[name] = e0.elapsed_time(e1) * 1e3 / (args.kernel_reps * n_inst)
+        del g
+    log("per-stage us: " + ", ".join(f"{k}={v:.2f}" for k, v in kernel_us.items()))
+
+    stage_bytes = {
+        "label_append": ab["label_append"],
+        "scores": ab["label_scan"] + ab["q"],
+        "select": ab["indices"],
+        "attention": ab["kv_gather"] + ab["q"] + ab["indices"] + ab["out"],
+    }
+    dominant = max(("scores", "attention", "select"), key=lambda k: kernel_us[k])
+    dom_gbs = stage_bytes[dominant] / (kernel_us[dominant] * 1e-6) / 1e9
+
+    gbs = ab["step"] / (us_step * 1e-6) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": us_step / 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "T": w.T, "r": w.r,
+                   "block": w.block, "k_units": w.k_units, "instances": n_inst, "launch": "hip graph replay",
+                   "parallelism": "single GPU"},
+        "us_per_step": round(us_step, 3),
+        "us_per_step_eager": round(us_step_eager, 3),
+        "algorithmic_bytes_per_step": ab["step"],
+        "step_roofline_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "label_build_us": round(label_build_us, 2),
+        "stage_us": {k: round(v, 3) for k, v in kernel_us.items()},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": stage_bytes[dominant], "avg_launch_us": round(kernel_us[dominant], 3)},
+    }
+
+    if not args.no_cpu and args.cpu_seconds > 0:
+        q, K, V = dsgen.gen_cache(w)
+        cb = cpu_baseline(w, q, K, V, ch, args.cpu_seconds)
+        cpu_us = cb["step_s"] * 1e6
+        result["cpu_baseline"] = {
+            "value": round(ab["step"] / cb["step_s"] / 1e9, 4), "unit": "GB/s", "us_per_step": round(cpu_us, 1),
+            "cores": cb["cores"], "kind": "oracle",
+            "sample": (f"float64 numpy oracle decode of {cb['sample_units']} of {cb['units']} (sequence, KV head) "
+                       f"units, {cb['reps']} repetitions in {cb['elapsed_s']:.1f}s over a pool of {cb['cores']} "
+                       f"single-threaded workers; scaled to the whole step")}
+        result["gpu_over_cpu"] = round(cpu_us / us_step, 1)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

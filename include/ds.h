@@ -1,0 +1,174 @@
+/*
+ * ds.h: C ABI of the Double Sparsity sparse-decode library for AMD MI355X (gfx950).
+ *
+ * One decode step of Double Sparsity ("Post-Training Sparse Attention with
+ * Double Sparsity", method details and abstract): a small set of r "label"
+ * channels of K, fixed offline by calibration, scores every cached token
+ * approximately; the k highest-scoring tokens (or blocks of tokens, the
+ * block-max variant of the Jenga page, core method item 1, and the top-k key
+ * framing of the HiP page, abstract) are kept; exact softmax attention then
+ * runs over the kept tokens' K and V rows only, read in place from the cache.
+ *
+ * Conventions shared by every entry point
+ *   - Plain pointers and sizes only.  "Device" pointers are HIP device memory
+ *     on the current device; "host" pointers are ordinary process memory.
+ *   - The caller owns every buffer, the workspace included.  The library
+ *     allocates no device memory and keeps no pointer after a call returns.
+ *     Buffers passed to a GPU entry point must stay valid until the work
+ *     queued on `stream` has finished.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  GPU
+ *     entry points only enqueue work; they never synchronise.  A fault inside
+ *     a kernel surfaces at the caller's next synchronisation.
+ *   - Every argument is validated before any HIP call.  On failure nothing is
+ *     written or enqueued, the status is returned, and ds_last_error() holds a
+ *     message.  A failed kernel launch returns DS_ERR_HIP.  No C++ exception
+ *     crosses the ABI.
+ *   - Re-entrant; calls that run concurrently need distinct output and
+ *     workspace buffers.
+ *   - Element types: DS_DTYPE_F32 (float) or DS_DTYPE_BF16 (bfloat16 bits in
+ *     uint16).  q, K, V and the label cache share one element type.  Scores
+ *     and outputs are float32.
+ *   - All device buffers must be 16-byte aligned, except int32 index buffers
+ *     (4-byte) and the workspace (256-byte).
+ *   - Head dimension d must be 128 (DS_ERR_UNSUPPORTED otherwise).  Any label
+ *     width 1 <= r <= d works; r * element_size a multiple of 16 bytes takes
+ *     the vectorised path.
+ */
+#ifndef DS_SPARSE_DECODE_H
+#define DS_SPARSE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DS_OK = 0,
+  DS_ERR_INVALID_ARGUMENT = 1,
+  DS_ERR_UNSUPPORTED = 2,
+  DS_ERR_WORKSPACE_TOO_SMALL = 3,
+  DS_ERR_HIP = 4
+} ds_status;
+
+typedef enum { DS_DTYPE_F32 = 0, DS_DTYPE_BF16 = 1 } ds_dtype;
+
+/* Message of the last failed call on this thread ("" if none).  Valid until the
+ * next ds_* call on the same thread. */
+const char* ds_last_error(void);
+
+/* Library version string, e.g. "dsparse 0.1.0 gfx950". */
+const char* ds_version(void);
+
+/*
+ * Offline calibration of the label channels (CPU, synchronous, host memory).
+ * Double Sparsity page, method details: the channel-sparsity pattern is close
+ * to static, so it is fixed once from a small calibration set.  The page does
+ * not give the rule; this library scores channel c of KV head g by
+ *     mean over (n, query heads h of group g) of |q_cal[n, h, c]|
+ *   * mean over n of |k_cal[g, n, c]|
+ * (the mean of |q_c| * |k_c| over all query/key pairs) in double precision,
+ * keeps the r highest (the lower channel id wins a tie) and writes them in
+ * ascending order.
+ *   q_cal        host float [n_q, Hq, d]
+ *   k_cal        host float [Hkv, n_k, d]
+ *   channels_out host int32 [Hkv, r], written only on success
+ * Errors: null pointer, n_q or n_k < 1, Hq % Hkv != 0, r outside [1, d].
+ */
+ds_status ds_calibrate_channels(const float* q_cal, int64_t n_q, const float* k_cal, int64_t n_k,
+                                int32_t Hq, int32_t Hkv, int32_t d, int32_t r, int32_t* channels_out);
+
+/*
+ * Label cache: label[b, g, t, j] = K[b, g, t, channels[g, j]] for t in
+ * [t_begin, t_end) (GPU, async).  Bit copy, no arithmetic.  Run once over the
+ * prefilled tokens, then for the one new row of each decode step (Double
+ * Sparsity page, abstract: the important channels are used to identify the
+ * important tokens, so only they are kept in a compact per-token row).
+ *   K            device [B, Hkv, T_cap, d]
+ *   channels_dev device int32 [Hkv, r], each in [0, d) (not checked)
+ *   label_out    device [B, Hkv, T_cap, r]; rows outside [t_begin, t_end) are
+ *                left untouched
+ * Errors: null pointer, bad dtype, B/Hkv/T_cap < 1, r outside [1, d],
+ * 0 <= t_begin <= t_end <= T_cap violated, misalignment, unsupported d.
+ */
+ds_status ds_build_label_cache(const void* K, ds_dtype dt, int32_t B, int32_t Hkv, int64_t T_cap, int32_t d,
+                               const int32_t* channels_dev, int32_t r, int64_t t_begin, int64_t t_end,
+                               void* label_out, void* stream);
+
+/*
+ * Workspace bytes that ds_decode_sparse_attn needs for this shape, or 0 (with
+ * ds_last_error set) if the shape is invalid.  The amount does not depend on
+ * the element type or r.
+ */
+size_t ds_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t T, int32_t block,
+                                 int64_t k_units);
+
+/*
+ * One Double Sparsity decode step for every (sequence b, KV head g) (GPU, async):
+ *   1. approximate score of each of the T valid tokens,
+ *        u[b,g,t] = sum over query heads h of group g, sum over j < r, of
+ *                   q[b,h,channels[g,j]] * label[b,g,t,j]
+ *      accumulated in double precision and rounded once to float32;
+ *      block > 1: the score of block i is the max of u over its tokens
+ *      (Jenga page, core method item 1), the last block may be partial;
+ *   2. keep the k_units highest-scoring tokens (block = 1) or blocks, the lower
+ *      index winning a tie (Double Sparsity page, method details; HiP page,
+ *      abstract), written ascending to `indices`; all query heads of a group
+ *      share the group's set;
+ *   3. for each query head, softmax(scale * q.K_t) over the kept tokens only
+ *      and the weighted sum of their V rows, read in place from the cache
+ *      (Jenga page, core method item 3), accumulated in float32.
+ *   q            device [B, Hq, d]
+ *   K, V         device [B, Hkv, T_cap, d]; rows >= T are never read
+ *   label        device [B, Hkv, T_cap, r] (from ds_build_label_cache)
+ *   channels_dev device int32 [Hkv, r]
+ *   T            valid tokens, 1 <= T <= T_cap
+ *   block        1, 2, 4, 8, 16, 32 or 64
+ *   k_units      tokens or blocks kept, 1 <= k_units <= ceil(T / block)
+ *   scale        softmax scale; <= 0 means 1/sqrt(d)
+ *   out          device float [B, Hq, d]
+ *   indices      device int32 [B, Hkv, k_units] (token ids, or block ids)
+ *   workspace    device, >= ds_decode_workspace_bytes(...) bytes; contents on
+ *                entry do not matter and are clobbered
+ * Errors: null pointer, bad dtype, Hq % Hkv != 0, r outside [1, d], T or
+ * k_units or block out of range, misalignment, unsupported d, workspace too
+ * small (DS_ERR_WORKSPACE_TOO_SMALL).
+ */
+ds_status ds_decode_sparse_attn(const void* q, const void* K, const void* V, const void* label,
+                                const int32_t* channels_dev, int32_t r, ds_dtype dt, int32_t B, int32_t Hq,
+                                int32_t Hkv, int32_t d, int64_t T_cap, int64_t T, int32_t block, int64_t k_units,
+                                float scale, float* out, int32_t* indices, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
+ * The three stages of ds_decode_sparse_attn, callable on their own so each can
+ * be checked in isolation.  They run the same kernels as the fused call.
+ */
+
+/* Step 1 only: scores[b, g, i] (float32) for i < ceil(T / block).
+ *   scores  device float [B, Hkv, ld], ld >= ceil(T / block), ld % 4 == 0 */
+ds_status ds_label_scores(const void* q, const void* label, const int32_t* channels_dev, int32_t r, ds_dtype dt,
+                          int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t T_cap, int64_t T, int32_t block,
+                          float* scores, int64_t ld, void* stream);
+
+/* Step 2 only: per row of `scores` (rows x n, row stride ld floats), the k
+ * largest values, the lower index winning a tie, written ascending to
+ * idx_out [rows, k].  Values are compared as float32 (-0.0 equals +0.0);
+ * NaN is not supported. */
+ds_status ds_topk_select(const float* scores, int64_t rows, int64_t n, int64_t ld, int64_t k, int32_t* idx_out,
+                         void* stream);
+
+/* Step 3 only: attention over the units listed in `indices` (as
+ * ds_decode_sparse_attn writes them: ascending, distinct, each < ceil(T/block)).
+ * Workspace as for ds_decode_sparse_attn. */
+ds_status ds_sparse_attn_from_indices(const void* q, const void* K, const void* V, ds_dtype dt, int32_t B,
+                                      int32_t Hq, int32_t Hkv, int32_t d, int64_t T_cap, int64_t T,
+                                      int32_t block, int64_t k_units, const int32_t* indices, float scale,
+                                      float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DS_SPARSE_DECODE_H */

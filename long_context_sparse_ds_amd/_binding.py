@@ -1,0 +1,230 @@
+"""ctypes binding of libdsparse.so.
+
+Argument marshalling only: every step runs in the library's HIP kernels (or,
+for the offline calibration, its C++ code).  torch supplies device memory and
+the current HIP stream.  If the library is missing, every call raises: there
+is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libdsparse.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "ds.h")
+
+DS_OK = 0
+DS_ERR_INVALID_ARGUMENT = 1
+DS_ERR_UNSUPPORTED = 2
+DS_ERR_WORKSPACE_TOO_SMALL = 3
+DS_ERR_HIP = 4
+DS_DTYPE_F32 = 0
+DS_DTYPE_BF16 = 1
+
+_c_i32, _c_i64, _c_size, _c_vp, _c_f32 = (ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p,
+                                          ctypes.c_float)
+
+_SIGNATURES = {
+    "ds_last_error": (ctypes.c_char_p, []),
+    "ds_version": (ctypes.c_char_p, []),
+    "ds_calibrate_channels": (_c_i32, [_c_vp, _c_i64, _c_vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_vp]),
+    "ds_build_label_cache": (_c_i32, [_c_vp, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_vp, _c_i32, _c_i64, _c_i64,
+                                      _c_vp, _c_vp]),
+    "ds_decode_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_i64]),
+    "ds_decode_sparse_attn": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                       _c_i32, _c_i64, _c_i64, _c_i32, _c_i64, _c_f32, _c_vp, _c_vp, _c_vp, _c_size,
+                                       _c_vp]),
+    "ds_label_scores": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i64,
+                                 _c_i32, _c_vp, _c_i64, _c_vp]),
+    "ds_topk_select": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp]),
+    "ds_sparse_attn_from_indices": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64,
+                                             _c_i64, _c_i32, _c_i64, _c_vp, _c_f32, _c_vp, _c_vp, _c_size, _c_vp]),
+}
+
+_lib = None
+
+
+class DsError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"ds status {status}: {message}")
+        self.status = status
+
+
+def header_symbols() -> list[str]:
+    """Every function the C header declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(ds_\w+)\s*\(", text, flags=re.M)))
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdsparse.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m long_context_sparse_ds_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def ds_last_error() -> str:
+    return lib().ds_last_error().decode()
+
+
+def ds_version() -> str:
+    return lib().ds_version().decode()
+
+
+def _check(status: int):
+    if status != DS_OK:
+        raise DsError(status, ds_last_error())
+
+
+# ---------------------------------------------------------------- torch helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return DS_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return DS_DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ---------------------------------------------------------------- entry points
+
+def ds_calibrate_channels(q_cal: np.ndarray, k_cal: np.ndarray, r: int) -> np.ndarray:
+    """Offline calibration on the CPU.  q_cal [n_q, Hq, d], k_cal [Hkv, n_k, d] -> int32 [Hkv, r]."""
+    q = np.ascontiguousarray(q_cal, dtype=np.float32)
+    k = np.ascontiguousarray(k_cal, dtype=np.float32)
+    n_q, Hq, d = q.shape
+    Hkv, n_k, d2 = k.shape
+    if d2 != d:
+        raise ValueError("q_cal and k_cal disagree on d")
+    out = np.empty((Hkv, r), dtype=np.int32)
+    _check(lib().ds_calibrate_channels(q.ctypes.data, n_q, k.ctypes.data, n_k, Hq, Hkv, d, r, out.ctypes.data))
+    return out
+
+
+def ds_build_label_cache(K, channels, t_begin: int = 0, t_end: int | None = None, label=None, stream=None):
+    """Pack label[b, g, t, :] = K[b, g, t, channels[g]] for t in [t_begin, t_end).  Returns label."""
+    torch = _torch()
+    B, Hkv, T_cap, d = K.shape
+    r = channels.shape[1]
+    if t_end is None:
+        t_end = T_cap
+    if label is None:
+        label = torch.empty((B, Hkv, T_cap, r), dtype=K.dtype, device=K.device)
+    if channels.dtype != torch.int32 or label.dtype != K.dtype or tuple(label.shape) != (B, Hkv, T_cap, r):
+        raise ValueError("channels must be int32 [Hkv, r]; label must match K's dtype and be [B, Hkv, T_cap, r]")
+    _check(lib().ds_build_label_cache(_dev(K, "K"), _dtype_code(K), B, Hkv, T_cap, d, _dev(channels, "channels"), r,
+                                      t_begin, t_end, _dev(label, "label"), _stream(stream)))
+    return label
+
+
+def ds_decode_workspace_bytes(B: int, Hq: int, Hkv: int, d: int, T: int, block: int, k_units: int) -> int:
+    n = lib().ds_decode_workspace_bytes(B, Hq, Hkv, d, T, block, k_units)
+    if n == 0:
+        raise DsError(DS_ERR_INVALID_ARGUMENT, ds_last_error())
+    return n
+
+
+def alloc_workspace(B, Hq, Hkv, d, T, block, k_units, device="cuda"):
+    torch = _torch()
+    return torch.empty(ds_decode_workspace_bytes(B, Hq, Hkv, d, T, block, k_units), dtype=torch.uint8, device=device)
+
+
+def ds_decode_sparse_attn(q, K, V, label, channels, T: int, k_units: int, block: int = 1, scale: float = 0.0,
+                          out=None, indices=None, workspace=None, stream=None):
+    """One Double Sparsity decode step.  Returns (out fp32 [B, Hq, d], indices int32 [B, Hkv, k_units])."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    _, Hkv, T_cap, _ = K.shape
+    r = channels.shape[1]
+    dt = _dtype_code(q)
+    if K.dtype != q.dtype or V.dtype != q.dtype or label.dtype != q.dtype:
+        raise ValueError("q, K, V and label must share one dtype")
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if indices is None:
+        indices = torch.empty((B, Hkv, k_units), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(B, Hq, Hkv, d, T, block, k_units, q.device)
+    _check(lib().ds_decode_sparse_attn(_dev(q, "q"), _dev(K, "K"), _dev(V, "V"), _dev(label, "label"),
+                                       _dev(channels, "channels"), r, dt, B, Hq, Hkv, d, T_cap, T, block, k_units,
+                                       scale, _dev(out, "out"), _dev(indices, "indices"), _dev(workspace, "workspace"),
+                                       workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, indices
+
+
+def ds_label_scores(q, label, channels, T: int, block: int = 1, scores=None, stream=None):
+    """Approximate scores only: float32 [B, Hkv, ld] with the first ceil(T/block) entries of each row valid."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    _, Hkv, T_cap, r = label.shape
+    n_units = -(-T // block)
+    ld = -(-n_units // 4) * 4
+    if scores is None:
+        scores = torch.empty((B, Hkv, ld), dtype=torch.float32, device=q.device)
+    ld = scores.shape[-1]
+    _check(lib().ds_label_scores(_dev(q, "q"), _dev(label, "label"), _dev(channels, "channels"), r, _dtype_code(q), B,
+                                 Hq, Hkv, d, T_cap, T, block, _dev(scores, "scores"), ld, _stream(stream)))
+    return scores
+
+
+def ds_topk_select(scores, n: int, k: int, idx=None, stream=None):
+    """Top-k per row of a float32 [..., ld] score tensor (first n entries of each row).  Returns int32 [..., k]."""
+    torch = _torch()
+    ld = scores.shape[-1]
+    rows = scores.numel() // ld
+    if idx is None:
+        idx = torch.empty((*scores.shape[:-1], k), dtype=torch.int32, device=scores.device)
+    _check(lib().ds_topk_select(_dev(scores, "scores"), rows, n, ld, k, _dev(idx, "idx"), _stream(stream)))
+    return idx
+
+
+def ds_sparse_attn_from_indices(q, K, V, indices, T: int, block: int = 1, scale: float = 0.0, out=None,
+                                workspace=None, stream=None):
+    """Attention over given kept units only.  Returns out fp32 [B, Hq, d]."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    _, Hkv, T_cap, _ = K.shape
+    k_units = indices.shape[-1]
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(B, Hq, Hkv, d, T, block, k_units, q.device)
+    _check(lib().ds_sparse_attn_from_indices(_dev(q, "q"), _dev(K, "K"), _dev(V, "V"), _dtype_code(q), B, Hq, Hkv,
+                                             d, T_cap, T, block, k_units, _dev(indices, "indices"), scale,
+                                             _dev(out, "out"), _dev(workspace, "workspace"),
+                                             workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out

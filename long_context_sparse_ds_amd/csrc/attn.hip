@@ -1,0 +1,257 @@
+// Exact softmax attention over the kept tokens, split along the kept set.
+//
+// Double Sparsity page, key points and abstract: token sparsity computes
+// self-attention with the important tokens only.  Jenga page, core method
+// item 3: kept rows are read in place from the original cache by index; no
+// reordered copy is ever materialised.
+//
+// Decode attention is a GEMV per query head, so this runs on the vector ALUs,
+// not the matrix cores.  Grid = (split, row = b * Hkv + g, head chunk).  A
+// workgroup streams its slice of the kept list: each 16-lane group (bf16; 32
+// lanes for fp32) owns one 256-byte K row and one V row per step, four rows per
+// group in flight, scores them for every query head of the chunk (the K and V
+// rows are read once for the whole GQA group), and keeps a running softmax
+// state (max m, sum l, unnormalised acc) that is rescaled once per four rows.
+// Lane groups and wavefronts are merged through LDS at the end; the splits of
+// a row are merged by log-sum-exp in a second small kernel (or directly when a
+// row has a single split).
+#include "ds_common.h"
+
+namespace ds {
+namespace {
+
+constexpr int kAT = 256;
+constexpr int kAW = kAT / 64;
+constexpr int kU = 4;   // kept rows per lane group per step
+
+template <typename TE>
+struct Lanes {
+  static constexpr int EPL = 16 / int(sizeof(TE));   // elements per lane: 8 (bf16), 4 (fp32)
+  static constexpr int LPT = kHeadDim / EPL;          // lanes per token row: 16, 32
+  static constexpr int GPW = 64 / LPT;                // lane groups per wavefront
+  static constexpr int NG = kAW * GPW;                // lane groups per workgroup
+};
+
+__device__ __forceinline__ void unpack(const uint4& w, float (&f)[8], uint16_t) {
+  f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x);
+  f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+  f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z);
+  f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+}
+__device__ __forceinline__ void unpack(const uint4& w, float (&f)[4], float) {
+  f[0] = __uint_as_float(w.x); f[1] = __uint_as_float(w.y);
+  f[2] = __uint_as_float(w.z); f[3] = __uint_as_float(w.w);
+}
+
+template <typename TE>
+__device__ __forceinline__ float group_sum(float v) {
+  v = row16_sum(v);
+  if constexpr (Lanes<TE>::LPT == 32) v += __shfl_xor(v, 16);
+  return v;
+}
+
+template <typename TE, int HC>
+__global__ __launch_bounds__(kAT) void attn_kernel(const TE* __restrict__ q, const TE* __restrict__ K,
+                                                   const TE* __restrict__ V, const int32_t* __restrict__ idx,
+                                                   int Hq, int Hkv, int64_t T_cap, int64_t T, int block,
+                                                   int64_t k_units, int64_t kv_virtual, int64_t chunk, int n_split,
+                                                   float scale, float* __restrict__ part_acc,
+                                                   float* __restrict__ part_ml, float* __restrict__ out) {
+  using LN = Lanes<TE>;
+  constexpr int EPL = LN::EPL, LPT = LN::LPT, GPW = LN::GPW, NG = LN::NG;
+  const int split = blockIdx.x;
+  const int64_t row = blockIdx.y;
+  const int b = int(row / Hkv), g = int(row % Hkv);
+  const int G = Hq / Hkv;
+  const int h0 = g * G + int(blockIdx.z) * HC;   // first query head of this chunk
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = lane / LPT, sub = lane % LPT;
+  const int gid = wave * GPW + grp;
+
+  float qv[HC][EPL];
+#pragma unroll
+  for (int h = 0; h < HC; ++h) {
+    const uint4 w = *reinterpret_cast<const uint4*>(q + (int64_t(b) * Hq + h0 + h) * kHeadDim + sub * EPL);
+    unpack(w, qv[h], TE());
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qv[h][e] *= scale;
+  }
+
+  float m[HC], l[HC], acc[HC][EPL];
+#pragma unroll
+  for (int h = 0; h < HC; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
+
+  const int64_t p_begin = int64_t(split) * chunk;
+  const int64_t p_end = min(p_begin + chunk, kv_virtual);
+  const int32_t* ridx = idx + row * k_units;
+  const TE* Kr = K + row * T_cap * kHeadDim + sub * EPL;
+  const TE* Vr = V + row * T_cap * kHeadDim + sub * EPL;
+
+  for (int64_t base = p_begin; base < p_end; base += int64_t(NG) * kU) {
+    int64_t tok[kU];
+    bool ok[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t p = base + int64_t(gid) * kU + u;
+      ok[u] = p < p_end;
+      tok[u] = 0;
+      if (ok[u]) {
+        const int64_t unit = ridx[block == 1 ? p : p / block];
+        tok[u] = block == 1 ? unit : unit * block + p % block;
+        ok[u] = unit >= 0 && tok[u] < T;
+      }
+    }
+    uint4 kr[kU], vr[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (ok[u]) {
+        kr[u] = *reinterpret_cast<const uint4*>(Kr + tok[u] * kHeadDim);
+        vr[u] = *reinterpret_cast<const uint4*>(Vr + tok[u] * kHeadDim);
+      } else {
+        kr[u] = make_uint4(0u, 0u, 0u, 0u);
+        vr[u] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    float kf[kU][EPL], vf[kU][EPL];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      unpack(kr[u], kf[u], TE());
+      unpack(vr[u], vf[u], TE());
+    }
+#pragma unroll
+    for (int h = 0; h < HC; ++h) {
+      float z[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        float dsum = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) dsum = fmaf(qv[h][e], kf[u][e], dsum);
+        dsum = group_sum<TE>(dsum);
+        z[u] = ok[u] ? dsum : -INFINITY;
+      }
+      float mx = m[h];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) mx = fmaxf(mx, z[u]);
+      if (mx == -INFINITY) continue;   // nothing valid seen yet (uniform across the lane group)
+      const float alpha = __expf(m[h] - mx);
+      float p[kU], psum = 0.f;
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        p[u] = __expf(z[u] - mx);
+        psum += p[u];
+      }
+      l[h] = l[h] * alpha + psum;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        float a = acc[h][e] * alpha;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) a = fmaf(p[u], vf[u][e], a);
+        acc[h][e] = a;
+      }
+      m[h] = mx;
+    }
+  }
+
+  // Merge the NG lane-group states of this workgroup.
+  __shared__ float sm_m[NG][HC], sm_l[NG][HC], sm_f[NG][HC];
+  __shared__ float sm_M[HC], sm_L[HC];
+  __shared__ float sm_acc[NG][HC][kHeadDim];
+#pragma unroll
+  for (int h = 0; h < HC; ++h) {
+    if (sub == 0) {
+      sm_m[gid][h] = m[h];
+      sm_l[gid][h] = l[h];
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) sm_acc[gid][h][sub * EPL + e] = acc[h][e];
+  }
+  __syncthreads();
+  if (threadIdx.x < HC) {
+    const int h = threadIdx.x;
+    float M = -INFINITY;
+    for (int gg = 0; gg < NG; ++gg) M = fmaxf(M, sm_m[gg][h]);
+    float Ls = 0.f;
+    for (int gg = 0; gg < NG; ++gg) {
+      const float f = M == -INFINITY ? 0.f : __expf(sm_m[gg][h] - M);
+      sm_f[gg][h] = f;
+      Ls += sm_l[gg][h] * f;
+    }
+    sm_M[h] = M;
+    sm_L[h] = Ls;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < HC * kHeadDim; i += kAT) {
+    const int h = i / kHeadDim, c = i % kHeadDim;
+    float A = 0.f;
+    for (int gg = 0; gg < NG; ++gg) A = fmaf(sm_acc[gg][h][c], sm_f[gg][h], A);
+    const int64_t bh = int64_t(b) * Hq + h0 + h;
+    if (n_split == 1) {
+      out[bh * kHeadDim + c] = A / sm_L[h];
+    } else {
+      part_acc[(bh * n_split + split) * kHeadDim + c] = A;
+      if (c == 0) {
+        part_ml[(bh * n_split + split) * 2 + 0] = sm_M[h];
+        part_ml[(bh * n_split + split) * 2 + 1] = sm_L[h];
+      }
+    }
+  }
+}
+
+// Log-sum-exp merge of the splits of one (sequence, query head): one thread per channel.
+__global__ __launch_bounds__(kHeadDim) void merge_kernel(const float* __restrict__ part_acc,
+                                                         const float* __restrict__ part_ml, int n_split,
+                                                         float* __restrict__ out) {
+  const int64_t bh = blockIdx.x;
+  const int c = threadIdx.x;
+  const float* ml = part_ml + bh * n_split * 2;
+  float M = -INFINITY;
+  for (int s = 0; s < n_split; ++s) M = fmaxf(M, ml[2 * s]);
+  float L = 0.f, A = 0.f;
+  for (int s = 0; s < n_split; ++s) {
+    const float f = __expf(ml[2 * s] - M);
+    L = fmaf(ml[2 * s + 1], f, L);
+    A = fmaf(part_acc[(bh * n_split + s) * kHeadDim + c], f, A);
+  }
+  out[bh * kHeadDim + c] = A / L;
+}
+
+template <typename TE>
+hipError_t dispatch(const TE* q, const TE* K, const TE* V, int B, int Hq, int Hkv, int64_t T_cap, int64_t T,
+                    int block, int64_t k_units, const int32_t* idx, float scale, const DecodePlan& pl,
+                    float* part_acc, float* part_ml, float* out, hipStream_t s) {
+  const int G = Hq / Hkv;
+  const int HC = G % 8 == 0 ? 8 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
+  const dim3 grid(unsigned(pl.n_split), unsigned(pl.rows), unsigned(G / HC));
+#define DS_ATTN(HH)                                                                                              \
+  hipLaunchKernelGGL((attn_kernel<TE, HH>), grid, dim3(kAT), 0, s, q, K, V, idx, Hq, Hkv, T_cap, T, block,       \
+                     k_units, pl.kv_virtual, pl.chunk, pl.n_split, scale, part_acc, part_ml, out)
+  if (HC == 8) DS_ATTN(8);
+  else if (HC == 4) DS_ATTN(4);
+  else if (HC == 2) DS_ATTN(2);
+  else DS_ATTN(1);
+#undef DS_ATTN
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || pl.n_split == 1) return e;
+  hipLaunchKernelGGL(merge_kernel, dim3(unsigned(int64_t(B) * Hq)), dim3(kHeadDim), 0, s, part_acc, part_ml,
+                     pl.n_split, out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention(const void* q, const void* K, const void* V, int is_bf16, int B, int Hq, int Hkv,
+                            int64_t T_cap, int64_t T, int block, int64_t k_units, const int32_t* idx, float scale,
+                            const DecodePlan& plan, float* part_acc, float* part_ml, float* out, hipStream_t s) {
+  if (is_bf16)
+    return dispatch(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V),
+                    B, Hq, Hkv, T_cap, T, block, k_units, idx, scale, plan, part_acc, part_ml, out, s);
+  return dispatch(static_cast<const float*>(q), static_cast<const float*>(K), static_cast<const float*>(V), B, Hq,
+                  Hkv, T_cap, T, block, k_units, idx, scale, plan, part_acc, part_ml, out, s);
+}
+
+}  // namespace ds

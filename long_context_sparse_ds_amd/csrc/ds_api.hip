@@ -1,0 +1,218 @@
+// C ABI entry points: argument validation, workspace planning, kernel launches.
+//
+// Every check runs before the first HIP call, so a rejected call enqueues
+// nothing and writes nothing.  No C++ exception leaves this file.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "ds.h"
+#include "ds_common.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+ds_status fail(ds_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool valid_block(int block) { return block >= 1 && block <= 64 && (block & (block - 1)) == 0; }
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+ds_status check_dtype(ds_dtype dt) {
+  if (dt != DS_DTYPE_F32 && dt != DS_DTYPE_BF16) return fail(DS_ERR_INVALID_ARGUMENT, "dt: unknown dtype %d", int(dt));
+  return DS_OK;
+}
+
+// Shape checks shared by the decode entry points.
+ds_status check_decode_shape(int B, int Hq, int Hkv, int d, int64_t T_cap, int64_t T, int block, int64_t k_units) {
+  if (B < 1 || Hq < 1 || Hkv < 1)
+    return fail(DS_ERR_INVALID_ARGUMENT, "B, Hq, Hkv must be >= 1 (got %d, %d, %d)", B, Hq, Hkv);
+  if (Hq % Hkv != 0) return fail(DS_ERR_INVALID_ARGUMENT, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (d != ds::kHeadDim) return fail(DS_ERR_UNSUPPORTED, "d = %d unsupported (only %d)", d, ds::kHeadDim);
+  if (T < 1 || T > T_cap)
+    return fail(DS_ERR_INVALID_ARGUMENT, "need 1 <= T <= T_cap (T = %lld, T_cap = %lld)", (long long)T,
+                (long long)T_cap);
+  if (T > INT32_MAX) return fail(DS_ERR_UNSUPPORTED, "T = %lld exceeds int32 token ids", (long long)T);
+  if (!valid_block(block)) return fail(DS_ERR_INVALID_ARGUMENT, "block = %d must be a power of two in [1, 64]", block);
+  const int64_t n_units = (T + block - 1) / block;
+  if (k_units < 1 || k_units > n_units)
+    return fail(DS_ERR_INVALID_ARGUMENT, "need 1 <= k_units <= ceil(T/block) = %lld (got %lld)",
+                (long long)n_units, (long long)k_units);
+  if (int64_t(B) * Hkv > 65535)
+    return fail(DS_ERR_UNSUPPORTED, "B * Hkv = %lld exceeds 65535 rows", (long long)(int64_t(B) * Hkv));
+  return DS_OK;
+}
+
+ds_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(DS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return DS_OK;
+}
+
+}  // namespace
+
+namespace ds {
+
+void set_error(const char* msg) { g_err = msg; }
+
+DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t T, int block, int64_t k_units) {
+  DecodePlan p{};
+  p.rows = int64_t(B) * Hkv;
+  p.n_units = (T + block - 1) / block;
+  p.score_ld = (p.n_units + 63) / 64 * 64;
+  p.kv_virtual = k_units * block;
+  // Aim for about 2048 attention workgroups over the whole batch, in slices of
+  // at least 64 kept positions.
+  const int64_t target_wg = 2048;
+  int64_t chunk = (p.kv_virtual * p.rows + target_wg - 1) / target_wg;
+  chunk = (chunk + 63) / 64 * 64;
+  if (chunk < 64) chunk = 64;
+  p.chunk = chunk;
+  p.n_split = int((p.kv_virtual + chunk - 1) / chunk);
+  const int64_t bhs = int64_t(B) * Hq * p.n_split;
+  size_t off = 0;
+  p.off_scores = off;
+  off += round256(size_t(p.rows) * size_t(p.score_ld) * sizeof(float));
+  p.off_acc = off;
+  off += round256(size_t(bhs) * kHeadDim * sizeof(float));
+  p.off_ml = off;
+  off += round256(size_t(bhs) * 2 * sizeof(float));
+  p.total_bytes = off;
+  return p;
+}
+
+}  // namespace ds
+
+extern "C" {
+
+const char* ds_last_error(void) { return g_err.c_str(); }
+
+const char* ds_version(void) { return "dsparse 0.1.0 gfx950"; }
+
+ds_status ds_build_label_cache(const void* K, ds_dtype dt, int32_t B, int32_t Hkv, int64_t T_cap, int32_t d,
+                               const int32_t* channels_dev, int32_t r, int64_t t_begin, int64_t t_end,
+                               void* label_out, void* stream) {
+  g_err.clear();
+  if (!K || !channels_dev || !label_out) return fail(DS_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (ds_status st = check_dtype(dt)) return st;
+  if (B < 1 || Hkv < 1 || T_cap < 1) return fail(DS_ERR_INVALID_ARGUMENT, "B, Hkv, T_cap must be >= 1");
+  if (d != ds::kHeadDim) return fail(DS_ERR_UNSUPPORTED, "d = %d unsupported (only %d)", d, ds::kHeadDim);
+  if (r < 1 || r > d) return fail(DS_ERR_INVALID_ARGUMENT, "need 1 <= r <= d (r = %d)", r);
+  if (t_begin < 0 || t_begin > t_end || t_end > T_cap)
+    return fail(DS_ERR_INVALID_ARGUMENT, "need 0 <= t_begin <= t_end <= T_cap (%lld, %lld, %lld)",
+                (long long)t_begin, (long long)t_end, (long long)T_cap);
+  if (!aligned(K, 16) || !aligned(label_out, 16) || !aligned(channels_dev, 4))
+    return fail(DS_ERR_INVALID_ARGUMENT, "misaligned device pointer");
+  return hip_status(ds::launch_pack(K, dt == DS_DTYPE_BF16, B, Hkv, T_cap, channels_dev, r, t_begin, t_end,
+                                    label_out, static_cast<hipStream_t>(stream)),
+                    "label pack launch");
+}
+
+size_t ds_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t T, int32_t block,
+                                 int64_t k_units) {
+  g_err.clear();
+  if (check_decode_shape(B, Hq, Hkv, d, T, T, block, k_units) != DS_OK) return 0;
+  return ds::plan_decode(B, Hq, Hkv, T, block, k_units).total_bytes;
+}
+
+ds_status ds_label_scores(const void* q, const void* label, const int32_t* channels_dev, int32_t r, ds_dtype dt,
+                          int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t T_cap, int64_t T, int32_t block,
+                          float* scores, int64_t ld, void* stream) {
+  g_err.clear();
+  if (!q || !label || !channels_dev || !scores) return fail(DS_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (ds_status st = check_dtype(dt)) return st;
+  if (ds_status st = check_decode_shape(B, Hq, Hkv, d, T_cap, T, block, 1)) return st;
+  if (r < 1 || r > d) return fail(DS_ERR_INVALID_ARGUMENT, "need 1 <= r <= d (r = %d)", r);
+  const int64_t n_units = (T + block - 1) / block;
+  if (ld < n_units || ld % 4 != 0)
+    return fail(DS_ERR_INVALID_ARGUMENT, "ld = %lld must be >= %lld and a multiple of 4", (long long)ld,
+                (long long)n_units);
+  if (!aligned(q, 16) || !aligned(label, 16) || !aligned(scores, 16) || !aligned(channels_dev, 4))
+    return fail(DS_ERR_INVALID_ARGUMENT, "misaligned device pointer");
+  return hip_status(ds::launch_scores(q, label, channels_dev, r, dt == DS_DTYPE_BF16, B, Hq, Hkv, T_cap, T, block,
+                                      scores, ld, static_cast<hipStream_t>(stream)),
+                    "score launch");
+}
+
+ds_status ds_topk_select(const float* scores, int64_t rows, int64_t n, int64_t ld, int64_t k, int32_t* idx_out,
+                         void* stream) {
+  g_err.clear();
+  if (!scores || !idx_out) return fail(DS_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (rows < 1 || rows > INT32_MAX) return fail(DS_ERR_INVALID_ARGUMENT, "rows = %lld out of range", (long long)rows);
+  if (n < 1 || n > INT32_MAX) return fail(DS_ERR_INVALID_ARGUMENT, "n = %lld out of range", (long long)n);
+  if (k < 1 || k > n) return fail(DS_ERR_INVALID_ARGUMENT, "need 1 <= k <= n (k = %lld)", (long long)k);
+  if (ld < n) return fail(DS_ERR_INVALID_ARGUMENT, "ld = %lld < n = %lld", (long long)ld, (long long)n);
+  if (!aligned(scores, 4) || !aligned(idx_out, 4)) return fail(DS_ERR_INVALID_ARGUMENT, "misaligned device pointer");
+  return hip_status(ds::launch_select(scores, rows, n, ld, k, idx_out, static_cast<hipStream_t>(stream)),
+                    "select launch");
+}
+
+ds_status ds_sparse_attn_from_indices(const void* q, const void* K, const void* V, ds_dtype dt, int32_t B,
+                                      int32_t Hq, int32_t Hkv, int32_t d, int64_t T_cap, int64_t T,
+                                      int32_t block, int64_t k_units, const int32_t* indices, float scale,
+                                      float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (!q || !K || !V || !indices || !out || !workspace) return fail(DS_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (ds_status st = check_dtype(dt)) return st;
+  if (ds_status st = check_decode_shape(B, Hq, Hkv, d, T_cap, T, block, k_units)) return st;
+  if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(out, 16) || !aligned(indices, 4) ||
+      !aligned(workspace, 256))
+    return fail(DS_ERR_INVALID_ARGUMENT, "misaligned device pointer");
+  const ds::DecodePlan pl = ds::plan_decode(B, Hq, Hkv, T, block, k_units);
+  if (workspace_bytes < pl.total_bytes)
+    return fail(DS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, pl.total_bytes);
+  if (!(scale > 0.f)) scale = 1.0f / std::sqrt(float(d));
+  char* ws = static_cast<char*>(workspace);
+  return hip_status(ds::launch_attention(q, K, V, dt == DS_DTYPE_BF16, B, Hq, Hkv, T_cap, T, block, k_units, indices,
+                                         scale, pl, reinterpret_cast<float*>(ws + pl.off_acc),
+                                         reinterpret_cast<float*>(ws + pl.off_ml), out,
+                                         static_cast<hipStream_t>(stream)),
+                    "attention launch");
+}
+
+ds_status ds_decode_sparse_attn(const void* q, const void* K, const void* V, const void* label,
+                                const int32_t* channels_dev, int32_t r, ds_dtype dt, int32_t B, int32_t Hq,
+                                int32_t Hkv, int32_t d, int64_t T_cap, int64_t T, int32_t block, int64_t k_units,
+                                float scale, float* out, int32_t* indices, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  g_err.clear();
+  if (!q || !K || !V || !label || !channels_dev || !out || !indices || !workspace)
+    return fail(DS_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (ds_status st = check_dtype(dt)) return st;
+  if (ds_status st = check_decode_shape(B, Hq, Hkv, d, T_cap, T, block, k_units)) return st;
+  if (r < 1 || r > d) return fail(DS_ERR_INVALID_ARGUMENT, "need 1 <= r <= d (r = %d)", r);
+  if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(label, 16) || !aligned(out, 16) ||
+      !aligned(indices, 4) || !aligned(channels_dev, 4) || !aligned(workspace, 256))
+    return fail(DS_ERR_INVALID_ARGUMENT, "misaligned device pointer");
+  const ds::DecodePlan pl = ds::plan_decode(B, Hq, Hkv, T, block, k_units);
+  if (workspace_bytes < pl.total_bytes)
+    return fail(DS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, pl.total_bytes);
+  if (!(scale > 0.f)) scale = 1.0f / std::sqrt(float(d));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* scores = reinterpret_cast<float*>(ws + pl.off_scores);
+  if (ds_status st = hip_status(ds::launch_scores(q, label, channels_dev, r, dt == DS_DTYPE_BF16, B, Hq, Hkv, T_cap,
+                                                  T, block, scores, pl.score_ld, s),
+                                "score launch"))
+    return st;
+  if (ds_status st = hip_status(ds::launch_select(scores, pl.rows, pl.n_units, pl.score_ld, k_units, indices, s),
+                                "select launch"))
+    return st;
+  return hip_status(ds::launch_attention(q, K, V, dt == DS_DTYPE_BF16, B, Hq, Hkv, T_cap, T, block, k_units, indices,
+                                         scale, pl, reinterpret_cast<float*>(ws + pl.off_acc),
+                                         reinterpret_cast<float*>(ws + pl.off_ml), out, s),
+                    "attention launch");
+}
+
+}  // extern "C"

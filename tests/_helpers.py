@@ -1,0 +1,67 @@
+"""Shared test helpers: device upload of seeded workloads and the parity rules."""
+from __future__ import annotations
+
+import numpy as np
+
+import dsgen
+import oracle as O
+
+# Output tolerances (max-abs), by element type of q, K, V.
+OUT_TOL = {"f32": 1e-5, "bf16": 2e-3}
+# Boundary-tie window of the index rule, relative to the k-th largest oracle score.
+TIE_REL = 1e-6
+
+
+def to_device(arr: np.ndarray, dtype: str, device="cuda"):
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
+
+
+def kth_largest(u: np.ndarray, k: int) -> float:
+    return float(np.partition(np.asarray(u, dtype=np.float64), len(u) - k)[len(u) - k])
+
+
+def check_index_parity(gpu_idx, u_oracle, k, what=""):
+    """Kept set must equal the oracle's, except boundary ties: every unit in the
+    symmetric difference must score within TIE_REL * |theta| of theta, the
+    oracle's k-th largest score (TIE_REL * max|u| when theta is 0)."""
+    gpu = np.asarray(gpu_idx, dtype=np.int64)
+    u = np.asarray(u_oracle, dtype=np.float64)
+    assert gpu.shape == (k,), (what, gpu.shape, k)
+    assert np.all(np.diff(gpu) > 0), f"{what}: indices not strictly ascending"
+    assert gpu[0] >= 0 and gpu[-1] < len(u), f"{what}: index out of range"
+    ref = O.select_topk(u, k)
+    diff = np.setxor1d(gpu, ref)
+    if len(diff):
+        theta = kth_largest(u, k)
+        tol = TIE_REL * (abs(theta) if theta != 0 else float(np.max(np.abs(u))))
+        bad = diff[np.abs(u[diff] - theta) > tol]
+        assert len(bad) == 0, (f"{what}: {len(bad)} kept/dropped units outside the tie window "
+                               f"(theta={theta}, tol={tol}, e.g. {bad[:5]} scores {u[bad[:5]]})")
+    return len(diff)
+
+
+def unit_inputs(w: dsgen.Workload, q, K, V, b, g):
+    """float64 (q_group [G, d], K [T, d], V [T, d]) of one unit from the stored batch arrays."""
+    G = w.G
+    return (dsgen.to_f64(q[b, g * G:(g + 1) * G], w.dtype), dsgen.to_f64(K[b, g, :w.T], w.dtype),
+            dsgen.to_f64(V[b, g, :w.T], w.dtype))
+
+
+def check_unit(w, q, K, V, ch, b, g, gpu_out, gpu_idx, scale=None):
+    """Full parity of one unit: kept indices by the index rule, output vs the oracle's
+    attention over the GPU's kept set.  Returns the number of legal tie swaps."""
+    qg, Kf, Vf = unit_inputs(w, q, K, V, b, g)
+    if scale is None:
+        scale = O.default_scale(w.d)
+    out_ref, kept_ref, scores = O.decode_unit(qg, Kf, Vf, ch[g], w.k_units, w.block, scale, w.T)
+    swaps = check_index_parity(gpu_idx[b, g], scores, w.k_units, what=f"unit b={b} g={g}")
+    S = O.tokens_of(gpu_idx[b, g], w.block, w.T)
+    ref = O.attend(qg, Kf, Vf, S, scale)
+    err = float(np.max(np.abs(gpu_out[b, g * w.G:(g + 1) * w.G] - ref)))
+    assert err <= OUT_TOL[w.dtype], f"unit b={b} g={g}: max-abs error {err} > {OUT_TOL[w.dtype]}"
+    if swaps == 0:
+        assert float(np.max(np.abs(ref - out_ref))) == 0.0
+    return swaps, err

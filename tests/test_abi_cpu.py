@@ -1,0 +1,118 @@
+"""Boundary tests that need no GPU: the library loads, exports every declared
+symbol, rejects bad arguments before any HIP call, sizes workspaces, and its
+CPU calibration agrees with the oracle.  Device pointers passed here are fake
+(never dereferenced): every call below fails validation first."""
+import ctypes
+import math
+
+import numpy as np
+import pytest
+
+import dsgen
+import long_context_sparse_ds_amd as L
+import oracle as O
+
+FAKE = 4096          # 256-byte aligned fake device address
+MISALIGNED = 4096 + 8
+
+
+def test_library_exports_every_header_symbol():
+    names = L.header_symbols()
+    assert {"ds_calibrate_channels", "ds_build_label_cache", "ds_decode_sparse_attn",
+            "ds_decode_workspace_bytes", "ds_last_error"} <= set(names)
+    handle = ctypes.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(handle, n), n
+    assert L.ds_version().startswith("dsparse")
+
+
+def _decode(**kw):
+    a = dict(q=FAKE, K=FAKE, V=FAKE, label=FAKE, ch=FAKE, r=16, dt=L.DS_DTYPE_BF16, B=1, Hq=32, Hkv=32, d=128,
+             T_cap=16384, T=16384, block=1, k=1024, scale=0.0, out=FAKE, idx=FAKE, ws=FAKE, ws_bytes=0, stream=None)
+    a.update(kw)
+    return L.lib().ds_decode_sparse_attn(a["q"], a["K"], a["V"], a["label"], a["ch"], a["r"], a["dt"], a["B"],
+                                         a["Hq"], a["Hkv"], a["d"], a["T_cap"], a["T"], a["block"], a["k"],
+                                         a["scale"], a["out"], a["idx"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), L.DS_ERR_INVALID_ARGUMENT, "null"),
+    (dict(ws=None), L.DS_ERR_INVALID_ARGUMENT, "null"),
+    (dict(dt=7), L.DS_ERR_INVALID_ARGUMENT, "dtype"),
+    (dict(d=64), L.DS_ERR_UNSUPPORTED, "d = 64"),
+    (dict(Hq=30, Hkv=8), L.DS_ERR_INVALID_ARGUMENT, "multiple"),
+    (dict(B=0), L.DS_ERR_INVALID_ARGUMENT, ">= 1"),
+    (dict(r=0), L.DS_ERR_INVALID_ARGUMENT, "r <= d"),
+    (dict(r=129), L.DS_ERR_INVALID_ARGUMENT, "r <= d"),
+    (dict(T=0), L.DS_ERR_INVALID_ARGUMENT, "T <= T_cap"),
+    (dict(T=20000), L.DS_ERR_INVALID_ARGUMENT, "T <= T_cap"),
+    (dict(k=0), L.DS_ERR_INVALID_ARGUMENT, "k_units"),
+    (dict(k=16385), L.DS_ERR_INVALID_ARGUMENT, "k_units"),
+    (dict(block=3), L.DS_ERR_INVALID_ARGUMENT, "power of two"),
+    (dict(block=128), L.DS_ERR_INVALID_ARGUMENT, "power of two"),
+    (dict(block=64, k=257), L.DS_ERR_INVALID_ARGUMENT, "k_units"),
+    (dict(K=MISALIGNED), L.DS_ERR_INVALID_ARGUMENT, "misaligned"),
+    (dict(ws=FAKE + 16), L.DS_ERR_INVALID_ARGUMENT, "misaligned"),
+    (dict(ws_bytes=100), L.DS_ERR_WORKSPACE_TOO_SMALL, "workspace"),
+])
+def test_decode_rejects_bad_arguments(kw, status, needle):
+    assert _decode(**kw) == status
+    assert needle in L.ds_last_error()
+
+
+def test_workspace_size_is_consistent_and_checked():
+    n = L.ds_decode_workspace_bytes(1, 32, 32, 128, 16384, 1, 1024)
+    assert n % 256 == 0 and n >= 32 * 16384 * 4
+    assert _decode(ws_bytes=n - 1) == L.DS_ERR_WORKSPACE_TOO_SMALL
+    with pytest.raises(L.DsError):
+        L.ds_decode_workspace_bytes(1, 32, 32, 128, 16384, 1, 0)
+    # sized independently of dtype and r, grows with the batch
+    assert L.ds_decode_workspace_bytes(16, 32, 32, 128, 32768, 1, 2048) > n
+
+
+def test_other_entry_points_validate_first():
+    lib = L.lib()
+    assert lib.ds_build_label_cache(FAKE, L.DS_DTYPE_BF16, 1, 1, 100, 128, FAKE, 16, 50, 40, FAKE, None) \
+        == L.DS_ERR_INVALID_ARGUMENT
+    assert "t_begin" in L.ds_last_error()
+    assert lib.ds_build_label_cache(FAKE, L.DS_DTYPE_BF16, 1, 1, 100, 96, FAKE, 16, 0, 1, FAKE, None) \
+        == L.DS_ERR_UNSUPPORTED
+    assert lib.ds_topk_select(FAKE, 4, 100, 100, 101, FAKE, None) == L.DS_ERR_INVALID_ARGUMENT
+    assert lib.ds_topk_select(FAKE, 4, 100, 50, 10, FAKE, None) == L.DS_ERR_INVALID_ARGUMENT
+    assert lib.ds_label_scores(FAKE, FAKE, FAKE, 16, L.DS_DTYPE_F32, 1, 1, 1, 128, 1024, 1024, 1, FAKE, 1022,
+                               None) == L.DS_ERR_INVALID_ARGUMENT
+    assert lib.ds_sparse_attn_from_indices(FAKE, FAKE, FAKE, L.DS_DTYPE_BF16, 1, 4, 4, 128, 100, 100, 1, 10, FAKE,
+                                           0.0, FAKE, FAKE, 10, None) == L.DS_ERR_WORKSPACE_TOO_SMALL
+    # a valid call afterwards clears the message
+    L.ds_decode_workspace_bytes(1, 1, 1, 128, 10, 1, 1)
+    assert L.ds_last_error() == ""
+
+
+def test_calibrate_rejects_bad_arguments():
+    lib = L.lib()
+    q = np.zeros((4, 2, 8), np.float32)
+    k = np.zeros((1, 4, 8), np.float32)
+    out = np.full((1, 3), -7, np.int32)
+    assert lib.ds_calibrate_channels(None, 4, k.ctypes.data, 4, 2, 1, 8, 3, out.ctypes.data) \
+        == L.DS_ERR_INVALID_ARGUMENT
+    assert lib.ds_calibrate_channels(q.ctypes.data, 4, k.ctypes.data, 4, 3, 2, 8, 3, out.ctypes.data) \
+        == L.DS_ERR_INVALID_ARGUMENT
+    assert lib.ds_calibrate_channels(q.ctypes.data, 4, k.ctypes.data, 4, 2, 1, 8, 9, out.ctypes.data) \
+        == L.DS_ERR_INVALID_ARGUMENT
+    assert list(out[0]) == [-7, -7, -7]   # untouched on failure
+
+
+@pytest.mark.parametrize("name", dsgen.WORKLOAD_ORDER)
+def test_calibrate_matches_oracle_on_workloads(name):
+    w = dsgen.get(name)
+    qc, kc = dsgen.gen_calib(w)
+    np.testing.assert_array_equal(L.ds_calibrate_channels(qc, kc, w.r), O.calibrate_channels(qc, kc, w.Hkv, w.r))
+
+
+def test_calibrate_matches_oracle_on_ties_and_small_shapes():
+    rng = np.random.default_rng(11)
+    for (n_q, Hq, Hkv, d, n_k) in [(3, 4, 2, 8, 5), (7, 6, 3, 16, 2), (1, 1, 1, 128, 1)]:
+        qc = rng.integers(-2, 3, size=(n_q, Hq, d)).astype(np.float32)   # integer data: exact ties
+        kc = rng.integers(-2, 3, size=(Hkv, n_k, d)).astype(np.float32)
+        for r in sorted({1, d // 3 + 1, d}):
+            np.testing.assert_array_equal(L.ds_calibrate_channels(qc, kc, r), O.calibrate_channels(qc, kc, Hkv, r))

@@ -1,0 +1,255 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Each stage is checked on its own (label pack bit-exact; scores against the
+oracle's float64 scores; selection fed float32 scores bit-exact against the
+oracle's selection of the same values; attention fed fixed index sets), then
+the whole decode step end to end: on small shapes that span several tiles
+with ragged tails, edge cases, and on every unit or a sample of units of the
+five full-size workloads in the launch configuration the benchmark times.
+
+Index rule: kept sets equal the oracle's except boundary ties within 1e-6
+relative of the oracle's k-th score.  Output rule: max-abs error against the
+oracle's attention over the GPU's kept set, 1e-5 (fp32) / 2e-3 (bf16).
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import dsgen
+import long_context_sparse_ds_amd as L
+import oracle as O
+from dsgen import Workload
+from _helpers import OUT_TOL, check_index_parity, check_unit, to_device, unit_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    L.lib()   # raises if the HIP library is missing
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def run_decode(w: Workload, threads=None):
+    _say(f"{w.name} {w.dtype} B={w.B} Hq={w.Hq} Hkv={w.Hkv} T={w.T} cap={w.cap} r={w.r} block={w.block} "
+         f"k={w.k_units}")
+    q, K, V = dsgen.gen_cache(w, threads)
+    qc, kc = dsgen.gen_calib(w)
+    ch = L.ds_calibrate_channels(qc, kc, w.r)
+    qd, Kd, Vd = to_device(q, w.dtype), to_device(K, w.dtype), to_device(V, w.dtype)
+    chd = torch.from_numpy(ch).cuda()
+    label = L.ds_build_label_cache(Kd, chd)
+    out, idx = L.ds_decode_sparse_attn(qd, Kd, Vd, label, chd, w.T, w.k_units, w.block)
+    torch.cuda.synchronize()
+    return q, K, V, ch, out.cpu().numpy(), idx.cpu().numpy()
+
+
+SMALL = [
+    Workload("mha_ragged", "bf16", B=2, Hq=4, Hkv=4, d=128, T=3000, r=16, block=1, k_units=190, seed_base=11000,
+             T_cap=3100),
+    Workload("gqa8_ragged", "bf16", B=2, Hq=16, Hkv=2, d=128, T=5000, r=8, block=1, k_units=333, seed_base=12000),
+    Workload("gqa4_r12", "bf16", B=1, Hq=8, Hkv=2, d=128, T=2500, r=12, block=1, k_units=100, seed_base=13000),
+    Workload("gqa3", "bf16", B=1, Hq=6, Hkv=2, d=128, T=777, r=16, block=1, k_units=50, seed_base=13500),
+    Workload("f32_gqa2", "f32", B=1, Hq=2, Hkv=1, d=128, T=1500, r=16, block=1, k_units=77, seed_base=14000,
+             fixed_outliers=True),
+    Workload("f32_r6", "f32", B=2, Hq=2, Hkv=2, d=128, T=900, r=6, block=1, k_units=64, seed_base=14500),
+    Workload("block64_partial", "bf16", B=2, Hq=4, Hkv=4, d=128, T=64 * 50 + 17, r=16, block=64, k_units=9,
+             seed_base=15000, T_cap=64 * 52),
+    Workload("block16_gqa2", "bf16", B=1, Hq=4, Hkv=2, d=128, T=4000, r=16, block=16, k_units=20, seed_base=16000),
+    Workload("dense_tokens", "bf16", B=1, Hq=2, Hkv=2, d=128, T=700, r=16, block=1, k_units=700, seed_base=17000),
+    Workload("dense_blocks", "bf16", B=1, Hq=2, Hkv=2, d=128, T=64 * 7 + 5, r=16, block=64, k_units=8,
+             seed_base=17500),
+    Workload("k1", "bf16", B=1, Hq=2, Hkv=2, d=128, T=4097, r=16, block=1, k_units=1, seed_base=18000),
+    Workload("T1", "bf16", B=2, Hq=2, Hkv=2, d=128, T=1, r=16, block=1, k_units=1, seed_base=18500, T_cap=64),
+    Workload("r_eq_d", "bf16", B=1, Hq=2, Hkv=2, d=128, T=2000, r=128, block=1, k_units=125, seed_base=19000),
+    Workload("select_multi_tile", "bf16", B=1, Hq=1, Hkv=1, d=128, T=70001, r=16, block=1, k_units=4000,
+             seed_base=19500),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_decode_small_all_units(w):
+    q, K, V, ch, out, idx = run_decode(w)
+    assert np.all(np.isfinite(out))
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            check_unit(w, q, K, V, ch, b, g, out, idx)
+
+
+@pytest.mark.parametrize("name", dsgen.WORKLOAD_ORDER)
+def test_decode_full_size_workload(name):
+    """The five workloads at full size, in the benchmark's launch configuration.  Every
+    row's kept set is checked for shape and order; the oracle checks a sample of units."""
+    w = dsgen.get(name)
+    q, K, V, ch, out, idx = run_decode(w)
+    assert np.all(np.isfinite(out))
+    rows = idx.reshape(-1, w.k_units)
+    assert np.all(np.diff(rows, axis=1) > 0) and rows.min() >= 0 and rows.max() < w.n_units
+    rng = np.random.default_rng(99)
+    units = {(0, 0), (w.B - 1, w.Hkv - 1)}
+    while len(units) < min(4, w.B * w.Hkv):
+        units.add((int(rng.integers(w.B)), int(rng.integers(w.Hkv))))
+    for b, g in sorted(units):
+        swaps, err = check_unit(w, q, K, V, ch, b, g, out, idx)
+        _say(f"{name} unit ({b},{g}): tie swaps {swaps}, max-abs err {err:.3g}")
+    del q, K, V
+    torch.cuda.empty_cache()
+
+
+def test_label_pack_bit_exact_and_append_leaves_other_rows():
+    w = Workload("pack", "bf16", B=2, Hq=4, Hkv=2, d=128, T=1000, r=16, block=1, k_units=10, seed_base=20000,
+                 T_cap=1030)
+    q, K, V = dsgen.gen_cache(w)
+    ch = np.sort(np.random.default_rng(1).choice(128, (w.Hkv, w.r)), axis=1).astype(np.int32)
+    Kd = to_device(K, w.dtype)
+    chd = torch.from_numpy(ch).cuda()
+    label = torch.full((w.B, w.Hkv, w.cap, w.r), 0, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    label.view(torch.int16).fill_(0x1234)
+    L.ds_build_label_cache(Kd, chd, 0, 600, label=label)
+    L.ds_build_label_cache(Kd, chd, 600, 601, label=label)   # one appended row
+    torch.cuda.synchronize()
+    got = label.view(torch.int16).cpu().numpy().view(np.uint16)
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            want = O.label_rows(K[b, g], ch[g])
+            np.testing.assert_array_equal(got[b, g, :601], want[:601])
+            assert np.all(got[b, g, 601:] == 0x1234)
+    # fp32 cache
+    wf = w.with_(dtype="f32", seed_base=20500)
+    qf, Kf, Vf = dsgen.gen_cache(wf)
+    lab = L.ds_build_label_cache(to_device(Kf, "f32"), chd)
+    torch.cuda.synchronize()
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            np.testing.assert_array_equal(lab.cpu().numpy()[b, g, :w.T], O.label_rows(Kf[b, g, :w.T], ch[g]))
+
+
+@pytest.mark.parametrize("w", [SMALL[0], SMALL[1], SMALL[2], SMALL[4], SMALL[5], SMALL[6], SMALL[7]],
+                         ids=lambda w: w.name)
+def test_label_scores_match_oracle(w):
+    q, K, V = dsgen.gen_cache(w)
+    qc, kc = dsgen.gen_calib(w)
+    ch = O.calibrate_channels(qc, kc, w.Hkv, w.r)
+    qd, Kd = to_device(q, w.dtype), to_device(K, w.dtype)
+    chd = torch.from_numpy(ch).cuda()
+    label = L.ds_build_label_cache(Kd, chd)
+    s = L.ds_label_scores(qd, label, chd, w.T, w.block)
+    torch.cuda.synchronize()
+    s = s.cpu().numpy()
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            qg, Kf, _ = unit_inputs(w, q, K, V, b, g)
+            u = O.label_scores(qg, O.label_rows(Kf, ch[g]), ch[g])
+            if w.block > 1:
+                u = O.block_scores(u, w.block)
+            got = s[b, g, :len(u)].astype(np.float64)
+            # double accumulation rounded once to float32: within one float32 rounding
+            np.testing.assert_allclose(got, u, rtol=2 ** -23, atol=1e-12)
+
+
+SELECT_CASES = [
+    ("ints_ties", 3, 5000, 700, "ints"),
+    ("tiny_n1", 2, 1, 1, "normal"),
+    ("n7_all", 1, 7, 7, "normal"),
+    ("all_equal", 2, 9000, 1234, "equal"),
+    ("signed_zeros", 2, 300, 150, "zeros"),
+    ("tile_edge", 2, 4096, 4096, "normal"),
+    ("tile_edge_plus1", 2, 4097, 100, "ints"),
+    ("long_row", 3, 131072, 8192, "normal"),
+    ("long_row_ties", 2, 100003, 6250, "ints"),
+    ("negative", 2, 2000, 1999, "negative"),
+]
+
+
+@pytest.mark.parametrize("name,rows,n,k,kind", SELECT_CASES, ids=[c[0] for c in SELECT_CASES])
+def test_topk_select_bit_exact(name, rows, n, k, kind):
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    if kind == "ints":
+        u = rng.integers(-20, 21, size=(rows, n)).astype(np.float32)
+    elif kind == "equal":
+        u = np.full((rows, n), 3.5, np.float32)
+    elif kind == "zeros":
+        u = np.where(rng.random((rows, n)) < 0.5, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
+        u[:, ::7] = 1.0
+    elif kind == "negative":
+        u = -np.abs(rng.standard_normal((rows, n))).astype(np.float32) * 100
+    else:
+        u = (rng.standard_normal((rows, n)) * 100).astype(np.float32)
+    ld = n + 5
+    buf = np.zeros((rows, ld), np.float32)
+    buf[:, :n] = u
+    idx = L.ds_topk_select(torch.from_numpy(buf).cuda(), n, k)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    for i in range(rows):
+        np.testing.assert_array_equal(idx[i], O.select_topk(u[i].astype(np.float64), k), err_msg=f"{name} row {i}")
+
+
+ATTN_CASES = [
+    Workload("attn_mha", "bf16", B=2, Hq=4, Hkv=4, d=128, T=3000, r=16, block=1, k_units=211, seed_base=21000),
+    Workload("attn_gqa8", "bf16", B=1, Hq=16, Hkv=2, d=128, T=4000, r=8, block=1, k_units=999, seed_base=22000),
+    Workload("attn_f32", "f32", B=1, Hq=2, Hkv=2, d=128, T=1024, r=16, block=1, k_units=64, seed_base=23000),
+    Workload("attn_block", "bf16", B=1, Hq=4, Hkv=4, d=128, T=64 * 30 + 9, r=16, block=64, k_units=7,
+             seed_base=24000),
+]
+
+
+@pytest.mark.parametrize("w", ATTN_CASES, ids=lambda w: w.name)
+def test_sparse_attention_from_fixed_indices(w):
+    q, K, V = dsgen.gen_cache(w)
+    rng = np.random.default_rng(5)
+    idx = np.stack([np.stack([np.sort(rng.choice(w.n_units, w.k_units, replace=False)) for _ in range(w.Hkv)])
+                    for _ in range(w.B)]).astype(np.int32)
+    if w.block > 1:   # make one row keep the partial last block
+        idx[0, 0] = np.append(np.sort(rng.choice(w.n_units - 1, w.k_units - 1, replace=False)), w.n_units - 1)
+    out = L.ds_sparse_attn_from_indices(to_device(q, w.dtype), to_device(K, w.dtype), to_device(V, w.dtype),
+                                        torch.from_numpy(idx).cuda(), w.T, w.block)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            qg, Kf, Vf = unit_inputs(w, q, K, V, b, g)
+            S = O.tokens_of(idx[b, g], w.block, w.T)
+            ref = O.attend(qg, Kf, Vf, S, O.default_scale(w.d))
+            err = np.max(np.abs(out[b, g * w.G:(g + 1) * w.G] - ref))
+            assert err <= OUT_TOL[w.dtype], (b, g, err)
+
+
+def test_decode_is_deterministic_and_address_independent():
+    w = SMALL[1]
+    q, K, V = dsgen.gen_cache(w)
+    qc, kc = dsgen.gen_calib(w)
+    chd = torch.from_numpy(L.ds_calibrate_channels(qc, kc, w.r)).cuda()
+    qd, Kd, Vd = to_device(q, w.dtype), to_device(K, w.dtype), to_device(V, w.dtype)
+    label = L.ds_build_label_cache(Kd, chd)
+    o1, i1 = L.ds_decode_sparse_attn(qd, Kd, Vd, label, chd, w.T, w.k_units)
+    o2, i2 = L.ds_decode_sparse_attn(qd, Kd, Vd, label, chd, w.T, w.k_units)
+    # a copy of the instance at other addresses
+    o3, i3 = L.ds_decode_sparse_attn(qd.clone(), Kd.clone(), Vd.clone(), label.clone(), chd.clone(), w.T, w.k_units)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2) and torch.equal(i1, i3)
+    assert torch.equal(o1.view(torch.int32), o2.view(torch.int32))
+    assert torch.equal(o1.view(torch.int32), o3.view(torch.int32))
+
+
+def test_decode_scale_argument():
+    w = SMALL[0]
+    q, K, V = dsgen.gen_cache(w)
+    qc, kc = dsgen.gen_calib(w)
+    ch = L.ds_calibrate_channels(qc, kc, w.r)
+    chd = torch.from_numpy(ch).cuda()
+    qd, Kd, Vd = to_device(q, w.dtype), to_device(K, w.dtype), to_device(V, w.dtype)
+    label = L.ds_build_label_cache(Kd, chd)
+    out, idx = L.ds_decode_sparse_attn(qd, Kd, Vd, label, chd, w.T, w.k_units, scale=0.02)
+    torch.cuda.synchronize()
+    out, idx = out.cpu().numpy(), idx.cpu().numpy()
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            check_unit(w, q, K, V, ch, b, g, out, idx, scale=0.02)
