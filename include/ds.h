@@ -106,6 +106,9 @@ size_t ds_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, 
 
 /*
  * One Double Sparsity decode step for every (sequence b, KV head g) (GPU, async):
+ *   0. label-row append: rows [t_append, T) of the label cache are rebuilt
+ *      from K (as ds_build_label_cache would) before they are scored, so the
+ *      newest tokens' rows need no separate call; t_append = T skips it;
  *   1. approximate score of each of the T valid tokens,
  *        u[b,g,t] = sum over query heads h of group g, sum over j < r, of
  *                   q[b,h,channels[g,j]] * label[b,g,t,j]
@@ -121,9 +124,11 @@ size_t ds_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, 
  *      (Jenga page, core method item 3), accumulated in float32.
  *   q            device [B, Hq, d]
  *   K, V         device [B, Hkv, T_cap, d]; rows >= T are never read
- *   label        device [B, Hkv, T_cap, r] (from ds_build_label_cache)
+ *   label        device [B, Hkv, T_cap, r] (from ds_build_label_cache); rows
+ *                [t_append, T) are written, the others only read
  *   channels_dev device int32 [Hkv, r]
  *   T            valid tokens, 1 <= T <= T_cap
+ *   t_append     0 <= t_append <= T
  *   block        1, 2, 4, 8, 16, 32 or 64
  *   k_units      tokens or blocks kept, 1 <= k_units <= ceil(T / block)
  *   scale        softmax scale; <= 0 means 1/sqrt(d)
@@ -131,19 +136,18 @@ size_t ds_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, 
  *   indices      device int32 [B, Hkv, k_units] (token ids, or block ids)
  *   workspace    device, >= ds_decode_workspace_bytes(...) bytes; contents on
  *                entry do not matter and are clobbered
- * Errors: null pointer, bad dtype, Hq % Hkv != 0, r outside [1, d], T or
- * k_units or block out of range, misalignment, unsupported d, workspace too
- * small (DS_ERR_WORKSPACE_TOO_SMALL).
+ * Errors: null pointer, bad dtype, Hq % Hkv != 0, r outside [1, d], T,
+ * t_append, k_units or block out of range, misalignment, unsupported d,
+ * workspace too small (DS_ERR_WORKSPACE_TOO_SMALL).
  */
-ds_status ds_decode_sparse_attn(const void* q, const void* K, const void* V, const void* label,
-                                const int32_t* channels_dev, int32_t r, ds_dtype dt, int32_t B, int32_t Hq,
-                                int32_t Hkv, int32_t d, int64_t T_cap, int64_t T, int32_t block, int64_t k_units,
-                                float scale, float* out, int32_t* indices, void* workspace,
-                                size_t workspace_bytes, void* stream);
+ds_status ds_decode_sparse_attn(const void* q, const void* K, const void* V, void* label, const int32_t* channels_dev,
+                                int32_t r, ds_dtype dt, int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t T_cap,
+                                int64_t T, int64_t t_append, int32_t block, int64_t k_units, float scale, float* out,
+                                int32_t* indices, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * The three stages of ds_decode_sparse_attn, callable on their own so each can
- * be checked in isolation.  They run the same kernels as the fused call.
+ * Stages of ds_decode_sparse_attn, callable on their own so each can be
+ * checked and timed in isolation.
  */
 
 /* Step 1 only: scores[b, g, i] (float32) for i < ceil(T / block).
@@ -158,6 +162,14 @@ ds_status ds_label_scores(const void* q, const void* label, const int32_t* chann
  * NaN is not supported. */
 ds_status ds_topk_select(const float* scores, int64_t rows, int64_t n, int64_t ld, int64_t k, int32_t* idx_out,
                          void* stream);
+
+/* Steps 2 and 3 from given scores (laid out as ds_label_scores writes them):
+ * selection and attention, exactly as ds_decode_sparse_attn runs them after
+ * scoring.  Workspace as for ds_decode_sparse_attn. */
+ds_status ds_select_attention(const void* q, const void* K, const void* V, ds_dtype dt, int32_t B, int32_t Hq,
+                              int32_t Hkv, int32_t d, int64_t T_cap, int64_t T, int32_t block, int64_t k_units,
+                              const float* scores, int64_t ld, float scale, float* out, int32_t* indices,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Step 3 only: attention over the units listed in `indices` (as
  * ds_decode_sparse_attn writes them: ascending, distinct, each < ceil(T/block)).

@@ -36,8 +36,10 @@ _SIGNATURES = {
                                       _c_vp, _c_vp]),
     "ds_decode_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_i64]),
     "ds_decode_sparse_attn": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
-                                       _c_i32, _c_i64, _c_i64, _c_i32, _c_i64, _c_f32, _c_vp, _c_vp, _c_vp, _c_size,
-                                       _c_vp]),
+                                       _c_i32, _c_i64, _c_i64, _c_i64, _c_i32, _c_i64, _c_f32, _c_vp, _c_vp, _c_vp,
+                                       _c_size, _c_vp]),
+    "ds_select_attention": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i64,
+                                     _c_i32, _c_i64, _c_vp, _c_i64, _c_f32, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
     "ds_label_scores": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i64,
                                  _c_i32, _c_vp, _c_i64, _c_vp]),
     "ds_topk_select": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp]),
@@ -164,8 +166,10 @@ def alloc_workspace(B, Hq, Hkv, d, T, block, k_units, device="cuda"):
 
 
 def ds_decode_sparse_attn(q, K, V, label, channels, T: int, k_units: int, block: int = 1, scale: float = 0.0,
-                          out=None, indices=None, workspace=None, stream=None):
-    """One Double Sparsity decode step.  Returns (out fp32 [B, Hq, d], indices int32 [B, Hkv, k_units])."""
+                          out=None, indices=None, workspace=None, stream=None, t_append: int | None = None):
+    """One Double Sparsity decode step.  Returns (out fp32 [B, Hq, d], indices int32 [B, Hkv, k_units]).
+
+    t_append < T first rebuilds label rows [t_append, T) from K inside the call."""
     torch = _torch()
     B, Hq, d = q.shape
     _, Hkv, T_cap, _ = K.shape
@@ -179,10 +183,32 @@ def ds_decode_sparse_attn(q, K, V, label, channels, T: int, k_units: int, block:
         indices = torch.empty((B, Hkv, k_units), dtype=torch.int32, device=q.device)
     if workspace is None:
         workspace = alloc_workspace(B, Hq, Hkv, d, T, block, k_units, q.device)
+    if t_append is None:
+        t_append = T
     _check(lib().ds_decode_sparse_attn(_dev(q, "q"), _dev(K, "K"), _dev(V, "V"), _dev(label, "label"),
-                                       _dev(channels, "channels"), r, dt, B, Hq, Hkv, d, T_cap, T, block, k_units,
-                                       scale, _dev(out, "out"), _dev(indices, "indices"), _dev(workspace, "workspace"),
-                                       workspace.numel() * workspace.element_size(), _stream(stream)))
+                                       _dev(channels, "channels"), r, dt, B, Hq, Hkv, d, T_cap, T, t_append, block,
+                                       k_units, scale, _dev(out, "out"), _dev(indices, "indices"),
+                                       _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                       _stream(stream)))
+    return out, indices
+
+
+def ds_select_attention(q, K, V, scores, T: int, k_units: int, block: int = 1, scale: float = 0.0, out=None,
+                        indices=None, workspace=None, stream=None):
+    """Selection + attention from a score tensor as ds_label_scores returns it.  Returns (out, indices)."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    _, Hkv, T_cap, _ = K.shape
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if indices is None:
+        indices = torch.empty((B, Hkv, k_units), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(B, Hq, Hkv, d, T, block, k_units, q.device)
+    _check(lib().ds_select_attention(_dev(q, "q"), _dev(K, "K"), _dev(V, "V"), _dtype_code(q), B, Hq, Hkv, d, T_cap,
+                                     T, block, k_units, _dev(scores, "scores"), scores.shape[-1], scale,
+                                     _dev(out, "out"), _dev(indices, "indices"), _dev(workspace, "workspace"),
+                                     workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, indices
 
 

@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdsparse.so")
 
-HIP_SOURCES = ["ds_api.hip", "pack.hip", "score.hip", "select.hip", "attn.hip"]
+HIP_SOURCES = ["ds_api.hip", "pack.hip", "score.hip", "select.hip", "selattn.hip", "attn.hip"]
 CPP_SOURCES = ["calibrate.cpp"]
 ARCH = "gfx950"
 
@@ -67,7 +67,7 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(min(8, len(jobs))) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))
     tmp = LIB + ".tmp"
-    _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
+    _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-Wl,--no-undefined", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
     return LIB
 

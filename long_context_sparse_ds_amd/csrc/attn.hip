@@ -1,4 +1,5 @@
-// Exact softmax attention over the kept tokens, split along the kept set.
+// Exact softmax attention over given kept units, split along the kept list,
+// and the log-sum-exp merge of the splits.
 //
 // Double Sparsity page, key points and abstract: token sparsity computes
 // self-attention with the important tokens only.  Jenga page, core method
@@ -12,9 +13,10 @@
 // group in flight, scores them for every query head of the chunk (the K and V
 // rows are read once for the whole GQA group), and keeps a running softmax
 // state (max m, sum l, unnormalised acc) that is rescaled once per four rows.
-// Lane groups and wavefronts are merged through LDS at the end; the splits of
-// a row are merged by log-sum-exp in a second small kernel (or directly when a
-// row has a single split).
+// Lane groups and wavefronts are merged through LDS.  A row with one split
+// writes its output directly; otherwise each split writes its state and the
+// merge kernel combines them (a kernel boundary orders the two without any
+// device-wide cache maintenance inside a kernel).
 #include "ds_common.h"
 
 namespace ds {
@@ -202,43 +204,58 @@ __global__ __launch_bounds__(kAT) void attn_kernel(const TE* __restrict__ q, con
   }
 }
 
-// Log-sum-exp merge of the splits of one (sequence, query head): one thread per channel.
+// Log-sum-exp merge of the splits of one (sequence, query head): one thread per
+// channel, every split's values requested before any is used.
+constexpr int kMergeBatch = 16;
+
 __global__ __launch_bounds__(kHeadDim) void merge_kernel(const float* __restrict__ part_acc,
                                                          const float* __restrict__ part_ml, int n_split,
                                                          float* __restrict__ out) {
   const int64_t bh = blockIdx.x;
   const int c = threadIdx.x;
   const float* ml = part_ml + bh * n_split * 2;
-  float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, ml[2 * s]);
-  float L = 0.f, A = 0.f;
-  for (int s = 0; s < n_split; ++s) {
-    const float f = __expf(ml[2 * s] - M);
-    L = fmaf(ml[2 * s + 1], f, L);
-    A = fmaf(part_acc[(bh * n_split + s) * kHeadDim + c], f, A);
+  const float* pa = part_acc + bh * n_split * kHeadDim + c;
+  float M = -INFINITY, L = 0.f, A = 0.f;
+  for (int s0 = 0; s0 < n_split; s0 += kMergeBatch) {
+    float a[kMergeBatch], m[kMergeBatch], l[kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const bool ok = s0 + j < n_split;
+      a[j] = ok ? pa[int64_t(s0 + j) * kHeadDim] : 0.f;
+      m[j] = ok ? ml[2 * (s0 + j)] : -INFINITY;
+      l[j] = ok ? ml[2 * (s0 + j) + 1] : 0.f;
+    }
+    float Mb = M;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) Mb = fmaxf(Mb, m[j]);
+    if (Mb == -INFINITY) continue;
+    const float r = __expf(M - Mb);   // M = -inf: 0
+    L *= r;
+    A *= r;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const float f = __expf(m[j] - Mb);   // empty split (m = -inf): 0
+      L = fmaf(l[j], f, L);
+      A = fmaf(a[j], f, A);
+    }
+    M = Mb;
   }
   out[bh * kHeadDim + c] = A / L;
 }
 
 template <typename TE>
-hipError_t dispatch(const TE* q, const TE* K, const TE* V, int B, int Hq, int Hkv, int64_t T_cap, int64_t T,
-                    int block, int64_t k_units, const int32_t* idx, float scale, const DecodePlan& pl,
-                    float* part_acc, float* part_ml, float* out, hipStream_t s) {
-  const int G = Hq / Hkv;
-  const int HC = G % 8 == 0 ? 8 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
-  const dim3 grid(unsigned(pl.n_split), unsigned(pl.rows), unsigned(G / HC));
+hipError_t dispatch(const TE* q, const TE* K, const TE* V, int Hq, int Hkv, int64_t T_cap, int64_t T, int block,
+                    int64_t k_units, const int32_t* idx, float scale, int64_t rows, int64_t kv_virtual,
+                    const SplitPlan& sp, float* part_acc, float* part_ml, float* out, hipStream_t s) {
+  const dim3 grid(unsigned(sp.n_split), unsigned(rows), unsigned(sp.head_chunks));
 #define DS_ATTN(HH)                                                                                              \
   hipLaunchKernelGGL((attn_kernel<TE, HH>), grid, dim3(kAT), 0, s, q, K, V, idx, Hq, Hkv, T_cap, T, block,       \
-                     k_units, pl.kv_virtual, pl.chunk, pl.n_split, scale, part_acc, part_ml, out)
-  if (HC == 8) DS_ATTN(8);
-  else if (HC == 4) DS_ATTN(4);
-  else if (HC == 2) DS_ATTN(2);
+                     k_units, kv_virtual, sp.chunk, sp.n_split, scale, part_acc, part_ml, out)
+  if (sp.head_chunk == 8) DS_ATTN(8);
+  else if (sp.head_chunk == 4) DS_ATTN(4);
+  else if (sp.head_chunk == 2) DS_ATTN(2);
   else DS_ATTN(1);
 #undef DS_ATTN
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || pl.n_split == 1) return e;
-  hipLaunchKernelGGL(merge_kernel, dim3(unsigned(int64_t(B) * Hq)), dim3(kHeadDim), 0, s, part_acc, part_ml,
-                     pl.n_split, out);
   return hipGetLastError();
 }
 
@@ -246,12 +263,32 @@ hipError_t dispatch(const TE* q, const TE* K, const TE* V, int B, int Hq, int Hk
 
 hipError_t launch_attention(const void* q, const void* K, const void* V, int is_bf16, int B, int Hq, int Hkv,
                             int64_t T_cap, int64_t T, int block, int64_t k_units, const int32_t* idx, float scale,
-                            const DecodePlan& plan, float* part_acc, float* part_ml, float* out, hipStream_t s) {
+                            int64_t kv_virtual, const SplitPlan& sp, float* part_acc, float* part_ml, float* out,
+                            hipStream_t s) {
+  const int64_t rows = int64_t(B) * Hkv;
   if (is_bf16)
     return dispatch(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V),
-                    B, Hq, Hkv, T_cap, T, block, k_units, idx, scale, plan, part_acc, part_ml, out, s);
-  return dispatch(static_cast<const float*>(q), static_cast<const float*>(K), static_cast<const float*>(V), B, Hq,
-                  Hkv, T_cap, T, block, k_units, idx, scale, plan, part_acc, part_ml, out, s);
+                    Hq, Hkv, T_cap, T, block, k_units, idx, scale, rows, kv_virtual, sp, part_acc, part_ml, out, s);
+  return dispatch(static_cast<const float*>(q), static_cast<const float*>(K), static_cast<const float*>(V), Hq, Hkv,
+                  T_cap, T, block, k_units, idx, scale, rows, kv_virtual, sp, part_acc, part_ml, out, s);
+}
+
+__global__ void zero_u32_kernel(unsigned* __restrict__ p, int64_t n) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
+    p[i] = 0u;
+}
+
+hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t want = (n + 255) / 256;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(unsigned(want < 1024 ? want : 1024)), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const float* part_acc, const float* part_ml, int64_t BH, int n_split, float* out,
+                        hipStream_t s) {
+  hipLaunchKernelGGL(merge_kernel, dim3(unsigned(BH)), dim3(kHeadDim), 0, s, part_acc, part_ml, n_split, out);
+  return hipGetLastError();
 }
 
 }  // namespace ds

@@ -66,39 +66,106 @@ namespace ds {
 
 void set_error(const char* msg) { g_err = msg; }
 
+SplitPlan plan_split(int64_t rows, int G, int64_t kv_virtual, bool fused) {
+  SplitPlan sp{};
+  // Fused workgroups are 1024 threads, one resident per CU, and aim at ~256 of
+  // them (each repeats the row's selection, so fewer is cheaper); separate
+  // attention workgroups are 256 threads and aim at ~2048.  Slices hold at
+  // least 64 kept positions, and a row is cut into at most 1024 splits.
+  const int64_t target = fused ? 256 : 2048;
+  int64_t chunk = (kv_virtual * rows + target - 1) / target;
+  chunk = (chunk + 63) / 64 * 64;
+  if (chunk < 64) chunk = 64;
+  const int64_t min_for_cap = ((kv_virtual + 1023) / 1024 + 63) / 64 * 64;
+  if (chunk < min_for_cap) chunk = min_for_cap;
+  if (fused && chunk > kFusedMaxChunk) chunk = kFusedMaxChunk;
+  sp.chunk = chunk;
+  sp.n_split = int((kv_virtual + chunk - 1) / chunk);
+  sp.head_chunk = fused ? head_chunk4(G) : head_chunk8(G);
+  sp.head_chunks = G / sp.head_chunk;
+  return sp;
+}
+
 DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t T, int block, int64_t k_units) {
   DecodePlan p{};
+  const int G = Hq / Hkv;
   p.rows = int64_t(B) * Hkv;
   p.n_units = (T + block - 1) / block;
   p.score_ld = (p.n_units + 63) / 64 * 64;
   p.kv_virtual = k_units * block;
-  // Aim for about 2048 attention workgroups over the whole batch, in slices of
-  // at least 64 kept positions.
-  const int64_t target_wg = 2048;
-  int64_t chunk = (p.kv_virtual * p.rows + target_wg - 1) / target_wg;
-  chunk = (chunk + 63) / 64 * 64;
-  if (chunk < 64) chunk = 64;
-  p.chunk = chunk;
-  p.n_split = int((p.kv_virtual + chunk - 1) / chunk);
-  const int64_t bhs = int64_t(B) * Hq * p.n_split;
+  p.fused = p.n_units <= kFusedMaxUnits;
+  p.sp = plan_split(p.rows, G, p.kv_virtual, p.fused);
+  p.tiles = (T + kScoreTile - 1) / kScoreTile;
+  // Worth it when several fused workgroups of a row would each histogram the whole row.
+  p.tile_hist = p.fused && p.sp.n_split * p.sp.head_chunks > 1 && p.tiles <= kMaxHistTiles;
+  p.sp_idx = plan_split(p.rows, G, p.kv_virtual, false);
+  const int max_split = p.sp.n_split > p.sp_idx.n_split ? p.sp.n_split : p.sp_idx.n_split;
+  const int64_t bhs = int64_t(B) * Hq * max_split;
   size_t off = 0;
   p.off_scores = off;
   off += round256(size_t(p.rows) * size_t(p.score_ld) * sizeof(float));
+  p.off_tile_hist = off;
+  if (p.tile_hist) off += round256(size_t(p.rows) * size_t(p.tiles) * kHistBins * sizeof(uint16_t));
   p.off_acc = off;
   off += round256(size_t(bhs) * kHeadDim * sizeof(float));
   p.off_ml = off;
   off += round256(size_t(bhs) * 2 * sizeof(float));
+  p.off_tickets = off;
+  off += round256(size_t(p.rows) * p.sp.head_chunks * sizeof(unsigned));
   p.total_bytes = off;
   return p;
 }
 
 }  // namespace ds
 
+namespace {
+
+// Attention over known kept units, then the merge when a row has several splits.
+ds_status run_attention(const void* q, const void* K, const void* V, ds_dtype dt, int B, int Hq, int Hkv,
+                        int64_t T_cap, int64_t T, int block, int64_t k_units, const int32_t* indices, float scale,
+                        const ds::DecodePlan& pl, const ds::SplitPlan& sp, float* out, char* ws, hipStream_t s) {
+  float* part_acc = reinterpret_cast<float*>(ws + pl.off_acc);
+  float* part_ml = reinterpret_cast<float*>(ws + pl.off_ml);
+  if (ds_status st = hip_status(ds::launch_attention(q, K, V, dt == DS_DTYPE_BF16, B, Hq, Hkv, T_cap, T, block,
+                                                     k_units, indices, scale, pl.kv_virtual, sp, part_acc, part_ml,
+                                                     out, s),
+                                "attention launch"))
+    return st;
+  if (sp.n_split == 1) return DS_OK;
+  return hip_status(ds::launch_merge(part_acc, part_ml, int64_t(B) * Hq, sp.n_split, out, s), "merge launch");
+}
+
+// Steps 2 and 3 of the decode step from a score buffer laid out as the plan says.
+// tickets_zeroed: the score kernel of this call already cleared the merge tickets.
+ds_status run_select_attend(const void* q, const void* K, const void* V, ds_dtype dt, int B, int Hq, int Hkv,
+                            int64_t T_cap, int64_t T, int block, int64_t k_units, const float* scores, int64_t ld,
+                            const uint16_t* tile_hist, bool tickets_zeroed, float scale, const ds::DecodePlan& pl,
+                            float* out, int32_t* indices, char* ws, hipStream_t s) {
+  if (pl.fused) {
+    float* part_acc = reinterpret_cast<float*>(ws + pl.off_acc);
+    float* part_ml = reinterpret_cast<float*>(ws + pl.off_ml);
+    unsigned* tickets = reinterpret_cast<unsigned*>(ws + pl.off_tickets);
+    if (!tickets_zeroed && pl.sp.n_split > 1)
+      if (ds_status st = hip_status(ds::launch_zero_u32(tickets, pl.rows * pl.sp.head_chunks, s), "ticket reset"))
+        return st;
+    return hip_status(ds::launch_select_attention(q, K, V, dt == DS_DTYPE_BF16, scores, ld, tile_hist, Hq, Hkv, T_cap,
+                                                  T, block, k_units, scale, pl, indices, part_acc, part_ml, out,
+                                                  tickets, s),
+                      "select-attention launch");
+  }
+  if (ds_status st = hip_status(ds::launch_select(scores, pl.rows, pl.n_units, ld, k_units, indices, s),
+                                "select launch"))
+    return st;
+  return run_attention(q, K, V, dt, B, Hq, Hkv, T_cap, T, block, k_units, indices, scale, pl, pl.sp, out, ws, s);
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* ds_last_error(void) { return g_err.c_str(); }
 
-const char* ds_version(void) { return "dsparse 0.1.0 gfx950"; }
+const char* ds_version(void) { return "dsparse 0.2.0 gfx950"; }
 
 ds_status ds_build_label_cache(const void* K, ds_dtype dt, int32_t B, int32_t Hkv, int64_t T_cap, int32_t d,
                                const int32_t* channels_dev, int32_t r, int64_t t_begin, int64_t t_end,
@@ -140,8 +207,10 @@ ds_status ds_label_scores(const void* q, const void* label, const int32_t* chann
                 (long long)n_units);
   if (!aligned(q, 16) || !aligned(label, 16) || !aligned(scores, 16) || !aligned(channels_dev, 4))
     return fail(DS_ERR_INVALID_ARGUMENT, "misaligned device pointer");
-  return hip_status(ds::launch_scores(q, label, channels_dev, r, dt == DS_DTYPE_BF16, B, Hq, Hkv, T_cap, T, block,
-                                      scores, ld, static_cast<hipStream_t>(stream)),
+  // No append: the label cache is only read.
+  return hip_status(ds::launch_scores(q, const_cast<void*>(label), nullptr, channels_dev, r, dt == DS_DTYPE_BF16, B,
+                                      Hq, Hkv, T_cap, T, T, block, scores, ld, nullptr, nullptr, 0,
+                                      static_cast<hipStream_t>(stream)),
                     "score launch");
 }
 
@@ -173,25 +242,22 @@ ds_status ds_sparse_attn_from_indices(const void* q, const void* K, const void* 
   if (workspace_bytes < pl.total_bytes)
     return fail(DS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, pl.total_bytes);
   if (!(scale > 0.f)) scale = 1.0f / std::sqrt(float(d));
-  char* ws = static_cast<char*>(workspace);
-  return hip_status(ds::launch_attention(q, K, V, dt == DS_DTYPE_BF16, B, Hq, Hkv, T_cap, T, block, k_units, indices,
-                                         scale, pl, reinterpret_cast<float*>(ws + pl.off_acc),
-                                         reinterpret_cast<float*>(ws + pl.off_ml), out,
-                                         static_cast<hipStream_t>(stream)),
-                    "attention launch");
+  return run_attention(q, K, V, dt, B, Hq, Hkv, T_cap, T, block, k_units, indices, scale, pl, pl.sp_idx, out,
+                       static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
 }
 
-ds_status ds_decode_sparse_attn(const void* q, const void* K, const void* V, const void* label,
-                                const int32_t* channels_dev, int32_t r, ds_dtype dt, int32_t B, int32_t Hq,
-                                int32_t Hkv, int32_t d, int64_t T_cap, int64_t T, int32_t block, int64_t k_units,
-                                float scale, float* out, int32_t* indices, void* workspace, size_t workspace_bytes,
-                                void* stream) {
+ds_status ds_decode_sparse_attn(const void* q, const void* K, const void* V, void* label, const int32_t* channels_dev,
+                                int32_t r, ds_dtype dt, int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t T_cap,
+                                int64_t T, int64_t t_append, int32_t block, int64_t k_units, float scale, float* out,
+                                int32_t* indices, void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   if (!q || !K || !V || !label || !channels_dev || !out || !indices || !workspace)
     return fail(DS_ERR_INVALID_ARGUMENT, "null pointer argument");
   if (ds_status st = check_dtype(dt)) return st;
   if (ds_status st = check_decode_shape(B, Hq, Hkv, d, T_cap, T, block, k_units)) return st;
   if (r < 1 || r > d) return fail(DS_ERR_INVALID_ARGUMENT, "need 1 <= r <= d (r = %d)", r);
+  if (t_append < 0 || t_append > T)
+    return fail(DS_ERR_INVALID_ARGUMENT, "need 0 <= t_append <= T (t_append = %lld)", (long long)t_append);
   if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(label, 16) || !aligned(out, 16) ||
       !aligned(indices, 4) || !aligned(channels_dev, 4) || !aligned(workspace, 256))
     return fail(DS_ERR_INVALID_ARGUMENT, "misaligned device pointer");
@@ -202,17 +268,40 @@ ds_status ds_decode_sparse_attn(const void* q, const void* K, const void* V, con
   const hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   float* scores = reinterpret_cast<float*>(ws + pl.off_scores);
-  if (ds_status st = hip_status(ds::launch_scores(q, label, channels_dev, r, dt == DS_DTYPE_BF16, B, Hq, Hkv, T_cap,
-                                                  T, block, scores, pl.score_ld, s),
+  const int is_bf16 = dt == DS_DTYPE_BF16;
+  uint16_t* tile_hist = pl.tile_hist ? reinterpret_cast<uint16_t*>(ws + pl.off_tile_hist) : nullptr;
+  unsigned* tickets = pl.fused ? reinterpret_cast<unsigned*>(ws + pl.off_tickets) : nullptr;
+  if (ds_status st = hip_status(ds::launch_scores(q, label, K, channels_dev, r, is_bf16, B, Hq, Hkv, T_cap, T,
+                                                  t_append, block, scores, pl.score_ld, tile_hist, tickets,
+                                                  pl.sp.head_chunks, s),
                                 "score launch"))
     return st;
-  if (ds_status st = hip_status(ds::launch_select(scores, pl.rows, pl.n_units, pl.score_ld, k_units, indices, s),
-                                "select launch"))
-    return st;
-  return hip_status(ds::launch_attention(q, K, V, dt == DS_DTYPE_BF16, B, Hq, Hkv, T_cap, T, block, k_units, indices,
-                                         scale, pl, reinterpret_cast<float*>(ws + pl.off_acc),
-                                         reinterpret_cast<float*>(ws + pl.off_ml), out, s),
-                    "attention launch");
+  return run_select_attend(q, K, V, dt, B, Hq, Hkv, T_cap, T, block, k_units, scores, pl.score_ld, tile_hist, true,
+                           scale, pl, out, indices, ws, s);
+}
+
+ds_status ds_select_attention(const void* q, const void* K, const void* V, ds_dtype dt, int32_t B, int32_t Hq,
+                              int32_t Hkv, int32_t d, int64_t T_cap, int64_t T, int32_t block, int64_t k_units,
+                              const float* scores, int64_t ld, float scale, float* out, int32_t* indices,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (!q || !K || !V || !scores || !out || !indices || !workspace)
+    return fail(DS_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (ds_status st = check_dtype(dt)) return st;
+  if (ds_status st = check_decode_shape(B, Hq, Hkv, d, T_cap, T, block, k_units)) return st;
+  const ds::DecodePlan pl = ds::plan_decode(B, Hq, Hkv, T, block, k_units);
+  if (ld < pl.n_units || ld % 4 != 0)
+    return fail(DS_ERR_INVALID_ARGUMENT, "ld = %lld must be >= %lld and a multiple of 4", (long long)ld,
+                (long long)pl.n_units);
+  if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(scores, 16) || !aligned(out, 16) ||
+      !aligned(indices, 4) || !aligned(workspace, 256))
+    return fail(DS_ERR_INVALID_ARGUMENT, "misaligned device pointer");
+  if (workspace_bytes < pl.total_bytes)
+    return fail(DS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, pl.total_bytes);
+  if (!(scale > 0.f)) scale = 1.0f / std::sqrt(float(d));
+  // Scores come from the caller here, so the fused kernel builds the top-digit histogram itself.
+  return run_select_attend(q, K, V, dt, B, Hq, Hkv, T_cap, T, block, k_units, scores, ld, nullptr, false, scale, pl,
+                           out, indices, static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -9,16 +9,42 @@ namespace ds {
 
 constexpr int kHeadDim = 128;
 
+// Rows of up to this many units take the fused select+attention kernel, whose
+// workgroups (1024 threads) hold a whole score row in registers.
+constexpr int64_t kFusedMaxUnits = 32768;
+// Kept positions handled by one fused split (its LDS list of unit ids).
+constexpr int64_t kFusedMaxChunk = 4096;
+// Tokens per score-kernel workgroup (one "tile"); a row's tile histograms are
+// summed by the fused kernel when a row has at most kMaxHistTiles tiles.
+constexpr int64_t kScoreTile = 1024;
+constexpr int64_t kMaxHistTiles = 32;
+constexpr int kHistBins = 2048;   // top 11 bits of a score key
+
+// Query heads processed together by one attention workgroup (divides G).
+inline __host__ __device__ int head_chunk8(int G) { return G % 8 == 0 ? 8 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1; }
+inline __host__ __device__ int head_chunk4(int G) { return G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1; }
+
+// How the kept positions of each row are split over attention workgroups.
+struct SplitPlan {
+  int64_t chunk;     // virtual kept positions per split (multiple of 64 and of the block size)
+  int n_split;       // splits per row
+  int head_chunk;    // query heads per workgroup
+  int head_chunks;   // G / head_chunk
+};
+
 // How one decode call is laid out on the device.  Computed identically by the
-// workspace query and by the launch, from the shape alone.
+// workspace query and by the launches, from the shape alone.
 struct DecodePlan {
   int64_t rows;        // B * Hkv selection rows
   int64_t n_units;     // ceil(T / block)
   int64_t score_ld;    // row stride of the score buffer, floats (multiple of 64)
   int64_t kv_virtual;  // k_units * block: attention positions per row (some may lie past T)
-  int64_t chunk;       // positions per split
-  int n_split;         // splits per row
-  size_t off_scores, off_acc, off_ml, total_bytes;
+  bool fused;          // select and attention in one kernel
+  bool tile_hist;      // the score kernel writes per-tile key histograms for the fused kernel
+  int64_t tiles;       // score tiles per row
+  SplitPlan sp;        // splits of the decode call
+  SplitPlan sp_idx;    // splits of the attention-from-indices call
+  size_t off_scores, off_tile_hist, off_acc, off_ml, off_tickets, total_bytes;
 };
 
 DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t T, int block, int64_t k_units);
@@ -27,15 +53,39 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t T, int block, int64_t k_u
 hipError_t launch_pack(const void* K, int is_bf16, int B, int Hkv, int64_t T_cap, const int32_t* ch, int r,
                        int64_t t_begin, int64_t t_end, void* label, hipStream_t s);
 
-hipError_t launch_scores(const void* q, const void* label, const int32_t* ch, int r, int is_bf16, int B, int Hq,
-                         int Hkv, int64_t T_cap, int64_t T, int block, float* scores, int64_t ld, hipStream_t s);
+// Scores of units [0, ceil(T/block)).  Rows [t_append, T) of the label cache
+// are first rebuilt from K (label-row append); pass t_append = T to skip, and
+// K may then be null.  tile_hist (may be null): uint16 [rows][tiles][2048]
+// histogram of the top 11 key bits of each tile's units.  tickets (may be
+// null): tickets_per_row merge tickets per row, zeroed here for the fused
+// kernel that follows.
+hipError_t launch_scores(const void* q, void* label, const void* K, const int32_t* ch, int r, int is_bf16, int B,
+                         int Hq, int Hkv, int64_t T_cap, int64_t T, int64_t t_append, int block, float* scores,
+                         int64_t ld, uint16_t* tile_hist, unsigned* tickets, int tickets_per_row, hipStream_t s);
 
 hipError_t launch_select(const float* scores, int64_t rows, int64_t n, int64_t ld, int64_t k, int32_t* idx,
                          hipStream_t s);
 
+// Attention over given kept units; writes out directly when sp.n_split == 1,
+// else partial states that launch_merge combines.
 hipError_t launch_attention(const void* q, const void* K, const void* V, int is_bf16, int B, int Hq, int Hkv,
                             int64_t T_cap, int64_t T, int block, int64_t k_units, const int32_t* idx, float scale,
-                            const DecodePlan& plan, float* part_acc, float* part_ml, float* out, hipStream_t s);
+                            int64_t kv_virtual, const SplitPlan& sp, float* part_acc, float* part_ml, float* out,
+                            hipStream_t s);
+
+// Fused selection + attention (rows of at most kFusedMaxUnits units).
+// tile_hist (may be null): the score kernel's per-tile histograms of this call.
+// tickets: rows * sp.head_chunks merge tickets, zero on entry (left zero).
+hipError_t launch_select_attention(const void* q, const void* K, const void* V, int is_bf16, const float* scores,
+                                   int64_t ld, const uint16_t* tile_hist, int Hq, int Hkv, int64_t T_cap, int64_t T,
+                                   int block, int64_t k_units, float scale, const DecodePlan& pl, int32_t* indices,
+                                   float* part_acc, float* part_ml, float* out, unsigned* tickets, hipStream_t s);
+
+hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t s);
+
+// Log-sum-exp merge of n_split partial states per (sequence, query head).
+hipError_t launch_merge(const float* part_acc, const float* part_ml, int64_t BH, int n_split, float* out,
+                        hipStream_t s);
 
 }  // namespace ds
 

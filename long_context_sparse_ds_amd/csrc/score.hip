@@ -12,6 +12,11 @@
 // load instruction.  Products are exact in double precision for bf16 and fp32
 // inputs and the sum of at most d of them is accumulated in double, so the
 // float32 result is the exact score rounded once.
+//
+// Tokens in [t_append, T) first get their label rows rebuilt from K (the
+// per-step label-row append of the newest tokens, fused here so a decode step
+// is a single pass over the label cache); they are scored from the values just
+// gathered, summed in the same channel order.
 #include "ds_common.h"
 
 namespace ds {
@@ -20,6 +25,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTPT = 4;                     // tokens per thread
 constexpr int kTile = kThreads * kTPT;      // tokens per workgroup
+static_assert(kTile == kScoreTile, "tile size shared with the fused kernel's histogram reader");
 
 template <int NV>
 __device__ __forceinline__ double dot_label(const uint4 (&raw)[NV], const double* qr, uint16_t) {
@@ -50,63 +56,96 @@ __device__ __forceinline__ double dot_label(const uint4 (&raw)[NV], const double
 
 // R > 0: label width known at compile time and R * sizeof(TE) a multiple of 16 bytes.
 // R == 0: any width, element loads.
+// Label-row append of token t: gather its r channels from K into the label
+// cache and return its score.
+template <typename TE>
+__device__ __forceinline__ float append_row(const TE* __restrict__ Krow, TE* __restrict__ Lrow, const int* sch,
+                                            const double* qs, int r) {
+  double a = 0.0;
+  for (int j = 0; j < r; ++j) {
+    const TE v = Krow[sch[j]];
+    Lrow[j] = v;
+    a = fma(qs[j], double(elem_to_f32(v)), a);
+  }
+  return float(a);
+}
+
 template <typename TE, int R>
-__global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ q, const TE* __restrict__ label,
-                                                         const int32_t* __restrict__ ch, int r, int Hq, int Hkv,
-                                                         int64_t T_cap, int64_t T, int block,
-                                                         float* __restrict__ scores, int64_t ld) {
+__global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ q, TE* __restrict__ label,
+                                                         const TE* __restrict__ Kc, const int32_t* __restrict__ ch,
+                                                         int r, int Hq, int Hkv, int64_t T_cap, int64_t T,
+                                                         int64_t t_append, int block, float* __restrict__ scores,
+                                                         int64_t ld, uint16_t* __restrict__ tile_hist,
+                                                         unsigned* __restrict__ tickets, int tickets_per_row) {
   const int64_t row = blockIdx.y;
+  if (tickets != nullptr && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < tickets_per_row; i += kThreads) tickets[row * tickets_per_row + i] = 0u;
   const int b = int(row / Hkv), g = int(row % Hkv);
   const int G = Hq / Hkv;
-  __shared__ double qs[kHeadDim];
-  for (int j = threadIdx.x; j < r; j += kThreads) {
-    const int c = ch[g * r + j];
-    double s = 0.0;
-    for (int h = 0; h < G; ++h) s += double(elem_to_f32(q[(int64_t(b) * Hq + int64_t(g) * G + h) * kHeadDim + c]));
-    qs[j] = s;
-  }
-  __syncthreads();
-
-  const TE* L = label + row * T_cap * r;
+  TE* L = label + row * T_cap * r;
   const int64_t t0 = int64_t(blockIdx.x) * kTile + threadIdx.x;
-  float u[kTPT];
+  constexpr int NV = R > 0 ? R * int(sizeof(TE)) / 16 : 1;
+  // The label rows are requested first: they do not depend on q or the
+  // channel table, so their latency overlaps the q-sum below.
+  uint4 raw[kTPT][NV];
   if constexpr (R > 0) {
-    constexpr int NV = R * int(sizeof(TE)) / 16;
-    double qr[R];
-#pragma unroll
-    for (int j = 0; j < R; ++j) qr[j] = qs[j];
-    uint4 raw[kTPT][NV];
 #pragma unroll
     for (int i = 0; i < kTPT; ++i) {
       const int64_t t = t0 + i * kThreads;
-      if (t < T) {
+      if (t < T && t < t_append) {
         const uint4* p = reinterpret_cast<const uint4*>(L + t * R);
 #pragma unroll
         for (int v = 0; v < NV; ++v) raw[i][v] = p[v];
       }
     }
+  }
+  __shared__ double qs[kHeadDim];
+  __shared__ int sch[kHeadDim];
+  for (int j = threadIdx.x; j < r; j += kThreads) {
+    const int c = ch[g * r + j];
+    double s = 0.0;
+    for (int h = 0; h < G; ++h) s += double(elem_to_f32(q[(int64_t(b) * Hq + int64_t(g) * G + h) * kHeadDim + c]));
+    qs[j] = s;
+    sch[j] = c;
+  }
+  __syncthreads();
+
+  float u[kTPT];
+  if constexpr (R > 0) {
+    double qr[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) qr[j] = qs[j];
 #pragma unroll
     for (int i = 0; i < kTPT; ++i) {
       const int64_t t = t0 + i * kThreads;
-      u[i] = t < T ? float(dot_label<NV>(raw[i], qr, TE())) : -INFINITY;
+      if (t >= T) u[i] = -INFINITY;
+      else if (t >= t_append) u[i] = append_row(Kc + (row * T_cap + t) * kHeadDim, L + t * R, sch, qs, R);
+      else u[i] = float(dot_label<NV>(raw[i], qr, TE()));
     }
   } else {
 #pragma unroll
     for (int i = 0; i < kTPT; ++i) {
       const int64_t t = t0 + i * kThreads;
       double a = 0.0;
-      if (t < T)
+      if (t < T && t < t_append)
         for (int j = 0; j < r; ++j) a = fma(qs[j], double(elem_to_f32(L[t * r + j])), a);
-      u[i] = t < T ? float(a) : -INFINITY;
+      if (t >= T) u[i] = -INFINITY;
+      else if (t >= t_append) u[i] = append_row(Kc + (row * T_cap + t) * kHeadDim, L + t * r, sch, qs, r);
+      else u[i] = float(a);
     }
   }
 
   float* out = scores + row * ld;
+  // Each unit score this thread writes: value and whether it exists.
+  float uv[kTPT];
+  bool has[kTPT];
   if (block == 1) {
 #pragma unroll
     for (int i = 0; i < kTPT; ++i) {
       const int64_t t = t0 + i * kThreads;
-      if (t < T) out[t] = u[i];
+      uv[i] = u[i];
+      has[i] = t < T;
+      if (has[i]) out[t] = u[i];
     }
   } else {
     // 64 consecutive tokens per wavefront, 64-aligned: blocks of `block` lanes.
@@ -115,19 +154,40 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
       float v = u[i];
       for (int off = block >> 1; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
       const int64_t t = t0 + i * kThreads;
-      if (t < T && (t % block) == 0) out[t / block] = v;
+      uv[i] = v;
+      has[i] = t < T && (t % block) == 0;
+      if (has[i]) out[t / block] = v;
     }
+  }
+  if (tile_hist != nullptr) {
+    // Dense histogram of the top 11 key bits of this tile's units, every bin
+    // written, so the buffer needs no clearing between calls.
+    __shared__ uint32_t h[kHistBins];
+    for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kTPT; ++i)
+      if (has[i]) atomicAdd(&h[float_key(uv[i]) >> 21], 1u);
+    __syncthreads();
+    constexpr int per = kHistBins / kThreads;   // 8 bins per thread: one 16-byte store
+    const int b0 = threadIdx.x * per;
+    uint32_t w[per / 2];
+#pragma unroll
+    for (int j = 0; j < per / 2; ++j) w[j] = h[b0 + 2 * j] | (h[b0 + 2 * j + 1] << 16);
+    uint16_t* dst = tile_hist + (row * gridDim.x + blockIdx.x) * kHistBins + b0;
+    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
 template <typename TE>
-hipError_t dispatch(const TE* q, const TE* label, const int32_t* ch, int r, int B, int Hq, int Hkv,
-                    int64_t T_cap, int64_t T, int block, float* scores, int64_t ld, hipStream_t s) {
+hipError_t dispatch(const TE* q, TE* label, const TE* Kc, const int32_t* ch, int r, int B, int Hq, int Hkv,
+                    int64_t T_cap, int64_t T, int64_t t_append, int block, float* scores, int64_t ld,
+                    uint16_t* tile_hist, unsigned* tickets, int tickets_per_row, hipStream_t s) {
   const dim3 grid(unsigned((T + kTile - 1) / kTile), unsigned(int64_t(B) * Hkv));
   const bool vec = (int64_t(r) * sizeof(TE)) % 16 == 0;
 #define DS_SCORE(RR) \
-  hipLaunchKernelGGL((score_kernel<TE, RR>), grid, dim3(kThreads), 0, s, q, label, ch, r, Hq, Hkv, T_cap, T, block, \
-                     scores, ld)
+  hipLaunchKernelGGL((score_kernel<TE, RR>), grid, dim3(kThreads), 0, s, q, label, Kc, ch, r, Hq, Hkv, T_cap, T,     \
+                     t_append, block, scores, ld, tile_hist, tickets, tickets_per_row)
   if (vec && r == 8) DS_SCORE(8);
   else if (vec && r == 16) DS_SCORE(16);
   else if (vec && r == 32) DS_SCORE(32);
@@ -138,13 +198,14 @@ hipError_t dispatch(const TE* q, const TE* label, const int32_t* ch, int r, int 
 
 }  // namespace
 
-hipError_t launch_scores(const void* q, const void* label, const int32_t* ch, int r, int is_bf16, int B, int Hq,
-                         int Hkv, int64_t T_cap, int64_t T, int block, float* scores, int64_t ld, hipStream_t s) {
+hipError_t launch_scores(const void* q, void* label, const void* K, const int32_t* ch, int r, int is_bf16, int B,
+                         int Hq, int Hkv, int64_t T_cap, int64_t T, int64_t t_append, int block, float* scores,
+                         int64_t ld, uint16_t* tile_hist, unsigned* tickets, int tickets_per_row, hipStream_t s) {
   if (is_bf16)
-    return dispatch(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(label), ch, r, B, Hq, Hkv, T_cap,
-                    T, block, scores, ld, s);
-  return dispatch(static_cast<const float*>(q), static_cast<const float*>(label), ch, r, B, Hq, Hkv, T_cap, T,
-                  block, scores, ld, s);
+    return dispatch(static_cast<const uint16_t*>(q), static_cast<uint16_t*>(label), static_cast<const uint16_t*>(K),
+                    ch, r, B, Hq, Hkv, T_cap, T, t_append, block, scores, ld, tile_hist, tickets, tickets_per_row, s);
+  return dispatch(static_cast<const float*>(q), static_cast<float*>(label), static_cast<const float*>(K), ch, r, B,
+                  Hq, Hkv, T_cap, T, t_append, block, scores, ld, tile_hist, tickets, tickets_per_row, s);
 }
 
 }  // namespace ds

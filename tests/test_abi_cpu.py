@@ -28,11 +28,14 @@ def test_library_exports_every_header_symbol():
 
 def _decode(**kw):
     a = dict(q=FAKE, K=FAKE, V=FAKE, label=FAKE, ch=FAKE, r=16, dt=L.DS_DTYPE_BF16, B=1, Hq=32, Hkv=32, d=128,
-             T_cap=16384, T=16384, block=1, k=1024, scale=0.0, out=FAKE, idx=FAKE, ws=FAKE, ws_bytes=0, stream=None)
+             T_cap=16384, T=16384, t_append=None, block=1, k=1024, scale=0.0, out=FAKE, idx=FAKE, ws=FAKE, ws_bytes=0,
+             stream=None)
     a.update(kw)
+    if a["t_append"] is None:
+        a["t_append"] = a["T"]
     return L.lib().ds_decode_sparse_attn(a["q"], a["K"], a["V"], a["label"], a["ch"], a["r"], a["dt"], a["B"],
-                                         a["Hq"], a["Hkv"], a["d"], a["T_cap"], a["T"], a["block"], a["k"],
-                                         a["scale"], a["out"], a["idx"], a["ws"], a["ws_bytes"], a["stream"])
+                                         a["Hq"], a["Hkv"], a["d"], a["T_cap"], a["T"], a["t_append"], a["block"],
+                                         a["k"], a["scale"], a["out"], a["idx"], a["ws"], a["ws_bytes"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -48,6 +51,8 @@ def _decode(**kw):
     (dict(T=20000), L.DS_ERR_INVALID_ARGUMENT, "T <= T_cap"),
     (dict(k=0), L.DS_ERR_INVALID_ARGUMENT, "k_units"),
     (dict(k=16385), L.DS_ERR_INVALID_ARGUMENT, "k_units"),
+    (dict(t_append=16385), L.DS_ERR_INVALID_ARGUMENT, "t_append"),
+    (dict(t_append=-1), L.DS_ERR_INVALID_ARGUMENT, "t_append"),
     (dict(block=3), L.DS_ERR_INVALID_ARGUMENT, "power of two"),
     (dict(block=128), L.DS_ERR_INVALID_ARGUMENT, "power of two"),
     (dict(block=64, k=257), L.DS_ERR_INVALID_ARGUMENT, "k_units"),
@@ -83,6 +88,10 @@ def test_other_entry_points_validate_first():
                                None) == L.DS_ERR_INVALID_ARGUMENT
     assert lib.ds_sparse_attn_from_indices(FAKE, FAKE, FAKE, L.DS_DTYPE_BF16, 1, 4, 4, 128, 100, 100, 1, 10, FAKE,
                                            0.0, FAKE, FAKE, 10, None) == L.DS_ERR_WORKSPACE_TOO_SMALL
+    assert lib.ds_select_attention(FAKE, FAKE, FAKE, L.DS_DTYPE_BF16, 1, 4, 4, 128, 100, 100, 1, 10, FAKE, 128, 0.0,
+                                   FAKE, FAKE, FAKE, 10, None) == L.DS_ERR_WORKSPACE_TOO_SMALL
+    assert lib.ds_select_attention(FAKE, FAKE, FAKE, L.DS_DTYPE_BF16, 1, 4, 4, 128, 100, 100, 1, 10, FAKE, 98, 0.0,
+                                   FAKE, FAKE, FAKE, 1 << 20, None) == L.DS_ERR_INVALID_ARGUMENT
     # a valid call afterwards clears the message
     L.ds_decode_workspace_bytes(1, 1, 1, 128, 10, 1, 1)
     assert L.ds_last_error() == ""

@@ -253,3 +253,136 @@ def test_decode_scale_argument():
     for b in range(w.B):
         for g in range(w.Hkv):
             check_unit(w, q, K, V, ch, b, g, out, idx, scale=0.02)
+
+
+def test_workspace_reuse_and_graph_replay_match_eager():
+    """One workspace reused across calls (the merge counters reset themselves), and the
+    decode step captured in a HIP graph: every replay, with eager work and
+    synchronisation in between, must reproduce the eager result bit for bit."""
+    w = SMALL[1]   # several splits per row: exercises the cross-split merge
+    q, K, V = dsgen.gen_cache(w)
+    qc, kc = dsgen.gen_calib(w)
+    chd = torch.from_numpy(L.ds_calibrate_channels(qc, kc, w.r)).cuda()
+    qd, Kd, Vd = to_device(q, w.dtype), to_device(K, w.dtype), to_device(V, w.dtype)
+    label = L.ds_build_label_cache(Kd, chd)
+    ref_o, ref_i = L.ds_decode_sparse_attn(qd, Kd, Vd, label, chd, w.T, w.k_units)
+    ws = L.alloc_workspace(w.B, w.Hq, w.Hkv, w.d, w.T, w.block, w.k_units)
+    ws.fill_(0xA5)   # arbitrary contents on entry
+    out = torch.empty_like(ref_o)
+    idx = torch.empty_like(ref_i)
+    for _ in range(3):
+        L.ds_decode_sparse_attn(qd, Kd, Vd, label, chd, w.T, w.k_units, out=out, indices=idx, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref_i) and torch.equal(out.view(torch.int32), ref_o.view(torch.int32))
+    # a different shape through the same workspace in between must not disturb it
+    L.ds_decode_sparse_attn(qd, Kd, Vd, label, chd, w.T - 100, 50, workspace=ws)
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        L.ds_decode_sparse_attn(qd, Kd, Vd, label, chd, w.T, w.k_units, out=out, indices=idx, workspace=ws)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            L.ds_decode_sparse_attn(qd, Kd, Vd, label, chd, w.T, w.k_units, out=out, indices=idx, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.zero_()
+        idx.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref_i), rep
+        assert torch.equal(out.view(torch.int32), ref_o.view(torch.int32)), rep
+        # eager work between replays
+        o2, _ = L.ds_decode_sparse_attn(qd, Kd, Vd, label, chd, w.T, w.k_units, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o2.view(torch.int32), ref_o.view(torch.int32))
+
+
+@pytest.mark.parametrize("w", [SMALL[0], SMALL[4], SMALL[6]], ids=lambda w: w.name)
+def test_decode_fused_label_append(w):
+    """Label rows [t_append, T) are rebuilt from K inside the decode call: start from a
+    cache whose newest rows hold garbage and check they come back bit-exact and the
+    step matches the oracle."""
+    q, K, V = dsgen.gen_cache(w)
+    qc, kc = dsgen.gen_calib(w)
+    ch = L.ds_calibrate_channels(qc, kc, w.r)
+    chd = torch.from_numpy(ch).cuda()
+    qd, Kd, Vd = to_device(q, w.dtype), to_device(K, w.dtype), to_device(V, w.dtype)
+    label = L.ds_build_label_cache(Kd, chd)
+    t_app = w.T - 37
+    raw = label.view(torch.int16) if w.dtype == "bf16" else label.view(torch.int32)
+    raw[:, :, t_app:w.T].fill_(0x3F00)   # garbage in the rows to be appended
+    out, idx = L.ds_decode_sparse_attn(qd, Kd, Vd, label, chd, w.T, w.k_units, w.block, t_append=t_app)
+    torch.cuda.synchronize()
+    got = label.cpu().view(torch.int16).numpy().view(np.uint16) if w.dtype == "bf16" else label.cpu().numpy()
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            np.testing.assert_array_equal(got[b, g, :w.T], O.label_rows(K[b, g, :w.T], ch[g]))
+    out, idx = out.cpu().numpy(), idx.cpu().numpy()
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            check_unit(w, q, K, V, ch, b, g, out, idx)
+
+
+FUSED_CASES = [SMALL[0], SMALL[1], SMALL[2], SMALL[4], SMALL[6], SMALL[7], SMALL[8], SMALL[13],
+               Workload("many_splits", "bf16", B=1, Hq=2, Hkv=2, d=128, T=30000, r=16, block=1, k_units=9000,
+                        seed_base=25000)]
+
+
+@pytest.mark.parametrize("w", FUSED_CASES, ids=lambda w: w.name)
+def test_select_attention_from_oracle_scores(w):
+    """Selection + attention fed the oracle's float64 scores rounded to float32: the kept
+    set must equal the oracle's selection of those same float32 values exactly, and the
+    output must match the oracle's attention over it."""
+    q, K, V = dsgen.gen_cache(w)
+    qc, kc = dsgen.gen_calib(w)
+    ch = O.calibrate_channels(qc, kc, w.Hkv, w.r)
+    ld = -(-w.n_units // 4) * 4
+    sc = np.zeros((w.B, w.Hkv, ld), np.float32)
+    units = {}
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            qg, Kf, Vf = unit_inputs(w, q, K, V, b, g)
+            u = O.label_scores(qg, O.label_rows(Kf, ch[g]), ch[g])
+            if w.block > 1:
+                u = O.block_scores(u, w.block)
+            sc[b, g, :len(u)] = u.astype(np.float32)
+            units[b, g] = (qg, Kf, Vf)
+    out, idx = L.ds_select_attention(to_device(q, w.dtype), to_device(K, w.dtype), to_device(V, w.dtype),
+                                     torch.from_numpy(sc).cuda(), w.T, w.k_units, w.block)
+    torch.cuda.synchronize()
+    out, idx = out.cpu().numpy(), idx.cpu().numpy()
+    for (b, g), (qg, Kf, Vf) in units.items():
+        want = O.select_topk(sc[b, g, :w.n_units].astype(np.float64), w.k_units)
+        np.testing.assert_array_equal(idx[b, g], want, err_msg=f"unit ({b},{g})")
+        ref = O.attend(qg, Kf, Vf, O.tokens_of(want, w.block, w.T), O.default_scale(w.d))
+        err = float(np.max(np.abs(out[b, g * w.G:(g + 1) * w.G] - ref)))
+        assert err <= OUT_TOL[w.dtype], (b, g, err)
+
+
+def test_alternating_inputs_through_one_workspace():
+    """Split states of one call must never leak into the next: two different decode
+    inputs alternate through one workspace (cross-split merge every call) and each
+    result must equal that input's own reference bit for bit."""
+    w = SMALL[1]
+    refs, ins = [], []
+    for seed in (40000, 41000):
+        wi = w.with_(seed_base=seed)
+        q, K, V = dsgen.gen_cache(wi)
+        qc, kc = dsgen.gen_calib(wi)
+        chd = torch.from_numpy(L.ds_calibrate_channels(qc, kc, wi.r)).cuda()
+        qd, Kd, Vd = to_device(q, wi.dtype), to_device(K, wi.dtype), to_device(V, wi.dtype)
+        label = L.ds_build_label_cache(Kd, chd)
+        o, i = L.ds_decode_sparse_attn(qd, Kd, Vd, label, chd, wi.T, wi.k_units)
+        torch.cuda.synchronize()
+        refs.append((o.clone(), i.clone()))
+        ins.append((qd, Kd, Vd, label, chd))
+    ws = L.alloc_workspace(w.B, w.Hq, w.Hkv, w.d, w.T, w.block, w.k_units)
+    outs = []
+    for rep in range(24):
+        qd, Kd, Vd, label, chd = ins[rep % 2]
+        outs.append(L.ds_decode_sparse_attn(qd, Kd, Vd, label, chd, w.T, w.k_units, workspace=ws))
+    torch.cuda.synchronize()
+    for rep, (o, i) in enumerate(outs):
+        ro, ri = refs[rep % 2]
+        assert torch.equal(i, ri), rep
+        assert torch.equal(o.view(torch.int32), ro.view(torch.int32)), rep
