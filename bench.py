@@ -45,6 +45,35 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def kernel_sources_digest() -> str:
+    """Digest of the HIP/C++ sources, to tell whether recorded counters still describe the kernels."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "long_context_sparse_ds_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(name.encode())
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str, stage: str):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by a copy kernel) and
+    recorded in profiles/, or None when no record matches the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    digest = kernel_sources_digest()
+    with open(path) as f:
+        for line in f:
+            if line.startswith("traffic-record:"):
+                kv = dict(item.split("=", 1) for item in line.split(":", 1)[1].split())
+                if kv.get("stage") == stage and kv.get("sources") == digest:
+                    return int(kv["bytes"])
+    return None
+
+
 def algorithmic_bytes(w: dsgen.Workload) -> dict:
     """Bytes the method must move per step (score workspace, split partials and
     the label build are excluded)."""
@@ -130,6 +159,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB ten times and exit (reference for "
+                         "hardware byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -142,6 +174,15 @@ def main():
     import long_context_sparse_ds_amd as L
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        n = args.copy_calibration * 2 ** 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 10}), flush=True)
+        return
     L.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -253,10 +294,15 @@ def main():
         it = inst[i % n_inst]
         L.ds_label_scores(it["q"], it["label"], chd, w.T, w.block, scores=scores_buf[i % n_inst])
 
-    def st_select_attention(i):
+    def st_decode_score(i):
         it = inst[i % n_inst]
-        L.ds_select_attention(it["q"], it["K"], it["V"], scores_buf[i % n_inst], w.T, w.k_units, w.block,
-                              out=it["out"], indices=it["idx"], workspace=it["ws"])
+        L.ds_decode_score(it["q"], it["K"], it["label"], chd, w.T, w.k_units, w.block, workspace=it["ws"],
+                          t_append=w.T - 1)
+
+    def st_decode_select_attend(i):
+        it = inst[i % n_inst]
+        L.ds_decode_select_attend(it["q"], it["K"], it["V"], w.T, w.k_units, it["ws"], w.block, out=it["out"],
+                                  indices=it["idx"])
 
     def st_select(i):
         it = inst[i % n_inst]
@@ -268,8 +314,10 @@ def main():
                                       workspace=it["ws"])
 
     kernel_us = {}
-    for name, fn in (("label_append", st_append), ("scores", st_scores), ("select_attention", st_select_attention),
-                     ("select", st_select), ("attention_from_indices", st_attn)):
+    # The decode step's two phases (its own kernels), then isolated stages for reference.
+    for name, fn in (("decode_score", st_decode_score), ("decode_select_attend", st_decode_select_attend),
+                     ("label_append", st_append), ("scores", st_scores), ("select", st_select),
+                     ("attention_from_indices", st_attn)):
         g = capture(n_inst, fn)
         with torch.cuda.stream(stream):
             g.replay()
@@ -284,14 +332,15 @@ def main():
     log("per-stage us: " + ", ".join(f"{k}={v:.2f}" for k, v in kernel_us.items()))
 
     stage_bytes = {
+        "decode_score": ab["label_scan"] + ab["q"] + ab["label_append"],
+        "decode_select_attend": ab["kv_gather"] + ab["q"] + ab["indices"] + ab["out"],
         "label_append": ab["label_append"],
         "scores": ab["label_scan"] + ab["q"],
-        "select_attention": ab["kv_gather"] + ab["q"] + ab["indices"] + ab["out"],
         "select": ab["indices"],
         "attention_from_indices": ab["kv_gather"] + ab["q"] + ab["indices"] + ab["out"],
     }
-    # the kernels the decode step actually runs: the score pass and the fused selection + attention
-    dominant = max(("scores", "select_attention"), key=lambda k: kernel_us[k])
+    # the decode step's phases: the score pass and selection + attention
+    dominant = max(("decode_score", "decode_select_attend"), key=lambda k: kernel_us[k])
     dom_gbs = stage_bytes[dominant] / (kernel_us[dominant] * 1e-6) / 1e9
 
     gbs = ab["step"] / (us_step * 1e-6) / 1e9
@@ -318,7 +367,8 @@ def main():
         "label_build_us": round(label_build_us, 2),
         "stage_us": {k: round(v, 3) for k, v in kernel_us.items()},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(w.name, dominant),
                      "bytes_per_launch": stage_bytes[dominant], "avg_launch_us": round(kernel_us[dominant], 3)},
     }
 

@@ -146,8 +146,27 @@ ds_status ds_decode_sparse_attn(const void* q, const void* K, const void* V, voi
                                 int32_t* indices, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Stages of ds_decode_sparse_attn, callable on their own so each can be
- * checked and timed in isolation.
+ * ds_decode_sparse_attn in two phases through one workspace: ds_decode_score
+ * runs steps 0 and 1 (label-row append and scoring) and leaves the scores and
+ * their per-tile histograms in the workspace; ds_decode_select_attend runs
+ * steps 2 and 3 from them.  Issued back to back on one stream with the same
+ * shape and workspace, they launch exactly the kernels of
+ * ds_decode_sparse_attn and give the same results; the split lets a caller
+ * time or schedule the phases.  Arguments as for ds_decode_sparse_attn.
+ */
+ds_status ds_decode_score(const void* q, const void* K, void* label, const int32_t* channels_dev, int32_t r,
+                          ds_dtype dt, int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t T_cap, int64_t T,
+                          int64_t t_append, int32_t block, int64_t k_units, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+ds_status ds_decode_select_attend(const void* q, const void* K, const void* V, ds_dtype dt, int32_t B, int32_t Hq,
+                                  int32_t Hkv, int32_t d, int64_t T_cap, int64_t T, int32_t block, int64_t k_units,
+                                  float scale, float* out, int32_t* indices, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/*
+ * Stages of the decode step fed from caller buffers, so each can be checked in
+ * isolation against independently computed inputs.
  */
 
 /* Step 1 only: scores[b, g, i] (float32) for i < ceil(T / block).

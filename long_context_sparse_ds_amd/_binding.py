@@ -38,6 +38,10 @@ _SIGNATURES = {
     "ds_decode_sparse_attn": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                        _c_i32, _c_i64, _c_i64, _c_i64, _c_i32, _c_i64, _c_f32, _c_vp, _c_vp, _c_vp,
                                        _c_size, _c_vp]),
+    "ds_decode_score": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64,
+                                 _c_i64, _c_i64, _c_i32, _c_i64, _c_vp, _c_size, _c_vp]),
+    "ds_decode_select_attend": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i64,
+                                         _c_i32, _c_i64, _c_f32, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
     "ds_select_attention": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i64,
                                      _c_i32, _c_i64, _c_vp, _c_i64, _c_f32, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
     "ds_label_scores": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i64,
@@ -190,6 +194,40 @@ def ds_decode_sparse_attn(q, K, V, label, channels, T: int, k_units: int, block:
                                        k_units, scale, _dev(out, "out"), _dev(indices, "indices"),
                                        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                                        _stream(stream)))
+    return out, indices
+
+
+def ds_decode_score(q, K, label, channels, T: int, k_units: int, block: int = 1, workspace=None, stream=None,
+                    t_append: int | None = None):
+    """First phase of ds_decode_sparse_attn (label-row append and scores into the workspace).  Returns workspace."""
+    B, Hq, d = q.shape
+    _, Hkv, T_cap, _ = K.shape
+    r = channels.shape[1]
+    if workspace is None:
+        workspace = alloc_workspace(B, Hq, Hkv, d, T, block, k_units, q.device)
+    if t_append is None:
+        t_append = T
+    _check(lib().ds_decode_score(_dev(q, "q"), _dev(K, "K"), _dev(label, "label"), _dev(channels, "channels"), r,
+                                 _dtype_code(q), B, Hq, Hkv, d, T_cap, T, t_append, block, k_units,
+                                 _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                 _stream(stream)))
+    return workspace
+
+
+def ds_decode_select_attend(q, K, V, T: int, k_units: int, workspace, block: int = 1, scale: float = 0.0, out=None,
+                            indices=None, stream=None):
+    """Second phase of ds_decode_sparse_attn, from a workspace ds_decode_score filled.  Returns (out, indices)."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    _, Hkv, T_cap, _ = K.shape
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if indices is None:
+        indices = torch.empty((B, Hkv, k_units), dtype=torch.int32, device=q.device)
+    _check(lib().ds_decode_select_attend(_dev(q, "q"), _dev(K, "K"), _dev(V, "V"), _dtype_code(q), B, Hq, Hkv, d,
+                                         T_cap, T, block, k_units, scale, _dev(out, "out"), _dev(indices, "indices"),
+                                         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                         _stream(stream)))
     return out, indices
 
 

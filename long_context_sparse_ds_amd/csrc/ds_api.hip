@@ -246,38 +246,94 @@ ds_status ds_sparse_attn_from_indices(const void* q, const void* K, const void* 
                        static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
 }
 
+// Shared validation of the decode calls; fills the plan on success.
+static ds_status check_decode_call(const void* q, const void* K, const void* V, const void* label,
+                                   const int32_t* channels_dev, int32_t r, ds_dtype dt, int32_t B, int32_t Hq,
+                                   int32_t Hkv, int32_t d, int64_t T_cap, int64_t T, int64_t t_append, int32_t block,
+                                   int64_t k_units, const void* out, const int32_t* indices, const void* workspace,
+                                   size_t workspace_bytes, bool need_label, bool need_out, ds::DecodePlan& pl) {
+  if (!q || !K || !workspace || (need_label && (!label || !channels_dev)) || (need_out && (!V || !out || !indices)))
+    return fail(DS_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (ds_status st = check_dtype(dt)) return st;
+  if (ds_status st = check_decode_shape(B, Hq, Hkv, d, T_cap, T, block, k_units)) return st;
+  if (need_label && (r < 1 || r > d)) return fail(DS_ERR_INVALID_ARGUMENT, "need 1 <= r <= d (r = %d)", r);
+  if (need_label && (t_append < 0 || t_append > T))
+    return fail(DS_ERR_INVALID_ARGUMENT, "need 0 <= t_append <= T (t_append = %lld)", (long long)t_append);
+  if (!aligned(q, 16) || !aligned(K, 16) || !aligned(workspace, 256) ||
+      (need_label && (!aligned(label, 16) || !aligned(channels_dev, 4))) ||
+      (need_out && (!aligned(V, 16) || !aligned(out, 16) || !aligned(indices, 4))))
+    return fail(DS_ERR_INVALID_ARGUMENT, "misaligned device pointer");
+  pl = ds::plan_decode(B, Hq, Hkv, T, block, k_units);
+  if (workspace_bytes < pl.total_bytes)
+    return fail(DS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, pl.total_bytes);
+  return DS_OK;
+}
+
+static ds_status decode_score_stage(const void* q, const void* K, void* label, const int32_t* channels_dev, int32_t r,
+                                    ds_dtype dt, int32_t B, int32_t Hq, int32_t Hkv, int64_t T_cap, int64_t T,
+                                    int64_t t_append, int32_t block, const ds::DecodePlan& pl, char* ws,
+                                    hipStream_t s) {
+  float* scores = reinterpret_cast<float*>(ws + pl.off_scores);
+  uint16_t* tile_hist = pl.tile_hist ? reinterpret_cast<uint16_t*>(ws + pl.off_tile_hist) : nullptr;
+  unsigned* tickets = pl.fused ? reinterpret_cast<unsigned*>(ws + pl.off_tickets) : nullptr;
+  return hip_status(ds::launch_scores(q, label, K, channels_dev, r, dt == DS_DTYPE_BF16, B, Hq, Hkv, T_cap, T,
+                                      t_append, block, scores, pl.score_ld, tile_hist, tickets, pl.sp.head_chunks, s),
+                    "score launch");
+}
+
+static ds_status decode_select_stage(const void* q, const void* K, const void* V, ds_dtype dt, int32_t B, int32_t Hq,
+                                     int32_t Hkv, int64_t T_cap, int64_t T, int32_t block, int64_t k_units,
+                                     float scale, const ds::DecodePlan& pl, float* out, int32_t* indices, char* ws,
+                                     hipStream_t s) {
+  const float* scores = reinterpret_cast<const float*>(ws + pl.off_scores);
+  const uint16_t* tile_hist = pl.tile_hist ? reinterpret_cast<const uint16_t*>(ws + pl.off_tile_hist) : nullptr;
+  return run_select_attend(q, K, V, dt, B, Hq, Hkv, T_cap, T, block, k_units, scores, pl.score_ld, tile_hist, true,
+                           scale, pl, out, indices, ws, s);
+}
+
 ds_status ds_decode_sparse_attn(const void* q, const void* K, const void* V, void* label, const int32_t* channels_dev,
                                 int32_t r, ds_dtype dt, int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t T_cap,
                                 int64_t T, int64_t t_append, int32_t block, int64_t k_units, float scale, float* out,
                                 int32_t* indices, void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
-  if (!q || !K || !V || !label || !channels_dev || !out || !indices || !workspace)
-    return fail(DS_ERR_INVALID_ARGUMENT, "null pointer argument");
-  if (ds_status st = check_dtype(dt)) return st;
-  if (ds_status st = check_decode_shape(B, Hq, Hkv, d, T_cap, T, block, k_units)) return st;
-  if (r < 1 || r > d) return fail(DS_ERR_INVALID_ARGUMENT, "need 1 <= r <= d (r = %d)", r);
-  if (t_append < 0 || t_append > T)
-    return fail(DS_ERR_INVALID_ARGUMENT, "need 0 <= t_append <= T (t_append = %lld)", (long long)t_append);
-  if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(label, 16) || !aligned(out, 16) ||
-      !aligned(indices, 4) || !aligned(channels_dev, 4) || !aligned(workspace, 256))
-    return fail(DS_ERR_INVALID_ARGUMENT, "misaligned device pointer");
-  const ds::DecodePlan pl = ds::plan_decode(B, Hq, Hkv, T, block, k_units);
-  if (workspace_bytes < pl.total_bytes)
-    return fail(DS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, pl.total_bytes);
+  ds::DecodePlan pl;
+  if (ds_status st = check_decode_call(q, K, V, label, channels_dev, r, dt, B, Hq, Hkv, d, T_cap, T, t_append, block,
+                                       k_units, out, indices, workspace, workspace_bytes, true, true, pl))
+    return st;
   if (!(scale > 0.f)) scale = 1.0f / std::sqrt(float(d));
   const hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  float* scores = reinterpret_cast<float*>(ws + pl.off_scores);
-  const int is_bf16 = dt == DS_DTYPE_BF16;
-  uint16_t* tile_hist = pl.tile_hist ? reinterpret_cast<uint16_t*>(ws + pl.off_tile_hist) : nullptr;
-  unsigned* tickets = pl.fused ? reinterpret_cast<unsigned*>(ws + pl.off_tickets) : nullptr;
-  if (ds_status st = hip_status(ds::launch_scores(q, label, K, channels_dev, r, is_bf16, B, Hq, Hkv, T_cap, T,
-                                                  t_append, block, scores, pl.score_ld, tile_hist, tickets,
-                                                  pl.sp.head_chunks, s),
-                                "score launch"))
+  if (ds_status st = decode_score_stage(q, K, label, channels_dev, r, dt, B, Hq, Hkv, T_cap, T, t_append, block, pl,
+                                        ws, s))
     return st;
-  return run_select_attend(q, K, V, dt, B, Hq, Hkv, T_cap, T, block, k_units, scores, pl.score_ld, tile_hist, true,
-                           scale, pl, out, indices, ws, s);
+  return decode_select_stage(q, K, V, dt, B, Hq, Hkv, T_cap, T, block, k_units, scale, pl, out, indices, ws, s);
+}
+
+ds_status ds_decode_score(const void* q, const void* K, void* label, const int32_t* channels_dev, int32_t r,
+                          ds_dtype dt, int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t T_cap, int64_t T,
+                          int64_t t_append, int32_t block, int64_t k_units, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  g_err.clear();
+  ds::DecodePlan pl;
+  if (ds_status st = check_decode_call(q, K, nullptr, label, channels_dev, r, dt, B, Hq, Hkv, d, T_cap, T, t_append,
+                                       block, k_units, nullptr, nullptr, workspace, workspace_bytes, true, false, pl))
+    return st;
+  return decode_score_stage(q, K, label, channels_dev, r, dt, B, Hq, Hkv, T_cap, T, t_append, block, pl,
+                            static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+ds_status ds_decode_select_attend(const void* q, const void* K, const void* V, ds_dtype dt, int32_t B, int32_t Hq,
+                                  int32_t Hkv, int32_t d, int64_t T_cap, int64_t T, int32_t block, int64_t k_units,
+                                  float scale, float* out, int32_t* indices, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  g_err.clear();
+  ds::DecodePlan pl;
+  if (ds_status st = check_decode_call(q, K, V, nullptr, nullptr, 0, dt, B, Hq, Hkv, d, T_cap, T, T, block, k_units,
+                                       out, indices, workspace, workspace_bytes, false, true, pl))
+    return st;
+  if (!(scale > 0.f)) scale = 1.0f / std::sqrt(float(d));
+  return decode_select_stage(q, K, V, dt, B, Hq, Hkv, T_cap, T, block, k_units, scale, pl, out, indices,
+                             static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
 }
 
 ds_status ds_select_attention(const void* q, const void* K, const void* V, ds_dtype dt, int32_t B, int32_t Hq,

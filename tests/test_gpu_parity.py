@@ -386,3 +386,20 @@ def test_alternating_inputs_through_one_workspace():
         ro, ri = refs[rep % 2]
         assert torch.equal(i, ri), rep
         assert torch.equal(o.view(torch.int32), ro.view(torch.int32)), rep
+
+
+@pytest.mark.parametrize("w", [SMALL[0], SMALL[1], SMALL[4], SMALL[6], SMALL[13]], ids=lambda w: w.name)
+def test_two_phase_decode_equals_single_call(w):
+    """ds_decode_score then ds_decode_select_attend through one workspace must give exactly
+    the results of ds_decode_sparse_attn (same kernels), including the fused label append."""
+    q, K, V = dsgen.gen_cache(w)
+    qc, kc = dsgen.gen_calib(w)
+    chd = torch.from_numpy(L.ds_calibrate_channels(qc, kc, w.r)).cuda()
+    qd, Kd, Vd = to_device(q, w.dtype), to_device(K, w.dtype), to_device(V, w.dtype)
+    label = L.ds_build_label_cache(Kd, chd)
+    o1, i1 = L.ds_decode_sparse_attn(qd, Kd, Vd, label, chd, w.T, w.k_units, w.block, t_append=w.T - 3)
+    ws = L.ds_decode_score(qd, Kd, label, chd, w.T, w.k_units, w.block, t_append=w.T - 3)
+    o2, i2 = L.ds_decode_select_attend(qd, Kd, Vd, w.T, w.k_units, ws, w.block)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2)
+    assert torch.equal(o1.view(torch.int32), o2.view(torch.int32))
