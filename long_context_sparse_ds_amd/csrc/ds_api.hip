@@ -96,8 +96,8 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t T, int block, int64_t k_u
   p.fused = p.n_units <= kFusedMaxUnits;
   p.sp = plan_split(p.rows, G, p.kv_virtual, p.fused);
   p.tiles = (T + kScoreTile - 1) / kScoreTile;
-  // Worth it when several fused workgroups of a row would each histogram the whole row.
-  p.tile_hist = p.fused && p.sp.n_split * p.sp.head_chunks > 1 && p.tiles <= kMaxHistTiles;
+  // The fused kernel then reads the row's top-digit histogram instead of building it.
+  p.tile_hist = p.fused && p.tiles <= kMaxHistTiles;
   p.sp_idx = plan_split(p.rows, G, p.kv_virtual, false);
   const int max_split = p.sp.n_split > p.sp_idx.n_split ? p.sp.n_split : p.sp_idx.n_split;
   const int64_t bhs = int64_t(B) * Hq * max_split;

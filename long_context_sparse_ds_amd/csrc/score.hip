@@ -99,14 +99,25 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
       }
     }
   }
+  // The group's q summed over its heads for all 128 channels, and the channel
+  // table, are fetched side by side (neither waits for the other); the label
+  // channels' sums are then picked out of LDS.
+  __shared__ double qall[kHeadDim];
   __shared__ double qs[kHeadDim];
   __shared__ int sch[kHeadDim];
-  for (int j = threadIdx.x; j < r; j += kThreads) {
-    const int c = ch[g * r + j];
+  static_assert(kThreads >= kHeadDim, "one thread per channel");
+  if (threadIdx.x < kHeadDim) {
+    const TE* qg = q + (int64_t(b) * Hq + int64_t(g) * G) * kHeadDim + threadIdx.x;
     double s = 0.0;
-    for (int h = 0; h < G; ++h) s += double(elem_to_f32(q[(int64_t(b) * Hq + int64_t(g) * G + h) * kHeadDim + c]));
-    qs[j] = s;
-    sch[j] = c;
+    for (int h = 0; h < G; ++h) s += double(elem_to_f32(qg[int64_t(h) * kHeadDim]));
+    qall[threadIdx.x] = s;
+  }
+  int cj = 0;
+  if (threadIdx.x < r) cj = ch[g * r + threadIdx.x];
+  __syncthreads();
+  if (threadIdx.x < r) {
+    qs[threadIdx.x] = qall[cj];
+    sch[threadIdx.x] = cj;
   }
   __syncthreads();
 

@@ -5,41 +5,114 @@
 // only.  Jenga page, core method item 3: kept K/V rows are read in place from
 // the cache by index.
 //
-// One workgroup per (row = b * Hkv + g, head chunk, split), 1024 threads.  Every workgroup
-// of a row reads the row's scores (from L2 / Infinity Cache: the row was just
-// written by the score kernel) into registers and finds the row's exact
-// threshold itself, so no workgroup waits for another and the kept indices
-// never make a round trip through memory before the gather.  Split s then owns
-// kept positions [s * chunk, (s + 1) * chunk) of the ascending kept list: it
-// writes those indices, and gathers and attends over those rows only.  When a
-// row has one split the workgroup writes the normalised output.  Otherwise it
-// publishes its softmax state (m, l, unnormalised acc) and takes a ticket; the
-// row's last workgroup merges the states by log-sum-exp and writes the output.
-// Workgroups of a row run on different XCDs, whose L2 caches are not kept
+// One workgroup per (row = b * Hkv + g, head chunk, split).  Every workgroup of
+// a row reads the row's scores (from L2 / Infinity Cache: the row was just
+// written by the score kernel) and finds the row's exact threshold itself, so
+// no workgroup waits for another before its gather and the kept indices never
+// make a round trip through memory.  Split s owns kept positions
+// [s * chunk, (s + 1) * chunk) of the ascending kept list: it writes those
+// indices, and gathers and attends over those rows only.  When a row has one
+// split the workgroup writes the normalised output.  Otherwise it publishes
+// its softmax state (m, l, unnormalised acc) and takes a ticket; the row's last
+// workgroup merges the states by log-sum-exp and writes the output.
+// Workgroups of a row may run on different XCDs, whose L2 caches are not kept
 // coherent with each other, so the states go through agent-scope accesses
 // (written through past the L2, read around it), and a workgroup's stores have
 // completed (s_waitcnt) before its ticket is taken.  No cache-wide writeback
 // or invalidate is needed.
+//
+// Selection (exact k largest, lower index wins a tie).  Thread t holds units
+// [t * ITEMS, (t + 1) * ITEMS) of the row.  The top 11 bits of the
+// order-preserving score key give the first radix digit; its histogram comes
+// from the score kernel's per-tile histograms (or is built here), and one
+// workgroup prefix sum over the bins, highest first, finds the digit d0 that
+// holds the k-th largest key.  Every unit is then classified with two float
+// comparisons against the bounds of d0 into two per-thread bit masks: "above
+// d0" (always kept) and "in d0" (candidates).  Only the few candidates are
+// revisited (bit scans over the mask, keys read back from LDS) for the 11-bit
+// and, when still needed, the 10-bit radix passes.  A last prefix sum over the
+// per-thread kept counts gives every kept unit its position in the ascending
+// output list.
 #include "select_dev.h"
 
 namespace ds {
 namespace {
 
-constexpr int kNT = 1024;
-constexpr int kNWave = kNT / 64;
 constexpr int kMaxChunk = int(kFusedMaxChunk);
-constexpr int kU = 2;             // kept rows per lane group per step
-constexpr int kXcds = 8;          // MI355X: 8 XCDs, each with its own L2
+constexpr int kXcds = 8;   // MI355X: 8 XCDs, each with its own L2
 
-template <typename TE>
+template <typename TE, int NT>
 struct Lanes {
+  static constexpr int NW = NT / 64;                  // wavefronts
   static constexpr int EPL = 16 / int(sizeof(TE));   // elements per lane: 8 (bf16), 4 (fp32)
   static constexpr int LPT = kHeadDim / EPL;          // lanes per 128-wide row: 16, 32
   static constexpr int GPW = 64 / LPT;                // lane groups per wavefront
-  static constexpr int NG = kNWave * GPW;             // lane groups per workgroup
+  static constexpr int NG = NW * GPW;                 // lane groups per workgroup
+  static constexpr int KU = NT >= 1024 ? 2 : 4;       // kept rows per lane group per step
 };
 
-__device__ __forceinline__ void unpack(const uint4& w, float (&f)[8], uint16_t) {
+template <int NT, int ITEMS, int HC>
+struct FusedSmem {
+  static constexpr int NW = NT / 64;
+  union {
+    float sc[NT * ITEMS];   // the row's scores, while the threshold is found
+    struct {
+      int32_t sel[kMaxChunk];                 // this split's kept unit ids
+      float wacc[NW][HC][kHeadDim];           // per-wavefront attention states
+    } a;
+  } u;
+  uint32_t hist1[2048];     // top-digit histogram (when built here), then bits 20..10 of the candidates
+  uint32_t hist2[1024];     // bits 9..0
+  uint32_t wsum[4][NW];     // one per prefix sum, so none needs a trailing barrier
+  float wm[NW][HC], wl[NW][HC], wf[NW][HC];
+  float sM[HC], sL[HC];
+  uint32_t pick[3];         // digit, count above it, count in it
+  unsigned ticket;
+};
+
+// Inverse of float_key for keys of non-NaN floats.
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Thread t of NT owns bins [NB - BPT * (t + 1), NB - BPT * t) of an NB-bin
+// histogram, highest first, so thread order is descending digit order.  c[i]
+// is the count of bin NB - 1 - BPT * t - i.  With the workgroup prefix sum of
+// the per-thread totals, the thread whose bins hold the kk-th largest key
+// stores (digit, count above it, count in it) to out.  The caller passes a
+// barrier before reading out.
+template <int NT, int NB>
+__device__ __forceinline__ void pick_bin(const uint32_t (&c)[NB / NT], uint32_t kk, uint32_t* wsum, uint32_t* out) {
+  constexpr int BPT = NB / NT;
+  uint32_t sum = 0u;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) sum += c[i];
+  uint32_t tot;
+  uint32_t above = block_exclusive_scan1<NT>(sum, wsum, tot);
+  if (above < kk && above + sum >= kk) {
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      if (above < kk && above + c[i] >= kk) {
+        out[0] = uint32_t(NB - 1 - BPT * int(threadIdx.x) - i);
+        out[1] = above;
+        out[2] = c[i];
+      }
+      above += c[i];
+    }
+  }
+}
+
+// Counts of this thread's bins of an LDS histogram, highest first.
+template <int NT, int NB>
+__device__ __forceinline__ void read_bins(const uint32_t* hist, uint32_t (&c)[NB / NT]) {
+  constexpr int BPT = NB / NT;
+  const int lo = NB - BPT * (int(threadIdx.x) + 1);
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) c[i] = hist[lo + BPT - 1 - i];
+}
+
+template <typename TE>
+__device__ __forceinline__ void unpack(const uint4& w, float (&f)[8], TE) {
   f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x);
   f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
   f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z);
@@ -50,10 +123,10 @@ __device__ __forceinline__ void unpack(const uint4& w, float (&f)[4], float) {
   f[2] = __uint_as_float(w.z); f[3] = __uint_as_float(w.w);
 }
 
-template <typename TE>
+template <typename TE, int NT>
 __device__ __forceinline__ float group_sum(float v) {
   v = row16_sum(v);
-  if constexpr (Lanes<TE>::LPT == 32) v += __shfl_xor(v, 16);
+  if constexpr (Lanes<TE, NT>::LPT == 32) v += __shfl_xor(v, 16);
   return v;
 }
 
@@ -74,23 +147,21 @@ __device__ __forceinline__ void merge_lanes(float (&m)[HC], float (&l)[HC], floa
   }
 }
 
-template <typename TE, int HC, int ITEMS>
-__global__ __launch_bounds__(kNT) void selattn_kernel(const TE* __restrict__ q, const TE* __restrict__ K,
-                                                      const TE* __restrict__ V, const float* __restrict__ scores,
-                                                      int64_t ld, const uint16_t* __restrict__ tile_hist,
-                                                      int tiles, int64_t n_units, int64_t k_units, int Hq, int Hkv,
-                                                      int64_t T_cap, int64_t T, int block, int64_t kv_virtual,
-                                                      int64_t chunk, int n_split, float scale,
-                                                      int32_t* __restrict__ indices, float* __restrict__ part_acc,
-                                                      float* __restrict__ part_ml, float* __restrict__ out,
-                                                      unsigned* __restrict__ tickets) {
-  using LN = Lanes<TE>;
-  constexpr int EPL = LN::EPL, LPT = LN::LPT, GPW = LN::GPW, NG = LN::NG;
-  __shared__ SelSmem<kNT> sm;
-  __shared__ int32_t sel[kMaxChunk];
-  __shared__ float wm[kNWave][HC], wl[kNWave][HC], wf[kNWave][HC];
-  __shared__ float wacc[kNWave][HC][kHeadDim];
-  __shared__ float sM[HC], sL[HC];
+template <typename TE, int NT, int ITEMS, int HC>
+__global__ __launch_bounds__(NT) void selattn_kernel(const TE* __restrict__ q, const TE* __restrict__ K,
+                                                     const TE* __restrict__ V, const float* __restrict__ scores,
+                                                     int64_t ld, const uint16_t* __restrict__ tile_hist, int tiles,
+                                                     int n_units, int k_units, int Hq, int Hkv, int64_t T_cap,
+                                                     int64_t T, int block, int64_t kv_virtual, int64_t chunk,
+                                                     int n_split, float scale, int32_t* __restrict__ indices,
+                                                     float* __restrict__ part_acc, float* __restrict__ part_ml,
+                                                     float* __restrict__ out, unsigned* __restrict__ tickets) {
+  using LN = Lanes<TE, NT>;
+  constexpr int NW = LN::NW, EPL = LN::EPL, LPT = LN::LPT, GPW = LN::GPW, NG = LN::NG, KU = LN::KU;
+  constexpr int BPT1 = 2048 / NT, BPT2 = 1024 / NT;
+  static_assert(ITEMS % 4 == 0 && ITEMS <= 32, "per-thread masks are 32 bits");
+  static_assert(BPT2 >= 1 && (BPT1 & 1) == 0, "two or more top-digit bins per thread");
+  __shared__ FusedSmem<NT, ITEMS, HC> sm;
 
   // 1-D grid over (row, head chunk, split).  Workgroups are dealt to the 8 XCDs
   // round-robin by id, so when the (row, chunk) count is a multiple of 8 the ids
@@ -114,61 +185,188 @@ __global__ __launch_bounds__(kNT) void selattn_kernel(const TE* __restrict__ q, 
   const int b = int(row / Hkv), g = int(row % Hkv);
   const int G = Hq / Hkv;
   const int h0 = g * G + hchunk * HC;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int grp = lane / LPT, sub = lane % LPT;
   const int gid = wave * GPW + grp;
 
-  // q slices for the chunk's heads, issued first (independent of the selection).
+  // Loads first: q (consumed only after the selection), the thread's scores,
+  // and the tile histograms of its top-digit bins.
+  uint4 qraw[HC];
+#pragma unroll
+  for (int h = 0; h < HC; ++h)
+    qraw[h] = *reinterpret_cast<const uint4*>(q + (int64_t(b) * Hq + h0 + h) * kHeadDim + sub * EPL);
+  const int first = tid * ITEMS;
+  const float* srow = scores + row * ld;   // 16-byte aligned: ld is a multiple of 4
+  float s[ITEMS];
+  if (first + ITEMS <= n_units) {
+#pragma unroll
+    for (int v = 0; v < ITEMS / 4; ++v) {
+      const float4 f = *reinterpret_cast<const float4*>(srow + first + 4 * v);
+      s[4 * v + 0] = f.x;
+      s[4 * v + 1] = f.y;
+      s[4 * v + 2] = f.z;
+      s[4 * v + 3] = f.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) s[j] = first + j < n_units ? srow[first + j] : -INFINITY;
+  }
+  // Packed pairs of 16-bit bin counts; a bin's total over the row is at most
+  // n_units <= 32768, so the packed sums never carry between halves.
+  uint32_t hw[BPT1 / 2];
+#pragma unroll
+  for (int i = 0; i < BPT1 / 2; ++i) hw[i] = 0u;
+  if (tile_hist != nullptr) {
+    const uint32_t* th = reinterpret_cast<const uint32_t*>(tile_hist + row * tiles * kHistBins) +
+                         (kHistBins - BPT1 * (tid + 1)) / 2;
+    uint32_t w[kMaxHistTiles][BPT1 / 2];
+#pragma unroll
+    for (int t = 0; t < int(kMaxHistTiles); ++t)
+#pragma unroll
+      for (int i = 0; i < BPT1 / 2; ++i) w[t][i] = t < tiles ? th[int64_t(t) * (kHistBins / 2) + i] : 0u;
+#pragma unroll
+    for (int t = 0; t < int(kMaxHistTiles); ++t)
+#pragma unroll
+      for (int i = 0; i < BPT1 / 2; ++i) hw[i] += w[t][i];
+  }
+
+  // The scores go to LDS as well, for the candidate passes' indexed reads.
+#pragma unroll
+  for (int v = 0; v < ITEMS / 4; ++v)
+    *reinterpret_cast<float4*>(&sm.u.sc[first + 4 * v]) = make_float4(s[4 * v], s[4 * v + 1], s[4 * v + 2], s[4 * v + 3]);
+  uint32_t c1[BPT1];
+  if (tile_hist != nullptr) {
+#pragma unroll
+    for (int i = 0; i < BPT1; ++i) sm.hist1[i * NT + tid] = 0u;
+    // Word i holds bins lo + 2i (low half) and lo + 2i + 1 (high half).
+#pragma unroll
+    for (int i = 0; i < BPT1 / 2; ++i) {
+      c1[BPT1 - 1 - 2 * i] = hw[i] & 0xFFFFu;
+      c1[BPT1 - 2 - 2 * i] = hw[i] >> 16;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < BPT1; ++i) sm.hist1[i * NT + tid] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j)
+      if (first + j < n_units) atomicAdd(&sm.hist1[float_key(s[j]) >> 21], 1u);
+    __syncthreads();
+    read_bins<NT, 2048>(sm.hist1, c1);
+    // Each bin is read by exactly one thread, which clears it for pass 1.
+    const int lo = 2048 - BPT1 * (tid + 1);
+#pragma unroll
+    for (int i = 0; i < BPT1; ++i) sm.hist1[lo + i] = 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < BPT2; ++i) sm.hist2[i * NT + tid] = 0u;
+
+  // Pass 0: the top digit d0 holding the k-th largest key.
+  const uint32_t k = uint32_t(k_units);
+  pick_bin<NT, 2048>(c1, k, sm.wsum[0], sm.pick);
+  __syncthreads();
+  const uint32_t d0 = sm.pick[0];
+  uint32_t kk = k - sm.pick[1];   // keys still needed from digit d0
+  const uint32_t cnt0 = sm.pick[2];
+
+  // Classify: finite scores have keys in [0x00800000, 0xFF7FFFFF], so
+  // 4 <= d0 <= 2043 and both bounds are non-NaN floats; comparing floats is
+  // comparing keys (-0.0 and +0.0 share a key and compare equal).  Padding
+  // units hold -inf, below every bound.
+  const float f_lo = key_float(d0 << 21), f_hi = key_float((d0 + 1u) << 21);
+  uint32_t gtm = 0u, cm = 0u;
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) {
+    const bool hi = s[j] >= f_hi;
+    const bool in = s[j] >= f_lo && !hi;
+    gtm |= uint32_t(hi) << j;
+    cm |= uint32_t(in) << j;
+  }
+
+  // Narrow the threshold inside d0: thr is a key, eq_take the number of keys
+  // equal to thr to keep (lowest unit ids first), all_eq when that is all of them.
+  uint32_t thr = d0 << 21, eq_take = 0u;
+  bool all_eq = true;
+  bool settled = kk == cnt0;   // every key of digit d0 is needed
+  if (!settled) {
+    for (uint32_t m = cm; m != 0u; m &= m - 1u) {
+      const uint32_t key = float_key(sm.u.sc[first + __builtin_ctz(m)]);
+      atomicAdd(&sm.hist1[(key >> 10) & 2047u], 1u);
+    }
+    __syncthreads();
+    uint32_t c[BPT1];
+    read_bins<NT, 2048>(sm.hist1, c);
+    pick_bin<NT, 2048>(c, kk, sm.wsum[1], sm.pick);
+    __syncthreads();
+    thr |= sm.pick[0] << 10;
+    kk -= sm.pick[1];
+    settled = kk == sm.pick[2];
+    if (!settled) {
+      for (uint32_t m = cm; m != 0u; m &= m - 1u) {
+        const uint32_t key = float_key(sm.u.sc[first + __builtin_ctz(m)]);
+        if ((key & 0xFFFFFC00u) == thr) atomicAdd(&sm.hist2[key & 1023u], 1u);
+      }
+      __syncthreads();
+      uint32_t c2[BPT2];
+      read_bins<NT, 1024>(sm.hist2, c2);
+      pick_bin<NT, 1024>(c2, kk, sm.wsum[2], sm.pick);
+      __syncthreads();
+      thr |= sm.pick[0];
+      kk -= sm.pick[1];
+      all_eq = kk == sm.pick[2];
+      eq_take = kk;
+    }
+  }
+
+  // Kept units of this thread: above d0, plus candidates at or above thr (when
+  // all keys equal to a full-precision thr are kept), or above thr and the
+  // first eq_take equal ones in unit order.
+  uint32_t keepm = gtm, eqm = 0u;
+  if (thr == (d0 << 21) && all_eq) {
+    keepm |= cm;
+  } else {
+    for (uint32_t m = cm; m != 0u; m &= m - 1u) {
+      const int j = __builtin_ctz(m);
+      const uint32_t key = float_key(sm.u.sc[first + j]);
+      if (key > thr || (all_eq && key == thr)) keepm |= 1u << j;
+      else if (key == thr) eqm |= 1u << j;
+    }
+  }
+  uint32_t tot;
+  const uint32_t ex = block_exclusive_scan1<NT>((uint32_t(__popc(keepm)) << 16) | uint32_t(__popc(eqm)),
+                                                sm.wsum[3], tot);
+  // Past this barrier (inside the scan) the scores in LDS are dead: sel reuses them.
+  const int64_t p_begin = int64_t(split) * chunk;   // virtual positions of this split
+  const int64_t p_end = min(p_begin + chunk, kv_virtual);
+  const int u_lo = int(p_begin / block), u_hi = int((p_end + block - 1) / block);   // kept-list positions
+  {
+    uint32_t eq_seen = ex & 0xFFFFu;
+    int pos = int(ex >> 16) + int(min(eq_seen, eq_take));
+    for (uint32_t m = keepm | eqm; m != 0u; m &= m - 1u) {
+      const int j = __builtin_ctz(m);
+      bool take = true;
+      if (eqm & (1u << j)) take = eq_seen++ < eq_take;
+      if (take) {
+        if (pos >= u_lo && pos < u_hi) sm.u.a.sel[pos - u_lo] = first + j;
+        ++pos;
+      }
+    }
+  }
+  __syncthreads();
+  if (hchunk == 0) {
+    int32_t* ridx = indices + row * k_units + u_lo;
+    for (int i = tid; i < u_hi - u_lo; i += NT) ridx[i] = sm.u.a.sel[i];
+  }
+
+  // Attention over the split's kept rows.
   float qv[HC][EPL];
 #pragma unroll
   for (int h = 0; h < HC; ++h) {
-    const uint4 w = *reinterpret_cast<const uint4*>(q + (int64_t(b) * Hq + h0 + h) * kHeadDim + sub * EPL);
-    unpack(w, qv[h], TE());
+    unpack(qraw[h], qv[h], TE());
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qv[h][e] *= scale;
   }
-
-  // 1. The row's exact threshold.
-  const int64_t p_begin = int64_t(split) * chunk;                 // virtual positions of this split
-  const int64_t p_end = min(p_begin + chunk, kv_virtual);
-  const int64_t u_lo = p_begin / block, u_hi = (p_end + block - 1) / block;   // kept-list positions
-  {
-    uint32_t key[ITEMS];
-    bool valid[ITEMS];
-    load_keys<ITEMS>(scores + row * ld, n_units, key, valid);
-    // Top-digit histogram of the row, when the score kernel left one per tile:
-    // thread t sums bins 2047 - 2t (high half of the word) and 2046 - 2t.
-    uint32_t hi = 0u, lo = 0u;
-    if (tile_hist != nullptr) {
-      static_assert(kHistBins == 2 * kNT, "two bins per thread");
-      const uint32_t* th = reinterpret_cast<const uint32_t*>(tile_hist + row * tiles * kHistBins) +
-                           (kHistBins / 2 - 1 - threadIdx.x);
-      // All tiles' words requested at once (at most kMaxHistTiles of them).
-      uint32_t w[kMaxHistTiles];
-#pragma unroll
-      for (int t = 0; t < int(kMaxHistTiles); ++t) w[t] = t < tiles ? th[int64_t(t) * (kHistBins / 2)] : 0u;
-#pragma unroll
-      for (int t = 0; t < int(kMaxHistTiles); ++t) {
-        hi += w[t] >> 16;
-        lo += w[t] & 0xFFFFu;
-      }
-    }
-    uint32_t kk, mask;
-    const uint32_t tau = select_threshold<kNT, ITEMS>(key, valid, uint32_t(k_units), sm, kk, mask,
-                                                      tile_hist != nullptr, hi, lo);
-    int32_t* ridx = indices + row * k_units;
-    const bool write_idx = hchunk == 0;
-    for_each_kept<kNT, ITEMS>(key, valid, int64_t(threadIdx.x) * ITEMS, tau, mask, kk, sm,
-                              [&](int64_t unit, int64_t pos) {
-      if (pos >= u_lo && pos < u_hi) {
-        sel[pos - u_lo] = int32_t(unit);
-        if (write_idx) ridx[pos] = int32_t(unit);
-      }
-    });
-  }
-  __syncthreads();
-
-  // 2. Attention over the split's kept rows.
   float m[HC], l[HC], acc[HC][EPL];
 #pragma unroll
   for (int h = 0; h < HC; ++h) {
@@ -179,24 +377,24 @@ __global__ __launch_bounds__(kNT) void selattn_kernel(const TE* __restrict__ q, 
   }
   const TE* Kr = K + row * T_cap * kHeadDim + sub * EPL;
   const TE* Vr = V + row * T_cap * kHeadDim + sub * EPL;
-  for (int64_t base = p_begin; base < p_end; base += int64_t(NG) * kU) {
-    int64_t tok[kU];
-    bool ok[kU];
+  for (int64_t base = p_begin; base < p_end; base += int64_t(NG) * KU) {
+    int64_t tok[KU];
+    bool ok[KU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int64_t p = base + int64_t(gid) * kU + u;
+    for (int u = 0; u < KU; ++u) {
+      const int64_t p = base + int64_t(gid) * KU + u;
       ok[u] = p < p_end;
       tok[u] = 0;
       if (ok[u]) {
         const int64_t rel = p - p_begin;
-        const int64_t unit = sel[rel / block];
+        const int64_t unit = sm.u.a.sel[rel / block];
         tok[u] = unit * block + rel % block;
-        ok[u] = tok[u] < T;
+        ok[u] = unit >= 0 && tok[u] < T;   // always true when the kept list is whole
       }
     }
-    uint4 kr[kU], vr[kU];
+    uint4 kr[KU], vr[KU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
+    for (int u = 0; u < KU; ++u) {
       if (ok[u]) {
         kr[u] = *reinterpret_cast<const uint4*>(Kr + tok[u] * kHeadDim);
         vr[u] = *reinterpret_cast<const uint4*>(Vr + tok[u] * kHeadDim);
@@ -205,31 +403,31 @@ __global__ __launch_bounds__(kNT) void selattn_kernel(const TE* __restrict__ q, 
         vr[u] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
-    float kf[kU][EPL], vf[kU][EPL];
+    float kf[KU][EPL], vf[KU][EPL];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
+    for (int u = 0; u < KU; ++u) {
       unpack(kr[u], kf[u], TE());
       unpack(vr[u], vf[u], TE());
     }
 #pragma unroll
     for (int h = 0; h < HC; ++h) {
-      float z[kU];
+      float z[KU];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
+      for (int u = 0; u < KU; ++u) {
         float d = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) d = fmaf(qv[h][e], kf[u][e], d);
-        d = group_sum<TE>(d);
+        d = group_sum<TE, NT>(d);
         z[u] = ok[u] ? d : -INFINITY;
       }
       float mx = m[h];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) mx = fmaxf(mx, z[u]);
+      for (int u = 0; u < KU; ++u) mx = fmaxf(mx, z[u]);
       if (mx == -INFINITY) continue;   // uniform across the lane group
       const float alpha = __expf(m[h] - mx);
-      float p[kU], psum = 0.f;
+      float p[KU], psum = 0.f;
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
+      for (int u = 0; u < KU; ++u) {
         p[u] = __expf(z[u] - mx);
         psum += p[u];
       }
@@ -238,128 +436,151 @@ __global__ __launch_bounds__(kNT) void selattn_kernel(const TE* __restrict__ q, 
       for (int e = 0; e < EPL; ++e) {
         float a = acc[h][e] * alpha;
 #pragma unroll
-        for (int u = 0; u < kU; ++u) a = fmaf(p[u], vf[u][e], a);
+        for (int u = 0; u < KU; ++u) a = fmaf(p[u], vf[u][e], a);
         acc[h][e] = a;
       }
       m[h] = mx;
     }
   }
 
-  // 3. Merge the lane groups of each wavefront, then the wavefronts.
+  // Merge the lane groups of each wavefront, then the wavefronts.
 #pragma unroll
   for (int off = LPT; off < 64; off <<= 1) merge_lanes<HC, EPL>(m, l, acc, off);
   if (grp == 0) {
 #pragma unroll
     for (int h = 0; h < HC; ++h) {
       if (sub == 0) {
-        wm[wave][h] = m[h];
-        wl[wave][h] = l[h];
+        sm.wm[wave][h] = m[h];
+        sm.wl[wave][h] = l[h];
       }
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) wacc[wave][h][sub * EPL + e] = acc[h][e];
+      for (int e = 0; e < EPL; ++e) sm.u.a.wacc[wave][h][sub * EPL + e] = acc[h][e];
     }
   }
   __syncthreads();
-  if (threadIdx.x < HC) {
-    const int h = threadIdx.x;
+  if (tid < HC) {
+    const int h = tid;
     float M = -INFINITY;
-    for (int w = 0; w < kNWave; ++w) M = fmaxf(M, wm[w][h]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.wm[w][h]);
     float Ls = 0.f;
-    for (int w = 0; w < kNWave; ++w) {
-      const float f = M == -INFINITY ? 0.f : __expf(wm[w][h] - M);
-      wf[w][h] = f;
-      Ls += wl[w][h] * f;
+    for (int w = 0; w < NW; ++w) {
+      const float f = M == -INFINITY ? 0.f : __expf(sm.wm[w][h] - M);
+      sm.wf[w][h] = f;
+      Ls += sm.wl[w][h] * f;
     }
-    sM[h] = M;
-    sL[h] = Ls;
+    sm.sM[h] = M;
+    sm.sL[h] = Ls;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < HC * kHeadDim; i += kNT) {
+  for (int i = tid; i < HC * kHeadDim; i += NT) {
     const int h = i / kHeadDim, c = i % kHeadDim;
     float A = 0.f;
-    for (int w = 0; w < kNWave; ++w) A = fmaf(wacc[w][h][c], wf[w][h], A);
+    for (int w = 0; w < NW; ++w) A = fmaf(sm.u.a.wacc[w][h][c], sm.wf[w][h], A);
     const int64_t bh = int64_t(b) * Hq + h0 + h;
     if (n_split == 1) {
-      out[bh * kHeadDim + c] = A / sL[h];
+      out[bh * kHeadDim + c] = A / sm.sL[h];
     } else {
       __hip_atomic_store(&part_acc[(bh * n_split + split) * kHeadDim + c], A, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
       if (c == 0) {
-        __hip_atomic_store(&part_ml[(bh * n_split + split) * 2 + 0], sM[h], __ATOMIC_RELAXED,
+        __hip_atomic_store(&part_ml[(bh * n_split + split) * 2 + 0], sm.sM[h], __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&part_ml[(bh * n_split + split) * 2 + 1], sL[h], __ATOMIC_RELAXED,
+        __hip_atomic_store(&part_ml[(bh * n_split + split) * 2 + 1], sm.sL[h], __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
   if (n_split == 1) return;
 
-  // 4. The row's last workgroup merges the splits.
-  __shared__ unsigned sh_ticket;
+  // The row's last workgroup merges the splits.
   __builtin_amdgcn_s_waitcnt(0);   // this thread's state stores have completed
   __syncthreads();
   unsigned* ticket = tickets + rc;
-  if (threadIdx.x == 0) sh_ticket = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) sm.ticket = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  if (sh_ticket != unsigned(n_split - 1)) return;
-  for (int i = threadIdx.x; i < HC * kHeadDim; i += kNT) {
+  if (sm.ticket != unsigned(n_split - 1)) return;
+  constexpr int kBatch = 8;   // splits whose states are requested together
+  for (int i = tid; i < HC * kHeadDim; i += NT) {
     const int h = i / kHeadDim, c = i % kHeadDim;
     const int64_t bh = int64_t(b) * Hq + h0 + h;
     const float* ml = part_ml + bh * n_split * 2;
     const float* pa = part_acc + bh * n_split * kHeadDim + c;
-    float M = -INFINITY;
-    for (int sp = 0; sp < n_split; ++sp)
-      M = fmaxf(M, __hip_atomic_load(&ml[2 * sp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    float L = 0.f, A = 0.f;
-    for (int sp = 0; sp < n_split; ++sp) {
-      const float m = __hip_atomic_load(&ml[2 * sp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float l = __hip_atomic_load(&ml[2 * sp + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float a = __hip_atomic_load(&pa[int64_t(sp) * kHeadDim], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float f = __expf(m - M);   // an empty split has m = -inf: f = 0
-      L = fmaf(l, f, L);
-      A = fmaf(a, f, A);
+    float M = -INFINITY, L = 0.f, A = 0.f;
+    for (int s0 = 0; s0 < n_split; s0 += kBatch) {
+      float mb[kBatch], lb[kBatch], ab[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int sp = s0 + u;
+        mb[u] = -INFINITY;
+        lb[u] = 0.f;
+        ab[u] = 0.f;
+        if (sp < n_split) {
+          mb[u] = __hip_atomic_load(&ml[2 * sp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          lb[u] = __hip_atomic_load(&ml[2 * sp + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ab[u] = __hip_atomic_load(&pa[int64_t(sp) * kHeadDim], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      float Mb = M;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) Mb = fmaxf(Mb, mb[u]);
+      if (Mb == -INFINITY) continue;   // only empty splits so far
+      const float f = __expf(M - Mb);  // M = -inf gives 0
+      L *= f;
+      A *= f;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const float e = __expf(mb[u] - Mb);   // an empty split has m = -inf: 0
+        L = fmaf(lb[u], e, L);
+        A = fmaf(ab[u], e, A);
+      }
+      M = Mb;
     }
     out[bh * kHeadDim + c] = A / L;
   }
-  if (threadIdx.x == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <typename TE, int HC>
-hipError_t dispatch_items(const TE* q, const TE* K, const TE* V, const float* scores, int64_t ld,
-                          const uint16_t* tile_hist, int64_t n_units,
-                          int64_t k_units, int Hq, int Hkv, int64_t T_cap, int64_t T, int block,
-                          const DecodePlan& pl, float scale, int32_t* indices, float* part_acc, float* part_ml,
-                          float* out, unsigned* tickets, hipStream_t s) {
+struct LaunchArgs {
+  const float* scores;
+  int64_t ld;
+  const uint16_t* tile_hist;
+  int k_units, Hq, Hkv;
+  int64_t T_cap, T;
+  int block;
+  const DecodePlan* pl;
+  float scale;
+  int32_t* indices;
+  float *part_acc, *part_ml, *out;
+  unsigned* tickets;
+  hipStream_t s;
+};
+
+template <typename TE, int NT, int ITEMS, int HC>
+hipError_t launch_one(const TE* q, const TE* K, const TE* V, const LaunchArgs& a) {
+  const DecodePlan& pl = *a.pl;
   const dim3 grid(unsigned(int64_t(pl.sp.n_split) * pl.rows * pl.sp.head_chunks));
-#define DS_SA(IT)                                                                                                  \
-  hipLaunchKernelGGL((selattn_kernel<TE, HC, IT>), grid, dim3(kNT), 0, s, q, K, V, scores, ld, tile_hist,        \
-                     int(pl.tiles), n_units, k_units, Hq,                                                          \
-                     Hkv, T_cap, T, block, pl.kv_virtual, pl.sp.chunk, pl.sp.n_split, scale, indices, part_acc, part_ml,    \
-                     out, tickets)
-  if (n_units <= kNT * 4) DS_SA(4);
-  else if (n_units <= kNT * 8) DS_SA(8);
-  else if (n_units <= kNT * 16) DS_SA(16);
-  else DS_SA(32);
-#undef DS_SA
+  hipLaunchKernelGGL((selattn_kernel<TE, NT, ITEMS, HC>), grid, dim3(NT), 0, a.s, q, K, V, a.scores, a.ld,
+                     a.tile_hist, int(pl.tiles), int(pl.n_units), a.k_units, a.Hq, a.Hkv, a.T_cap, a.T, a.block,
+                     pl.kv_virtual, pl.sp.chunk, pl.sp.n_split, a.scale, a.indices, a.part_acc, a.part_ml, a.out,
+                     a.tickets);
   return hipGetLastError();
 }
 
+template <typename TE, int HC>
+hipError_t dispatch_items(const TE* q, const TE* K, const TE* V, const LaunchArgs& a) {
+  const int64_t n = a.pl->n_units;
+  if (n <= 1024 * 4) return launch_one<TE, 1024, 4, HC>(q, K, V, a);
+  if (n <= 1024 * 8) return launch_one<TE, 1024, 8, HC>(q, K, V, a);
+  if (n <= 1024 * 16) return launch_one<TE, 1024, 16, HC>(q, K, V, a);
+  return launch_one<TE, 1024, 32, HC>(q, K, V, a);
+}
+
 template <typename TE>
-hipError_t dispatch(const TE* q, const TE* K, const TE* V, const float* scores, int64_t ld,
-                    const uint16_t* tile_hist, int64_t n_units,
-                    int64_t k_units, int Hq, int Hkv, int64_t T_cap, int64_t T, int block, const DecodePlan& pl,
-                    float scale, int32_t* indices, float* part_acc, float* part_ml, float* out, unsigned* tickets,
-                    hipStream_t s) {
-  switch (pl.sp.head_chunk) {
-    case 4:
-      return dispatch_items<TE, 4>(q, K, V, scores, ld, tile_hist, n_units, k_units, Hq, Hkv, T_cap, T, block, pl, scale,
-                                   indices, part_acc, part_ml, out, tickets, s);
-    case 2:
-      return dispatch_items<TE, 2>(q, K, V, scores, ld, tile_hist, n_units, k_units, Hq, Hkv, T_cap, T, block, pl, scale,
-                                   indices, part_acc, part_ml, out, tickets, s);
-    default:
-      return dispatch_items<TE, 1>(q, K, V, scores, ld, tile_hist, n_units, k_units, Hq, Hkv, T_cap, T, block, pl, scale,
-                                   indices, part_acc, part_ml, out, tickets, s);
+hipError_t dispatch(const TE* q, const TE* K, const TE* V, const LaunchArgs& a) {
+  switch (a.pl->sp.head_chunk) {
+    case 4: return dispatch_items<TE, 4>(q, K, V, a);
+    case 2: return dispatch_items<TE, 2>(q, K, V, a);
+    default: return dispatch_items<TE, 1>(q, K, V, a);
   }
 }
 
@@ -369,13 +590,12 @@ hipError_t launch_select_attention(const void* q, const void* K, const void* V, 
                                    int64_t ld, const uint16_t* tile_hist, int Hq, int Hkv, int64_t T_cap, int64_t T,
                                    int block, int64_t k_units, float scale, const DecodePlan& pl, int32_t* indices,
                                    float* part_acc, float* part_ml, float* out, unsigned* tickets, hipStream_t s) {
+  const LaunchArgs a{scores, ld, tile_hist, int(k_units), Hq, Hkv, T_cap, T, block, &pl, scale, indices,
+                     part_acc, part_ml, out, tickets, s};
   if (is_bf16)
-    return dispatch(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V),
-                    scores, ld, tile_hist, pl.n_units, k_units, Hq, Hkv, T_cap, T, block, pl, scale, indices,
-                    part_acc, part_ml, out, tickets, s);
-  return dispatch(static_cast<const float*>(q), static_cast<const float*>(K), static_cast<const float*>(V), scores, ld,
-                  tile_hist, pl.n_units, k_units, Hq, Hkv, T_cap, T, block, pl, scale, indices, part_acc, part_ml,
-                  out, tickets, s);
+    return dispatch(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(K),
+                    static_cast<const uint16_t*>(V), a);
+  return dispatch(static_cast<const float*>(q), static_cast<const float*>(K), static_cast<const float*>(V), a);
 }
 
 }  // namespace ds

@@ -403,3 +403,100 @@ def test_two_phase_decode_equals_single_call(w):
     torch.cuda.synchronize()
     assert torch.equal(i1, i2)
     assert torch.equal(o1.view(torch.int32), o2.view(torch.int32))
+
+
+def _adversarial_row(kind, n, rng):
+    """Finite float32 score rows that stress the selection's digit bounds and tie rule."""
+    if kind == "ints":          # heavy exact ties everywhere, also at the k-th score
+        return rng.integers(-6, 7, size=n).astype(np.float32)
+    if kind == "equal":         # one value: the k lowest ids are kept
+        return np.full(n, -2.75, np.float32)
+    if kind == "zeros":         # +0.0 / -0.0 are one key; a few positives above them
+        u = np.where(rng.random(n) < 0.5, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
+        u[::97] = 1.0
+        return u
+    if kind == "denormal":      # positive and negative subnormals around zero
+        mags = rng.integers(1, 1 << 12, size=n).astype(np.uint32)
+        signs = np.where(rng.random(n) < 0.5, np.uint32(0x80000000), np.uint32(0))
+        return (mags | signs).view(np.float32)
+    if kind == "boundaries":    # powers of two and their neighbours: values on the 11-bit digit edges
+        sign = np.where(rng.random(n) < 0.3, -1.0, 1.0)
+        base = (sign * np.ldexp(1.0, rng.integers(-3, 4, size=n))).astype(np.float32)
+        step = rng.integers(-1, 2, size=n)
+        up = np.nextafter(base, np.float32(np.inf))
+        down = np.nextafter(base, np.float32(-np.inf))
+        return np.where(step > 0, up, np.where(step < 0, down, base)).astype(np.float32)
+    if kind == "one_digit":     # every score in one top digit: all are candidates
+        return (1.0 + rng.random(n) * 0.2).astype(np.float32)
+    if kind == "huge":          # magnitudes near the float32 maximum
+        return (rng.standard_normal(n) * 1e37).astype(np.float32)
+    raise ValueError(kind)
+
+
+ADV_KINDS = ["ints", "equal", "zeros", "denormal", "boundaries", "one_digit", "huge"]
+ADV_SHAPES = [(3000, 1000), (5000, 4999), (16384, 1024), (30000, 9000), (777, 1)]
+
+
+@pytest.mark.parametrize("kind", ADV_KINDS)
+def test_select_attention_adversarial_scores(kind):
+    """Selection inside the fused kernel on caller score rows built to sit on digit
+    bounds, signed zeros, subnormals and exact ties: kept ids bit-exact against the
+    oracle's selection of the same float32 values, outputs against the oracle."""
+    for T, k in ADV_SHAPES:
+        w = Workload(f"adv_{kind}_{T}", "bf16", B=1, Hq=4, Hkv=2, d=128, T=T, r=16, block=1, k_units=k,
+                     seed_base=26000 + T)
+        _say(f"{w.name} k={k}")
+        q, K, V = dsgen.gen_cache(w)
+        rng = np.random.default_rng(zlib.crc32(w.name.encode()))
+        ld = -(-T // 4) * 4
+        sc = np.zeros((1, 2, ld), np.float32)
+        for g in range(2):
+            sc[0, g, :T] = _adversarial_row(kind, T, rng)
+        out, idx = L.ds_select_attention(to_device(q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16"),
+                                         torch.from_numpy(sc).cuda(), T, k, 1)
+        torch.cuda.synchronize()
+        out, idx = out.cpu().numpy(), idx.cpu().numpy()
+        for g in range(2):
+            want = O.select_topk(sc[0, g, :T].astype(np.float64), k)
+            np.testing.assert_array_equal(idx[0, g], want, err_msg=f"{w.name} g={g}")
+            qg, Kf, Vf = unit_inputs(w, q, K, V, 0, g)
+            ref = O.attend(qg, Kf, Vf, want, O.default_scale(w.d))
+            err = float(np.max(np.abs(out[0, g * 2:(g + 1) * 2] - ref)))
+            assert err <= OUT_TOL["bf16"], (w.name, g, err)
+
+
+def _bf16_ints(arr):
+    """Small integers are exact in bfloat16: the bit patterns of those values."""
+    return dsgen.f32_to_bf16_bits(np.ascontiguousarray(arr, dtype=np.float32))
+
+
+@pytest.mark.parametrize("T,k,span", [(20000, 3000, 2), (9000, 4500, 0), (32768, 777, 1)],
+                         ids=["ties_20k", "q_zero_9k", "ties_32k"])
+def test_decode_integer_scores_exact_ties(T, k, span):
+    """The whole decode step (score kernel with its tile histograms, then the fused
+    kernel) on q and K with small integer values, so every score is an exact integer
+    and the k-th score is shared by many tokens (span 0: q = 0, all scores equal).
+    Ties go to the lower token id on both sides, so the kept ids match exactly."""
+    B, Hq, Hkv, d, r = 1, 4, 2, 128, 8
+    rng = np.random.default_rng(T + span)
+    qf = rng.integers(-span, span + 1, size=(B, Hq, d)).astype(np.float32)
+    Kf = rng.integers(-2, 3, size=(B, Hkv, T, d)).astype(np.float32)
+    Vf = rng.standard_normal((B, Hkv, T, d)).astype(np.float32)
+    ch = np.stack([np.sort(rng.choice(d, r, replace=False)) for _ in range(Hkv)]).astype(np.int32)
+    q, K, V = _bf16_ints(qf), _bf16_ints(Kf), _bf16_ints(Vf)
+    _say(f"integer scores T={T} k={k} span={span}")
+    qd, Kd, Vd = to_device(q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16")
+    chd = torch.from_numpy(ch).cuda()
+    label = L.ds_build_label_cache(Kd, chd)
+    out, idx = L.ds_decode_sparse_attn(qd, Kd, Vd, label, chd, T, k, 1)
+    torch.cuda.synchronize()
+    out, idx = out.cpu().numpy(), idx.cpu().numpy()
+    w = Workload("ints", "bf16", B=B, Hq=Hq, Hkv=Hkv, d=d, T=T, r=r, block=1, k_units=k, seed_base=0)
+    for g in range(Hkv):
+        qg, Kg, Vg = unit_inputs(w, q, K, V, 0, g)
+        u = O.label_scores(qg, O.label_rows(Kg, ch[g]), ch[g])
+        want = O.select_topk(u, k)
+        np.testing.assert_array_equal(idx[0, g], want, err_msg=f"g={g}")
+        ref = O.attend(qg, Kg, Vg, want, O.default_scale(d))
+        err = float(np.max(np.abs(out[0, g * 2:(g + 1) * 2] - ref)))
+        assert err <= OUT_TOL["bf16"], (g, err)
