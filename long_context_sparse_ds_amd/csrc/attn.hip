@@ -62,9 +62,10 @@ __global__ __launch_bounds__(kAT) void attn_kernel(const TE* __restrict__ q, con
   using LN = Lanes<TE>;
   constexpr int EPL = LN::EPL, LPT = LN::LPT, GPW = LN::GPW, NG = LN::NG;
   const int split = blockIdx.x;
-  const int64_t row = blockIdx.y;
-  const int b = int(row / Hkv), g = int(row % Hkv);
-  const int G = Hq / Hkv;
+  const uint32_t row = blockIdx.y;
+  const uint32_t b = row / uint32_t(Hkv), g = row - b * uint32_t(Hkv);
+  const int G = int(uint32_t(Hq) / uint32_t(Hkv));
+  const int lb = __builtin_ctz(unsigned(block));
   const int h0 = g * G + int(blockIdx.z) * HC;   // first query head of this chunk
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = lane / LPT, sub = lane % LPT;
@@ -90,9 +91,9 @@ __global__ __launch_bounds__(kAT) void attn_kernel(const TE* __restrict__ q, con
 
   const int64_t p_begin = int64_t(split) * chunk;
   const int64_t p_end = min(p_begin + chunk, kv_virtual);
-  const int32_t* ridx = idx + row * k_units;
-  const TE* Kr = K + row * T_cap * kHeadDim + sub * EPL;
-  const TE* Vr = V + row * T_cap * kHeadDim + sub * EPL;
+  const int32_t* ridx = idx + int64_t(row) * k_units;
+  const TE* Kr = K + int64_t(row) * T_cap * kHeadDim + sub * EPL;
+  const TE* Vr = V + int64_t(row) * T_cap * kHeadDim + sub * EPL;
 
   for (int64_t base = p_begin; base < p_end; base += int64_t(NG) * kU) {
     int64_t tok[kU];
@@ -103,8 +104,8 @@ __global__ __launch_bounds__(kAT) void attn_kernel(const TE* __restrict__ q, con
       ok[u] = p < p_end;
       tok[u] = 0;
       if (ok[u]) {
-        const int64_t unit = ridx[block == 1 ? p : p / block];
-        tok[u] = block == 1 ? unit : unit * block + p % block;
+        const int64_t unit = ridx[p >> lb];
+        tok[u] = (unit << lb) + (p & (block - 1));
         ok[u] = unit >= 0 && tok[u] < T;
       }
     }

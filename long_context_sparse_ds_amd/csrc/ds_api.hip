@@ -174,6 +174,9 @@ ds_status ds_build_label_cache(const void* K, ds_dtype dt, int32_t B, int32_t Hk
   if (!K || !channels_dev || !label_out) return fail(DS_ERR_INVALID_ARGUMENT, "null pointer argument");
   if (ds_status st = check_dtype(dt)) return st;
   if (B < 1 || Hkv < 1 || T_cap < 1) return fail(DS_ERR_INVALID_ARGUMENT, "B, Hkv, T_cap must be >= 1");
+  if (T_cap > INT32_MAX) return fail(DS_ERR_UNSUPPORTED, "T_cap = %lld exceeds int32 token ids", (long long)T_cap);
+  if (int64_t(B) * Hkv > 65535)
+    return fail(DS_ERR_UNSUPPORTED, "B * Hkv = %lld exceeds 65535 rows", (long long)(int64_t(B) * Hkv));
   if (d != ds::kHeadDim) return fail(DS_ERR_UNSUPPORTED, "d = %d unsupported (only %d)", d, ds::kHeadDim);
   if (r < 1 || r > d) return fail(DS_ERR_INVALID_ARGUMENT, "need 1 <= r <= d (r = %d)", r);
   if (t_begin < 0 || t_begin > t_end || t_end > T_cap)

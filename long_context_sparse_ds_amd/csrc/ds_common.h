@@ -16,8 +16,8 @@ constexpr int64_t kFusedMaxUnits = 32768;
 constexpr int64_t kFusedMaxChunk = 4096;
 // Tokens per score-kernel workgroup (one "tile"); a row's tile histograms are
 // summed by the fused kernel when a row has at most kMaxHistTiles tiles.
-constexpr int64_t kScoreTile = 1024;
-constexpr int64_t kMaxHistTiles = 32;
+constexpr int64_t kScoreTile = 2048;
+constexpr int64_t kMaxHistTiles = 16;
 constexpr int kHistBins = 2048;   // top 11 bits of a score key
 
 // Query heads processed together by one attention workgroup (divides G).

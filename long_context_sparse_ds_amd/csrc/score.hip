@@ -7,8 +7,8 @@
 // method item 1: a block's score is the max of its tokens' scores.
 //
 // This is the only O(T) stream of the decode step: each token contributes
-// r * element_size bytes.  One thread per token, four tokens per thread issued
-// before any arithmetic, so a wavefront reads 64 consecutive label rows per
+// r * element_size bytes.  Four tokens per thread, all requested before any
+// arithmetic, so a wavefront reads 64 consecutive label rows per
 // load instruction.  Products are exact in double precision for bf16 and fp32
 // inputs and the sum of at most d of them is accumulated in double, so the
 // float32 result is the exact score rounded once.
@@ -22,7 +22,7 @@
 namespace ds {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kTPT = 4;                     // tokens per thread
 constexpr int kTile = kThreads * kTPT;      // tokens per workgroup
 static_assert(kTile == kScoreTile, "tile size shared with the fused kernel's histogram reader");
@@ -77,43 +77,57 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
                                                          int64_t t_append, int block, float* __restrict__ scores,
                                                          int64_t ld, uint16_t* __restrict__ tile_hist,
                                                          unsigned* __restrict__ tickets, int tickets_per_row) {
-  const int64_t row = blockIdx.y;
+  // 32-bit index math throughout (T < 2^31 is checked on the host); 64-bit
+  // only for element offsets.
+  // Grid (tiles, Hkv, B): no division to find the row.
+  const uint32_t g = blockIdx.y, b = blockIdx.z;
+  const uint32_t row = b * uint32_t(Hkv) + g;
   if (tickets != nullptr && blockIdx.x == 0)
-    for (int i = threadIdx.x; i < tickets_per_row; i += kThreads) tickets[row * tickets_per_row + i] = 0u;
-  const int b = int(row / Hkv), g = int(row % Hkv);
-  const int G = Hq / Hkv;
-  TE* L = label + row * T_cap * r;
-  const int64_t t0 = int64_t(blockIdx.x) * kTile + threadIdx.x;
+    for (int i = threadIdx.x; i < tickets_per_row; i += kThreads) tickets[int64_t(row) * tickets_per_row + i] = 0u;
+  TE* L = label + int64_t(row) * T_cap * r;
+  const int t0 = int(blockIdx.x) * kTile + int(threadIdx.x);
+  const int Ti = int(T), ta = int(t_append);
+  const int G = int(uint32_t(Hq) / uint32_t(Hkv));
   constexpr int NV = R > 0 ? R * int(sizeof(TE)) / 16 : 1;
-  // The label rows are requested first: they do not depend on q or the
-  // channel table, so their latency overlaps the q-sum below.
+  // Requests in the order they are needed: the group's q values for every
+  // channel (up to 8 heads at a time) and the channel table first, since they
+  // gate the arithmetic; then the label rows, whose latency the q-sum and the
+  // histogram clearing overlap.
+  __shared__ double qall[kHeadDim];
+  __shared__ double qs[kHeadDim];
+  __shared__ int sch[kHeadDim];
+  __shared__ uint32_t h[kHistBins];
+  static_assert(kThreads >= kHeadDim, "one thread per channel");
+  constexpr int kQB = 8;
+  float qv[kQB];
+  const TE* qg = q + int64_t(row) * G * kHeadDim + threadIdx.x;
+  if (threadIdx.x < kHeadDim) {
+#pragma unroll
+    for (int h8 = 0; h8 < kQB; ++h8) qv[h8] = h8 < G ? elem_to_f32(qg[int64_t(h8) * kHeadDim]) : 0.f;
+  }
+  int cj = 0;
+  if (threadIdx.x < r) cj = ch[g * r + threadIdx.x];
   uint4 raw[kTPT][NV];
   if constexpr (R > 0) {
 #pragma unroll
     for (int i = 0; i < kTPT; ++i) {
-      const int64_t t = t0 + i * kThreads;
-      if (t < T && t < t_append) {
-        const uint4* p = reinterpret_cast<const uint4*>(L + t * R);
+      const int t = t0 + i * kThreads;
+      if (t < Ti && t < ta) {
+        const uint4* p = reinterpret_cast<const uint4*>(L + int64_t(t) * R);
 #pragma unroll
         for (int v = 0; v < NV; ++v) raw[i][v] = p[v];
       }
     }
   }
-  // The group's q summed over its heads for all 128 channels, and the channel
-  // table, are fetched side by side (neither waits for the other); the label
-  // channels' sums are then picked out of LDS.
-  __shared__ double qall[kHeadDim];
-  __shared__ double qs[kHeadDim];
-  __shared__ int sch[kHeadDim];
-  static_assert(kThreads >= kHeadDim, "one thread per channel");
+  if (tile_hist != nullptr)
+    for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0u;
   if (threadIdx.x < kHeadDim) {
-    const TE* qg = q + (int64_t(b) * Hq + int64_t(g) * G) * kHeadDim + threadIdx.x;
     double s = 0.0;
-    for (int h = 0; h < G; ++h) s += double(elem_to_f32(qg[int64_t(h) * kHeadDim]));
+#pragma unroll
+    for (int h8 = 0; h8 < kQB; ++h8) s += double(qv[h8]);
+    for (int h = kQB; h < G; ++h) s += double(elem_to_f32(qg[int64_t(h) * kHeadDim]));
     qall[threadIdx.x] = s;
   }
-  int cj = 0;
-  if (threadIdx.x < r) cj = ch[g * r + threadIdx.x];
   __syncthreads();
   if (threadIdx.x < r) {
     qs[threadIdx.x] = qall[cj];
@@ -128,65 +142,62 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
     for (int j = 0; j < R; ++j) qr[j] = qs[j];
 #pragma unroll
     for (int i = 0; i < kTPT; ++i) {
-      const int64_t t = t0 + i * kThreads;
-      if (t >= T) u[i] = -INFINITY;
-      else if (t >= t_append) u[i] = append_row(Kc + (row * T_cap + t) * kHeadDim, L + t * R, sch, qs, R);
+      const int t = t0 + i * kThreads;
+      if (t >= Ti) u[i] = -INFINITY;
+      else if (t >= ta) u[i] = append_row(Kc + (int64_t(row) * T_cap + t) * kHeadDim, L + int64_t(t) * R, sch, qs, R);
       else u[i] = float(dot_label<NV>(raw[i], qr, TE()));
     }
   } else {
 #pragma unroll
     for (int i = 0; i < kTPT; ++i) {
-      const int64_t t = t0 + i * kThreads;
+      const int t = t0 + i * kThreads;
       double a = 0.0;
-      if (t < T && t < t_append)
-        for (int j = 0; j < r; ++j) a = fma(qs[j], double(elem_to_f32(L[t * r + j])), a);
-      if (t >= T) u[i] = -INFINITY;
-      else if (t >= t_append) u[i] = append_row(Kc + (row * T_cap + t) * kHeadDim, L + t * r, sch, qs, r);
+      if (t < Ti && t < ta)
+        for (int j = 0; j < r; ++j) a = fma(qs[j], double(elem_to_f32(L[int64_t(t) * r + j])), a);
+      if (t >= Ti) u[i] = -INFINITY;
+      else if (t >= ta) u[i] = append_row(Kc + (int64_t(row) * T_cap + t) * kHeadDim, L + int64_t(t) * r, sch, qs, r);
       else u[i] = float(a);
     }
   }
 
-  float* out = scores + row * ld;
+  float* out = scores + int64_t(row) * ld;
   // Each unit score this thread writes: value and whether it exists.
   float uv[kTPT];
   bool has[kTPT];
   if (block == 1) {
 #pragma unroll
     for (int i = 0; i < kTPT; ++i) {
-      const int64_t t = t0 + i * kThreads;
+      const int t = t0 + i * kThreads;
       uv[i] = u[i];
-      has[i] = t < T;
+      has[i] = t < Ti;
       if (has[i]) out[t] = u[i];
     }
   } else {
     // 64 consecutive tokens per wavefront, 64-aligned: blocks of `block` lanes.
+    const int lb = __builtin_ctz(unsigned(block));
 #pragma unroll
     for (int i = 0; i < kTPT; ++i) {
       float v = u[i];
       for (int off = block >> 1; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-      const int64_t t = t0 + i * kThreads;
+      const int t = t0 + i * kThreads;
       uv[i] = v;
-      has[i] = t < T && (t % block) == 0;
-      if (has[i]) out[t / block] = v;
+      has[i] = t < Ti && (t & (block - 1)) == 0;
+      if (has[i]) out[t >> lb] = v;
     }
   }
   if (tile_hist != nullptr) {
-    // Dense histogram of the top 11 key bits of this tile's units, every bin
-    // written, so the buffer needs no clearing between calls.
-    __shared__ uint32_t h[kHistBins];
-    for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0u;
-    __syncthreads();
+    // Dense histogram of the top 11 key bits of this tile's units (cleared
+    // above, before the barriers), every bin written, so the buffer needs no
+    // clearing between calls.
 #pragma unroll
     for (int i = 0; i < kTPT; ++i)
       if (has[i]) atomicAdd(&h[float_key(uv[i]) >> 21], 1u);
     __syncthreads();
-    constexpr int per = kHistBins / kThreads;   // 8 bins per thread: one 16-byte store
+    constexpr int per = kHistBins / kThreads;   // 4 bins per thread: one 8-byte store
+    static_assert(per == 4, "one uint2 of packed 16-bit counts per thread");
     const int b0 = threadIdx.x * per;
-    uint32_t w[per / 2];
-#pragma unroll
-    for (int j = 0; j < per / 2; ++j) w[j] = h[b0 + 2 * j] | (h[b0 + 2 * j + 1] << 16);
-    uint16_t* dst = tile_hist + (row * gridDim.x + blockIdx.x) * kHistBins + b0;
-    *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    uint16_t* dst = tile_hist + (int64_t(row) * gridDim.x + blockIdx.x) * kHistBins + b0;
+    *reinterpret_cast<uint2*>(dst) = make_uint2(h[b0] | (h[b0 + 1] << 16), h[b0 + 2] | (h[b0 + 3] << 16));
   }
 }
 
@@ -194,7 +205,7 @@ template <typename TE>
 hipError_t dispatch(const TE* q, TE* label, const TE* Kc, const int32_t* ch, int r, int B, int Hq, int Hkv,
                     int64_t T_cap, int64_t T, int64_t t_append, int block, float* scores, int64_t ld,
                     uint16_t* tile_hist, unsigned* tickets, int tickets_per_row, hipStream_t s) {
-  const dim3 grid(unsigned((T + kTile - 1) / kTile), unsigned(int64_t(B) * Hkv));
+  const dim3 grid(unsigned((T + kTile - 1) / kTile), unsigned(Hkv), unsigned(B));
   const bool vec = (int64_t(r) * sizeof(TE)) % 16 == 0;
 #define DS_SCORE(RR) \
   hipLaunchKernelGGL((score_kernel<TE, RR>), grid, dim3(kThreads), 0, s, q, label, Kc, ch, r, Hq, Hkv, T_cap, T,     \

@@ -64,8 +64,7 @@ struct FusedSmem {
   uint32_t hist1[2048];     // top-digit histogram (when built here), then bits 20..10 of the candidates
   uint32_t hist2[1024];     // bits 9..0
   uint32_t wsum[4][NW];     // one per prefix sum, so none needs a trailing barrier
-  float wm[NW][HC], wl[NW][HC], wf[NW][HC];
-  float sM[HC], sL[HC];
+  float wm[NW][HC], wl[NW][HC];
   uint32_t pick[3];         // digit, count above it, count in it
   unsigned ticket;
 };
@@ -130,32 +129,68 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-// Merge the softmax state of lane groups `off` apart within a wavefront.
-template <int HC, int EPL>
-__device__ __forceinline__ void merge_lanes(float (&m)[HC], float (&l)[HC], float (&acc)[HC][EPL], int off) {
+// The values of a pair of lane groups: with OFF = 16, rows 0-1 and rows 2-3 of
+// the wavefront (v_permlane16_swap); with OFF = 32, its two halves
+// (v_permlane32_swap).  Both lanes of a pair receive the same two values, so a
+// symmetric combination of them leaves the pair holding one identical result.
+template <int OFF>
+__device__ __forceinline__ void pair_values(float v, float& a, float& b) {
+  const uint32_t u = __float_as_uint(v);
+  if constexpr (OFF == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  }
+}
+
+// Merge the softmax states (m, l, acc) of the lane-group pairs OFF lanes apart.
+template <int OFF, int HC, int EPL>
+__device__ __forceinline__ void merge_pairs(float (&m)[HC], float (&l)[HC], float (&acc)[HC][EPL]) {
 #pragma unroll
   for (int h = 0; h < HC; ++h) {
-    const float mo = __shfl_xor(m[h], off);
-    const float lo = __shfl_xor(l[h], off);
-    const float M = fmaxf(m[h], mo);
-    const float fa = m[h] == -INFINITY ? 0.f : __expf(m[h] - M);
-    const float fb = mo == -INFINITY ? 0.f : __expf(mo - M);
-    l[h] = l[h] * fa + lo * fb;
+    float ma, mb, la, lb;
+    pair_values<OFF>(m[h], ma, mb);
+    pair_values<OFF>(l[h], la, lb);
+    const float M = fmaxf(ma, mb);
+    const float fa = ma == -INFINITY ? 0.f : __expf(ma - M);
+    const float fb = mb == -INFINITY ? 0.f : __expf(mb - M);
+    l[h] = la * fa + lb * fb;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = acc[h][e] * fa + __shfl_xor(acc[h][e], off) * fb;
+    for (int e = 0; e < EPL; ++e) {
+      float xa, xb;
+      pair_values<OFF>(acc[h][e], xa, xb);
+      acc[h][e] = xa * fa + xb * fb;
+    }
     m[h] = M;
   }
 }
 
+// Kernel arguments, with the derived sizes precomputed on the host so the
+// kernel's prologue is a few 32-bit operations.
+struct FusedArgs {
+  const void* q;
+  const void* K;
+  const void* V;
+  const float* scores;
+  const uint16_t* tile_hist;   // null: the kernel builds the top-digit histogram itself
+  int32_t* indices;
+  float* part_acc;
+  float* part_ml;
+  float* out;
+  unsigned* tickets;
+  int64_t ld, T_cap;
+  int32_t T, n_units, k_units, G, head_chunks, tiles;
+  int32_t lb;                  // log2(block)
+  int32_t kv_virtual, chunk, n_split;
+  float scale;
+};
+
 template <typename TE, int NT, int ITEMS, int HC>
-__global__ __launch_bounds__(NT) void selattn_kernel(const TE* __restrict__ q, const TE* __restrict__ K,
-                                                     const TE* __restrict__ V, const float* __restrict__ scores,
-                                                     int64_t ld, const uint16_t* __restrict__ tile_hist, int tiles,
-                                                     int n_units, int k_units, int Hq, int Hkv, int64_t T_cap,
-                                                     int64_t T, int block, int64_t kv_virtual, int64_t chunk,
-                                                     int n_split, float scale, int32_t* __restrict__ indices,
-                                                     float* __restrict__ part_acc, float* __restrict__ part_ml,
-                                                     float* __restrict__ out, unsigned* __restrict__ tickets) {
+__global__ __launch_bounds__(NT) void selattn_kernel(const FusedArgs a) {
   using LN = Lanes<TE, NT>;
   constexpr int NW = LN::NW, EPL = LN::EPL, LPT = LN::LPT, GPW = LN::GPW, NG = LN::NG, KU = LN::KU;
   constexpr int BPT1 = 2048 / NT, BPT2 = 1024 / NT;
@@ -163,28 +198,23 @@ __global__ __launch_bounds__(NT) void selattn_kernel(const TE* __restrict__ q, c
   static_assert(BPT2 >= 1 && (BPT1 & 1) == 0, "two or more top-digit bins per thread");
   __shared__ FusedSmem<NT, ITEMS, HC> sm;
 
-  // 1-D grid over (row, head chunk, split).  Workgroups are dealt to the 8 XCDs
-  // round-robin by id, so when the (row, chunk) count is a multiple of 8 the ids
-  // are arranged to keep every split of a row on one XCD: the row's scores
-  // and histograms are then fetched into that XCD's L2 once and shared.
-  const int64_t wg = blockIdx.x;
-  const int64_t n_rc = int64_t(gridDim.x) / n_split;   // rows * head chunks
-  const int head_chunks = (Hq / Hkv) / HC;
-  int64_t rc;
-  int split;
-  if (n_rc % kXcds == 0) {
-    const int64_t j = wg / kXcds;
-    split = int(j % n_split);
-    rc = (j / n_split) * kXcds + wg % kXcds;
-  } else {
-    split = int(wg % n_split);
-    rc = wg / n_split;
-  }
-  const int64_t row = rc / head_chunks;
-  const int hchunk = int(rc % head_chunks);
-  const int b = int(row / Hkv), g = int(row % Hkv);
-  const int G = Hq / Hkv;
-  const int h0 = g * G + hchunk * HC;
+  // Grid (8, n_split, n_rc / 8) when the (row, head chunk) count n_rc is a
+  // multiple of 8, else (1, n_split, n_rc).  Workgroups are dealt to the 8 XCDs
+  // round-robin by linear id (x fastest), so blockIdx.x is the XCD and every
+  // split of a (row, chunk) lands on the same one: the row's scores and
+  // histograms are fetched into that XCD's L2 once and shared.  No division:
+  // rc = 8 * z + x; queries of the row are heads row * G + [0, G).
+  const uint32_t split = blockIdx.y;
+  const uint32_t rc = blockIdx.z * gridDim.x + blockIdx.x;
+  const uint32_t hcs = uint32_t(a.head_chunks);
+  const uint32_t row = hcs == 1 ? rc : rc / hcs;
+  const uint32_t hchunk = rc - row * hcs;
+  const int64_t bh0 = int64_t(row) * a.G + int64_t(hchunk) * HC;   // first (b, h) of this chunk
+  const TE* __restrict__ q = static_cast<const TE*>(a.q);
+  const TE* __restrict__ K = static_cast<const TE*>(a.K);
+  const TE* __restrict__ V = static_cast<const TE*>(a.V);
+  const int n_units = a.n_units, k_units = a.k_units, lb = a.lb, block = 1 << a.lb;
+  const int n_split = a.n_split;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int grp = lane / LPT, sub = lane % LPT;
@@ -195,9 +225,9 @@ __global__ __launch_bounds__(NT) void selattn_kernel(const TE* __restrict__ q, c
   uint4 qraw[HC];
 #pragma unroll
   for (int h = 0; h < HC; ++h)
-    qraw[h] = *reinterpret_cast<const uint4*>(q + (int64_t(b) * Hq + h0 + h) * kHeadDim + sub * EPL);
+    qraw[h] = *reinterpret_cast<const uint4*>(q + (bh0 + h) * kHeadDim + sub * EPL);
   const int first = tid * ITEMS;
-  const float* srow = scores + row * ld;   // 16-byte aligned: ld is a multiple of 4
+  const float* srow = a.scores + int64_t(row) * a.ld;   // 16-byte aligned: ld is a multiple of 4
   float s[ITEMS];
   if (first + ITEMS <= n_units) {
 #pragma unroll
@@ -217,14 +247,15 @@ __global__ __launch_bounds__(NT) void selattn_kernel(const TE* __restrict__ q, c
   uint32_t hw[BPT1 / 2];
 #pragma unroll
   for (int i = 0; i < BPT1 / 2; ++i) hw[i] = 0u;
-  if (tile_hist != nullptr) {
-    const uint32_t* th = reinterpret_cast<const uint32_t*>(tile_hist + row * tiles * kHistBins) +
+  const int tiles = a.tiles;
+  if (a.tile_hist != nullptr) {
+    const uint32_t* th = reinterpret_cast<const uint32_t*>(a.tile_hist + int64_t(row) * tiles * kHistBins) +
                          (kHistBins - BPT1 * (tid + 1)) / 2;
     uint32_t w[kMaxHistTiles][BPT1 / 2];
 #pragma unroll
     for (int t = 0; t < int(kMaxHistTiles); ++t)
 #pragma unroll
-      for (int i = 0; i < BPT1 / 2; ++i) w[t][i] = t < tiles ? th[int64_t(t) * (kHistBins / 2) + i] : 0u;
+      for (int i = 0; i < BPT1 / 2; ++i) w[t][i] = t < tiles ? th[t * (kHistBins / 2) + i] : 0u;
 #pragma unroll
     for (int t = 0; t < int(kMaxHistTiles); ++t)
 #pragma unroll
@@ -236,7 +267,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(const TE* __restrict__ q, c
   for (int v = 0; v < ITEMS / 4; ++v)
     *reinterpret_cast<float4*>(&sm.u.sc[first + 4 * v]) = make_float4(s[4 * v], s[4 * v + 1], s[4 * v + 2], s[4 * v + 3]);
   uint32_t c1[BPT1];
-  if (tile_hist != nullptr) {
+  if (a.tile_hist != nullptr) {
 #pragma unroll
     for (int i = 0; i < BPT1; ++i) sm.hist1[i * NT + tid] = 0u;
     // Word i holds bins lo + 2i (low half) and lo + 2i + 1 (high half).
@@ -337,9 +368,9 @@ __global__ __launch_bounds__(NT) void selattn_kernel(const TE* __restrict__ q, c
   const uint32_t ex = block_exclusive_scan1<NT>((uint32_t(__popc(keepm)) << 16) | uint32_t(__popc(eqm)),
                                                 sm.wsum[3], tot);
   // Past this barrier (inside the scan) the scores in LDS are dead: sel reuses them.
-  const int64_t p_begin = int64_t(split) * chunk;   // virtual positions of this split
-  const int64_t p_end = min(p_begin + chunk, kv_virtual);
-  const int u_lo = int(p_begin / block), u_hi = int((p_end + block - 1) / block);   // kept-list positions
+  const int p_begin = int(split) * a.chunk;   // virtual positions of this split
+  const int p_end = min(p_begin + a.chunk, a.kv_virtual);
+  const int u_lo = p_begin >> lb, u_hi = (p_end + block - 1) >> lb;   // kept-list positions
   {
     uint32_t eq_seen = ex & 0xFFFFu;
     int pos = int(ex >> 16) + int(min(eq_seen, eq_take));
@@ -355,7 +386,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(const TE* __restrict__ q, c
   }
   __syncthreads();
   if (hchunk == 0) {
-    int32_t* ridx = indices + row * k_units + u_lo;
+    int32_t* ridx = a.indices + int64_t(row) * k_units + u_lo;
     for (int i = tid; i < u_hi - u_lo; i += NT) ridx[i] = sm.u.a.sel[i];
   }
 
@@ -365,7 +396,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(const TE* __restrict__ q, c
   for (int h = 0; h < HC; ++h) {
     unpack(qraw[h], qv[h], TE());
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) qv[h][e] *= scale;
+    for (int e = 0; e < EPL; ++e) qv[h][e] *= a.scale;
   }
   float m[HC], l[HC], acc[HC][EPL];
 #pragma unroll
@@ -375,21 +406,21 @@ __global__ __launch_bounds__(NT) void selattn_kernel(const TE* __restrict__ q, c
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
-  const TE* Kr = K + row * T_cap * kHeadDim + sub * EPL;
-  const TE* Vr = V + row * T_cap * kHeadDim + sub * EPL;
-  for (int64_t base = p_begin; base < p_end; base += int64_t(NG) * KU) {
+  const TE* Kr = K + int64_t(row) * a.T_cap * kHeadDim + sub * EPL;
+  const TE* Vr = V + int64_t(row) * a.T_cap * kHeadDim + sub * EPL;
+  for (int base = p_begin; base < p_end; base += NG * KU) {
     int64_t tok[KU];
     bool ok[KU];
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
-      const int64_t p = base + int64_t(gid) * KU + u;
+      const int p = base + gid * KU + u;
       ok[u] = p < p_end;
       tok[u] = 0;
       if (ok[u]) {
-        const int64_t rel = p - p_begin;
-        const int64_t unit = sm.u.a.sel[rel / block];
-        tok[u] = unit * block + rel % block;
-        ok[u] = unit >= 0 && tok[u] < T;   // always true when the kept list is whole
+        const int rel = p - p_begin;
+        const int unit = sm.u.a.sel[rel >> lb];
+        tok[u] = (int64_t(unit) << lb) + (rel & (block - 1));
+        ok[u] = unit >= 0 && tok[u] < a.T;   // always true when the kept list is whole
       }
     }
     uint4 kr[KU], vr[KU];
@@ -443,9 +474,11 @@ __global__ __launch_bounds__(NT) void selattn_kernel(const TE* __restrict__ q, c
     }
   }
 
-  // Merge the lane groups of each wavefront, then the wavefronts.
-#pragma unroll
-  for (int off = LPT; off < 64; off <<= 1) merge_lanes<HC, EPL>(m, l, acc, off);
+  // Merge the lane groups of each wavefront (pairwise lane swaps), then the
+  // wavefronts through LDS: every output channel combines the NW wavefront
+  // states itself, so one barrier suffices.
+  if constexpr (LPT == 16) merge_pairs<16, HC, EPL>(m, l, acc);
+  merge_pairs<32, HC, EPL>(m, l, acc);
   if (grp == 0) {
 #pragma unroll
     for (int h = 0; h < HC; ++h) {
@@ -458,34 +491,28 @@ __global__ __launch_bounds__(NT) void selattn_kernel(const TE* __restrict__ q, c
     }
   }
   __syncthreads();
-  if (tid < HC) {
-    const int h = tid;
-    float M = -INFINITY;
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.wm[w][h]);
-    float Ls = 0.f;
-    for (int w = 0; w < NW; ++w) {
-      const float f = M == -INFINITY ? 0.f : __expf(sm.wm[w][h] - M);
-      sm.wf[w][h] = f;
-      Ls += sm.wl[w][h] * f;
-    }
-    sm.sM[h] = M;
-    sm.sL[h] = Ls;
-  }
-  __syncthreads();
   for (int i = tid; i < HC * kHeadDim; i += NT) {
     const int h = i / kHeadDim, c = i % kHeadDim;
-    float A = 0.f;
-    for (int w = 0; w < NW; ++w) A = fmaf(sm.u.a.wacc[w][h][c], sm.wf[w][h], A);
-    const int64_t bh = int64_t(b) * Hq + h0 + h;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.wm[w][h]);
+    float Ls = 0.f, A = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = M == -INFINITY ? 0.f : __expf(sm.wm[w][h] - M);   // empty wavefronts: 0
+      Ls = fmaf(sm.wl[w][h], f, Ls);
+      A = fmaf(sm.u.a.wacc[w][h][c], f, A);
+    }
+    const int64_t bh = bh0 + h;
     if (n_split == 1) {
-      out[bh * kHeadDim + c] = A / sm.sL[h];
+      a.out[bh * kHeadDim + c] = A / Ls;
     } else {
-      __hip_atomic_store(&part_acc[(bh * n_split + split) * kHeadDim + c], A, __ATOMIC_RELAXED,
+      __hip_atomic_store(&a.part_acc[(bh * n_split + split) * kHeadDim + c], A, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
       if (c == 0) {
-        __hip_atomic_store(&part_ml[(bh * n_split + split) * 2 + 0], sm.sM[h], __ATOMIC_RELAXED,
+        __hip_atomic_store(&a.part_ml[(bh * n_split + split) * 2 + 0], M, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&part_ml[(bh * n_split + split) * 2 + 1], sm.sL[h], __ATOMIC_RELAXED,
+        __hip_atomic_store(&a.part_ml[(bh * n_split + split) * 2 + 1], Ls, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -495,16 +522,16 @@ __global__ __launch_bounds__(NT) void selattn_kernel(const TE* __restrict__ q, c
   // The row's last workgroup merges the splits.
   __builtin_amdgcn_s_waitcnt(0);   // this thread's state stores have completed
   __syncthreads();
-  unsigned* ticket = tickets + rc;
+  unsigned* ticket = a.tickets + rc;
   if (tid == 0) sm.ticket = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (sm.ticket != unsigned(n_split - 1)) return;
   constexpr int kBatch = 8;   // splits whose states are requested together
   for (int i = tid; i < HC * kHeadDim; i += NT) {
     const int h = i / kHeadDim, c = i % kHeadDim;
-    const int64_t bh = int64_t(b) * Hq + h0 + h;
-    const float* ml = part_ml + bh * n_split * 2;
-    const float* pa = part_acc + bh * n_split * kHeadDim + c;
+    const int64_t bh = bh0 + h;
+    const float* ml = a.part_ml + bh * n_split * 2;
+    const float* pa = a.part_acc + bh * n_split * kHeadDim + c;
     float M = -INFINITY, L = 0.f, A = 0.f;
     for (int s0 = 0; s0 < n_split; s0 += kBatch) {
       float mb[kBatch], lb[kBatch], ab[kBatch];
@@ -535,52 +562,32 @@ __global__ __launch_bounds__(NT) void selattn_kernel(const TE* __restrict__ q, c
       }
       M = Mb;
     }
-    out[bh * kHeadDim + c] = A / L;
+    a.out[bh * kHeadDim + c] = A / L;
   }
   if (tid == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-struct LaunchArgs {
-  const float* scores;
-  int64_t ld;
-  const uint16_t* tile_hist;
-  int k_units, Hq, Hkv;
-  int64_t T_cap, T;
-  int block;
-  const DecodePlan* pl;
-  float scale;
-  int32_t* indices;
-  float *part_acc, *part_ml, *out;
-  unsigned* tickets;
-  hipStream_t s;
-};
-
 template <typename TE, int NT, int ITEMS, int HC>
-hipError_t launch_one(const TE* q, const TE* K, const TE* V, const LaunchArgs& a) {
-  const DecodePlan& pl = *a.pl;
-  const dim3 grid(unsigned(int64_t(pl.sp.n_split) * pl.rows * pl.sp.head_chunks));
-  hipLaunchKernelGGL((selattn_kernel<TE, NT, ITEMS, HC>), grid, dim3(NT), 0, a.s, q, K, V, a.scores, a.ld,
-                     a.tile_hist, int(pl.tiles), int(pl.n_units), a.k_units, a.Hq, a.Hkv, a.T_cap, a.T, a.block,
-                     pl.kv_virtual, pl.sp.chunk, pl.sp.n_split, a.scale, a.indices, a.part_acc, a.part_ml, a.out,
-                     a.tickets);
+hipError_t launch_one(const FusedArgs& a, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((selattn_kernel<TE, NT, ITEMS, HC>), grid, dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
 template <typename TE, int HC>
-hipError_t dispatch_items(const TE* q, const TE* K, const TE* V, const LaunchArgs& a) {
-  const int64_t n = a.pl->n_units;
-  if (n <= 1024 * 4) return launch_one<TE, 1024, 4, HC>(q, K, V, a);
-  if (n <= 1024 * 8) return launch_one<TE, 1024, 8, HC>(q, K, V, a);
-  if (n <= 1024 * 16) return launch_one<TE, 1024, 16, HC>(q, K, V, a);
-  return launch_one<TE, 1024, 32, HC>(q, K, V, a);
+hipError_t dispatch_items(const FusedArgs& a, dim3 grid, hipStream_t s) {
+  const int n = a.n_units;
+  if (n <= 1024 * 4) return launch_one<TE, 1024, 4, HC>(a, grid, s);
+  if (n <= 1024 * 8) return launch_one<TE, 1024, 8, HC>(a, grid, s);
+  if (n <= 1024 * 16) return launch_one<TE, 1024, 16, HC>(a, grid, s);
+  return launch_one<TE, 1024, 32, HC>(a, grid, s);
 }
 
 template <typename TE>
-hipError_t dispatch(const TE* q, const TE* K, const TE* V, const LaunchArgs& a) {
-  switch (a.pl->sp.head_chunk) {
-    case 4: return dispatch_items<TE, 4>(q, K, V, a);
-    case 2: return dispatch_items<TE, 2>(q, K, V, a);
-    default: return dispatch_items<TE, 1>(q, K, V, a);
+hipError_t dispatch(const FusedArgs& a, int head_chunk, dim3 grid, hipStream_t s) {
+  switch (head_chunk) {
+    case 4: return dispatch_items<TE, 4>(a, grid, s);
+    case 2: return dispatch_items<TE, 2>(a, grid, s);
+    default: return dispatch_items<TE, 1>(a, grid, s);
   }
 }
 
@@ -590,12 +597,38 @@ hipError_t launch_select_attention(const void* q, const void* K, const void* V, 
                                    int64_t ld, const uint16_t* tile_hist, int Hq, int Hkv, int64_t T_cap, int64_t T,
                                    int block, int64_t k_units, float scale, const DecodePlan& pl, int32_t* indices,
                                    float* part_acc, float* part_ml, float* out, unsigned* tickets, hipStream_t s) {
-  const LaunchArgs a{scores, ld, tile_hist, int(k_units), Hq, Hkv, T_cap, T, block, &pl, scale, indices,
-                     part_acc, part_ml, out, tickets, s};
-  if (is_bf16)
-    return dispatch(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(K),
-                    static_cast<const uint16_t*>(V), a);
-  return dispatch(static_cast<const float*>(q), static_cast<const float*>(K), static_cast<const float*>(V), a);
+  FusedArgs a{};
+  a.q = q;
+  a.K = K;
+  a.V = V;
+  a.scores = scores;
+  a.tile_hist = tile_hist;
+  a.indices = indices;
+  a.part_acc = part_acc;
+  a.part_ml = part_ml;
+  a.out = out;
+  a.tickets = tickets;
+  a.ld = ld;
+  a.T_cap = T_cap;
+  a.T = int32_t(T);
+  a.n_units = int32_t(pl.n_units);
+  a.k_units = int32_t(k_units);
+  a.G = Hq / Hkv;
+  a.head_chunks = pl.sp.head_chunks;
+  a.tiles = int32_t(pl.tiles);
+  a.lb = __builtin_ctz(unsigned(block));
+  a.kv_virtual = int32_t(pl.kv_virtual);
+  a.chunk = int32_t(pl.sp.chunk);
+  a.n_split = pl.sp.n_split;
+  a.scale = scale;
+  // XCD-grouped layout when it fits the grid limits, else (n_rc, n_split, 1):
+  // the kernel's rc = z * gridDim.x + x covers both.
+  const unsigned n_rc = unsigned(pl.rows * pl.sp.head_chunks);
+  const bool grouped = n_rc % kXcds == 0 && n_rc / kXcds <= 65535u;
+  const dim3 grid = grouped ? dim3(unsigned(kXcds), unsigned(pl.sp.n_split), n_rc / kXcds)
+                            : dim3(n_rc, unsigned(pl.sp.n_split), 1u);
+  if (is_bf16) return dispatch<uint16_t>(a, pl.sp.head_chunk, grid, s);
+  return dispatch<float>(a, pl.sp.head_chunk, grid, s);
 }
 
 }  // namespace ds

@@ -82,6 +82,11 @@ def test_other_entry_points_validate_first():
     assert "t_begin" in L.ds_last_error()
     assert lib.ds_build_label_cache(FAKE, L.DS_DTYPE_BF16, 1, 1, 100, 96, FAKE, 16, 0, 1, FAKE, None) \
         == L.DS_ERR_UNSUPPORTED
+    assert lib.ds_build_label_cache(FAKE, L.DS_DTYPE_BF16, 1, 1, 1 << 31, 128, FAKE, 16, 0, 1, FAKE, None) \
+        == L.DS_ERR_UNSUPPORTED
+    assert "T_cap" in L.ds_last_error()
+    assert lib.ds_build_label_cache(FAKE, L.DS_DTYPE_BF16, 300, 300, 100, 128, FAKE, 16, 0, 1, FAKE, None) \
+        == L.DS_ERR_UNSUPPORTED
     assert lib.ds_topk_select(FAKE, 4, 100, 100, 101, FAKE, None) == L.DS_ERR_INVALID_ARGUMENT
     assert lib.ds_topk_select(FAKE, 4, 100, 50, 10, FAKE, None) == L.DS_ERR_INVALID_ARGUMENT
     assert lib.ds_label_scores(FAKE, FAKE, FAKE, 16, L.DS_DTYPE_F32, 1, 1, 1, 128, 1024, 1024, 1, FAKE, 1022,
