@@ -4,7 +4,7 @@
 
 Every HIP source is compiled with hipcc for gfx950 only; the CPU calibration
 file with g++.  Packed-fp32 instruction selection is disabled for all device
-code.  Objects go to long_context_sparse_ds_amd/_build/, the shared library
+code, and kernel arguments are preloaded into SGPRs where supported.  Objects go to long_context_sparse_ds_amd/_build/, the shared library
 next to this file.
 """
 from __future__ import annotations
@@ -44,8 +44,11 @@ def _run(cmd, verbose):
 
 
 def hip_flags():
+    # Kernel arguments: the first 14 dwords are preloaded into SGPRs at wave
+    # launch where the firmware supports it (the code keeps a fallback path).
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-munsafe-fp-atomics",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-kernarg-preload-count=16",
             "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 

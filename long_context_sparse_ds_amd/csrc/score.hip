@@ -70,24 +70,23 @@ __device__ __forceinline__ float append_row(const TE* __restrict__ Krow, TE* __r
   return float(a);
 }
 
+// The arguments the first loads need come first: the first 14 dwords are
+// preloaded into SGPRs at wave launch where the firmware supports it, so the
+// label stream starts without a kernel-argument round trip.
 template <typename TE, int R>
 __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ q, TE* __restrict__ label,
-                                                         const TE* __restrict__ Kc, const int32_t* __restrict__ ch,
-                                                         int r, int Hq, int Hkv, int64_t T_cap, int64_t T,
-                                                         int64_t t_append, int block, float* __restrict__ scores,
+                                                         const int32_t* __restrict__ ch, int64_t T_cap, int T,
+                                                         int t_append, int G, int Hkv, int r, int block,
+                                                         const TE* __restrict__ Kc, float* __restrict__ scores,
                                                          int64_t ld, uint16_t* __restrict__ tile_hist,
                                                          unsigned* __restrict__ tickets, int tickets_per_row) {
   // 32-bit index math throughout (T < 2^31 is checked on the host); 64-bit
-  // only for element offsets.
-  // Grid (tiles, Hkv, B): no division to find the row.
+  // only for element offsets.  Grid (tiles, Hkv, B): no division to find the row.
   const uint32_t g = blockIdx.y, b = blockIdx.z;
   const uint32_t row = b * uint32_t(Hkv) + g;
-  if (tickets != nullptr && blockIdx.x == 0)
-    for (int i = threadIdx.x; i < tickets_per_row; i += kThreads) tickets[int64_t(row) * tickets_per_row + i] = 0u;
   TE* L = label + int64_t(row) * T_cap * r;
   const int t0 = int(blockIdx.x) * kTile + int(threadIdx.x);
-  const int Ti = int(T), ta = int(t_append);
-  const int G = int(uint32_t(Hq) / uint32_t(Hkv));
+  const int Ti = T, ta = t_append;
   constexpr int NV = R > 0 ? R * int(sizeof(TE)) / 16 : 1;
   // Requests in the order they are needed: the group's q values for every
   // channel (up to 8 heads at a time) and the channel table first, since they
@@ -98,34 +97,34 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
   __shared__ int sch[kHeadDim];
   __shared__ uint32_t h[kHistBins];
   static_assert(kThreads >= kHeadDim, "one thread per channel");
+  // All loads below are unconditional, with clamped indices and masked values:
+  // conditional loads leave the compiler unable to count the loads in flight,
+  // and it then waits for all of them at the first use of any.
   constexpr int kQB = 8;
+  const int ql = threadIdx.x < kHeadDim ? int(threadIdx.x) : 0;
+  const TE* qg = q + int64_t(row) * G * kHeadDim + ql;
   float qv[kQB];
-  const TE* qg = q + int64_t(row) * G * kHeadDim + threadIdx.x;
-  if (threadIdx.x < kHeadDim) {
 #pragma unroll
-    for (int h8 = 0; h8 < kQB; ++h8) qv[h8] = h8 < G ? elem_to_f32(qg[int64_t(h8) * kHeadDim]) : 0.f;
-  }
-  int cj = 0;
-  if (threadIdx.x < r) cj = ch[g * r + threadIdx.x];
+  for (int h8 = 0; h8 < kQB; ++h8) qv[h8] = elem_to_f32(qg[int64_t(h8 < G ? h8 : 0) * kHeadDim]);
+  double qrest = 0.0;   // heads past the first 8 (rare), fetched before the label rows
+  for (int h = kQB; h < G; ++h) qrest += double(elem_to_f32(qg[int64_t(h) * kHeadDim]));
+  const int cj = ch[g * r + (int(threadIdx.x) < r ? int(threadIdx.x) : 0)];
   uint4 raw[kTPT][NV];
   if constexpr (R > 0) {
 #pragma unroll
     for (int i = 0; i < kTPT; ++i) {
       const int t = t0 + i * kThreads;
-      if (t < Ti && t < ta) {
-        const uint4* p = reinterpret_cast<const uint4*>(L + int64_t(t) * R);
+      const uint4* p = reinterpret_cast<const uint4*>(L + int64_t(t < Ti ? t : 0) * R);   // token 0 exists
 #pragma unroll
-        for (int v = 0; v < NV; ++v) raw[i][v] = p[v];
-      }
+      for (int v = 0; v < NV; ++v) raw[i][v] = p[v];
     }
   }
   if (tile_hist != nullptr)
     for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0u;
   if (threadIdx.x < kHeadDim) {
-    double s = 0.0;
+    double s = qrest;
 #pragma unroll
-    for (int h8 = 0; h8 < kQB; ++h8) s += double(qv[h8]);
-    for (int h = kQB; h < G; ++h) s += double(elem_to_f32(qg[int64_t(h) * kHeadDim]));
+    for (int h8 = 0; h8 < kQB; ++h8) s += h8 < G ? double(qv[h8]) : 0.0;
     qall[threadIdx.x] = s;
   }
   __syncthreads();
@@ -199,6 +198,9 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
     uint16_t* dst = tile_hist + (int64_t(row) * gridDim.x + blockIdx.x) * kHistBins + b0;
     *reinterpret_cast<uint2*>(dst) = make_uint2(h[b0] | (h[b0 + 1] << 16), h[b0 + 2] | (h[b0 + 3] << 16));
   }
+  // The row's merge tickets for the fused kernel that follows start at zero.
+  if (tickets != nullptr && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < tickets_per_row; i += kThreads) tickets[int64_t(row) * tickets_per_row + i] = 0u;
 }
 
 template <typename TE>
@@ -208,8 +210,8 @@ hipError_t dispatch(const TE* q, TE* label, const TE* Kc, const int32_t* ch, int
   const dim3 grid(unsigned((T + kTile - 1) / kTile), unsigned(Hkv), unsigned(B));
   const bool vec = (int64_t(r) * sizeof(TE)) % 16 == 0;
 #define DS_SCORE(RR) \
-  hipLaunchKernelGGL((score_kernel<TE, RR>), grid, dim3(kThreads), 0, s, q, label, Kc, ch, r, Hq, Hkv, T_cap, T,     \
-                     t_append, block, scores, ld, tile_hist, tickets, tickets_per_row)
+  hipLaunchKernelGGL((score_kernel<TE, RR>), grid, dim3(kThreads), 0, s, q, label, ch, T_cap, int(T), int(t_append), \
+                     Hq / Hkv, Hkv, r, block, Kc, scores, ld, tile_hist, tickets, tickets_per_row)
   if (vec && r == 8) DS_SCORE(8);
   else if (vec && r == 16) DS_SCORE(16);
   else if (vec && r == 32) DS_SCORE(32);

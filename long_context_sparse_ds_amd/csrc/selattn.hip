@@ -170,7 +170,8 @@ __device__ __forceinline__ void merge_pairs(float (&m)[HC], float (&l)[HC], floa
 }
 
 // Kernel arguments, with the derived sizes precomputed on the host so the
-// kernel's prologue is a few 32-bit operations.
+// kernel's prologue is a few 32-bit operations (passed to the kernel as
+// separate scalars).
 struct FusedArgs {
   const void* q;
   const void* K;
@@ -189,8 +190,38 @@ struct FusedArgs {
   float scale;
 };
 
+// Scalar arguments, those of the first loads first: the first 14 dwords are
+// preloaded into SGPRs at wave launch where the firmware supports it.
 template <typename TE, int NT, int ITEMS, int HC>
-__global__ __launch_bounds__(NT) void selattn_kernel(const FusedArgs a) {
+__global__ __launch_bounds__(NT) void selattn_kernel(
+    const void* q_, const float* scores_, const uint16_t* tile_hist_, int64_t ld_, int32_t G_,
+    int32_t head_chunks_, int32_t n_units_, int32_t tiles_, int32_t k_units_, int32_t lb_, const void* K_,
+    const void* V_, int32_t* indices_, float* part_acc_, float* part_ml_, float* out_, unsigned* tickets_,
+    int64_t T_cap_, int32_t T_, int32_t kv_virtual_, int32_t chunk_, int32_t n_split_, float scale_) {
+  FusedArgs a;
+  a.q = q_;
+  a.K = K_;
+  a.V = V_;
+  a.scores = scores_;
+  a.tile_hist = tile_hist_;
+  a.indices = indices_;
+  a.part_acc = part_acc_;
+  a.part_ml = part_ml_;
+  a.out = out_;
+  a.tickets = tickets_;
+  a.ld = ld_;
+  a.T_cap = T_cap_;
+  a.T = T_;
+  a.n_units = n_units_;
+  a.k_units = k_units_;
+  a.G = G_;
+  a.head_chunks = head_chunks_;
+  a.tiles = tiles_;
+  a.lb = lb_;
+  a.kv_virtual = kv_virtual_;
+  a.chunk = chunk_;
+  a.n_split = n_split_;
+  a.scale = scale_;
   using LN = Lanes<TE, NT>;
   constexpr int NW = LN::NW, EPL = LN::EPL, LPT = LN::LPT, GPW = LN::GPW, NG = LN::NG, KU = LN::KU;
   constexpr int BPT1 = 2048 / NT, BPT2 = 1024 / NT;
@@ -205,7 +236,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(const FusedArgs a) {
   // histograms are fetched into that XCD's L2 once and shared.  No division:
   // rc = 8 * z + x; queries of the row are heads row * G + [0, G).
   const uint32_t split = blockIdx.y;
-  const uint32_t rc = blockIdx.z * gridDim.x + blockIdx.x;
+  const uint32_t rc = blockIdx.z * kXcds + blockIdx.x;   // (n_rc, n_split, 1) layout: z = 0
   const uint32_t hcs = uint32_t(a.head_chunks);
   const uint32_t row = hcs == 1 ? rc : rc / hcs;
   const uint32_t hchunk = rc - row * hcs;
@@ -251,15 +282,17 @@ __global__ __launch_bounds__(NT) void selattn_kernel(const FusedArgs a) {
   if (a.tile_hist != nullptr) {
     const uint32_t* th = reinterpret_cast<const uint32_t*>(a.tile_hist + int64_t(row) * tiles * kHistBins) +
                          (kHistBins - BPT1 * (tid + 1)) / 2;
+    // Every load is issued unconditionally (tile index clamped, value masked):
+    // a load inside a branch makes the compiler wait for it at the join.
     uint32_t w[kMaxHistTiles][BPT1 / 2];
 #pragma unroll
     for (int t = 0; t < int(kMaxHistTiles); ++t)
 #pragma unroll
-      for (int i = 0; i < BPT1 / 2; ++i) w[t][i] = t < tiles ? th[t * (kHistBins / 2) + i] : 0u;
+      for (int i = 0; i < BPT1 / 2; ++i) w[t][i] = th[(t < tiles ? t : 0) * (kHistBins / 2) + i];
 #pragma unroll
     for (int t = 0; t < int(kMaxHistTiles); ++t)
 #pragma unroll
-      for (int i = 0; i < BPT1 / 2; ++i) hw[i] += w[t][i];
+      for (int i = 0; i < BPT1 / 2; ++i) hw[i] += t < tiles ? w[t][i] : 0u;
   }
 
   // The scores go to LDS as well, for the candidate passes' indexed reads.
@@ -409,30 +442,27 @@ __global__ __launch_bounds__(NT) void selattn_kernel(const FusedArgs a) {
   const TE* Kr = K + int64_t(row) * a.T_cap * kHeadDim + sub * EPL;
   const TE* Vr = V + int64_t(row) * a.T_cap * kHeadDim + sub * EPL;
   for (int base = p_begin; base < p_end; base += NG * KU) {
+    // Loads are unconditional: a position past the split or an invalid entry
+    // reads token 0 of the row (which exists) and is masked out of the
+    // softmax; a load inside a branch would make the compiler wait for it
+    // where the branches join.
     int64_t tok[KU];
     bool ok[KU];
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
       const int p = base + gid * KU + u;
-      ok[u] = p < p_end;
-      tok[u] = 0;
-      if (ok[u]) {
-        const int rel = p - p_begin;
-        const int unit = sm.u.a.sel[rel >> lb];
-        tok[u] = (int64_t(unit) << lb) + (rel & (block - 1));
-        ok[u] = unit >= 0 && tok[u] < a.T;   // always true when the kept list is whole
-      }
+      const bool in = p < p_end;
+      const int rel = in ? p - p_begin : 0;
+      const int unit = in ? sm.u.a.sel[rel >> lb] : 0;
+      const int64_t t = (int64_t(unit) << lb) + (rel & (block - 1));
+      ok[u] = in && unit >= 0 && t < a.T;   // always true for p < p_end when the kept list is whole
+      tok[u] = ok[u] ? t : 0;
     }
     uint4 kr[KU], vr[KU];
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
-      if (ok[u]) {
-        kr[u] = *reinterpret_cast<const uint4*>(Kr + tok[u] * kHeadDim);
-        vr[u] = *reinterpret_cast<const uint4*>(Vr + tok[u] * kHeadDim);
-      } else {
-        kr[u] = make_uint4(0u, 0u, 0u, 0u);
-        vr[u] = make_uint4(0u, 0u, 0u, 0u);
-      }
+      kr[u] = *reinterpret_cast<const uint4*>(Kr + tok[u] * kHeadDim);
+      vr[u] = *reinterpret_cast<const uint4*>(Vr + tok[u] * kHeadDim);
     }
     float kf[KU][EPL], vf[KU][EPL];
 #pragma unroll
@@ -536,15 +566,16 @@ __global__ __launch_bounds__(NT) void selattn_kernel(const FusedArgs a) {
     for (int s0 = 0; s0 < n_split; s0 += kBatch) {
       float mb[kBatch], lb[kBatch], ab[kBatch];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int sp = s0 + u;
-        mb[u] = -INFINITY;
-        lb[u] = 0.f;
-        ab[u] = 0.f;
-        if (sp < n_split) {
-          mb[u] = __hip_atomic_load(&ml[2 * sp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          lb[u] = __hip_atomic_load(&ml[2 * sp + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          ab[u] = __hip_atomic_load(&pa[int64_t(sp) * kHeadDim], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int u = 0; u < kBatch; ++u) {   // unconditional loads (index clamped), then masked
+        const bool in = s0 + u < n_split;
+        const int sp = in ? s0 + u : 0;
+        mb[u] = __hip_atomic_load(&ml[2 * sp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lb[u] = __hip_atomic_load(&ml[2 * sp + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ab[u] = __hip_atomic_load(&pa[int64_t(sp) * kHeadDim], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!in) {
+          mb[u] = -INFINITY;
+          lb[u] = 0.f;
+          ab[u] = 0.f;
         }
       }
       float Mb = M;
@@ -569,7 +600,9 @@ __global__ __launch_bounds__(NT) void selattn_kernel(const FusedArgs a) {
 
 template <typename TE, int NT, int ITEMS, int HC>
 hipError_t launch_one(const FusedArgs& a, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((selattn_kernel<TE, NT, ITEMS, HC>), grid, dim3(NT), 0, s, a);
+  hipLaunchKernelGGL((selattn_kernel<TE, NT, ITEMS, HC>), grid, dim3(NT), 0, s, a.q, a.scores, a.tile_hist, a.ld,
+                     a.G, a.head_chunks, a.n_units, a.tiles, a.k_units, a.lb, a.K, a.V, a.indices, a.part_acc,
+                     a.part_ml, a.out, a.tickets, a.T_cap, a.T, a.kv_virtual, a.chunk, a.n_split, a.scale);
   return hipGetLastError();
 }
 
@@ -622,7 +655,7 @@ hipError_t launch_select_attention(const void* q, const void* K, const void* V, 
   a.n_split = pl.sp.n_split;
   a.scale = scale;
   // XCD-grouped layout when it fits the grid limits, else (n_rc, n_split, 1):
-  // the kernel's rc = z * gridDim.x + x covers both.
+  // the kernel's rc = 8 z + x covers both.
   const unsigned n_rc = unsigned(pl.rows * pl.sp.head_chunks);
   const bool grouped = n_rc % kXcds == 0 && n_rc / kXcds <= 65535u;
   const dim3 grid = grouped ? dim3(unsigned(kXcds), unsigned(pl.sp.n_split), n_rc / kXcds)
