@@ -113,22 +113,24 @@ __device__ __forceinline__ void pick_digit(SelSmem<NT>& sm, int nb, int shift, u
 
 // Exclusive prefix sum over the workgroup in thread order with a single
 // barrier; `wsum` (NT/64 words) must not be written again until every thread
-// has returned.
+// has returned.  After the barrier every wavefront reads the NT/64 wave totals
+// (one per lane, at most 16), scans them inside its first 16-lane row with DPP,
+// and takes its own offset and the total with two lane reads.
 template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan1(uint32_t v, uint32_t* wsum, uint32_t& total) {
   constexpr int NW = NT / 64;
+  static_assert(NW <= 16, "wave totals scanned inside one 16-lane row");
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const uint32_t x = wave_inclusive_scan(v);
   if (lane == 63) wsum[wid] = x;
   __syncthreads();
-  uint32_t before = 0u, tot = 0u;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const uint32_t s = wsum[w];
-    before += w < wid ? s : 0u;
-    tot += s;
-  }
-  total = tot;
+  uint32_t w = lane < NW ? wsum[lane] : 0u;
+  w += dpp_u32<0x111>(w);   // row_shr:1
+  w += dpp_u32<0x112>(w);   // row_shr:2
+  w += dpp_u32<0x114>(w);   // row_shr:4
+  w += dpp_u32<0x118>(w);   // row_shr:8: lane i < 16 holds the total of waves 0..i
+  total = uint32_t(__builtin_amdgcn_readlane(int(w), NW - 1));
+  const uint32_t before = wid > 0 ? uint32_t(__builtin_amdgcn_readlane(int(w), wid - 1)) : 0u;
   return before + x - v;
 }
 
