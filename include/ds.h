@@ -146,6 +146,33 @@ ds_status ds_decode_sparse_attn(const void* q, const void* K, const void* V, voi
                                 int32_t* indices, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The decode step for a batch of sequences of unequal lengths (GPU, async): the
+ * incremental decode loop of serving, where the Double Sparsity page's online
+ * stage runs on sequences that each hold their own number of tokens.
+ * Sequence b holds T_b = seq_lens[b] tokens; every step of
+ * ds_decode_sparse_attn is applied to its rows with T replaced by T_b:
+ *   0. its last n_append label rows, [T_b - n_append, T_b), are rebuilt from K;
+ *   1. it scores its T_b tokens (or ceil(T_b / block) blocks);
+ *   2. it keeps k_b = min(k_units, ceil(T_b / block)) units, written ascending
+ *      to indices[b, g, 0 .. k_b); slots k_b .. k_units - 1 are set to -1;
+ *   3. attention runs over its kept tokens below T_b.
+ *   T_max        longest sequence, 1 <= T_max <= T_cap; sizes the workspace
+ *                (ds_decode_workspace_bytes with T = T_max) and the score rows
+ *   seq_lens_dev device int32 [B]; values are clamped to [1, T_max] on the device
+ *   n_append     >= 0 (1 for one decode step; 0 skips the append)
+ *   k_units      1 <= k_units <= ceil(T_max / block)
+ *   other arguments as for ds_decode_sparse_attn (T = T_max).
+ * Errors: as ds_decode_sparse_attn, plus a null or misaligned seq_lens_dev,
+ * n_append < 0, and DS_ERR_UNSUPPORTED when ceil(T_max / block) > 32768.
+ */
+ds_status ds_decode_sparse_attn_ragged(const void* q, const void* K, const void* V, void* label,
+                                       const int32_t* channels_dev, int32_t r, ds_dtype dt, int32_t B, int32_t Hq,
+                                       int32_t Hkv, int32_t d, int64_t T_cap, int64_t T_max,
+                                       const int32_t* seq_lens_dev, int32_t n_append, int32_t block, int64_t k_units,
+                                       float scale, float* out, int32_t* indices, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/*
  * ds_decode_sparse_attn in two phases through one workspace: ds_decode_score
  * runs steps 0 and 1 (label-row append and scoring) and leaves the scores and
  * their per-tile histograms in the workspace; ds_decode_select_attend runs

@@ -38,6 +38,9 @@ _SIGNATURES = {
     "ds_decode_sparse_attn": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                        _c_i32, _c_i64, _c_i64, _c_i64, _c_i32, _c_i64, _c_f32, _c_vp, _c_vp, _c_vp,
                                        _c_size, _c_vp]),
+    "ds_decode_sparse_attn_ragged": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32,
+                                              _c_i32, _c_i32, _c_i64, _c_i64, _c_vp, _c_i32, _c_i32, _c_i64, _c_f32,
+                                              _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
     "ds_decode_score": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64,
                                  _c_i64, _c_i64, _c_i32, _c_i64, _c_vp, _c_size, _c_vp]),
     "ds_decode_select_attend": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i64,
@@ -194,6 +197,34 @@ def ds_decode_sparse_attn(q, K, V, label, channels, T: int, k_units: int, block:
                                        k_units, scale, _dev(out, "out"), _dev(indices, "indices"),
                                        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                                        _stream(stream)))
+    return out, indices
+
+
+def ds_decode_sparse_attn_ragged(q, K, V, label, channels, seq_lens, T_max: int, k_units: int, block: int = 1,
+                                 n_append: int = 1, scale: float = 0.0, out=None, indices=None, workspace=None,
+                                 stream=None):
+    """The decode step for sequences of unequal lengths: seq_lens is a device int32 [B] tensor.
+    Returns (out fp32 [B, Hq, d], indices int32 [B, Hkv, k_units], -1 past each row's kept count)."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    _, Hkv, T_cap, _ = K.shape
+    r = channels.shape[1]
+    dt = _dtype_code(q)
+    if K.dtype != q.dtype or V.dtype != q.dtype or label.dtype != q.dtype:
+        raise ValueError("q, K, V and label must share one dtype")
+    if seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if indices is None:
+        indices = torch.empty((B, Hkv, k_units), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(B, Hq, Hkv, d, T_max, block, k_units, q.device)
+    _check(lib().ds_decode_sparse_attn_ragged(_dev(q, "q"), _dev(K, "K"), _dev(V, "V"), _dev(label, "label"),
+                                              _dev(channels, "channels"), r, dt, B, Hq, Hkv, d, T_cap, T_max,
+                                              _dev(seq_lens, "seq_lens"), n_append, block, k_units, scale,
+                                              _dev(out, "out"), _dev(indices, "indices"), _dev(workspace, "workspace"),
+                                              workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, indices
 
 

@@ -140,7 +140,8 @@ ds_status run_attention(const void* q, const void* K, const void* V, ds_dtype dt
 ds_status run_select_attend(const void* q, const void* K, const void* V, ds_dtype dt, int B, int Hq, int Hkv,
                             int64_t T_cap, int64_t T, int block, int64_t k_units, const float* scores, int64_t ld,
                             const uint16_t* tile_hist, bool tickets_zeroed, float scale, const ds::DecodePlan& pl,
-                            float* out, int32_t* indices, char* ws, hipStream_t s) {
+                            float* out, int32_t* indices, char* ws, hipStream_t s,
+                            const int32_t* seq_lens = nullptr) {
   if (pl.fused) {
     float* part_acc = reinterpret_cast<float*>(ws + pl.off_acc);
     float* part_ml = reinterpret_cast<float*>(ws + pl.off_ml);
@@ -150,7 +151,7 @@ ds_status run_select_attend(const void* q, const void* K, const void* V, ds_dtyp
         return st;
     return hip_status(ds::launch_select_attention(q, K, V, dt == DS_DTYPE_BF16, scores, ld, tile_hist, Hq, Hkv, T_cap,
                                                   T, block, k_units, scale, pl, indices, part_acc, part_ml, out,
-                                                  tickets, s),
+                                                  tickets, seq_lens, s),
                       "select-attention launch");
   }
   if (ds_status st = hip_status(ds::launch_select(scores, pl.rows, pl.n_units, ld, k_units, indices, s),
@@ -212,7 +213,7 @@ ds_status ds_label_scores(const void* q, const void* label, const int32_t* chann
     return fail(DS_ERR_INVALID_ARGUMENT, "misaligned device pointer");
   // No append: the label cache is only read.
   return hip_status(ds::launch_scores(q, const_cast<void*>(label), nullptr, channels_dev, r, dt == DS_DTYPE_BF16, B,
-                                      Hq, Hkv, T_cap, T, T, block, scores, ld, nullptr, nullptr, 0,
+                                      Hq, Hkv, T_cap, T, T, block, scores, ld, nullptr, nullptr, 0, nullptr, 0,
                                       static_cast<hipStream_t>(stream)),
                     "score launch");
 }
@@ -275,23 +276,24 @@ static ds_status check_decode_call(const void* q, const void* K, const void* V, 
 static ds_status decode_score_stage(const void* q, const void* K, void* label, const int32_t* channels_dev, int32_t r,
                                     ds_dtype dt, int32_t B, int32_t Hq, int32_t Hkv, int64_t T_cap, int64_t T,
                                     int64_t t_append, int32_t block, const ds::DecodePlan& pl, char* ws,
-                                    hipStream_t s) {
+                                    hipStream_t s, const int32_t* seq_lens = nullptr, int32_t n_append = 0) {
   float* scores = reinterpret_cast<float*>(ws + pl.off_scores);
   uint16_t* tile_hist = pl.tile_hist ? reinterpret_cast<uint16_t*>(ws + pl.off_tile_hist) : nullptr;
   unsigned* tickets = pl.fused ? reinterpret_cast<unsigned*>(ws + pl.off_tickets) : nullptr;
   return hip_status(ds::launch_scores(q, label, K, channels_dev, r, dt == DS_DTYPE_BF16, B, Hq, Hkv, T_cap, T,
-                                      t_append, block, scores, pl.score_ld, tile_hist, tickets, pl.sp.head_chunks, s),
+                                      t_append, block, scores, pl.score_ld, tile_hist, tickets, pl.sp.head_chunks,
+                                      seq_lens, n_append, s),
                     "score launch");
 }
 
 static ds_status decode_select_stage(const void* q, const void* K, const void* V, ds_dtype dt, int32_t B, int32_t Hq,
                                      int32_t Hkv, int64_t T_cap, int64_t T, int32_t block, int64_t k_units,
                                      float scale, const ds::DecodePlan& pl, float* out, int32_t* indices, char* ws,
-                                     hipStream_t s) {
+                                     hipStream_t s, const int32_t* seq_lens = nullptr) {
   const float* scores = reinterpret_cast<const float*>(ws + pl.off_scores);
   const uint16_t* tile_hist = pl.tile_hist ? reinterpret_cast<const uint16_t*>(ws + pl.off_tile_hist) : nullptr;
   return run_select_attend(q, K, V, dt, B, Hq, Hkv, T_cap, T, block, k_units, scores, pl.score_ld, tile_hist, true,
-                           scale, pl, out, indices, ws, s);
+                           scale, pl, out, indices, ws, s, seq_lens);
 }
 
 ds_status ds_decode_sparse_attn(const void* q, const void* K, const void* V, void* label, const int32_t* channels_dev,
@@ -310,6 +312,33 @@ ds_status ds_decode_sparse_attn(const void* q, const void* K, const void* V, voi
                                         ws, s))
     return st;
   return decode_select_stage(q, K, V, dt, B, Hq, Hkv, T_cap, T, block, k_units, scale, pl, out, indices, ws, s);
+}
+
+ds_status ds_decode_sparse_attn_ragged(const void* q, const void* K, const void* V, void* label,
+                                       const int32_t* channels_dev, int32_t r, ds_dtype dt, int32_t B, int32_t Hq,
+                                       int32_t Hkv, int32_t d, int64_t T_cap, int64_t T_max,
+                                       const int32_t* seq_lens_dev, int32_t n_append, int32_t block, int64_t k_units,
+                                       float scale, float* out, int32_t* indices, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  ds::DecodePlan pl;
+  if (ds_status st = check_decode_call(q, K, V, label, channels_dev, r, dt, B, Hq, Hkv, d, T_cap, T_max, T_max, block,
+                                       k_units, out, indices, workspace, workspace_bytes, true, true, pl))
+    return st;
+  if (!seq_lens_dev) return fail(DS_ERR_INVALID_ARGUMENT, "null pointer argument (seq_lens)");
+  if (!aligned(seq_lens_dev, 4)) return fail(DS_ERR_INVALID_ARGUMENT, "misaligned device pointer (seq_lens)");
+  if (n_append < 0) return fail(DS_ERR_INVALID_ARGUMENT, "n_append = %d must be >= 0", int(n_append));
+  if (!pl.fused)
+    return fail(DS_ERR_UNSUPPORTED, "ragged lengths need ceil(T_max / block) <= %lld units per row (got %lld)",
+                (long long)ds::kFusedMaxUnits, (long long)pl.n_units);
+  if (!(scale > 0.f)) scale = 1.0f / std::sqrt(float(d));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  if (ds_status st = decode_score_stage(q, K, label, channels_dev, r, dt, B, Hq, Hkv, T_cap, T_max, T_max, block, pl,
+                                        ws, s, seq_lens_dev, n_append))
+    return st;
+  return decode_select_stage(q, K, V, dt, B, Hq, Hkv, T_cap, T_max, block, k_units, scale, pl, out, indices, ws, s,
+                             seq_lens_dev);
 }
 
 ds_status ds_decode_score(const void* q, const void* K, void* label, const int32_t* channels_dev, int32_t r,

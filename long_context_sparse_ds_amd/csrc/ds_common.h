@@ -59,9 +59,13 @@ hipError_t launch_pack(const void* K, int is_bf16, int B, int Hkv, int64_t T_cap
 // histogram of the top 11 key bits of each tile's units.  tickets (may be
 // null): tickets_per_row merge tickets per row, zeroed here for the fused
 // kernel that follows.
+// seq_lens (may be null): device int32 [B]; sequence b then holds seq_lens[b]
+// tokens (clamped to [1, T]), its last n_append rows are rebuilt (t_append is
+// ignored), and its scores past its length are written as -inf up to T.
 hipError_t launch_scores(const void* q, void* label, const void* K, const int32_t* ch, int r, int is_bf16, int B,
                          int Hq, int Hkv, int64_t T_cap, int64_t T, int64_t t_append, int block, float* scores,
-                         int64_t ld, uint16_t* tile_hist, unsigned* tickets, int tickets_per_row, hipStream_t s);
+                         int64_t ld, uint16_t* tile_hist, unsigned* tickets, int tickets_per_row,
+                         const int32_t* seq_lens, int n_append, hipStream_t s);
 
 hipError_t launch_select(const float* scores, int64_t rows, int64_t n, int64_t ld, int64_t k, int32_t* idx,
                          hipStream_t s);
@@ -76,10 +80,14 @@ hipError_t launch_attention(const void* q, const void* K, const void* V, int is_
 // Fused selection + attention (rows of at most kFusedMaxUnits units).
 // tile_hist (may be null): the score kernel's per-tile histograms of this call.
 // tickets: rows * sp.head_chunks merge tickets, zero on entry (left zero).
+// seq_lens (may be null): device int32 [B]; sequence b holds seq_lens[b] tokens
+// (clamped to [1, T]), keeps min(k_units, its unit count) units, and its index
+// slots past that are set to -1.
 hipError_t launch_select_attention(const void* q, const void* K, const void* V, int is_bf16, const float* scores,
                                    int64_t ld, const uint16_t* tile_hist, int Hq, int Hkv, int64_t T_cap, int64_t T,
                                    int block, int64_t k_units, float scale, const DecodePlan& pl, int32_t* indices,
-                                   float* part_acc, float* part_ml, float* out, unsigned* tickets, hipStream_t s);
+                                   float* part_acc, float* part_ml, float* out, unsigned* tickets,
+                                   const int32_t* seq_lens, hipStream_t s);
 
 hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t s);
 

@@ -73,20 +73,28 @@ __device__ __forceinline__ float append_row(const TE* __restrict__ Krow, TE* __r
 // The arguments the first loads need come first: the first 14 dwords are
 // preloaded into SGPRs at wave launch where the firmware supports it, so the
 // label stream starts without a kernel-argument round trip.
-template <typename TE, int R>
+// RAGGED: sequence b holds seq_lens[b] tokens (clamped to [1, T]); its last
+// n_append rows are rebuilt, and its scores past its length are written as
+// -inf up to T, so a row's score buffer is always T entries long.
+template <typename TE, int R, bool RAGGED>
 __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ q, TE* __restrict__ label,
                                                          const int32_t* __restrict__ ch, int64_t T_cap, int T,
                                                          int t_append, int G, int Hkv, int r, int block,
                                                          const TE* __restrict__ Kc, float* __restrict__ scores,
                                                          int64_t ld, uint16_t* __restrict__ tile_hist,
-                                                         unsigned* __restrict__ tickets, int tickets_per_row) {
+                                                         unsigned* __restrict__ tickets, int tickets_per_row,
+                                                         const int32_t* __restrict__ seq_lens, int n_append) {
   // 32-bit index math throughout (T < 2^31 is checked on the host); 64-bit
   // only for element offsets.  Grid (tiles, Hkv, B): no division to find the row.
   const uint32_t g = blockIdx.y, b = blockIdx.z;
   const uint32_t row = b * uint32_t(Hkv) + g;
   TE* L = label + int64_t(row) * T_cap * r;
   const int t0 = int(blockIdx.x) * kTile + int(threadIdx.x);
-  const int Ti = T, ta = t_append;
+  int Ti = T, ta = t_append;
+  if constexpr (RAGGED) {
+    Ti = min(max(seq_lens[b], 1), T);
+    ta = max(Ti - n_append, 0);
+  }
   constexpr int NV = R > 0 ? R * int(sizeof(TE)) / 16 : 1;
   // Requests in the order they are needed: the group's q values for every
   // channel (up to 8 heads at a time) and the channel table first, since they
@@ -169,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
       const int t = t0 + i * kThreads;
       uv[i] = u[i];
       has[i] = t < Ti;
-      if (has[i]) out[t] = u[i];
+      if (t < T) out[t] = u[i];   // -inf past this sequence's length
     }
   } else {
     // 64 consecutive tokens per wavefront, 64-aligned: blocks of `block` lanes.
@@ -181,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
       const int t = t0 + i * kThreads;
       uv[i] = v;
       has[i] = t < Ti && (t & (block - 1)) == 0;
-      if (has[i]) out[t >> lb] = v;
+      if (t < T && (t & (block - 1)) == 0) out[t >> lb] = v;   // -inf past this sequence's length
     }
   }
   if (tile_hist != nullptr) {
@@ -203,15 +211,17 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
     for (int i = threadIdx.x; i < tickets_per_row; i += kThreads) tickets[int64_t(row) * tickets_per_row + i] = 0u;
 }
 
-template <typename TE>
-hipError_t dispatch(const TE* q, TE* label, const TE* Kc, const int32_t* ch, int r, int B, int Hq, int Hkv,
-                    int64_t T_cap, int64_t T, int64_t t_append, int block, float* scores, int64_t ld,
-                    uint16_t* tile_hist, unsigned* tickets, int tickets_per_row, hipStream_t s) {
+template <typename TE, bool RAGGED>
+hipError_t dispatch_r(const TE* q, TE* label, const TE* Kc, const int32_t* ch, int r, int B, int Hq, int Hkv,
+                      int64_t T_cap, int64_t T, int64_t t_append, int block, float* scores, int64_t ld,
+                      uint16_t* tile_hist, unsigned* tickets, int tickets_per_row, const int32_t* seq_lens,
+                      int n_append, hipStream_t s) {
   const dim3 grid(unsigned((T + kTile - 1) / kTile), unsigned(Hkv), unsigned(B));
   const bool vec = (int64_t(r) * sizeof(TE)) % 16 == 0;
-#define DS_SCORE(RR) \
-  hipLaunchKernelGGL((score_kernel<TE, RR>), grid, dim3(kThreads), 0, s, q, label, ch, T_cap, int(T), int(t_append), \
-                     Hq / Hkv, Hkv, r, block, Kc, scores, ld, tile_hist, tickets, tickets_per_row)
+#define DS_SCORE(RR)                                                                                               \
+  hipLaunchKernelGGL((score_kernel<TE, RR, RAGGED>), grid, dim3(kThreads), 0, s, q, label, ch, T_cap, int(T),     \
+                     int(t_append), Hq / Hkv, Hkv, r, block, Kc, scores, ld, tile_hist, tickets, tickets_per_row,  \
+                     seq_lens, n_append)
   if (vec && r == 8) DS_SCORE(8);
   else if (vec && r == 16) DS_SCORE(16);
   else if (vec && r == 32) DS_SCORE(32);
@@ -220,16 +230,31 @@ hipError_t dispatch(const TE* q, TE* label, const TE* Kc, const int32_t* ch, int
   return hipGetLastError();
 }
 
+template <typename TE>
+hipError_t dispatch(const TE* q, TE* label, const TE* Kc, const int32_t* ch, int r, int B, int Hq, int Hkv,
+                    int64_t T_cap, int64_t T, int64_t t_append, int block, float* scores, int64_t ld,
+                    uint16_t* tile_hist, unsigned* tickets, int tickets_per_row, const int32_t* seq_lens,
+                    int n_append, hipStream_t s) {
+  if (seq_lens != nullptr)
+    return dispatch_r<TE, true>(q, label, Kc, ch, r, B, Hq, Hkv, T_cap, T, t_append, block, scores, ld, tile_hist,
+                                tickets, tickets_per_row, seq_lens, n_append, s);
+  return dispatch_r<TE, false>(q, label, Kc, ch, r, B, Hq, Hkv, T_cap, T, t_append, block, scores, ld, tile_hist,
+                               tickets, tickets_per_row, nullptr, 0, s);
+}
+
 }  // namespace
 
 hipError_t launch_scores(const void* q, void* label, const void* K, const int32_t* ch, int r, int is_bf16, int B,
                          int Hq, int Hkv, int64_t T_cap, int64_t T, int64_t t_append, int block, float* scores,
-                         int64_t ld, uint16_t* tile_hist, unsigned* tickets, int tickets_per_row, hipStream_t s) {
+                         int64_t ld, uint16_t* tile_hist, unsigned* tickets, int tickets_per_row,
+                         const int32_t* seq_lens, int n_append, hipStream_t s) {
   if (is_bf16)
     return dispatch(static_cast<const uint16_t*>(q), static_cast<uint16_t*>(label), static_cast<const uint16_t*>(K),
-                    ch, r, B, Hq, Hkv, T_cap, T, t_append, block, scores, ld, tile_hist, tickets, tickets_per_row, s);
+                    ch, r, B, Hq, Hkv, T_cap, T, t_append, block, scores, ld, tile_hist, tickets, tickets_per_row,
+                    seq_lens, n_append, s);
   return dispatch(static_cast<const float*>(q), static_cast<float*>(label), static_cast<const float*>(K), ch, r, B,
-                  Hq, Hkv, T_cap, T, t_append, block, scores, ld, tile_hist, tickets, tickets_per_row, s);
+                  Hq, Hkv, T_cap, T, t_append, block, scores, ld, tile_hist, tickets, tickets_per_row, seq_lens,
+                  n_append, s);
 }
 
 }  // namespace ds

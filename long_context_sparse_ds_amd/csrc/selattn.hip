@@ -188,16 +188,21 @@ struct FusedArgs {
   int32_t lb;                  // log2(block)
   int32_t kv_virtual, chunk, n_split;
   float scale;
+  const int32_t* seq_lens;     // null: every sequence holds T tokens
+  int32_t Hkv;
 };
 
 // Scalar arguments, those of the first loads first: the first 14 dwords are
 // preloaded into SGPRs at wave launch where the firmware supports it.
-template <typename TE, int NT, int ITEMS, int HC>
+// RAGGED: sequence b holds seq_lens[b] tokens (clamped to [1, T]) and keeps
+// min(k_units, its unit count) units; index slots past that are set to -1.
+template <typename TE, int NT, int ITEMS, int HC, bool RAGGED>
 __global__ __launch_bounds__(NT) void selattn_kernel(
     const void* q_, const float* scores_, const uint16_t* tile_hist_, int64_t ld_, int32_t G_,
     int32_t head_chunks_, int32_t n_units_, int32_t tiles_, int32_t k_units_, int32_t lb_, const void* K_,
     const void* V_, int32_t* indices_, float* part_acc_, float* part_ml_, float* out_, unsigned* tickets_,
-    int64_t T_cap_, int32_t T_, int32_t kv_virtual_, int32_t chunk_, int32_t n_split_, float scale_) {
+    int64_t T_cap_, int32_t T_, int32_t kv_virtual_, int32_t chunk_, int32_t n_split_, float scale_,
+    const int32_t* seq_lens_, int32_t Hkv_) {
   FusedArgs a;
   a.q = q_;
   a.K = K_;
@@ -222,6 +227,8 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
   a.chunk = chunk_;
   a.n_split = n_split_;
   a.scale = scale_;
+  a.seq_lens = seq_lens_;
+  a.Hkv = Hkv_;
   using LN = Lanes<TE, NT>;
   constexpr int NW = LN::NW, EPL = LN::EPL, LPT = LN::LPT, GPW = LN::GPW, NG = LN::NG, KU = LN::KU;
   constexpr int BPT1 = 2048 / NT, BPT2 = 1024 / NT;
@@ -246,6 +253,13 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
   const TE* __restrict__ V = static_cast<const TE*>(a.V);
   const int n_units = a.n_units, k_units = a.k_units, lb = a.lb, block = 1 << a.lb;
   const int n_split = a.n_split;
+  // This row's token count and kept-unit count.
+  int T_row = a.T, k_row = k_units;
+  if constexpr (RAGGED) {
+    const uint32_t b = row / uint32_t(a.Hkv);
+    T_row = min(max(a.seq_lens[b], 1), a.T);
+    k_row = min(k_units, (T_row + block - 1) >> lb);
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int grp = lane / LPT, sub = lane % LPT;
@@ -327,7 +341,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
   for (int i = 0; i < BPT2; ++i) sm.hist2[i * NT + tid] = 0u;
 
   // Pass 0: the top digit d0 holding the k-th largest key.
-  const uint32_t k = uint32_t(k_units);
+  const uint32_t k = uint32_t(k_row);
   pick_bin<NT, 2048>(c1, k, sm.wsum[0], sm.pick);
   __syncthreads();
   const uint32_t d0 = sm.pick[0];
@@ -402,8 +416,9 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
                                                 sm.wsum[3], tot);
   // Past this barrier (inside the scan) the scores in LDS are dead: sel reuses them.
   const int p_begin = int(split) * a.chunk;   // virtual positions of this split
-  const int p_end = min(p_begin + a.chunk, a.kv_virtual);
-  const int u_lo = p_begin >> lb, u_hi = (p_end + block - 1) >> lb;   // kept-list positions
+  const int p_end = min(min(p_begin + a.chunk, a.kv_virtual), k_row << lb);
+  const int u_lo = p_begin >> lb;
+  const int u_hi = (min(p_begin + a.chunk, a.kv_virtual) + block - 1) >> lb;   // kept-list slots of this split
   {
     uint32_t eq_seen = ex & 0xFFFFu;
     int pos = int(ex >> 16) + int(min(eq_seen, eq_take));
@@ -420,7 +435,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
   __syncthreads();
   if (hchunk == 0) {
     int32_t* ridx = a.indices + int64_t(row) * k_units + u_lo;
-    for (int i = tid; i < u_hi - u_lo; i += NT) ridx[i] = sm.u.a.sel[i];
+    for (int i = tid; i < u_hi - u_lo; i += NT) ridx[i] = u_lo + i < k_row ? sm.u.a.sel[i] : -1;
   }
 
   // Attention over the split's kept rows.
@@ -455,7 +470,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
       const int rel = in ? p - p_begin : 0;
       const int unit = in ? sm.u.a.sel[rel >> lb] : 0;
       const int64_t t = (int64_t(unit) << lb) + (rel & (block - 1));
-      ok[u] = in && unit >= 0 && t < a.T;   // always true for p < p_end when the kept list is whole
+      ok[u] = in && unit >= 0 && t < T_row;   // always true for p < p_end when the kept list is whole
       tok[u] = ok[u] ? t : 0;
     }
     uint4 kr[KU], vr[KU];
@@ -600,9 +615,16 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
 
 template <typename TE, int NT, int ITEMS, int HC>
 hipError_t launch_one(const FusedArgs& a, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((selattn_kernel<TE, NT, ITEMS, HC>), grid, dim3(NT), 0, s, a.q, a.scores, a.tile_hist, a.ld,
-                     a.G, a.head_chunks, a.n_units, a.tiles, a.k_units, a.lb, a.K, a.V, a.indices, a.part_acc,
-                     a.part_ml, a.out, a.tickets, a.T_cap, a.T, a.kv_virtual, a.chunk, a.n_split, a.scale);
+  if (a.seq_lens != nullptr)
+    hipLaunchKernelGGL((selattn_kernel<TE, NT, ITEMS, HC, true>), grid, dim3(NT), 0, s, a.q, a.scores, a.tile_hist,
+                       a.ld, a.G, a.head_chunks, a.n_units, a.tiles, a.k_units, a.lb, a.K, a.V, a.indices, a.part_acc,
+                       a.part_ml, a.out, a.tickets, a.T_cap, a.T, a.kv_virtual, a.chunk, a.n_split, a.scale,
+                       a.seq_lens, a.Hkv);
+  else
+    hipLaunchKernelGGL((selattn_kernel<TE, NT, ITEMS, HC, false>), grid, dim3(NT), 0, s, a.q, a.scores, a.tile_hist,
+                       a.ld, a.G, a.head_chunks, a.n_units, a.tiles, a.k_units, a.lb, a.K, a.V, a.indices, a.part_acc,
+                       a.part_ml, a.out, a.tickets, a.T_cap, a.T, a.kv_virtual, a.chunk, a.n_split, a.scale,
+                       nullptr, a.Hkv);
   return hipGetLastError();
 }
 
@@ -629,8 +651,11 @@ hipError_t dispatch(const FusedArgs& a, int head_chunk, dim3 grid, hipStream_t s
 hipError_t launch_select_attention(const void* q, const void* K, const void* V, int is_bf16, const float* scores,
                                    int64_t ld, const uint16_t* tile_hist, int Hq, int Hkv, int64_t T_cap, int64_t T,
                                    int block, int64_t k_units, float scale, const DecodePlan& pl, int32_t* indices,
-                                   float* part_acc, float* part_ml, float* out, unsigned* tickets, hipStream_t s) {
+                                   float* part_acc, float* part_ml, float* out, unsigned* tickets,
+                                   const int32_t* seq_lens, hipStream_t s) {
   FusedArgs a{};
+  a.seq_lens = seq_lens;
+  a.Hkv = Hkv;
   a.q = q;
   a.K = K;
   a.V = V;

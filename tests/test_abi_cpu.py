@@ -97,6 +97,21 @@ def test_other_entry_points_validate_first():
                                    FAKE, FAKE, FAKE, 10, None) == L.DS_ERR_WORKSPACE_TOO_SMALL
     assert lib.ds_select_attention(FAKE, FAKE, FAKE, L.DS_DTYPE_BF16, 1, 4, 4, 128, 100, 100, 1, 10, FAKE, 98, 0.0,
                                    FAKE, FAKE, FAKE, 1 << 20, None) == L.DS_ERR_INVALID_ARGUMENT
+    # ragged decode: seq_lens, n_append and the fused-path limit are checked on the host
+    ws = L.ds_decode_workspace_bytes(2, 4, 4, 128, 1000, 1, 50)
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, 16, L.DS_DTYPE_BF16, 2, 4, 4, 128, 1000, 1000)
+    assert lib.ds_decode_sparse_attn_ragged(*args, None, 1, 1, 50, 0.0, FAKE, FAKE, FAKE, ws, None) \
+        == L.DS_ERR_INVALID_ARGUMENT
+    assert "seq_lens" in L.ds_last_error()
+    assert lib.ds_decode_sparse_attn_ragged(*args, FAKE, -1, 1, 50, 0.0, FAKE, FAKE, FAKE, ws, None) \
+        == L.DS_ERR_INVALID_ARGUMENT
+    assert "n_append" in L.ds_last_error()
+    big = L.ds_decode_workspace_bytes(1, 1, 1, 128, 40000, 1, 50)
+    assert lib.ds_decode_sparse_attn_ragged(FAKE, FAKE, FAKE, FAKE, FAKE, 16, L.DS_DTYPE_BF16, 1, 1, 1, 128, 40000,
+                                            40000, FAKE, 1, 1, 50, 0.0, FAKE, FAKE, FAKE, big, None) \
+        == L.DS_ERR_UNSUPPORTED
+    assert lib.ds_decode_sparse_attn_ragged(*args, FAKE, 1, 1, 1001, 0.0, FAKE, FAKE, FAKE, ws, None) \
+        == L.DS_ERR_INVALID_ARGUMENT
     # a valid call afterwards clears the message
     L.ds_decode_workspace_bytes(1, 1, 1, 128, 10, 1, 1)
     assert L.ds_last_error() == ""

@@ -500,3 +500,71 @@ def test_decode_integer_scores_exact_ties(T, k, span):
         ref = O.attend(qg, Kg, Vg, want, O.default_scale(d))
         err = float(np.max(np.abs(out[0, g * 2:(g + 1) * 2] - ref)))
         assert err <= OUT_TOL["bf16"], (g, err)
+
+
+RAGGED_CASES = [
+    # (workload shape, per-sequence lengths, rows rebuilt per sequence)
+    (Workload("ragged_mha", "bf16", B=4, Hq=2, Hkv=2, d=128, T=5000, r=16, block=1, k_units=300, seed_base=27000),
+     [5000, 1, 777, 3001], 1),
+    (Workload("ragged_gqa4", "bf16", B=3, Hq=8, Hkv=2, d=128, T=9000, r=8, block=1, k_units=256, seed_base=27100),
+     [9000, 2049, 100], 3),
+    (Workload("ragged_block64", "bf16", B=3, Hq=2, Hkv=2, d=128, T=64 * 40 + 5, r=16, block=64, k_units=8,
+              seed_base=27200), [64 * 40 + 5, 64 * 3 + 1, 10], 2),
+    (Workload("ragged_f32", "f32", B=2, Hq=1, Hkv=1, d=128, T=1500, r=16, block=1, k_units=77, seed_base=27300,
+              fixed_outliers=True), [1500, 64], 1),
+]
+
+
+@pytest.mark.parametrize("w,lens,n_append", RAGGED_CASES, ids=[c[0].name for c in RAGGED_CASES])
+def test_decode_ragged_lengths(w, lens, n_append):
+    """Sequences of unequal lengths in one call: each (sequence, KV head) row is the
+    oracle's decode of its own prefix of T_b tokens keeping min(k, its units) units;
+    index slots past that are -1; the last n_append label rows of every sequence are
+    rebuilt from K (planted garbage is overwritten bit-exactly)."""
+    _say(f"{w.name} lens={lens} n_append={n_append} k={w.k_units}")
+    q, K, V = dsgen.gen_cache(w)
+    qc, kc = dsgen.gen_calib(w)
+    ch = L.ds_calibrate_channels(qc, kc, w.r)
+    qd, Kd, Vd = to_device(q, w.dtype), to_device(K, w.dtype), to_device(V, w.dtype)
+    chd = torch.from_numpy(ch).cuda()
+    label = L.ds_build_label_cache(Kd, chd)
+    raw = label.view(torch.int16) if w.dtype == "bf16" else label.view(torch.int32)
+    for b, Tb in enumerate(lens):
+        raw[b, :, max(Tb - n_append, 0):Tb].fill_(0x3F00)   # garbage where the append must write
+    seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out, idx = L.ds_decode_sparse_attn_ragged(qd, Kd, Vd, label, chd, seq, w.T, w.k_units, w.block,
+                                              n_append=n_append)
+    torch.cuda.synchronize()
+    out, idx = out.cpu().numpy(), idx.cpu().numpy()
+    want_label = L.ds_build_label_cache(Kd, chd)
+    torch.cuda.synchronize()
+    assert torch.equal(label, want_label), "appended label rows not rebuilt exactly"
+    scale = O.default_scale(w.d)
+    for b, Tb in enumerate(lens):
+        n_b = -(-Tb // w.block)
+        k_b = min(w.k_units, n_b)
+        for g in range(w.Hkv):
+            qg, Kf, Vf = unit_inputs(w, q, K, V, b, g)
+            out_ref, kept, scores = O.decode_unit(qg, Kf[:Tb], Vf[:Tb], ch[g], k_b, w.block, scale, Tb)
+            check_index_parity(idx[b, g, :k_b], scores, k_b, what=f"{w.name} b={b} g={g}")
+            assert np.all(idx[b, g, k_b:] == -1), (b, g)
+            ref = O.attend(qg, Kf[:Tb], Vf[:Tb], O.tokens_of(idx[b, g, :k_b], w.block, Tb), scale)
+            err = float(np.max(np.abs(out[b, g * w.G:(g + 1) * w.G] - ref)))
+            assert err <= OUT_TOL[w.dtype], (w.name, b, g, err)
+
+
+def test_decode_ragged_equal_lengths_match_uniform_call():
+    """All sequences at the full length: the ragged call returns exactly the uniform call's results."""
+    w = SMALL[1]   # gqa8_ragged: B=2, Hq=16, Hkv=2, T=5000
+    _say(f"ragged == uniform on {w.name}")
+    q, K, V = dsgen.gen_cache(w)
+    qc, kc = dsgen.gen_calib(w)
+    ch = torch.from_numpy(L.ds_calibrate_channels(qc, kc, w.r)).cuda()
+    qd, Kd, Vd = to_device(q, w.dtype), to_device(K, w.dtype), to_device(V, w.dtype)
+    label = L.ds_build_label_cache(Kd, ch)
+    o1, i1 = L.ds_decode_sparse_attn(qd, Kd, Vd, label, ch, w.T, w.k_units, w.block, t_append=w.T - 1)
+    seq = torch.full((w.B,), w.T, dtype=torch.int32, device="cuda")
+    o2, i2 = L.ds_decode_sparse_attn_ragged(qd, Kd, Vd, label, ch, seq, w.T, w.k_units, w.block, n_append=1)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2)
+    assert torch.equal(o1, o2)
