@@ -6,7 +6,9 @@ A step is one pass of the whole per-step path over one decode batch: one
 ds_decode_sparse_attn call that appends the newest token's label row (row
 T-1, rebuilt from K inside the call), scores every token from the label
 cache, selects the top-k and runs attention over the kept K/V rows (with the
-cross-split merge).  Offline calibration is outside the step.  Steps rotate
+cross-split merge).  A ragged workload (--workload ragged_16k) runs
+ds_decode_sparse_attn_ragged instead: each sequence is scored, selected and
+attended over its own length.  Offline calibration is outside the step.  Steps rotate
 over N independent copies of the cache ("layers") so the per-step working set
 cannot be served from the 256 MB Infinity Cache.  K steps are captured into
 HIP graphs and replayed; the timed region is bracketed by device
@@ -74,19 +76,25 @@ def recorded_traffic(workload: str, stage: str):
     return None
 
 
-def algorithmic_bytes(w: dsgen.Workload) -> dict:
+def algorithmic_bytes(w: dsgen.Workload, lens=None) -> dict:
     """Bytes the method must move per step (score workspace, split partials and
-    the label build are excluded)."""
+    the label build are excluded).  lens: per-sequence lengths of a ragged batch."""
     e = w.elem_bytes
-    k_tok = min(w.k_units * w.block, w.T)
+    if lens is None:
+        lens = [w.T] * w.B
+    tokens = sum(int(t) for t in lens)
+    kept = sum(min(w.k_units * w.block, int(t)) for t in lens)
+    kept_units = sum(min(w.k_units, -(-int(t) // w.block)) for t in lens)
     parts = {
-        "label_scan": w.B * w.Hkv * w.T * w.r * e,
-        "kv_gather": 2 * w.B * w.Hkv * k_tok * w.d * e,
+        "label_scan": w.Hkv * tokens * w.r * e,
+        "kv_gather": 2 * w.Hkv * kept * w.d * e,
         "q": w.B * w.Hq * w.d * e,
         "out": 4 * w.B * w.Hq * w.d,
-        "indices": 4 * w.B * w.Hkv * w.k_units,
+        "indices": 4 * w.Hkv * kept_units,
         "label_append": 2 * w.B * w.Hkv * w.r * e,   # read r channels of K row T-1, write one label row
     }
+    if w.ragged:
+        parts["seq_lens"] = 4 * w.B
     parts["step"] = sum(parts.values())
     return parts
 
@@ -119,16 +127,27 @@ def _oracle_task(i):
     return i
 
 
-def cpu_baseline(w, q, K, V, ch, seconds: float):
+def cpu_baseline(w, q, K, V, ch, seconds: float, lens):
     """Wall time of the oracle's decode step on the host cores, over a bounded sample."""
     global _ORACLE_UNITS
     import multiprocessing as mp
     units = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
-    # A sample of whole units; at most 64 units (about 2 GB of float64 inputs at T=16K).
-    sample = units[:64]
+    # A sample of whole units; at most 64 units (about 2 GB of float64 inputs at T=16K).  A ragged batch
+    # samples the same number of heads from every sequence, so the sample's mean unit stands for the batch's.
+    if w.ragged:
+        per = max(1, min(w.Hkv, 64 // w.B))
+        sample = [(b, g) for b in range(w.B) for g in range(per)]
+    else:
+        sample = units[:64]
     G = w.G
-    _ORACLE_UNITS = [(dsgen.to_f64(q[b, g * G:(g + 1) * G], w.dtype), dsgen.to_f64(K[b, g, :w.T], w.dtype),
-                      dsgen.to_f64(V[b, g, :w.T], w.dtype), ch[g], w.k_units, w.block, w.T) for b, g in sample]
+
+    def unit(b, g):
+        Tb = int(lens[b])
+        k_b = min(w.k_units, -(-Tb // w.block))
+        return (dsgen.to_f64(q[b, g * G:(g + 1) * G], w.dtype), dsgen.to_f64(K[b, g, :Tb], w.dtype),
+                dsgen.to_f64(V[b, g, :Tb], w.dtype), ch[g], k_b, w.block, Tb)
+
+    _ORACLE_UNITS = [unit(b, g) for b, g in sample]
     cores = max(1, min(16, len(os.sched_getaffinity(0)), len(sample)))
     ctx = mp.get_context("fork")
     with ctx.Pool(cores, initializer=_oracle_init) as pool:
@@ -154,7 +173,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=640)
     ap.add_argument("--warmup", type=int, default=64)
-    ap.add_argument("--workload", default=dsgen.HEADLINE, choices=dsgen.WORKLOAD_ORDER)
+    ap.add_argument("--workload", default=dsgen.HEADLINE, choices=dsgen.WORKLOAD_ORDER + dsgen.RAGGED_ORDER)
     ap.add_argument("--instances", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -187,9 +206,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = dsgen.get(args.workload)
-    ab = algorithmic_bytes(w)
+    lens = dsgen.seq_lengths(w)
+    ab = algorithmic_bytes(w, lens)
     n_inst = args.instances or default_instances(w)
-    log(f"workload {w.name}: {w}")
+    log(f"workload {w.name}: {w}" + (f", lengths {lens.tolist()}" if w.ragged else ""))
     log(f"algorithmic bytes/step {ab['step']}, instances {n_inst}")
 
     t0 = time.perf_counter()
@@ -205,6 +225,7 @@ def main():
 
     q0, K0, V0 = up(q), up(K), up(V)
     chd = torch.from_numpy(ch).to(dev)
+    seq = torch.from_numpy(lens).to(dev)
     # full label build, timed on its own (prefill cost, not part of the step)
     lab0 = L.ds_build_label_cache(K0, chd)
     torch.cuda.synchronize()
@@ -231,8 +252,13 @@ def main():
 
     def step(i):
         it = inst[i % n_inst]
-        L.ds_decode_sparse_attn(it["q"], it["K"], it["V"], it["label"], chd, w.T, w.k_units, w.block,
-                                out=it["out"], indices=it["idx"], workspace=it["ws"], t_append=w.T - 1)
+        if w.ragged:
+            L.ds_decode_sparse_attn_ragged(it["q"], it["K"], it["V"], it["label"], chd, seq, w.T, w.k_units,
+                                           w.block, n_append=1, out=it["out"], indices=it["idx"],
+                                           workspace=it["ws"])
+        else:
+            L.ds_decode_sparse_attn(it["q"], it["K"], it["V"], it["label"], chd, w.T, w.k_units, w.block,
+                                    out=it["out"], indices=it["idx"], workspace=it["ws"], t_append=w.T - 1)
 
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
@@ -296,13 +322,21 @@ def main():
 
     def st_decode_score(i):
         it = inst[i % n_inst]
-        L.ds_decode_score(it["q"], it["K"], it["label"], chd, w.T, w.k_units, w.block, workspace=it["ws"],
-                          t_append=w.T - 1)
+        if w.ragged:
+            L.ds_decode_score_ragged(it["q"], it["K"], it["label"], chd, seq, w.T, w.k_units, w.block, n_append=1,
+                                     workspace=it["ws"])
+        else:
+            L.ds_decode_score(it["q"], it["K"], it["label"], chd, w.T, w.k_units, w.block, workspace=it["ws"],
+                              t_append=w.T - 1)
 
     def st_decode_select_attend(i):
         it = inst[i % n_inst]
-        L.ds_decode_select_attend(it["q"], it["K"], it["V"], w.T, w.k_units, it["ws"], w.block, out=it["out"],
-                                  indices=it["idx"])
+        if w.ragged:
+            L.ds_decode_select_attend_ragged(it["q"], it["K"], it["V"], seq, w.T, w.k_units, it["ws"], w.block,
+                                             out=it["out"], indices=it["idx"])
+        else:
+            L.ds_decode_select_attend(it["q"], it["K"], it["V"], w.T, w.k_units, it["ws"], w.block,
+                                      out=it["out"], indices=it["idx"])
 
     def st_select(i):
         it = inst[i % n_inst]
@@ -314,10 +348,13 @@ def main():
                                       workspace=it["ws"])
 
     kernel_us = {}
-    # The decode step's two phases (its own kernels), then isolated stages for reference.
-    for name, fn in (("decode_score", st_decode_score), ("decode_select_attend", st_decode_select_attend),
-                     ("label_append", st_append), ("scores", st_scores), ("select", st_select),
-                     ("attention_from_indices", st_attn)):
+    # The decode step's two phases (its own kernels), then isolated stages for reference
+    # (uniform-length stages, so not for a ragged batch).
+    stages = [("decode_score", st_decode_score), ("decode_select_attend", st_decode_select_attend)]
+    if not w.ragged:
+        stages += [("label_append", st_append), ("scores", st_scores), ("select", st_select),
+                   ("attention_from_indices", st_attn)]
+    for name, fn in stages:
         g = capture(n_inst, fn)
         with torch.cuda.stream(stream):
             g.replay()
@@ -332,8 +369,8 @@ def main():
     log("per-stage us: " + ", ".join(f"{k}={v:.2f}" for k, v in kernel_us.items()))
 
     stage_bytes = {
-        "decode_score": ab["label_scan"] + ab["q"] + ab["label_append"],
-        "decode_select_attend": ab["kv_gather"] + ab["q"] + ab["indices"] + ab["out"],
+        "decode_score": ab["label_scan"] + ab["q"] + ab["label_append"] + ab.get("seq_lens", 0),
+        "decode_select_attend": ab["kv_gather"] + ab["q"] + ab["indices"] + ab["out"] + ab.get("seq_lens", 0),
         "label_append": ab["label_append"],
         "scores": ab["label_scan"] + ab["q"],
         "select": ab["indices"],
@@ -359,7 +396,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "T": w.T, "r": w.r,
                    "block": w.block, "k_units": w.k_units, "instances": n_inst, "launch": "hip graph replay",
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", **({"seq_lens": lens.tolist()} if w.ragged else {})},
         "us_per_step": round(us_step, 3),
         "us_per_step_eager": round(us_step_eager, 3),
         "algorithmic_bytes_per_step": ab["step"],
@@ -374,7 +411,7 @@ def main():
 
     if not args.no_cpu and args.cpu_seconds > 0:
         q, K, V = dsgen.gen_cache(w)
-        cb = cpu_baseline(w, q, K, V, ch, args.cpu_seconds)
+        cb = cpu_baseline(w, q, K, V, ch, args.cpu_seconds, lens)
         cpu_us = cb["step_s"] * 1e6
         result["cpu_baseline"] = {
             "value": round(ab["step"] / cb["step_s"] / 1e9, 4), "unit": "GB/s", "us_per_step": round(cpu_us, 1),

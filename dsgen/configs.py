@@ -35,6 +35,7 @@ class Workload:
     fixed_outliers: bool = False   # True: channels 0..n_outliers-1 in every head
     T_cap: int = 0      # allocated cache length (0 means T)
     n_calib: int = 256  # calibration queries per query head and keys per KV head
+    ragged: bool = False   # True: sequence lengths drawn per sequence in [T // 16, T] (T is the longest)
 
     @property
     def G(self) -> int:
@@ -77,6 +78,16 @@ WORKLOADS = {
 
 WORKLOAD_ORDER = ["tiny_f32", "llama7b_16k", "batched_32k", "gqa70b_128k", "block64_256k"]
 
+# A decode batch of sequences of unequal lengths (a serving batch): the Llama-2-7B
+# shape of llama7b_16k, eight sequences whose lengths are drawn uniformly from
+# [1024, 16384] (gen.seq_lengths), the first one at the full 16384.
+RAGGED_WORKLOADS = {
+    "ragged_16k": Workload("ragged_16k", "bf16", B=8, Hq=32, Hkv=32, d=128, T=16384, r=16, block=1, k_units=1024,
+                           seed_base=6000, ragged=True),
+}
+WORKLOADS.update(RAGGED_WORKLOADS)
+RAGGED_ORDER = ["ragged_16k"]
+
 # The decode benchmark's headline workload: T=16K, 32 heads, bf16.
 HEADLINE = "llama7b_16k"
 
@@ -97,3 +108,7 @@ def unit_seed(w: Workload, b: int, g: int) -> int:
 
 def calib_seed(w: Workload) -> int:
     return w.seed_base + 17
+
+
+def lengths_seed(w: Workload) -> int:
+    return w.seed_base + 29

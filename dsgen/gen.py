@@ -13,6 +13,10 @@ Recipe (shared by the HIP path's tests and benchmark and by the oracle's tests):
   bf16 tensors travel as their raw uint16 bit patterns.
 * The offline calibration set is n_calib queries per query head and n_calib
   keys per KV head, drawn the same way from a separate seed, kept in float32.
+* Ragged batches draw each sequence's length uniformly from [T // 16, T] on
+  their own seed, with sequence 0 at the full T; the cache holds T valid rows
+  for every sequence, so rows past a sequence's length are ordinary data that
+  a kernel must not use.
 * Rows between T and T_cap are filled with NaN, so a kernel that reads past the
   valid tokens poisons its output.
 
@@ -25,7 +29,7 @@ import os
 
 import numpy as np
 
-from .configs import Workload, calib_seed, model_seed, unit_seed
+from .configs import Workload, calib_seed, lengths_seed, model_seed, unit_seed
 
 BF16_NAN = np.uint16(0x7FC0)
 
@@ -131,3 +135,13 @@ def gen_calib(w: Workload):
         for h in range(g * w.G, (g + 1) * w.G):
             qc[:, h, ch] *= s
     return qc, kc
+
+
+def seq_lengths(w: Workload) -> np.ndarray:
+    """int32 [B] lengths of a ragged batch: uniform in [T // 16, T], sequence 0 at T."""
+    if not w.ragged:
+        return np.full(w.B, w.T, dtype=np.int32)
+    rng = np.random.Generator(np.random.PCG64(lengths_seed(w)))
+    lens = rng.integers(max(1, w.T // 16), w.T, size=w.B, endpoint=True).astype(np.int32)
+    lens[0] = w.T
+    return lens

@@ -192,6 +192,25 @@ ds_status ds_decode_select_attend(const void* q, const void* K, const void* V, d
                                   void* stream);
 
 /*
+ * ds_decode_sparse_attn_ragged in the same two phases: ds_decode_score_ragged
+ * runs its steps 0 and 1, ds_decode_select_attend_ragged its steps 2 and 3.
+ * Issued back to back on one stream with the same shape, seq_lens and
+ * workspace, they launch exactly the kernels of ds_decode_sparse_attn_ragged
+ * and give the same results.  Arguments and errors as for that call; the
+ * select phase reads seq_lens again, so it must not change in between.
+ */
+ds_status ds_decode_score_ragged(const void* q, const void* K, void* label, const int32_t* channels_dev, int32_t r,
+                                 ds_dtype dt, int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t T_cap,
+                                 int64_t T_max, const int32_t* seq_lens_dev, int32_t n_append, int32_t block,
+                                 int64_t k_units, void* workspace, size_t workspace_bytes, void* stream);
+
+ds_status ds_decode_select_attend_ragged(const void* q, const void* K, const void* V, ds_dtype dt, int32_t B,
+                                         int32_t Hq, int32_t Hkv, int32_t d, int64_t T_cap, int64_t T_max,
+                                         const int32_t* seq_lens_dev, int32_t block, int64_t k_units, float scale,
+                                         float* out, int32_t* indices, void* workspace, size_t workspace_bytes,
+                                         void* stream);
+
+/*
  * Stages of the decode step fed from caller buffers, so each can be checked in
  * isolation against independently computed inputs.
  */

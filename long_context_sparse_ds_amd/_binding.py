@@ -45,6 +45,11 @@ _SIGNATURES = {
                                  _c_i64, _c_i64, _c_i32, _c_i64, _c_vp, _c_size, _c_vp]),
     "ds_decode_select_attend": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i64,
                                          _c_i32, _c_i64, _c_f32, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
+    "ds_decode_score_ragged": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                        _c_i64, _c_i64, _c_vp, _c_i32, _c_i32, _c_i64, _c_vp, _c_size, _c_vp]),
+    "ds_decode_select_attend_ragged": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64,
+                                                _c_i64, _c_vp, _c_i32, _c_i64, _c_f32, _c_vp, _c_vp, _c_vp, _c_size,
+                                                _c_vp]),
     "ds_select_attention": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i64,
                                      _c_i32, _c_i64, _c_vp, _c_i64, _c_f32, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
     "ds_label_scores": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i64,
@@ -259,6 +264,49 @@ def ds_decode_select_attend(q, K, V, T: int, k_units: int, workspace, block: int
                                          T_cap, T, block, k_units, scale, _dev(out, "out"), _dev(indices, "indices"),
                                          _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                                          _stream(stream)))
+    return out, indices
+
+
+def _check_seq_lens(seq_lens, B):
+    torch = _torch()
+    if seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+
+
+def ds_decode_score_ragged(q, K, label, channels, seq_lens, T_max: int, k_units: int, block: int = 1,
+                           n_append: int = 1, workspace=None, stream=None):
+    """First phase of ds_decode_sparse_attn_ragged (label-row rebuild and scores into the workspace).
+    Returns workspace."""
+    B, Hq, d = q.shape
+    _, Hkv, T_cap, _ = K.shape
+    r = channels.shape[1]
+    _check_seq_lens(seq_lens, B)
+    if workspace is None:
+        workspace = alloc_workspace(B, Hq, Hkv, d, T_max, block, k_units, q.device)
+    _check(lib().ds_decode_score_ragged(_dev(q, "q"), _dev(K, "K"), _dev(label, "label"), _dev(channels, "channels"),
+                                        r, _dtype_code(q), B, Hq, Hkv, d, T_cap, T_max, _dev(seq_lens, "seq_lens"),
+                                        n_append, block, k_units, _dev(workspace, "workspace"),
+                                        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return workspace
+
+
+def ds_decode_select_attend_ragged(q, K, V, seq_lens, T_max: int, k_units: int, workspace, block: int = 1,
+                                   scale: float = 0.0, out=None, indices=None, stream=None):
+    """Second phase of ds_decode_sparse_attn_ragged, from a workspace ds_decode_score_ragged filled.
+    Returns (out, indices)."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    _, Hkv, T_cap, _ = K.shape
+    _check_seq_lens(seq_lens, B)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if indices is None:
+        indices = torch.empty((B, Hkv, k_units), dtype=torch.int32, device=q.device)
+    _check(lib().ds_decode_select_attend_ragged(_dev(q, "q"), _dev(K, "K"), _dev(V, "V"), _dtype_code(q), B, Hq,
+                                                Hkv, d, T_cap, T_max, _dev(seq_lens, "seq_lens"), block, k_units,
+                                                scale, _dev(out, "out"), _dev(indices, "indices"),
+                                                _dev(workspace, "workspace"),
+                                                workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, indices
 
 

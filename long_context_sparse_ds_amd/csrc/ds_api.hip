@@ -314,6 +314,17 @@ ds_status ds_decode_sparse_attn(const void* q, const void* K, const void* V, voi
   return decode_select_stage(q, K, V, dt, B, Hq, Hkv, T_cap, T, block, k_units, scale, pl, out, indices, ws, s);
 }
 
+// Validation shared by the ragged-length calls, after check_decode_call.
+static ds_status check_ragged(const int32_t* seq_lens_dev, int32_t n_append, const ds::DecodePlan& pl) {
+  if (!seq_lens_dev) return fail(DS_ERR_INVALID_ARGUMENT, "null pointer argument (seq_lens)");
+  if (!aligned(seq_lens_dev, 4)) return fail(DS_ERR_INVALID_ARGUMENT, "misaligned device pointer (seq_lens)");
+  if (n_append < 0) return fail(DS_ERR_INVALID_ARGUMENT, "n_append = %d must be >= 0", int(n_append));
+  if (!pl.fused)
+    return fail(DS_ERR_UNSUPPORTED, "ragged lengths need ceil(T_max / block) <= %lld units per row (got %lld)",
+                (long long)ds::kFusedMaxUnits, (long long)pl.n_units);
+  return DS_OK;
+}
+
 ds_status ds_decode_sparse_attn_ragged(const void* q, const void* K, const void* V, void* label,
                                        const int32_t* channels_dev, int32_t r, ds_dtype dt, int32_t B, int32_t Hq,
                                        int32_t Hkv, int32_t d, int64_t T_cap, int64_t T_max,
@@ -325,12 +336,7 @@ ds_status ds_decode_sparse_attn_ragged(const void* q, const void* K, const void*
   if (ds_status st = check_decode_call(q, K, V, label, channels_dev, r, dt, B, Hq, Hkv, d, T_cap, T_max, T_max, block,
                                        k_units, out, indices, workspace, workspace_bytes, true, true, pl))
     return st;
-  if (!seq_lens_dev) return fail(DS_ERR_INVALID_ARGUMENT, "null pointer argument (seq_lens)");
-  if (!aligned(seq_lens_dev, 4)) return fail(DS_ERR_INVALID_ARGUMENT, "misaligned device pointer (seq_lens)");
-  if (n_append < 0) return fail(DS_ERR_INVALID_ARGUMENT, "n_append = %d must be >= 0", int(n_append));
-  if (!pl.fused)
-    return fail(DS_ERR_UNSUPPORTED, "ragged lengths need ceil(T_max / block) <= %lld units per row (got %lld)",
-                (long long)ds::kFusedMaxUnits, (long long)pl.n_units);
+  if (ds_status st = check_ragged(seq_lens_dev, n_append, pl)) return st;
   if (!(scale > 0.f)) scale = 1.0f / std::sqrt(float(d));
   const hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
@@ -339,6 +345,36 @@ ds_status ds_decode_sparse_attn_ragged(const void* q, const void* K, const void*
     return st;
   return decode_select_stage(q, K, V, dt, B, Hq, Hkv, T_cap, T_max, block, k_units, scale, pl, out, indices, ws, s,
                              seq_lens_dev);
+}
+
+ds_status ds_decode_score_ragged(const void* q, const void* K, void* label, const int32_t* channels_dev, int32_t r,
+                                 ds_dtype dt, int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t T_cap,
+                                 int64_t T_max, const int32_t* seq_lens_dev, int32_t n_append, int32_t block,
+                                 int64_t k_units, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  ds::DecodePlan pl;
+  if (ds_status st = check_decode_call(q, K, nullptr, label, channels_dev, r, dt, B, Hq, Hkv, d, T_cap, T_max, T_max,
+                                       block, k_units, nullptr, nullptr, workspace, workspace_bytes, true, false, pl))
+    return st;
+  if (ds_status st = check_ragged(seq_lens_dev, n_append, pl)) return st;
+  return decode_score_stage(q, K, label, channels_dev, r, dt, B, Hq, Hkv, T_cap, T_max, T_max, block, pl,
+                            static_cast<char*>(workspace), static_cast<hipStream_t>(stream), seq_lens_dev, n_append);
+}
+
+ds_status ds_decode_select_attend_ragged(const void* q, const void* K, const void* V, ds_dtype dt, int32_t B,
+                                         int32_t Hq, int32_t Hkv, int32_t d, int64_t T_cap, int64_t T_max,
+                                         const int32_t* seq_lens_dev, int32_t block, int64_t k_units, float scale,
+                                         float* out, int32_t* indices, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  g_err.clear();
+  ds::DecodePlan pl;
+  if (ds_status st = check_decode_call(q, K, V, nullptr, nullptr, 0, dt, B, Hq, Hkv, d, T_cap, T_max, T_max, block,
+                                       k_units, out, indices, workspace, workspace_bytes, false, true, pl))
+    return st;
+  if (ds_status st = check_ragged(seq_lens_dev, 0, pl)) return st;
+  if (!(scale > 0.f)) scale = 1.0f / std::sqrt(float(d));
+  return decode_select_stage(q, K, V, dt, B, Hq, Hkv, T_cap, T_max, block, k_units, scale, pl, out, indices,
+                             static_cast<char*>(workspace), static_cast<hipStream_t>(stream), seq_lens_dev);
 }
 
 ds_status ds_decode_score(const void* q, const void* K, void* label, const int32_t* channels_dev, int32_t r,

@@ -112,6 +112,18 @@ def test_other_entry_points_validate_first():
         == L.DS_ERR_UNSUPPORTED
     assert lib.ds_decode_sparse_attn_ragged(*args, FAKE, 1, 1, 1001, 0.0, FAKE, FAKE, FAKE, ws, None) \
         == L.DS_ERR_INVALID_ARGUMENT
+    # the ragged phases validate the same way
+    sargs = (FAKE, FAKE, FAKE, FAKE, 16, L.DS_DTYPE_BF16, 2, 4, 4, 128, 1000, 1000)
+    assert lib.ds_decode_score_ragged(*sargs, None, 1, 1, 50, FAKE, ws, None) == L.DS_ERR_INVALID_ARGUMENT
+    assert lib.ds_decode_score_ragged(*sargs, FAKE, -2, 1, 50, FAKE, ws, None) == L.DS_ERR_INVALID_ARGUMENT
+    assert lib.ds_decode_score_ragged(*sargs, FAKE, 1, 1, 50, FAKE, 10, None) == L.DS_ERR_WORKSPACE_TOO_SMALL
+    aargs = (FAKE, FAKE, FAKE, L.DS_DTYPE_BF16, 2, 4, 4, 128, 1000, 1000)
+    assert lib.ds_decode_select_attend_ragged(*aargs, None, 1, 50, 0.0, FAKE, FAKE, FAKE, ws, None) \
+        == L.DS_ERR_INVALID_ARGUMENT
+    assert lib.ds_decode_select_attend_ragged(FAKE, FAKE, FAKE, L.DS_DTYPE_BF16, 1, 1, 1, 128, 40000, 40000, FAKE, 1,
+                                              50, 0.0, FAKE, FAKE, FAKE, big, None) == L.DS_ERR_UNSUPPORTED
+    assert lib.ds_decode_select_attend_ragged(*aargs, FAKE, 1, 50, 0.0, None, FAKE, FAKE, ws, None) \
+        == L.DS_ERR_INVALID_ARGUMENT
     # a valid call afterwards clears the message
     L.ds_decode_workspace_bytes(1, 1, 1, 128, 10, 1, 1)
     assert L.ds_last_error() == ""

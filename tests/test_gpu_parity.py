@@ -568,3 +568,63 @@ def test_decode_ragged_equal_lengths_match_uniform_call():
     torch.cuda.synchronize()
     assert torch.equal(i1, i2)
     assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("case", [RAGGED_CASES[0], RAGGED_CASES[2]], ids=lambda c: c[0].name)
+def test_decode_ragged_two_phases_match_one_call(case):
+    """ds_decode_score_ragged then ds_decode_select_attend_ragged through one workspace give
+    exactly what ds_decode_sparse_attn_ragged gives (the same kernels, split in two calls)."""
+    w, lens, n_append = case
+    _say(f"ragged two phases on {w.name} lens={lens}")
+    q, K, V = dsgen.gen_cache(w)
+    qc, kc = dsgen.gen_calib(w)
+    ch = torch.from_numpy(L.ds_calibrate_channels(qc, kc, w.r)).cuda()
+    qd, Kd, Vd = to_device(q, w.dtype), to_device(K, w.dtype), to_device(V, w.dtype)
+    seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    lab1 = L.ds_build_label_cache(Kd, ch)
+    lab2 = lab1.clone()
+    o1, i1 = L.ds_decode_sparse_attn_ragged(qd, Kd, Vd, lab1, ch, seq, w.T, w.k_units, w.block, n_append=n_append)
+    ws = L.ds_decode_score_ragged(qd, Kd, lab2, ch, seq, w.T, w.k_units, w.block, n_append=n_append)
+    o2, i2 = L.ds_decode_select_attend_ragged(qd, Kd, Vd, seq, w.T, w.k_units, ws, w.block)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2)
+    assert torch.equal(o1, o2)
+    assert torch.equal(lab1, lab2)
+
+
+@pytest.mark.parametrize("name", dsgen.RAGGED_ORDER)
+def test_decode_ragged_full_size_workload(name):
+    """The ragged benchmark batch at full size, called as the benchmark calls it (one label
+    row rebuilt per sequence): every row's kept set has its sequence's count, ascending and
+    in range, -1 after it; the oracle checks a sample of units, one per sequence."""
+    w = dsgen.get(name)
+    lens = dsgen.seq_lengths(w)
+    _say(f"{w.name} lens={lens.tolist()} k={w.k_units}")
+    q, K, V = dsgen.gen_cache(w)
+    qc, kc = dsgen.gen_calib(w)
+    ch = L.ds_calibrate_channels(qc, kc, w.r)
+    qd, Kd, Vd = to_device(q, w.dtype), to_device(K, w.dtype), to_device(V, w.dtype)
+    chd = torch.from_numpy(ch).cuda()
+    label = L.ds_build_label_cache(Kd, chd)
+    seq = torch.from_numpy(lens).cuda()
+    out, idx = L.ds_decode_sparse_attn_ragged(qd, Kd, Vd, label, chd, seq, w.T, w.k_units, w.block, n_append=1)
+    torch.cuda.synchronize()
+    out, idx = out.cpu().numpy(), idx.cpu().numpy()
+    assert np.all(np.isfinite(out))
+    rng = np.random.default_rng(5)
+    scale = O.default_scale(w.d)
+    for b, Tb in enumerate(lens.tolist()):
+        k_b = min(w.k_units, -(-Tb // w.block))
+        rows = idx[b, :, :k_b]
+        assert np.all(np.diff(rows, axis=1) > 0) and rows.min() >= 0 and rows.max() < -(-Tb // w.block)
+        assert np.all(idx[b, :, k_b:] == -1)
+        g = int(rng.integers(w.Hkv))
+        qg, Kf, Vf = unit_inputs(w, q, K, V, b, g)
+        _, _, scores = O.decode_unit(qg, Kf[:Tb], Vf[:Tb], ch[g], k_b, w.block, scale, Tb)
+        swaps = check_index_parity(idx[b, g, :k_b], scores, k_b, what=f"{w.name} b={b} g={g}")
+        ref = O.attend(qg, Kf[:Tb], Vf[:Tb], O.tokens_of(idx[b, g, :k_b], w.block, Tb), scale)
+        err = float(np.max(np.abs(out[b, g * w.G:(g + 1) * w.G] - ref)))
+        _say(f"{name} unit ({b},{g}) T_b={Tb}: tie swaps {swaps}, max-abs err {err:.3g}")
+        assert err <= OUT_TOL[w.dtype], (w.name, b, g, err)
+    del q, K, V
+    torch.cuda.empty_cache()
