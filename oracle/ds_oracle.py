@@ -26,6 +26,18 @@ Where the pages leave a step open, the reading taken is:
     ascending index order;
   * attention: softmax of q.K / sqrt(d) over the selected tokens only, no
     forced sink or recent tokens, no causal mask (a decode query sees all T).
+
+The threshold rule (Jenga page, core method item 1) is read as follows:
+  * a token's informativeness is the sum over the group's query heads of the
+    head's label score, counting only the heads whose score is positive; with
+    one decode query, the sum over the other queries of the page's definition
+    is that query's score, and the query's own (just appended) key is scored
+    like every other;
+  * a block's informativeness is the maximum over its tokens, as above;
+  * a unit is kept when its informativeness is at least the threshold; when
+    more than k_max units pass, the k_max largest of them are kept (lower
+    index first on ties);
+  * with no unit kept, the attention output is zero.
 """
 from __future__ import annotations
 
@@ -194,3 +206,59 @@ def tokens_of(kept, block, T):
     """Token ids attended for a kept-unit list (identity for block == 1)."""
     kept = np.asarray(kept, dtype=np.int64)
     return kept if block == 1 else blocks_to_tokens(kept, block, T)
+
+
+# -- threshold selection with positive-only head aggregation ----------------
+
+def label_scores_positive(q_group: np.ndarray, L: np.ndarray, ch: np.ndarray) -> np.ndarray:
+    """Informativeness of every token: u[t] = sum_h max(0, sum_j q[h, ch[j]] * L[t, j]).
+
+    Jenga page, core method item 1: per-token informativeness aggregates the
+    attention scores over heads counting only positive ones.  The score of
+    head h is its label-channel approximation (Double Sparsity page,
+    abstract).  q_group: [G, d]; L: [T, r].  Returns float64 [T].
+    """
+    qs = np.asarray(q_group, dtype=np.float64)[:, np.asarray(ch)]    # [G, r]
+    per_head = np.asarray(L, dtype=np.float64) @ qs.T                 # [T, G]
+    return np.maximum(per_head, 0.0).sum(axis=1)
+
+
+def select_threshold(u: np.ndarray, tau: float, k_max: int) -> np.ndarray:
+    """Units whose score is at least tau, ascending; when more than k_max pass,
+    the k_max largest of them, ties to the lower index.
+
+    Jenga page, core method item 1: block informativeness is compared with a
+    layer-specific threshold and the blocks below it are eliminated.  k_max is
+    the capacity of the caller's index buffer.
+    """
+    u = np.asarray(u, dtype=np.float64)
+    if k_max < 1:
+        raise ValueError("k_max out of range")
+    passing = np.flatnonzero(u >= tau)
+    if len(passing) <= k_max:
+        return passing.astype(np.int64)
+    order = passing[np.argsort(-u[passing], kind="stable")]   # passing is ascending: ties keep the lower index
+    return np.sort(order[:k_max]).astype(np.int64)
+
+
+def decode_unit_threshold(q_group, K, V, ch, k_max, tau, block=1, scale=None, T=None):
+    """Decode for one unit with the threshold rule: positive-only head
+    aggregation, block max, keep the units at or above tau (at most k_max),
+    attention over their tokens (zero when none is kept).
+
+    Returns (out [G, d], kept unit ids ascending, scores of the units).
+    """
+    K = np.asarray(K, dtype=np.float64)
+    if T is None:
+        T = K.shape[0]
+    K = K[:T]
+    V = np.asarray(V, dtype=np.float64)[:T]
+    if scale is None:
+        scale = default_scale(K.shape[1])
+    u = label_scores_positive(q_group, label_rows(K, ch), ch)
+    scores = u if block == 1 else block_scores(u, block)
+    kept = select_threshold(scores, tau, k_max)
+    S = tokens_of(kept, block, T)
+    if len(S) == 0:
+        return np.zeros((np.asarray(q_group).shape[0], K.shape[1])), kept, scores
+    return attend(q_group, K, V, S, scale), kept, scores

@@ -194,6 +194,82 @@ def check_golden(ns):
                                    rtol=0, atol=1e-12, err_msg=case["why"])
 
 
+def brute_positive_score(q_group, K, ch, t):
+    return math.fsum(max(0.0, math.fsum(float(q_group[h, c]) * float(K[t, c]) for c in ch))
+                     for h in range(q_group.shape[0]))
+
+
+def brute_threshold_select(u, tau, k):
+    """Units at or above tau; past k of them, the ones fewer than k passing units beat."""
+    passing = [t for t in range(len(u)) if u[t] >= tau]
+    if len(passing) <= k:
+        return passing
+    keep = []
+    for t in passing:
+        beat = sum(1 for s in passing if u[s] > u[t] or (u[s] == u[t] and s < t))
+        if beat < k:
+            keep.append(t)
+    return keep
+
+
+def check_positive_scores_brute(ns, seed=7):
+    rng = np.random.default_rng(seed)
+    G, d, T = 3, 16, 25
+    q = rng.standard_normal((G, d))
+    K = rng.standard_normal((T, d))
+    for ch in (np.arange(d), np.array([0, 5, 6, 11]), np.array([15])):
+        u = ns.label_scores_positive(q, ns.label_rows(K, ch), ch)
+        want = [brute_positive_score(q, K, ch, t) for t in range(T)]
+        np.testing.assert_allclose(u, want, rtol=0, atol=1e-12)
+
+
+def check_threshold_select_brute(ns, seed=8):
+    rng = np.random.default_rng(seed)
+    for n in (1, 2, 17, 40):
+        u = rng.integers(-3, 4, size=n).astype(np.float64)   # many exact ties, and scores equal to tau
+        for tau in (-math.inf, -3.0, -0.5, 0.0, 1.0, 2.5, 3.0, 4.0):
+            for k in sorted({1, n // 3 + 1, n // 2 + 1, n, n + 3}):
+                got = list(ns.select_threshold(u, tau, k))
+                assert got == brute_threshold_select(list(u), tau, k), (n, tau, k, got)
+
+
+def _golden_threshold():
+    with open(os.path.join(HERE, "golden", "hand_worked.json")) as f:
+        gold = json.load(f)
+    dec = gold["decode"]
+    return (gold["threshold"], np.array(dec["K"], dtype=np.float64), np.array(dec["V"], dtype=np.float64),
+            np.array(dec["channels"]), 1 / math.sqrt(dec["d"]))
+
+
+def check_golden_threshold(ns):
+    """The threshold cases, step by step through the namespace's functions."""
+    gold, K, V, ch, scale = _golden_threshold()
+    T = K.shape[0]
+    for case in gold["cases"]:
+        q = np.array(case["q"], dtype=np.float64)
+        u = ns.label_scores_positive(q, ns.label_rows(K, ch), ch)
+        scores = u if case["block"] == 1 else ns.block_scores(u, case["block"])
+        assert list(scores) == case["scores"], case["why"]
+        kept = ns.select_threshold(scores, case["tau"], case["k_max"])
+        assert list(kept) == case["kept"], case["why"]
+        if case["out"] is not None:
+            S = ns.tokens_of(kept, case["block"], T)
+            out = ns.attend(q, K, V, S, scale) if len(S) else np.zeros((q.shape[0], K.shape[1]))
+            np.testing.assert_allclose(out, np.array(case["out"]), rtol=0, atol=1e-12, err_msg=case["why"])
+
+
+def check_golden_threshold_unit(ns):
+    """The same cases through the one-call decode of a unit."""
+    gold, K, V, ch, scale = _golden_threshold()
+    for case in gold["cases"]:
+        q = np.array(case["q"], dtype=np.float64)
+        out, kept, scores = ns.decode_unit_threshold(q, K, V, ch, case["k_max"], case["tau"], case["block"], scale)
+        assert list(kept) == case["kept"] and list(scores) == case["scores"], case["why"]
+        assert np.all(np.isfinite(out)), case["why"]
+        if case["out"] is not None:
+            np.testing.assert_allclose(out, np.array(case["out"]), rtol=0, atol=1e-12, err_msg=case["why"])
+
+
 # ---------------------------------------------------------------- pins
 
 def test_calibration_matches_all_pairs_brute_force():
@@ -335,6 +411,77 @@ def test_decode_unit_on_workload_slice():
     assert np.all(np.isfinite(out))
 
 
+def test_positive_scores_match_exact_brute_force():
+    check_positive_scores_brute(O)
+
+
+def test_positive_scores_bounds_and_special_cases():
+    """u+ is at least the signed group score and at least every single head's clipped score;
+    with one query head it is the clipped signed score; with every head's score of one sign it
+    is the signed score (all positive) or zero (all negative)."""
+    rng = np.random.default_rng(9)
+    G, d, T = 4, 20, 30
+    q = rng.standard_normal((G, d))
+    K = rng.standard_normal((T, d))
+    ch = np.array([1, 2, 3, 8, 13, 19])
+    L = O.label_rows(K, ch)
+    up = O.label_scores_positive(q, L, ch)
+    assert np.all(up >= O.label_scores(q, L, ch) - 1e-12) and np.all(up >= 0)
+    for h in range(G):
+        assert np.all(up >= np.maximum(O.label_scores(q[h:h + 1], L, ch), 0) - 1e-12)
+    np.testing.assert_allclose(O.label_scores_positive(q[:1], L, ch), np.maximum(O.label_scores(q[:1], L, ch), 0),
+                               rtol=0, atol=1e-12)
+    qa, Ka = np.abs(q), np.abs(K)
+    La = O.label_rows(Ka, ch)
+    np.testing.assert_allclose(O.label_scores_positive(qa, La, ch), O.label_scores(qa, La, ch), rtol=0, atol=1e-12)
+    assert np.all(O.label_scores_positive(-qa, La, ch) == 0)
+
+
+def test_threshold_select_matches_brute_force_with_ties():
+    check_threshold_select_brute(O)
+
+
+def test_threshold_select_special_cases():
+    """tau below every score is plain top-k; tau above every score keeps nothing; a cap at or
+    above the unit count keeps exactly the units at or above tau; with no cap, raising tau
+    never adds a unit."""
+    rng = np.random.default_rng(10)
+    u = rng.standard_normal(200)
+    for k in (1, 17, 200):
+        assert list(O.select_threshold(u, -math.inf, k)) == list(O.select_topk(u, k))
+        assert len(O.select_threshold(u, u.max() + 1, k)) == 0
+    for tau in (-1.0, 0.0, 0.7):
+        assert list(O.select_threshold(u, tau, 200)) == list(np.flatnonzero(u >= tau))
+    prev = set(range(200))
+    for tau in np.linspace(-3, 3, 25):
+        cur = set(O.select_threshold(u, tau, 200))
+        assert cur <= prev
+        prev = cur
+
+
+def test_threshold_hand_worked_fixture():
+    check_golden_threshold(O)
+    check_golden_threshold_unit(O)
+
+
+def test_threshold_decode_reduces_to_topk_on_positive_scores():
+    """With tau = -inf the threshold decode is the top-k decode run on the positive-only scores."""
+    rng = np.random.default_rng(11)
+    G, d, T = 4, 32, 300
+    q = rng.standard_normal((G, d))
+    K = rng.standard_normal((T, d))
+    V = rng.standard_normal((T, d))
+    ch = np.array([0, 3, 9, 10, 22, 31])
+    for block, k in ((1, 40), (16, 5)):
+        out, kept, scores = O.decode_unit_threshold(q, K, V, ch, k, -math.inf, block)
+        u = O.label_scores_positive(q, O.label_rows(K, ch), ch)
+        U = u if block == 1 else O.block_scores(u, block)
+        want = O.select_topk(U, k)
+        assert list(kept) == list(want)
+        np.testing.assert_allclose(out, O.attend(q, K, V, O.tokens_of(want, block, T), O.default_scale(d)),
+                                   rtol=0, atol=1e-12)
+
+
 # ---------------------------------------------------------------- planted mistakes
 
 def _mut_calib_sum_not_product(q_cal, k_cal, Hkv, r):
@@ -405,7 +552,70 @@ def _mut_merge_no_rescale(parts):
     return sum(p[2] for p in parts) / l[:, None]
 
 
+def _mut_pos_signed(q_group, L, ch):
+    return O.label_scores(q_group, L, ch)
+
+
+def _mut_pos_clip_after_sum(q_group, L, ch):
+    return np.maximum(O.label_scores(q_group, L, ch), 0.0)
+
+
+def _mut_pos_abs(q_group, L, ch):
+    qs = np.asarray(q_group, np.float64)[:, np.asarray(ch)]
+    return np.abs(np.asarray(L, np.float64) @ qs.T).sum(axis=1)
+
+
+def _mut_thr_strict(u, tau, k_max):
+    u = np.asarray(u, np.float64)
+    p = np.flatnonzero(u > tau)
+    return p if len(p) <= k_max else np.sort(p[np.argsort(-u[p], kind="stable")][:k_max])
+
+
+def _mut_thr_cap_lowest_ids(u, tau, k_max):
+    p = np.flatnonzero(np.asarray(u, np.float64) >= tau)
+    return p[:k_max]
+
+
+def _mut_thr_cap_ties_high(u, tau, k_max):
+    u = np.asarray(u, np.float64)
+    p = np.flatnonzero(u >= tau)
+    if len(p) <= k_max:
+        return p
+    rev = p[::-1]
+    return np.sort(rev[np.argsort(-u[rev], kind="stable")][:k_max])
+
+
+def _mut_thr_no_cap(u, tau, k_max):
+    return np.flatnonzero(np.asarray(u, np.float64) >= tau)
+
+
+def _mut_thr_topk_only(u, tau, k_max):
+    return O.select_topk(u, min(k_max, len(u)))
+
+
+def _mut_unit_empty_nan(q_group, K, V, ch, k_max, tau, block=1, scale=None, T=None):
+    K = np.asarray(K, np.float64)
+    T = K.shape[0] if T is None else T
+    scale = O.default_scale(K.shape[1]) if scale is None else scale
+    u = O.label_scores_positive(q_group, O.label_rows(K[:T], ch), ch)
+    scores = u if block == 1 else O.block_scores(u, block)
+    kept = O.select_threshold(scores, tau, k_max)
+    S = O.tokens_of(kept, block, T)
+    G = np.asarray(q_group).shape[0]
+    out = O.attend(q_group, K[:T], np.asarray(V)[:T], S, scale) if len(S) else np.full((G, K.shape[1]), np.nan)
+    return out, kept, scores
+
+
 MUTANTS = [
+    ("label_scores_positive", _mut_pos_signed, check_positive_scores_brute),
+    ("label_scores_positive", _mut_pos_clip_after_sum, check_positive_scores_brute),
+    ("label_scores_positive", _mut_pos_abs, check_positive_scores_brute),
+    ("select_threshold", _mut_thr_strict, check_threshold_select_brute),
+    ("select_threshold", _mut_thr_cap_lowest_ids, check_threshold_select_brute),
+    ("select_threshold", _mut_thr_cap_ties_high, check_threshold_select_brute),
+    ("select_threshold", _mut_thr_no_cap, check_threshold_select_brute),
+    ("select_threshold", _mut_thr_topk_only, check_threshold_select_brute),
+    ("decode_unit_threshold", _mut_unit_empty_nan, check_golden_threshold_unit),
     ("calibrate_channels", _mut_calib_sum_not_product, check_calibration_brute),
     ("calibrate_channels", _mut_calib_ties_high, check_calibration_ties),
     ("label_rows", _mut_label_wrong_index, check_label_gather),
@@ -437,6 +647,26 @@ GOLDEN_MUTANTS = [
     ("select_topk", _mut_select_smallest),
     ("attend", _mut_attend_transposed),
 ]
+
+
+THRESHOLD_GOLDEN_MUTANTS = [
+    ("label_scores_positive", _mut_pos_signed),
+    ("label_scores_positive", _mut_pos_clip_after_sum),
+    ("label_scores_positive", _mut_pos_abs),
+    ("select_threshold", _mut_thr_strict),
+    ("select_threshold", _mut_thr_cap_lowest_ids),
+    ("select_threshold", _mut_thr_cap_ties_high),
+    ("select_threshold", _mut_thr_no_cap),
+    ("select_threshold", _mut_thr_topk_only),
+    ("block_scores", _mut_block_mean),
+]
+
+
+@pytest.mark.parametrize("fn,mutant", THRESHOLD_GOLDEN_MUTANTS,
+                         ids=[f"{m[0]}:{m[1].__name__}" for m in THRESHOLD_GOLDEN_MUTANTS])
+def test_threshold_fixture_catches_planted_mistake(fn, mutant):
+    with pytest.raises(AssertionError):
+        check_golden_threshold(_ns(**{fn: mutant}))
 
 
 @pytest.mark.parametrize("fn,mutant", GOLDEN_MUTANTS, ids=[f"{m[0]}:{m[1].__name__}" for m in GOLDEN_MUTANTS])
