@@ -8,7 +8,11 @@ T-1, rebuilt from K inside the call), scores every token from the label
 cache, selects the top-k and runs attention over the kept K/V rows (with the
 cross-split merge).  A ragged workload (--workload ragged_16k) runs
 ds_decode_sparse_attn_ragged instead: each sequence is scored, selected and
-attended over its own length.  Offline calibration is outside the step.  Steps rotate
+attended over its own length.  The threshold workload (--workload
+jenga_gqa_32k) runs ds_decode_sparse_attn_threshold: positive-only head
+aggregation, block max, and every block scoring at least tau kept (at most
+k_max); its kept-token count, and so its byte count, comes from the call's own
+counts.  Offline calibration is outside the step.  Steps rotate
 over N independent copies of the cache ("layers") so the per-step working set
 cannot be served from the 256 MB Infinity Cache.  K steps are captured into
 HIP graphs and replayed; the timed region is bracketed by device
@@ -76,25 +80,32 @@ def recorded_traffic(workload: str, stage: str):
     return None
 
 
-def algorithmic_bytes(w: dsgen.Workload, lens=None) -> dict:
+def algorithmic_bytes(w: dsgen.Workload, lens=None, kept=None) -> dict:
     """Bytes the method must move per step (score workspace, split partials and
-    the label build are excluded).  lens: per-sequence lengths of a ragged batch."""
+    the label build are excluded).  lens: per-sequence lengths of a ragged batch.
+    kept: (kept tokens, kept units) summed over the rows, for the threshold rule,
+    whose kept counts depend on the data."""
     e = w.elem_bytes
     if lens is None:
         lens = [w.T] * w.B
     tokens = sum(int(t) for t in lens)
-    kept = sum(min(w.k_units * w.block, int(t)) for t in lens)
-    kept_units = sum(min(w.k_units, -(-int(t) // w.block)) for t in lens)
+    if kept is None:
+        kept_tokens = w.Hkv * sum(min(w.k_units * w.block, int(t)) for t in lens)
+        kept_units = w.Hkv * sum(min(w.k_units, -(-int(t) // w.block)) for t in lens)
+    else:
+        kept_tokens, kept_units = kept
     parts = {
         "label_scan": w.Hkv * tokens * w.r * e,
-        "kv_gather": 2 * w.Hkv * kept * w.d * e,
+        "kv_gather": 2 * kept_tokens * w.d * e,
         "q": w.B * w.Hq * w.d * e,
         "out": 4 * w.B * w.Hq * w.d,
-        "indices": 4 * w.Hkv * kept_units,
+        "indices": 4 * kept_units,
         "label_append": 2 * w.B * w.Hkv * w.r * e,   # read r channels of K row T-1, write one label row
     }
     if w.ragged:
         parts["seq_lens"] = 4 * w.B
+    if w.tau is not None:
+        parts["counts"] = 4 * w.B * w.Hkv
     parts["step"] = sum(parts.values())
     return parts
 
@@ -122,8 +133,11 @@ def _oracle_init():
 
 def _oracle_task(i):
     import oracle as O
-    qg, Kf, Vf, ch, k, block, T = _ORACLE_UNITS[i]
-    O.decode_unit(qg, Kf, Vf, ch, k, block, None, T)
+    qg, Kf, Vf, ch, k, block, T, tau = _ORACLE_UNITS[i]
+    if tau is None:
+        O.decode_unit(qg, Kf, Vf, ch, k, block, None, T)
+    else:
+        O.decode_unit_threshold(qg, Kf, Vf, ch, k, tau, block, None, T)
     return i
 
 
@@ -145,7 +159,7 @@ def cpu_baseline(w, q, K, V, ch, seconds: float, lens):
         Tb = int(lens[b])
         k_b = min(w.k_units, -(-Tb // w.block))
         return (dsgen.to_f64(q[b, g * G:(g + 1) * G], w.dtype), dsgen.to_f64(K[b, g, :Tb], w.dtype),
-                dsgen.to_f64(V[b, g, :Tb], w.dtype), ch[g], k_b, w.block, Tb)
+                dsgen.to_f64(V[b, g, :Tb], w.dtype), ch[g], k_b, w.block, Tb, w.tau)
 
     _ORACLE_UNITS = [unit(b, g) for b, g in sample]
     cores = max(1, min(16, len(os.sched_getaffinity(0)), len(sample)))
@@ -173,7 +187,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=640)
     ap.add_argument("--warmup", type=int, default=64)
-    ap.add_argument("--workload", default=dsgen.HEADLINE, choices=dsgen.WORKLOAD_ORDER + dsgen.RAGGED_ORDER)
+    ap.add_argument("--workload", default=dsgen.HEADLINE, choices=dsgen.WORKLOAD_ORDER + dsgen.RAGGED_ORDER + dsgen.THRESHOLD_ORDER)
     ap.add_argument("--instances", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -245,7 +259,8 @@ def main():
         ws = L.alloc_workspace(w.B, w.Hq, w.Hkv, w.d, w.T, w.block, w.k_units, dev)
         out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
         idx = torch.empty((w.B, w.Hkv, w.k_units), dtype=torch.int32, device=dev)
-        inst.append(dict(q=qi, K=Ki, V=Vi, label=li, ws=ws, out=out, idx=idx))
+        cnt = torch.empty((w.B, w.Hkv), dtype=torch.int32, device=dev)
+        inst.append(dict(q=qi, K=Ki, V=Vi, label=li, ws=ws, out=out, idx=idx, cnt=cnt))
     del q, K, V
     torch.cuda.synchronize()
     log(f"{n_inst} instances resident ({torch.cuda.memory_allocated() / 2 ** 30:.1f} GiB)")
@@ -256,12 +271,31 @@ def main():
             L.ds_decode_sparse_attn_ragged(it["q"], it["K"], it["V"], it["label"], chd, seq, w.T, w.k_units,
                                            w.block, n_append=1, out=it["out"], indices=it["idx"],
                                            workspace=it["ws"])
+        elif w.tau is not None:
+            L.ds_decode_sparse_attn_threshold(it["q"], it["K"], it["V"], it["label"], chd, w.T, w.k_units, w.tau,
+                                              w.block, out=it["out"], indices=it["idx"], counts=it["cnt"],
+                                              workspace=it["ws"], t_append=w.T - 1)
         else:
             L.ds_decode_sparse_attn(it["q"], it["K"], it["V"], it["label"], chd, w.T, w.k_units, w.block,
                                     out=it["out"], indices=it["idx"], workspace=it["ws"], t_append=w.T - 1)
 
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
+    if w.tau is not None:
+        # The threshold rule keeps a data-dependent number of units: count the kept
+        # tokens from the call's own output (the tests check it against the oracle).
+        step(0)
+        torch.cuda.synchronize()
+        cnt0 = inst[0]["cnt"].cpu().numpy()
+        idx0 = inst[0]["idx"].cpu().numpy()
+        kept_tokens = 0
+        for b in range(w.B):
+            for g in range(w.Hkv):
+                ids = idx0[b, g, :int(cnt0[b, g])].astype(np.int64)
+                kept_tokens += int(np.minimum(w.block, w.T - ids * w.block).sum())
+        ab = algorithmic_bytes(w, lens, (kept_tokens, int(cnt0.sum())))
+        log(f"threshold rule: kept units per row {cnt0.reshape(-1).tolist()}, {kept_tokens} tokens; "
+            f"algorithmic bytes/step {ab['step']}")
 
     def capture(n_steps, fn):
         g = torch.cuda.CUDAGraph()
@@ -325,6 +359,9 @@ def main():
         if w.ragged:
             L.ds_decode_score_ragged(it["q"], it["K"], it["label"], chd, seq, w.T, w.k_units, w.block, n_append=1,
                                      workspace=it["ws"])
+        elif w.tau is not None:
+            L.ds_decode_score_threshold(it["q"], it["K"], it["label"], chd, w.T, w.k_units, w.block,
+                                        workspace=it["ws"], t_append=w.T - 1)
         else:
             L.ds_decode_score(it["q"], it["K"], it["label"], chd, w.T, w.k_units, w.block, workspace=it["ws"],
                               t_append=w.T - 1)
@@ -334,6 +371,9 @@ def main():
         if w.ragged:
             L.ds_decode_select_attend_ragged(it["q"], it["K"], it["V"], seq, w.T, w.k_units, it["ws"], w.block,
                                              out=it["out"], indices=it["idx"])
+        elif w.tau is not None:
+            L.ds_decode_select_attend_threshold(it["q"], it["K"], it["V"], w.T, w.k_units, w.tau, it["ws"], w.block,
+                                                out=it["out"], indices=it["idx"], counts=it["cnt"])
         else:
             L.ds_decode_select_attend(it["q"], it["K"], it["V"], w.T, w.k_units, it["ws"], w.block,
                                       out=it["out"], indices=it["idx"])
@@ -349,9 +389,9 @@ def main():
 
     kernel_us = {}
     # The decode step's two phases (its own kernels), then isolated stages for reference
-    # (uniform-length stages, so not for a ragged batch).
+    # (uniform-length top-k stages, so not for a ragged batch or the threshold rule).
     stages = [("decode_score", st_decode_score), ("decode_select_attend", st_decode_select_attend)]
-    if not w.ragged:
+    if not w.ragged and w.tau is None:
         stages += [("label_append", st_append), ("scores", st_scores), ("select", st_select),
                    ("attention_from_indices", st_attn)]
     for name, fn in stages:
@@ -370,7 +410,8 @@ def main():
 
     stage_bytes = {
         "decode_score": ab["label_scan"] + ab["q"] + ab["label_append"] + ab.get("seq_lens", 0),
-        "decode_select_attend": ab["kv_gather"] + ab["q"] + ab["indices"] + ab["out"] + ab.get("seq_lens", 0),
+        "decode_select_attend": ab["kv_gather"] + ab["q"] + ab["indices"] + ab["out"] + ab.get("seq_lens", 0) +
+        ab.get("counts", 0),
         "label_append": ab["label_append"],
         "scores": ab["label_scan"] + ab["q"],
         "select": ab["indices"],
@@ -396,7 +437,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "T": w.T, "r": w.r,
                    "block": w.block, "k_units": w.k_units, "instances": n_inst, "launch": "hip graph replay",
-                   "parallelism": "single GPU", **({"seq_lens": lens.tolist()} if w.ragged else {})},
+                   "parallelism": "single GPU", **({"seq_lens": lens.tolist()} if w.ragged else {}),
+                   **({"rule": "threshold", "tau": w.tau} if w.tau is not None else {})},
         "us_per_step": round(us_step, 3),
         "us_per_step_eager": round(us_step_eager, 3),
         "algorithmic_bytes_per_step": ab["step"],

@@ -36,6 +36,7 @@ class Workload:
     T_cap: int = 0      # allocated cache length (0 means T)
     n_calib: int = 256  # calibration queries per query head and keys per KV head
     ragged: bool = False   # True: sequence lengths drawn per sequence in [T // 16, T] (T is the longest)
+    tau: float | None = None   # threshold rule (keep units scoring >= tau, at most k_units); None: top-k
 
     @property
     def G(self) -> int:
@@ -87,6 +88,18 @@ RAGGED_WORKLOADS = {
 }
 WORKLOADS.update(RAGGED_WORKLOADS)
 RAGGED_ORDER = ["ragged_16k"]
+
+# The threshold rule (Jenga page, core method item 1: positive-only head
+# aggregation, block-wise max over 64-token blocks, a layer threshold): a GQA
+# batch with four query heads per KV head, at most 128 blocks kept per row.
+# tau = 650 on these inputs keeps between 0 and all 128 blocks per row (mean
+# about 60): some rows keep nothing, some are capped.
+THRESHOLD_WORKLOADS = {
+    "jenga_gqa_32k": Workload("jenga_gqa_32k", "bf16", B=4, Hq=32, Hkv=8, d=128, T=32768, r=16, block=64,
+                              k_units=128, seed_base=7000, tau=650.0),
+}
+WORKLOADS.update(THRESHOLD_WORKLOADS)
+THRESHOLD_ORDER = ["jenga_gqa_32k"]
 
 # The decode benchmark's headline workload: T=16K, 32 heads, bf16.
 HEADLINE = "llama7b_16k"

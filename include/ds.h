@@ -211,6 +211,59 @@ ds_status ds_decode_select_attend_ragged(const void* q, const void* K, const voi
                                          void* stream);
 
 /*
+ * The decode step with the threshold rule instead of a fixed k (GPU, async).
+ * Jenga: Enhancing LLM Long-Context Fine-tuning with Contextual Token Sparsity,
+ * core method item 1: a token's informativeness sums the attention scores of
+ * the heads, counting only positive ones; a block's is the maximum over its
+ * tokens; blocks below a layer-specific threshold are eliminated.  Per row
+ * (sequence b, KV head g), with the label approximation of each head's score
+ * (Post-Training Sparse Attention with Double Sparsity, abstract):
+ *   0. label rows [t_append, T) are rebuilt from K, as in ds_decode_sparse_attn;
+ *   1. u[t] = sum over the group's query heads h of max(0, sum_j q[h, ch[g, j]]
+ *      * label[t, j]) (float32 of a double-precision sum); block > 1: the
+ *      maximum over the block's tokens;
+ *   2. the units with score >= tau are kept; when more than k_max pass, the
+ *      k_max largest of them (lower index first on ties).  Their number n goes
+ *      to counts[b, g]; indices[b, g, 0 .. n) holds them ascending and slots
+ *      n .. k_max - 1 are set to -1;
+ *   3. attention over the kept tokens, as in ds_decode_sparse_attn; a row that
+ *      keeps nothing writes a zero output.
+ *   tau     float threshold (a layer's); NaN is rejected, -inf keeps the k_max
+ *           largest, +inf keeps nothing
+ *   k_max   1 <= k_max <= ceil(T / block): capacity of the index buffer
+ *   counts  device int32 [B, Hkv], written by the call
+ *   other arguments as for ds_decode_sparse_attn (k_units = k_max).
+ * Errors: as ds_decode_sparse_attn, plus a null or misaligned counts, a NaN
+ * tau, and DS_ERR_UNSUPPORTED when Hq / Hkv > 8, (Hq / Hkv) * r > 512 or
+ * ceil(T / block) > 32768.
+ */
+ds_status ds_decode_sparse_attn_threshold(const void* q, const void* K, const void* V, void* label,
+                                          const int32_t* channels_dev, int32_t r, ds_dtype dt, int32_t B, int32_t Hq,
+                                          int32_t Hkv, int32_t d, int64_t T_cap, int64_t T, int64_t t_append,
+                                          int32_t block, int64_t k_max, float tau, float scale, float* out,
+                                          int32_t* indices, int32_t* counts, void* workspace, size_t workspace_bytes,
+                                          void* stream);
+
+/*
+ * ds_decode_sparse_attn_threshold in two phases through one workspace:
+ * ds_decode_score_threshold runs its steps 0 and 1, and
+ * ds_decode_select_attend_threshold its steps 2 and 3.  Issued back to back on
+ * one stream with the same shape and workspace, they launch exactly the
+ * kernels of the one call and give the same results.  Arguments and errors as
+ * for that call.
+ */
+ds_status ds_decode_score_threshold(const void* q, const void* K, void* label, const int32_t* channels_dev, int32_t r,
+                                    ds_dtype dt, int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t T_cap,
+                                    int64_t T, int64_t t_append, int32_t block, int64_t k_max, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+ds_status ds_decode_select_attend_threshold(const void* q, const void* K, const void* V, ds_dtype dt, int32_t B,
+                                            int32_t Hq, int32_t Hkv, int32_t d, int64_t T_cap, int64_t T,
+                                            int32_t block, int64_t k_max, float tau, float scale, float* out,
+                                            int32_t* indices, int32_t* counts, void* workspace,
+                                            size_t workspace_bytes, void* stream);
+
+/*
  * Stages of the decode step fed from caller buffers, so each can be checked in
  * isolation against independently computed inputs.
  */
@@ -220,6 +273,13 @@ ds_status ds_decode_select_attend_ragged(const void* q, const void* K, const voi
 ds_status ds_label_scores(const void* q, const void* label, const int32_t* channels_dev, int32_t r, ds_dtype dt,
                           int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t T_cap, int64_t T, int32_t block,
                           float* scores, int64_t ld, void* stream);
+
+/* Step 1 of the threshold rule only: scores[b, g, i] = the positive-only
+ * aggregation of ds_decode_sparse_attn_threshold, laid out as for
+ * ds_label_scores.  DS_ERR_UNSUPPORTED when Hq / Hkv > 8 or (Hq / Hkv) * r > 512. */
+ds_status ds_label_scores_positive(const void* q, const void* label, const int32_t* channels_dev, int32_t r,
+                                   ds_dtype dt, int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t T_cap,
+                                   int64_t T, int32_t block, float* scores, int64_t ld, void* stream);
 
 /* Step 2 only: per row of `scores` (rows x n, row stride ld floats), the k
  * largest values, the lower index winning a tie, written ascending to

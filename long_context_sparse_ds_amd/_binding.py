@@ -50,6 +50,16 @@ _SIGNATURES = {
     "ds_decode_select_attend_ragged": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64,
                                                 _c_i64, _c_vp, _c_i32, _c_i64, _c_f32, _c_vp, _c_vp, _c_vp, _c_size,
                                                 _c_vp]),
+    "ds_decode_sparse_attn_threshold": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32,
+                                                 _c_i32, _c_i32, _c_i64, _c_i64, _c_i64, _c_i32, _c_i64, _c_f32,
+                                                 _c_f32, _c_vp, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
+    "ds_decode_score_threshold": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                           _c_i32, _c_i64, _c_i64, _c_i64, _c_i32, _c_i64, _c_vp, _c_size, _c_vp]),
+    "ds_decode_select_attend_threshold": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                                   _c_i64, _c_i64, _c_i32, _c_i64, _c_f32, _c_f32, _c_vp, _c_vp,
+                                                   _c_vp, _c_vp, _c_size, _c_vp]),
+    "ds_label_scores_positive": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64,
+                                          _c_i64, _c_i32, _c_vp, _c_i64, _c_vp]),
     "ds_select_attention": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i64,
                                      _c_i32, _c_i64, _c_vp, _c_i64, _c_f32, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
     "ds_label_scores": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i64,
@@ -205,6 +215,77 @@ def ds_decode_sparse_attn(q, K, V, label, channels, T: int, k_units: int, block:
     return out, indices
 
 
+def ds_decode_sparse_attn_threshold(q, K, V, label, channels, T: int, k_max: int, tau: float, block: int = 1,
+                                    scale: float = 0.0, out=None, indices=None, counts=None, workspace=None,
+                                    stream=None, t_append: int | None = None):
+    """The decode step with the threshold rule (positive-only head aggregation, keep the units scoring
+    >= tau, at most k_max).  Returns (out fp32 [B, Hq, d], indices int32 [B, Hkv, k_max] with -1 past
+    each row's count, counts int32 [B, Hkv])."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    _, Hkv, T_cap, _ = K.shape
+    r = channels.shape[1]
+    dt = _dtype_code(q)
+    if K.dtype != q.dtype or V.dtype != q.dtype or label.dtype != q.dtype:
+        raise ValueError("q, K, V and label must share one dtype")
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if indices is None:
+        indices = torch.empty((B, Hkv, k_max), dtype=torch.int32, device=q.device)
+    if counts is None:
+        counts = torch.empty((B, Hkv), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(B, Hq, Hkv, d, T, block, k_max, q.device)
+    if t_append is None:
+        t_append = T
+    _check(lib().ds_decode_sparse_attn_threshold(_dev(q, "q"), _dev(K, "K"), _dev(V, "V"), _dev(label, "label"),
+                                                 _dev(channels, "channels"), r, dt, B, Hq, Hkv, d, T_cap, T,
+                                                 t_append, block, k_max, tau, scale, _dev(out, "out"),
+                                                 _dev(indices, "indices"), _dev(counts, "counts"),
+                                                 _dev(workspace, "workspace"),
+                                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, indices, counts
+
+
+def ds_decode_score_threshold(q, K, label, channels, T: int, k_max: int, block: int = 1, workspace=None,
+                              stream=None, t_append: int | None = None):
+    """First phase of ds_decode_sparse_attn_threshold (label-row append and positive-only scores into the
+    workspace).  Returns workspace."""
+    B, Hq, d = q.shape
+    _, Hkv, T_cap, _ = K.shape
+    r = channels.shape[1]
+    if workspace is None:
+        workspace = alloc_workspace(B, Hq, Hkv, d, T, block, k_max, q.device)
+    if t_append is None:
+        t_append = T
+    _check(lib().ds_decode_score_threshold(_dev(q, "q"), _dev(K, "K"), _dev(label, "label"),
+                                           _dev(channels, "channels"), r, _dtype_code(q), B, Hq, Hkv, d, T_cap, T,
+                                           t_append, block, k_max, _dev(workspace, "workspace"),
+                                           workspace.numel() * workspace.element_size(), _stream(stream)))
+    return workspace
+
+
+def ds_decode_select_attend_threshold(q, K, V, T: int, k_max: int, tau: float, workspace, block: int = 1,
+                                      scale: float = 0.0, out=None, indices=None, counts=None, stream=None):
+    """Second phase of ds_decode_sparse_attn_threshold, from a workspace ds_decode_score_threshold filled.
+    Returns (out, indices, counts)."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    _, Hkv, T_cap, _ = K.shape
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if indices is None:
+        indices = torch.empty((B, Hkv, k_max), dtype=torch.int32, device=q.device)
+    if counts is None:
+        counts = torch.empty((B, Hkv), dtype=torch.int32, device=q.device)
+    _check(lib().ds_decode_select_attend_threshold(_dev(q, "q"), _dev(K, "K"), _dev(V, "V"), _dtype_code(q), B, Hq,
+                                                   Hkv, d, T_cap, T, block, k_max, tau, scale, _dev(out, "out"),
+                                                   _dev(indices, "indices"), _dev(counts, "counts"),
+                                                   _dev(workspace, "workspace"),
+                                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, indices, counts
+
+
 def ds_decode_sparse_attn_ragged(q, K, V, label, channels, seq_lens, T_max: int, k_units: int, block: int = 1,
                                  n_append: int = 1, scale: float = 0.0, out=None, indices=None, workspace=None,
                                  stream=None):
@@ -341,6 +422,22 @@ def ds_label_scores(q, label, channels, T: int, block: int = 1, scores=None, str
     ld = scores.shape[-1]
     _check(lib().ds_label_scores(_dev(q, "q"), _dev(label, "label"), _dev(channels, "channels"), r, _dtype_code(q), B,
                                  Hq, Hkv, d, T_cap, T, block, _dev(scores, "scores"), ld, _stream(stream)))
+    return scores
+
+
+def ds_label_scores_positive(q, label, channels, T: int, block: int = 1, scores=None, stream=None):
+    """Positive-only aggregated scores (the threshold rule's step 1), laid out as ds_label_scores."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    _, Hkv, T_cap, r = label.shape
+    n_units = -(-T // block)
+    ld = -(-n_units // 4) * 4
+    if scores is None:
+        scores = torch.empty((B, Hkv, ld), dtype=torch.float32, device=q.device)
+    ld = scores.shape[-1]
+    _check(lib().ds_label_scores_positive(_dev(q, "q"), _dev(label, "label"), _dev(channels, "channels"), r,
+                                          _dtype_code(q), B, Hq, Hkv, d, T_cap, T, block, _dev(scores, "scores"), ld,
+                                          _stream(stream)))
     return scores
 
 

@@ -141,7 +141,7 @@ ds_status run_select_attend(const void* q, const void* K, const void* V, ds_dtyp
                             int64_t T_cap, int64_t T, int block, int64_t k_units, const float* scores, int64_t ld,
                             const uint16_t* tile_hist, bool tickets_zeroed, float scale, const ds::DecodePlan& pl,
                             float* out, int32_t* indices, char* ws, hipStream_t s,
-                            const int32_t* seq_lens = nullptr) {
+                            const int32_t* seq_lens = nullptr, float tau = 0.f, int32_t* counts = nullptr) {
   if (pl.fused) {
     float* part_acc = reinterpret_cast<float*>(ws + pl.off_acc);
     float* part_ml = reinterpret_cast<float*>(ws + pl.off_ml);
@@ -151,7 +151,7 @@ ds_status run_select_attend(const void* q, const void* K, const void* V, ds_dtyp
         return st;
     return hip_status(ds::launch_select_attention(q, K, V, dt == DS_DTYPE_BF16, scores, ld, tile_hist, Hq, Hkv, T_cap,
                                                   T, block, k_units, scale, pl, indices, part_acc, part_ml, out,
-                                                  tickets, seq_lens, s),
+                                                  tickets, seq_lens, tau, counts, s),
                       "select-attention launch");
   }
   if (ds_status st = hip_status(ds::launch_select(scores, pl.rows, pl.n_units, ld, k_units, indices, s),
@@ -214,7 +214,38 @@ ds_status ds_label_scores(const void* q, const void* label, const int32_t* chann
   // No append: the label cache is only read.
   return hip_status(ds::launch_scores(q, const_cast<void*>(label), nullptr, channels_dev, r, dt == DS_DTYPE_BF16, B,
                                       Hq, Hkv, T_cap, T, T, block, scores, ld, nullptr, nullptr, 0, nullptr, 0,
-                                      static_cast<hipStream_t>(stream)),
+                                      false, static_cast<hipStream_t>(stream)),
+                    "score launch");
+}
+
+// Positive-only head aggregation (one double per (head, label channel) in the
+// score kernel's LDS table, filled by one thread each).
+static ds_status check_positive(int32_t Hq, int32_t Hkv, int32_t r) {
+  const int G = Hq / Hkv;
+  if (G > 8) return fail(DS_ERR_UNSUPPORTED, "positive-only aggregation needs Hq / Hkv <= 8 (got %d)", G);
+  if (G * r > 512) return fail(DS_ERR_UNSUPPORTED, "positive-only aggregation needs (Hq / Hkv) * r <= 512 (got %d)",
+                               G * r);
+  return DS_OK;
+}
+
+ds_status ds_label_scores_positive(const void* q, const void* label, const int32_t* channels_dev, int32_t r,
+                                   ds_dtype dt, int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t T_cap,
+                                   int64_t T, int32_t block, float* scores, int64_t ld, void* stream) {
+  g_err.clear();
+  if (!q || !label || !channels_dev || !scores) return fail(DS_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (ds_status st = check_dtype(dt)) return st;
+  if (ds_status st = check_decode_shape(B, Hq, Hkv, d, T_cap, T, block, 1)) return st;
+  if (r < 1 || r > d) return fail(DS_ERR_INVALID_ARGUMENT, "need 1 <= r <= d (r = %d)", r);
+  if (ds_status st = check_positive(Hq, Hkv, r)) return st;
+  const int64_t n_units = (T + block - 1) / block;
+  if (ld < n_units || ld % 4 != 0)
+    return fail(DS_ERR_INVALID_ARGUMENT, "ld = %lld must be >= %lld and a multiple of 4", (long long)ld,
+                (long long)n_units);
+  if (!aligned(q, 16) || !aligned(label, 16) || !aligned(scores, 16) || !aligned(channels_dev, 4))
+    return fail(DS_ERR_INVALID_ARGUMENT, "misaligned device pointer");
+  return hip_status(ds::launch_scores(q, const_cast<void*>(label), nullptr, channels_dev, r, dt == DS_DTYPE_BF16, B,
+                                      Hq, Hkv, T_cap, T, T, block, scores, ld, nullptr, nullptr, 0, nullptr, 0,
+                                      true, static_cast<hipStream_t>(stream)),
                     "score launch");
 }
 
@@ -276,24 +307,26 @@ static ds_status check_decode_call(const void* q, const void* K, const void* V, 
 static ds_status decode_score_stage(const void* q, const void* K, void* label, const int32_t* channels_dev, int32_t r,
                                     ds_dtype dt, int32_t B, int32_t Hq, int32_t Hkv, int64_t T_cap, int64_t T,
                                     int64_t t_append, int32_t block, const ds::DecodePlan& pl, char* ws,
-                                    hipStream_t s, const int32_t* seq_lens = nullptr, int32_t n_append = 0) {
+                                    hipStream_t s, const int32_t* seq_lens = nullptr, int32_t n_append = 0,
+                                    bool positive = false) {
   float* scores = reinterpret_cast<float*>(ws + pl.off_scores);
   uint16_t* tile_hist = pl.tile_hist ? reinterpret_cast<uint16_t*>(ws + pl.off_tile_hist) : nullptr;
   unsigned* tickets = pl.fused ? reinterpret_cast<unsigned*>(ws + pl.off_tickets) : nullptr;
   return hip_status(ds::launch_scores(q, label, K, channels_dev, r, dt == DS_DTYPE_BF16, B, Hq, Hkv, T_cap, T,
                                       t_append, block, scores, pl.score_ld, tile_hist, tickets, pl.sp.head_chunks,
-                                      seq_lens, n_append, s),
+                                      seq_lens, n_append, positive, s),
                     "score launch");
 }
 
 static ds_status decode_select_stage(const void* q, const void* K, const void* V, ds_dtype dt, int32_t B, int32_t Hq,
                                      int32_t Hkv, int64_t T_cap, int64_t T, int32_t block, int64_t k_units,
                                      float scale, const ds::DecodePlan& pl, float* out, int32_t* indices, char* ws,
-                                     hipStream_t s, const int32_t* seq_lens = nullptr) {
+                                     hipStream_t s, const int32_t* seq_lens = nullptr, float tau = 0.f,
+                                     int32_t* counts = nullptr) {
   const float* scores = reinterpret_cast<const float*>(ws + pl.off_scores);
   const uint16_t* tile_hist = pl.tile_hist ? reinterpret_cast<const uint16_t*>(ws + pl.off_tile_hist) : nullptr;
   return run_select_attend(q, K, V, dt, B, Hq, Hkv, T_cap, T, block, k_units, scores, pl.score_ld, tile_hist, true,
-                           scale, pl, out, indices, ws, s, seq_lens);
+                           scale, pl, out, indices, ws, s, seq_lens, tau, counts);
 }
 
 ds_status ds_decode_sparse_attn(const void* q, const void* K, const void* V, void* label, const int32_t* channels_dev,
@@ -402,6 +435,71 @@ ds_status ds_decode_select_attend(const void* q, const void* K, const void* V, d
   if (!(scale > 0.f)) scale = 1.0f / std::sqrt(float(d));
   return decode_select_stage(q, K, V, dt, B, Hq, Hkv, T_cap, T, block, k_units, scale, pl, out, indices,
                              static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+}
+
+// Validation shared by the threshold-rule calls, after check_decode_call.
+static ds_status check_threshold(float tau, const int32_t* counts, bool need_counts, const ds::DecodePlan& pl) {
+  if (std::isnan(tau)) return fail(DS_ERR_INVALID_ARGUMENT, "tau is NaN");
+  if (need_counts && !counts) return fail(DS_ERR_INVALID_ARGUMENT, "null pointer argument (counts)");
+  if (need_counts && !aligned(counts, 4)) return fail(DS_ERR_INVALID_ARGUMENT, "misaligned device pointer (counts)");
+  if (!pl.fused)
+    return fail(DS_ERR_UNSUPPORTED, "the threshold rule needs ceil(T / block) <= %lld units per row (got %lld)",
+                (long long)ds::kFusedMaxUnits, (long long)pl.n_units);
+  return DS_OK;
+}
+
+ds_status ds_decode_sparse_attn_threshold(const void* q, const void* K, const void* V, void* label,
+                                          const int32_t* channels_dev, int32_t r, ds_dtype dt, int32_t B, int32_t Hq,
+                                          int32_t Hkv, int32_t d, int64_t T_cap, int64_t T, int64_t t_append,
+                                          int32_t block, int64_t k_max, float tau, float scale, float* out,
+                                          int32_t* indices, int32_t* counts, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  g_err.clear();
+  ds::DecodePlan pl;
+  if (ds_status st = check_decode_call(q, K, V, label, channels_dev, r, dt, B, Hq, Hkv, d, T_cap, T, t_append, block,
+                                       k_max, out, indices, workspace, workspace_bytes, true, true, pl))
+    return st;
+  if (ds_status st = check_positive(Hq, Hkv, r)) return st;
+  if (ds_status st = check_threshold(tau, counts, true, pl)) return st;
+  if (!(scale > 0.f)) scale = 1.0f / std::sqrt(float(d));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  if (ds_status st = decode_score_stage(q, K, label, channels_dev, r, dt, B, Hq, Hkv, T_cap, T, t_append, block, pl,
+                                        ws, s, nullptr, 0, true))
+    return st;
+  return decode_select_stage(q, K, V, dt, B, Hq, Hkv, T_cap, T, block, k_max, scale, pl, out, indices, ws, s, nullptr,
+                             tau, counts);
+}
+
+ds_status ds_decode_score_threshold(const void* q, const void* K, void* label, const int32_t* channels_dev, int32_t r,
+                                    ds_dtype dt, int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t T_cap,
+                                    int64_t T, int64_t t_append, int32_t block, int64_t k_max, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  ds::DecodePlan pl;
+  if (ds_status st = check_decode_call(q, K, nullptr, label, channels_dev, r, dt, B, Hq, Hkv, d, T_cap, T, t_append,
+                                       block, k_max, nullptr, nullptr, workspace, workspace_bytes, true, false, pl))
+    return st;
+  if (ds_status st = check_positive(Hq, Hkv, r)) return st;
+  if (ds_status st = check_threshold(0.f, nullptr, false, pl)) return st;
+  return decode_score_stage(q, K, label, channels_dev, r, dt, B, Hq, Hkv, T_cap, T, t_append, block, pl,
+                            static_cast<char*>(workspace), static_cast<hipStream_t>(stream), nullptr, 0, true);
+}
+
+ds_status ds_decode_select_attend_threshold(const void* q, const void* K, const void* V, ds_dtype dt, int32_t B,
+                                            int32_t Hq, int32_t Hkv, int32_t d, int64_t T_cap, int64_t T,
+                                            int32_t block, int64_t k_max, float tau, float scale, float* out,
+                                            int32_t* indices, int32_t* counts, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  ds::DecodePlan pl;
+  if (ds_status st = check_decode_call(q, K, V, nullptr, nullptr, 0, dt, B, Hq, Hkv, d, T_cap, T, T, block, k_max,
+                                       out, indices, workspace, workspace_bytes, false, true, pl))
+    return st;
+  if (ds_status st = check_threshold(tau, counts, true, pl)) return st;
+  if (!(scale > 0.f)) scale = 1.0f / std::sqrt(float(d));
+  return decode_select_stage(q, K, V, dt, B, Hq, Hkv, T_cap, T, block, k_max, scale, pl, out, indices,
+                             static_cast<char*>(workspace), static_cast<hipStream_t>(stream), nullptr, tau, counts);
 }
 
 ds_status ds_select_attention(const void* q, const void* K, const void* V, ds_dtype dt, int32_t B, int32_t Hq,

@@ -65,7 +65,7 @@ hipError_t launch_pack(const void* K, int is_bf16, int B, int Hkv, int64_t T_cap
 hipError_t launch_scores(const void* q, void* label, const void* K, const int32_t* ch, int r, int is_bf16, int B,
                          int Hq, int Hkv, int64_t T_cap, int64_t T, int64_t t_append, int block, float* scores,
                          int64_t ld, uint16_t* tile_hist, unsigned* tickets, int tickets_per_row,
-                         const int32_t* seq_lens, int n_append, hipStream_t s);
+                         const int32_t* seq_lens, int n_append, bool positive, hipStream_t s);
 
 hipError_t launch_select(const float* scores, int64_t rows, int64_t n, int64_t ld, int64_t k, int32_t* idx,
                          hipStream_t s);
@@ -87,7 +87,7 @@ hipError_t launch_select_attention(const void* q, const void* K, const void* V, 
                                    int64_t ld, const uint16_t* tile_hist, int Hq, int Hkv, int64_t T_cap, int64_t T,
                                    int block, int64_t k_units, float scale, const DecodePlan& pl, int32_t* indices,
                                    float* part_acc, float* part_ml, float* out, unsigned* tickets,
-                                   const int32_t* seq_lens, hipStream_t s);
+                                   const int32_t* seq_lens, float tau, int32_t* counts, hipStream_t s);
 
 hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t s);
 

@@ -13,6 +13,12 @@
 // inputs and the sum of at most d of them is accumulated in double, so the
 // float32 result is the exact score rounded once.
 //
+// POS (Jenga page, core method item 1): a token's informativeness counts only
+// the query heads whose score is positive, u[t] = sum_h max(0, s_h[t]) with
+// s_h[t] = sum_j q[h, ch[g, j]] * label[t, j]; each head's sum and the sum over
+// heads are accumulated in double, so here too the float32 result is the
+// exact value rounded once (up to double rounding of the sums).
+//
 // Tokens in [t_append, T) first get their label rows rebuilt from K (the
 // per-step label-row append of the newest tokens, fused here so a decode step
 // is a single pass over the label cache); they are scored from the values just
@@ -54,6 +60,30 @@ __device__ __forceinline__ double dot_label(const uint4 (&raw)[NV], const double
   return a;
 }
 
+// Unpack NV 16-byte words of label values into doubles.
+template <int NV>
+__device__ __forceinline__ void label_values(const uint4 (&raw)[NV], double* lv, uint16_t) {
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const uint32_t w[4] = {raw[v].x, raw[v].y, raw[v].z, raw[v].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      lv[v * 8 + 2 * k] = double(bf16_lo(w[k]));
+      lv[v * 8 + 2 * k + 1] = double(bf16_hi(w[k]));
+    }
+  }
+}
+template <int NV>
+__device__ __forceinline__ void label_values(const uint4 (&raw)[NV], double* lv, float) {
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    lv[v * 4 + 0] = double(__uint_as_float(raw[v].x));
+    lv[v * 4 + 1] = double(__uint_as_float(raw[v].y));
+    lv[v * 4 + 2] = double(__uint_as_float(raw[v].z));
+    lv[v * 4 + 3] = double(__uint_as_float(raw[v].w));
+  }
+}
+
 // R > 0: label width known at compile time and R * sizeof(TE) a multiple of 16 bytes.
 // R == 0: any width, element loads.
 // Label-row append of token t: gather its r channels from K into the label
@@ -70,13 +100,28 @@ __device__ __forceinline__ float append_row(const TE* __restrict__ Krow, TE* __r
   return float(a);
 }
 
+// The same with positive-only head aggregation; qh holds q[h, ch[j]] at h * r + j.
+template <typename TE>
+__device__ __forceinline__ float append_row_pos(const TE* __restrict__ Krow, TE* __restrict__ Lrow, const int* sch,
+                                                const double* qh, int r, int G) {
+  for (int j = 0; j < r; ++j) Lrow[j] = Krow[sch[j]];
+  double a = 0.0;
+  for (int h = 0; h < G; ++h) {
+    double s = 0.0;
+    for (int j = 0; j < r; ++j) s = fma(qh[h * r + j], double(elem_to_f32(Krow[sch[j]])), s);
+    a += fmax(s, 0.0);
+  }
+  return float(a);
+}
+
 // The arguments the first loads need come first: the first 14 dwords are
 // preloaded into SGPRs at wave launch where the firmware supports it, so the
 // label stream starts without a kernel-argument round trip.
 // RAGGED: sequence b holds seq_lens[b] tokens (clamped to [1, T]); its last
 // n_append rows are rebuilt, and its scores past its length are written as
 // -inf up to T, so a row's score buffer is always T entries long.
-template <typename TE, int R, bool RAGGED>
+// POS: positive-only head aggregation (G <= 8, checked on the host).
+template <typename TE, int R, bool RAGGED, bool POS>
 __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ q, TE* __restrict__ label,
                                                          const int32_t* __restrict__ ch, int64_t T_cap, int T,
                                                          int t_append, int G, int Hkv, int r, int block,
@@ -100,15 +145,15 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
   // channel (up to 8 heads at a time) and the channel table first, since they
   // gate the arithmetic; then the label rows, whose latency the q-sum and the
   // histogram clearing overlap.
-  __shared__ double qall[kHeadDim];
-  __shared__ double qs[kHeadDim];
+  constexpr int kQB = 8;
+  __shared__ double qall[POS ? kQB : 1][kHeadDim];
+  __shared__ double qs[POS ? kQB * kHeadDim : kHeadDim];   // POS: q[h, ch[j]] at h * r + j
   __shared__ int sch[kHeadDim];
   __shared__ uint32_t h[kHistBins];
   static_assert(kThreads >= kHeadDim, "one thread per channel");
   // All loads below are unconditional, with clamped indices and masked values:
   // conditional loads leave the compiler unable to count the loads in flight,
   // and it then waits for all of them at the first use of any.
-  constexpr int kQB = 8;
   const int ql = threadIdx.x < kHeadDim ? int(threadIdx.x) : 0;
   const TE* qg = q + int64_t(row) * G * kHeadDim + ql;
   float qv[kQB];
@@ -116,7 +161,10 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
   for (int h8 = 0; h8 < kQB; ++h8) qv[h8] = elem_to_f32(qg[int64_t(h8 < G ? h8 : 0) * kHeadDim]);
   double qrest = 0.0;   // heads past the first 8 (rare), fetched before the label rows
   for (int h = kQB; h < G; ++h) qrest += double(elem_to_f32(qg[int64_t(h) * kHeadDim]));
-  const int cj = ch[g * r + (int(threadIdx.x) < r ? int(threadIdx.x) : 0)];
+  // POS: thread i < G * r needs channel i % r (and thread j < r channel j).
+  const int tx = int(threadIdx.x);
+  const int jj = POS ? (tx < kQB * r ? tx % r : 0) : (tx < r ? tx : 0);
+  const int cj = ch[g * r + jj];
   uint4 raw[kTPT][NV];
   if constexpr (R > 0) {
 #pragma unroll
@@ -130,20 +178,76 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
   if (tile_hist != nullptr)
     for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0u;
   if (threadIdx.x < kHeadDim) {
-    double s = qrest;
+    if constexpr (POS) {
 #pragma unroll
-    for (int h8 = 0; h8 < kQB; ++h8) s += h8 < G ? double(qv[h8]) : 0.0;
-    qall[threadIdx.x] = s;
+      for (int h8 = 0; h8 < kQB; ++h8) qall[h8][threadIdx.x] = double(qv[h8]);
+    } else {
+      double s = qrest;
+#pragma unroll
+      for (int h8 = 0; h8 < kQB; ++h8) s += h8 < G ? double(qv[h8]) : 0.0;
+      qall[0][threadIdx.x] = s;
+    }
   }
   __syncthreads();
-  if (threadIdx.x < r) {
-    qs[threadIdx.x] = qall[cj];
-    sch[threadIdx.x] = cj;
+  if constexpr (POS) {
+    if (int(threadIdx.x) < G * r) qs[threadIdx.x] = qall[int(threadIdx.x) / r][cj];
+  } else {
+    if (threadIdx.x < r) qs[threadIdx.x] = qall[0][cj];
   }
+  if (threadIdx.x < r) sch[threadIdx.x] = cj;
   __syncthreads();
 
   float u[kTPT];
-  if constexpr (R > 0) {
+  if constexpr (POS && R > 0) {
+    // Head-outer: one head's q values (LDS broadcast reads) against the label
+    // values of TCH tokens held in double.
+    constexpr int TCH = R <= 16 ? kTPT : 1;
+#pragma unroll
+    for (int c0 = 0; c0 < kTPT; c0 += TCH) {
+      double lv[TCH][R];
+#pragma unroll
+      for (int i = 0; i < TCH; ++i) label_values<NV>(raw[c0 + i], lv[i], TE());
+      double acc[TCH];
+#pragma unroll
+      for (int i = 0; i < TCH; ++i) acc[i] = 0.0;
+      for (int h = 0; h < G; ++h) {
+        double qh[R];
+#pragma unroll
+        for (int j = 0; j < R; ++j) qh[j] = qs[h * R + j];
+#pragma unroll
+        for (int i = 0; i < TCH; ++i) {
+          double sdot = 0.0;
+#pragma unroll
+          for (int j = 0; j < R; ++j) sdot = fma(qh[j], lv[i][j], sdot);
+          acc[i] += fmax(sdot, 0.0);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < TCH; ++i) {
+        const int t = t0 + (c0 + i) * kThreads;
+        if (t >= Ti) u[c0 + i] = -INFINITY;
+        else if (t >= ta)
+          u[c0 + i] = append_row_pos(Kc + (int64_t(row) * T_cap + t) * kHeadDim, L + int64_t(t) * R, sch, qs, R, G);
+        else u[c0 + i] = float(acc[i]);
+      }
+    }
+  } else if constexpr (POS) {
+#pragma unroll
+    for (int i = 0; i < kTPT; ++i) {
+      const int t = t0 + i * kThreads;
+      double a = 0.0;
+      if (t < Ti && t < ta)
+        for (int h = 0; h < G; ++h) {
+          double sdot = 0.0;
+          for (int j = 0; j < r; ++j) sdot = fma(qs[h * r + j], double(elem_to_f32(L[int64_t(t) * r + j])), sdot);
+          a += fmax(sdot, 0.0);
+        }
+      if (t >= Ti) u[i] = -INFINITY;
+      else if (t >= ta)
+        u[i] = append_row_pos(Kc + (int64_t(row) * T_cap + t) * kHeadDim, L + int64_t(t) * r, sch, qs, r, G);
+      else u[i] = float(a);
+    }
+  } else if constexpr (R > 0) {
     double qr[R];
 #pragma unroll
     for (int j = 0; j < R; ++j) qr[j] = qs[j];
@@ -211,7 +315,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
     for (int i = threadIdx.x; i < tickets_per_row; i += kThreads) tickets[int64_t(row) * tickets_per_row + i] = 0u;
 }
 
-template <typename TE, bool RAGGED>
+template <typename TE, bool RAGGED, bool POS>
 hipError_t dispatch_r(const TE* q, TE* label, const TE* Kc, const int32_t* ch, int r, int B, int Hq, int Hkv,
                       int64_t T_cap, int64_t T, int64_t t_append, int block, float* scores, int64_t ld,
                       uint16_t* tile_hist, unsigned* tickets, int tickets_per_row, const int32_t* seq_lens,
@@ -219,7 +323,7 @@ hipError_t dispatch_r(const TE* q, TE* label, const TE* Kc, const int32_t* ch, i
   const dim3 grid(unsigned((T + kTile - 1) / kTile), unsigned(Hkv), unsigned(B));
   const bool vec = (int64_t(r) * sizeof(TE)) % 16 == 0;
 #define DS_SCORE(RR)                                                                                               \
-  hipLaunchKernelGGL((score_kernel<TE, RR, RAGGED>), grid, dim3(kThreads), 0, s, q, label, ch, T_cap, int(T),     \
+  hipLaunchKernelGGL((score_kernel<TE, RR, RAGGED, POS>), grid, dim3(kThreads), 0, s, q, label, ch, T_cap, int(T),     \
                      int(t_append), Hq / Hkv, Hkv, r, block, Kc, scores, ld, tile_hist, tickets, tickets_per_row,  \
                      seq_lens, n_append)
   if (vec && r == 8) DS_SCORE(8);
@@ -234,12 +338,15 @@ template <typename TE>
 hipError_t dispatch(const TE* q, TE* label, const TE* Kc, const int32_t* ch, int r, int B, int Hq, int Hkv,
                     int64_t T_cap, int64_t T, int64_t t_append, int block, float* scores, int64_t ld,
                     uint16_t* tile_hist, unsigned* tickets, int tickets_per_row, const int32_t* seq_lens,
-                    int n_append, hipStream_t s) {
+                    int n_append, bool positive, hipStream_t s) {
+  if (positive)
+    return dispatch_r<TE, false, true>(q, label, Kc, ch, r, B, Hq, Hkv, T_cap, T, t_append, block, scores, ld,
+                                       tile_hist, tickets, tickets_per_row, nullptr, 0, s);
   if (seq_lens != nullptr)
-    return dispatch_r<TE, true>(q, label, Kc, ch, r, B, Hq, Hkv, T_cap, T, t_append, block, scores, ld, tile_hist,
-                                tickets, tickets_per_row, seq_lens, n_append, s);
-  return dispatch_r<TE, false>(q, label, Kc, ch, r, B, Hq, Hkv, T_cap, T, t_append, block, scores, ld, tile_hist,
-                               tickets, tickets_per_row, nullptr, 0, s);
+    return dispatch_r<TE, true, false>(q, label, Kc, ch, r, B, Hq, Hkv, T_cap, T, t_append, block, scores, ld,
+                                       tile_hist, tickets, tickets_per_row, seq_lens, n_append, s);
+  return dispatch_r<TE, false, false>(q, label, Kc, ch, r, B, Hq, Hkv, T_cap, T, t_append, block, scores, ld,
+                                      tile_hist, tickets, tickets_per_row, nullptr, 0, s);
 }
 
 }  // namespace
@@ -247,14 +354,14 @@ hipError_t dispatch(const TE* q, TE* label, const TE* Kc, const int32_t* ch, int
 hipError_t launch_scores(const void* q, void* label, const void* K, const int32_t* ch, int r, int is_bf16, int B,
                          int Hq, int Hkv, int64_t T_cap, int64_t T, int64_t t_append, int block, float* scores,
                          int64_t ld, uint16_t* tile_hist, unsigned* tickets, int tickets_per_row,
-                         const int32_t* seq_lens, int n_append, hipStream_t s) {
+                         const int32_t* seq_lens, int n_append, bool positive, hipStream_t s) {
   if (is_bf16)
     return dispatch(static_cast<const uint16_t*>(q), static_cast<uint16_t*>(label), static_cast<const uint16_t*>(K),
                     ch, r, B, Hq, Hkv, T_cap, T, t_append, block, scores, ld, tile_hist, tickets, tickets_per_row,
-                    seq_lens, n_append, s);
+                    seq_lens, n_append, positive, s);
   return dispatch(static_cast<const float*>(q), static_cast<float*>(label), static_cast<const float*>(K), ch, r, B,
                   Hq, Hkv, T_cap, T, t_append, block, scores, ld, tile_hist, tickets, tickets_per_row, seq_lens,
-                  n_append, s);
+                  n_append, positive, s);
 }
 
 }  // namespace ds

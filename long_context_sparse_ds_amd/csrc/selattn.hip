@@ -33,6 +33,14 @@
 // and, when still needed, the 10-bit radix passes.  A last prefix sum over the
 // per-thread kept counts gives every kept unit its position in the ascending
 // output list.
+//
+// Threshold rule (Jenga page, core method item 1), when a counts buffer is
+// given: the units scoring at least tau are kept, at most k of them (the k
+// largest when more pass).  Their number comes with the first prefix sum (a
+// second 16-bit count packed beside the bin counts); when it is at most k the
+// kept set is exactly the passing units, so the radix passes are skipped and
+// the prefix sum over the pass masks alone places them.  Otherwise the top-k
+// search runs as usual and every unit it keeps passes.
 #include "select_dev.h"
 
 namespace ds {
@@ -79,15 +87,18 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 // is the count of bin NB - 1 - BPT * t - i.  With the workgroup prefix sum of
 // the per-thread totals, the thread whose bins hold the kk-th largest key
 // stores (digit, count above it, count in it) to out.  The caller passes a
-// barrier before reading out.
+// barrier before reading out.  `extra` (a per-thread count) is summed over the
+// workgroup in the same prefix sum, in the high 16 bits (every total here is at
+// most 32768), and its workgroup total is returned.
 template <int NT, int NB>
-__device__ __forceinline__ void pick_bin(const uint32_t (&c)[NB / NT], uint32_t kk, uint32_t* wsum, uint32_t* out) {
+__device__ __forceinline__ uint32_t pick_bin(const uint32_t (&c)[NB / NT], uint32_t kk, uint32_t* wsum, uint32_t* out,
+                                             uint32_t extra = 0u) {
   constexpr int BPT = NB / NT;
   uint32_t sum = 0u;
 #pragma unroll
   for (int i = 0; i < BPT; ++i) sum += c[i];
   uint32_t tot;
-  uint32_t above = block_exclusive_scan1<NT>(sum, wsum, tot);
+  uint32_t above = block_exclusive_scan1<NT>(sum | (extra << 16), wsum, tot) & 0xFFFFu;
   if (above < kk && above + sum >= kk) {
 #pragma unroll
     for (int i = 0; i < BPT; ++i) {
@@ -99,6 +110,7 @@ __device__ __forceinline__ void pick_bin(const uint32_t (&c)[NB / NT], uint32_t 
       above += c[i];
     }
   }
+  return tot >> 16;
 }
 
 // Counts of this thread's bins of an LDS histogram, highest first.
@@ -190,19 +202,23 @@ struct FusedArgs {
   float scale;
   const int32_t* seq_lens;     // null: every sequence holds T tokens
   int32_t Hkv;
+  float tau;                   // threshold rule: keep units scoring >= tau (at most k_units)
+  int32_t* counts;             // threshold rule: kept units per row; null: plain top-k
 };
 
 // Scalar arguments, those of the first loads first: the first 14 dwords are
 // preloaded into SGPRs at wave launch where the firmware supports it.
 // RAGGED: sequence b holds seq_lens[b] tokens (clamped to [1, T]) and keeps
 // min(k_units, its unit count) units; index slots past that are set to -1.
+// counts_ != null: the threshold rule with tau_ (index slots past a row's kept
+// count are -1; a row that keeps nothing gets a zero output).
 template <typename TE, int NT, int ITEMS, int HC, bool RAGGED>
 __global__ __launch_bounds__(NT) void selattn_kernel(
     const void* q_, const float* scores_, const uint16_t* tile_hist_, int64_t ld_, int32_t G_,
     int32_t head_chunks_, int32_t n_units_, int32_t tiles_, int32_t k_units_, int32_t lb_, const void* K_,
     const void* V_, int32_t* indices_, float* part_acc_, float* part_ml_, float* out_, unsigned* tickets_,
     int64_t T_cap_, int32_t T_, int32_t kv_virtual_, int32_t chunk_, int32_t n_split_, float scale_,
-    const int32_t* seq_lens_, int32_t Hkv_) {
+    const int32_t* seq_lens_, int32_t Hkv_, float tau_, int32_t* counts_) {
   FusedArgs a;
   a.q = q_;
   a.K = K_;
@@ -229,6 +245,8 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
   a.scale = scale_;
   a.seq_lens = seq_lens_;
   a.Hkv = Hkv_;
+  a.tau = tau_;
+  a.counts = counts_;
   using LN = Lanes<TE, NT>;
   constexpr int NW = LN::NW, EPL = LN::EPL, LPT = LN::LPT, GPW = LN::GPW, NG = LN::NG, KU = LN::KU;
   constexpr int BPT1 = 2048 / NT, BPT2 = 1024 / NT;
@@ -312,7 +330,8 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
   // The scores go to LDS as well, for the candidate passes' indexed reads.
 #pragma unroll
   for (int v = 0; v < ITEMS / 4; ++v)
-    *reinterpret_cast<float4*>(&sm.u.sc[first + 4 * v]) = make_float4(s[4 * v], s[4 * v + 1], s[4 * v + 2], s[4 * v + 3]);
+    *reinterpret_cast<float4*>(&sm.u.sc[first + 4 * v]) =
+        make_float4(s[4 * v], s[4 * v + 1], s[4 * v + 2], s[4 * v + 3]);
   uint32_t c1[BPT1];
   if (a.tile_hist != nullptr) {
 #pragma unroll
@@ -340,83 +359,105 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
 #pragma unroll
   for (int i = 0; i < BPT2; ++i) sm.hist2[i * NT + tid] = 0u;
 
-  // Pass 0: the top digit d0 holding the k-th largest key.
-  const uint32_t k = uint32_t(k_row);
-  pick_bin<NT, 2048>(c1, k, sm.wsum[0], sm.pick);
-  __syncthreads();
-  const uint32_t d0 = sm.pick[0];
-  uint32_t kk = k - sm.pick[1];   // keys still needed from digit d0
-  const uint32_t cnt0 = sm.pick[2];
-
-  // Classify: finite scores have keys in [0x00800000, 0xFF7FFFFF], so
-  // 4 <= d0 <= 2043 and both bounds are non-NaN floats; comparing floats is
-  // comparing keys (-0.0 and +0.0 share a key and compare equal).  Padding
-  // units hold -inf, below every bound.
-  const float f_lo = key_float(d0 << 21), f_hi = key_float((d0 + 1u) << 21);
-  uint32_t gtm = 0u, cm = 0u;
+  // Threshold rule: this thread's units scoring at least tau (-inf padding and
+  // units past a short sequence never count).
+  const bool thresh = a.counts != nullptr;
+  uint32_t passm = 0u;
+  if (thresh) {
+    const int nu_row = RAGGED ? ((T_row + block - 1) >> lb) : n_units;
 #pragma unroll
-  for (int j = 0; j < ITEMS; ++j) {
-    const bool hi = s[j] >= f_hi;
-    const bool in = s[j] >= f_lo && !hi;
-    gtm |= uint32_t(hi) << j;
-    cm |= uint32_t(in) << j;
+    for (int j = 0; j < ITEMS; ++j) passm |= uint32_t(first + j < nu_row && s[j] >= a.tau) << j;
   }
 
-  // Narrow the threshold inside d0: thr is a key, eq_take the number of keys
-  // equal to thr to keep (lowest unit ids first), all_eq when that is all of them.
-  uint32_t thr = d0 << 21, eq_take = 0u;
-  bool all_eq = true;
-  bool settled = kk == cnt0;   // every key of digit d0 is needed
-  if (!settled) {
-    for (uint32_t m = cm; m != 0u; m &= m - 1u) {
-      const uint32_t key = float_key(sm.u.sc[first + __builtin_ctz(m)]);
-      atomicAdd(&sm.hist1[(key >> 10) & 2047u], 1u);
+  // Pass 0: the top digit d0 holding the k-th largest key (and the number of
+  // units passing the threshold).
+  const uint32_t k = uint32_t(k_row);
+  const uint32_t n_pass = pick_bin<NT, 2048>(c1, k, sm.wsum[0], sm.pick, uint32_t(__popc(passm)));
+  __syncthreads();
+  // Kept units of the row; with the threshold rule, when no more than k pass,
+  // they are exactly the passing ones and the search below is skipped.
+  int k_keep = k_row;
+  bool compact = false;
+  if (thresh) {
+    k_keep = min(k_row, int(n_pass));
+    compact = int(n_pass) <= k_row;
+  }
+  uint32_t keepm = passm, eqm = 0u, eq_take = 0u;
+  if (!compact) {
+    const uint32_t d0 = sm.pick[0];
+    uint32_t kk = k - sm.pick[1];   // keys still needed from digit d0
+    const uint32_t cnt0 = sm.pick[2];
+
+    // Classify: finite scores have keys in [0x00800000, 0xFF7FFFFF], so
+    // 4 <= d0 <= 2043 and both bounds are non-NaN floats; comparing floats is
+    // comparing keys (-0.0 and +0.0 share a key and compare equal).  Padding
+    // units hold -inf, below every bound.
+    const float f_lo = key_float(d0 << 21), f_hi = key_float((d0 + 1u) << 21);
+    uint32_t gtm = 0u, cm = 0u;
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      const bool hi = s[j] >= f_hi;
+      const bool in = s[j] >= f_lo && !hi;
+      gtm |= uint32_t(hi) << j;
+      cm |= uint32_t(in) << j;
     }
-    __syncthreads();
-    uint32_t c[BPT1];
-    read_bins<NT, 2048>(sm.hist1, c);
-    pick_bin<NT, 2048>(c, kk, sm.wsum[1], sm.pick);
-    __syncthreads();
-    thr |= sm.pick[0] << 10;
-    kk -= sm.pick[1];
-    settled = kk == sm.pick[2];
+
+    // Narrow the threshold inside d0: thr is a key, eq_take the number of keys
+    // equal to thr to keep (lowest unit ids first), all_eq when that is all of them.
+    uint32_t thr = d0 << 21;
+    bool all_eq = true;
+    bool settled = kk == cnt0;   // every key of digit d0 is needed
     if (!settled) {
       for (uint32_t m = cm; m != 0u; m &= m - 1u) {
         const uint32_t key = float_key(sm.u.sc[first + __builtin_ctz(m)]);
-        if ((key & 0xFFFFFC00u) == thr) atomicAdd(&sm.hist2[key & 1023u], 1u);
+        atomicAdd(&sm.hist1[(key >> 10) & 2047u], 1u);
       }
       __syncthreads();
-      uint32_t c2[BPT2];
-      read_bins<NT, 1024>(sm.hist2, c2);
-      pick_bin<NT, 1024>(c2, kk, sm.wsum[2], sm.pick);
+      uint32_t c[BPT1];
+      read_bins<NT, 2048>(sm.hist1, c);
+      pick_bin<NT, 2048>(c, kk, sm.wsum[1], sm.pick);
       __syncthreads();
-      thr |= sm.pick[0];
+      thr |= sm.pick[0] << 10;
       kk -= sm.pick[1];
-      all_eq = kk == sm.pick[2];
-      eq_take = kk;
+      settled = kk == sm.pick[2];
+      if (!settled) {
+        for (uint32_t m = cm; m != 0u; m &= m - 1u) {
+          const uint32_t key = float_key(sm.u.sc[first + __builtin_ctz(m)]);
+          if ((key & 0xFFFFFC00u) == thr) atomicAdd(&sm.hist2[key & 1023u], 1u);
+        }
+        __syncthreads();
+        uint32_t c2[BPT2];
+        read_bins<NT, 1024>(sm.hist2, c2);
+        pick_bin<NT, 1024>(c2, kk, sm.wsum[2], sm.pick);
+        __syncthreads();
+        thr |= sm.pick[0];
+        kk -= sm.pick[1];
+        all_eq = kk == sm.pick[2];
+        eq_take = kk;
+      }
     }
-  }
 
-  // Kept units of this thread: above d0, plus candidates at or above thr (when
-  // all keys equal to a full-precision thr are kept), or above thr and the
-  // first eq_take equal ones in unit order.
-  uint32_t keepm = gtm, eqm = 0u;
-  if (thr == (d0 << 21) && all_eq) {
-    keepm |= cm;
-  } else {
-    for (uint32_t m = cm; m != 0u; m &= m - 1u) {
-      const int j = __builtin_ctz(m);
-      const uint32_t key = float_key(sm.u.sc[first + j]);
-      if (key > thr || (all_eq && key == thr)) keepm |= 1u << j;
-      else if (key == thr) eqm |= 1u << j;
+    // Kept units of this thread: above d0, plus candidates at or above thr (when
+    // all keys equal to a full-precision thr are kept), or above thr and the
+    // first eq_take equal ones in unit order.
+    keepm = gtm;
+    if (thr == (d0 << 21) && all_eq) {
+      keepm |= cm;
+    } else {
+      for (uint32_t m = cm; m != 0u; m &= m - 1u) {
+        const int j = __builtin_ctz(m);
+        const uint32_t key = float_key(sm.u.sc[first + j]);
+        if (key > thr || (all_eq && key == thr)) keepm |= 1u << j;
+        else if (key == thr) eqm |= 1u << j;
+      }
     }
-  }
+  }   // !compact
   uint32_t tot;
   const uint32_t ex = block_exclusive_scan1<NT>((uint32_t(__popc(keepm)) << 16) | uint32_t(__popc(eqm)),
                                                 sm.wsum[3], tot);
   // Past this barrier (inside the scan) the scores in LDS are dead: sel reuses them.
   const int p_begin = int(split) * a.chunk;   // virtual positions of this split
-  const int p_end = min(min(p_begin + a.chunk, a.kv_virtual), k_row << lb);
+  const int p_end = min(min(p_begin + a.chunk, a.kv_virtual), k_keep << lb);
   const int u_lo = p_begin >> lb;
   const int u_hi = (min(p_begin + a.chunk, a.kv_virtual) + block - 1) >> lb;   // kept-list slots of this split
   {
@@ -435,7 +476,8 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
   __syncthreads();
   if (hchunk == 0) {
     int32_t* ridx = a.indices + int64_t(row) * k_units + u_lo;
-    for (int i = tid; i < u_hi - u_lo; i += NT) ridx[i] = u_lo + i < k_row ? sm.u.a.sel[i] : -1;
+    for (int i = tid; i < u_hi - u_lo; i += NT) ridx[i] = u_lo + i < k_keep ? sm.u.a.sel[i] : -1;
+    if (thresh && split == 0 && tid == 0) a.counts[row] = k_keep;
   }
 
   // Attention over the split's kept rows.
@@ -550,7 +592,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
     }
     const int64_t bh = bh0 + h;
     if (n_split == 1) {
-      a.out[bh * kHeadDim + c] = A / Ls;
+      a.out[bh * kHeadDim + c] = Ls > 0.f ? A / Ls : 0.f;   // nothing kept (threshold rule): zero
     } else {
       __hip_atomic_store(&a.part_acc[(bh * n_split + split) * kHeadDim + c], A, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
@@ -608,7 +650,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
       }
       M = Mb;
     }
-    a.out[bh * kHeadDim + c] = A / L;
+    a.out[bh * kHeadDim + c] = L > 0.f ? A / L : 0.f;   // nothing kept (threshold rule): zero
   }
   if (tid == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -619,12 +661,12 @@ hipError_t launch_one(const FusedArgs& a, dim3 grid, hipStream_t s) {
     hipLaunchKernelGGL((selattn_kernel<TE, NT, ITEMS, HC, true>), grid, dim3(NT), 0, s, a.q, a.scores, a.tile_hist,
                        a.ld, a.G, a.head_chunks, a.n_units, a.tiles, a.k_units, a.lb, a.K, a.V, a.indices, a.part_acc,
                        a.part_ml, a.out, a.tickets, a.T_cap, a.T, a.kv_virtual, a.chunk, a.n_split, a.scale,
-                       a.seq_lens, a.Hkv);
+                       a.seq_lens, a.Hkv, a.tau, a.counts);
   else
     hipLaunchKernelGGL((selattn_kernel<TE, NT, ITEMS, HC, false>), grid, dim3(NT), 0, s, a.q, a.scores, a.tile_hist,
                        a.ld, a.G, a.head_chunks, a.n_units, a.tiles, a.k_units, a.lb, a.K, a.V, a.indices, a.part_acc,
                        a.part_ml, a.out, a.tickets, a.T_cap, a.T, a.kv_virtual, a.chunk, a.n_split, a.scale,
-                       nullptr, a.Hkv);
+                       nullptr, a.Hkv, a.tau, a.counts);
   return hipGetLastError();
 }
 
@@ -652,9 +694,11 @@ hipError_t launch_select_attention(const void* q, const void* K, const void* V, 
                                    int64_t ld, const uint16_t* tile_hist, int Hq, int Hkv, int64_t T_cap, int64_t T,
                                    int block, int64_t k_units, float scale, const DecodePlan& pl, int32_t* indices,
                                    float* part_acc, float* part_ml, float* out, unsigned* tickets,
-                                   const int32_t* seq_lens, hipStream_t s) {
+                                   const int32_t* seq_lens, float tau, int32_t* counts, hipStream_t s) {
   FusedArgs a{};
   a.seq_lens = seq_lens;
+  a.tau = tau;
+  a.counts = counts;
   a.Hkv = Hkv;
   a.q = q;
   a.K = K;

@@ -65,3 +65,54 @@ def check_unit(w, q, K, V, ch, b, g, gpu_out, gpu_idx, scale=None):
     if swaps == 0:
         assert float(np.max(np.abs(ref - out_ref))) == 0.0
     return swaps, err
+
+
+def check_threshold_parity(gpu_idx, gpu_count, u_oracle, tau, k_max, what=""):
+    """Threshold rule: the GPU's kept set (its first `gpu_count` index slots, -1 after them)
+    must equal the oracle's except units whose oracle score lies within TIE_REL of a
+    boundary of the rule: tau, or the k_max-th largest score when the cap can bind.
+    Returns the number of such boundary swaps."""
+    idx = np.asarray(gpu_idx, dtype=np.int64)
+    u = np.asarray(u_oracle, dtype=np.float64)
+    n = int(gpu_count)
+    assert 0 <= n <= k_max and idx.shape == (k_max,), (what, n, idx.shape)
+    assert np.all(idx[n:] == -1), f"{what}: slots past the count are not -1"
+    got = idx[:n]
+    assert np.all(np.diff(got) > 0), f"{what}: indices not strictly ascending"
+    assert n == 0 or (got[0] >= 0 and got[-1] < len(u)), f"{what}: index out of range"
+    ref = O.select_threshold(u, tau, k_max)
+    diff = np.setxor1d(got, ref)
+    if len(diff):
+        bounds = [tau] if np.isfinite(tau) else []
+        if k_max <= len(u):
+            theta = kth_largest(u, k_max)
+            if not np.isfinite(tau) or theta >= tau - TIE_REL * abs(tau):
+                bounds.append(theta)
+        ok = np.zeros(len(diff), dtype=bool)
+        for b in bounds:
+            ok |= np.abs(u[diff] - b) <= TIE_REL * (abs(b) if b != 0 else float(np.max(np.abs(u))))
+        assert ok.all(), (f"{what}: {int((~ok).sum())} kept/dropped units away from the rule's boundaries "
+                          f"(tau={tau}, e.g. {diff[~ok][:5]} scores {u[diff[~ok][:5]]})")
+    return len(diff)
+
+
+def check_threshold_unit(w, q, K, V, ch, b, g, gpu_out, gpu_idx, gpu_counts, tau, scale=None):
+    """Full parity of one unit under the threshold rule: kept set by check_threshold_parity,
+    output against the oracle's attention over the GPU's kept set (zero when it is empty).
+    Returns (boundary swaps, max-abs error, kept count)."""
+    qg, Kf, Vf = unit_inputs(w, q, K, V, b, g)
+    if scale is None:
+        scale = O.default_scale(w.d)
+    out_ref, kept_ref, scores = O.decode_unit_threshold(qg, Kf, Vf, ch[g], w.k_units, tau, w.block, scale, w.T)
+    n = int(gpu_counts[b, g])
+    swaps = check_threshold_parity(gpu_idx[b, g], n, scores, tau, w.k_units, what=f"unit b={b} g={g}")
+    S = O.tokens_of(gpu_idx[b, g, :n], w.block, w.T)
+    ref = O.attend(qg, Kf, Vf, S, scale) if len(S) else np.zeros((w.G, w.d))
+    got = gpu_out[b, g * w.G:(g + 1) * w.G]
+    err = float(np.max(np.abs(got - ref)))
+    assert err <= OUT_TOL[w.dtype], f"unit b={b} g={g}: max-abs error {err} > {OUT_TOL[w.dtype]}"
+    if n == 0:
+        assert np.all(got == 0), f"unit b={b} g={g}: nothing kept but the output is not zero"
+    if swaps == 0:
+        assert float(np.max(np.abs(ref - out_ref))) == 0.0
+    return swaps, err, n

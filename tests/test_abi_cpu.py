@@ -124,6 +124,37 @@ def test_other_entry_points_validate_first():
                                               50, 0.0, FAKE, FAKE, FAKE, big, None) == L.DS_ERR_UNSUPPORTED
     assert lib.ds_decode_select_attend_ragged(*aargs, FAKE, 1, 50, 0.0, None, FAKE, FAKE, ws, None) \
         == L.DS_ERR_INVALID_ARGUMENT
+    # threshold rule: counts, tau, the group size and the fused-path limit are checked on the host
+    ws8 = L.ds_decode_workspace_bytes(2, 8, 2, 128, 1000, 1, 50)
+    targs = (FAKE, FAKE, FAKE, FAKE, FAKE, 16, L.DS_DTYPE_BF16, 2, 8, 2, 128, 1000, 1000, 999, 1, 50)
+    assert lib.ds_decode_sparse_attn_threshold(*targs, 1.0, 0.0, FAKE, FAKE, None, FAKE, ws8, None) \
+        == L.DS_ERR_INVALID_ARGUMENT
+    assert "counts" in L.ds_last_error()
+    assert lib.ds_decode_sparse_attn_threshold(*targs, float("nan"), 0.0, FAKE, FAKE, FAKE, FAKE, ws8, None) \
+        == L.DS_ERR_INVALID_ARGUMENT
+    assert "NaN" in L.ds_last_error()
+    ws16 = L.ds_decode_workspace_bytes(2, 32, 2, 128, 1000, 1, 50)
+    assert lib.ds_decode_sparse_attn_threshold(FAKE, FAKE, FAKE, FAKE, FAKE, 16, L.DS_DTYPE_BF16, 2, 32, 2, 128, 1000,
+                                               1000, 999, 1, 50, 1.0, 0.0, FAKE, FAKE, FAKE, FAKE, ws16, None) \
+        == L.DS_ERR_UNSUPPORTED
+    ws_g8 = L.ds_decode_workspace_bytes(2, 16, 2, 128, 1000, 1, 50)
+    assert lib.ds_decode_sparse_attn_threshold(FAKE, FAKE, FAKE, FAKE, FAKE, 65, L.DS_DTYPE_BF16, 2, 16, 2, 128,
+                                               1000, 1000, 999, 1, 50, 1.0, 0.0, FAKE, FAKE, FAKE, FAKE, ws_g8, None) \
+        == L.DS_ERR_UNSUPPORTED
+    assert "512" in L.ds_last_error()
+    big = L.ds_decode_workspace_bytes(1, 1, 1, 128, 40000, 1, 50)
+    assert lib.ds_decode_sparse_attn_threshold(FAKE, FAKE, FAKE, FAKE, FAKE, 16, L.DS_DTYPE_BF16, 1, 1, 1, 128,
+                                               40000, 40000, 40000, 1, 50, 1.0, 0.0, FAKE, FAKE, FAKE, FAKE, big,
+                                               None) == L.DS_ERR_UNSUPPORTED
+    assert lib.ds_decode_score_threshold(FAKE, FAKE, FAKE, FAKE, 16, L.DS_DTYPE_BF16, 2, 32, 2, 128, 1000, 1000,
+                                         1000, 1, 50, FAKE, ws16, None) == L.DS_ERR_UNSUPPORTED
+    assert lib.ds_decode_select_attend_threshold(FAKE, FAKE, FAKE, L.DS_DTYPE_BF16, 2, 8, 2, 128, 1000, 1000, 1, 50,
+                                                 1.0, 0.0, FAKE, FAKE, None, FAKE, ws8, None) \
+        == L.DS_ERR_INVALID_ARGUMENT
+    assert lib.ds_label_scores_positive(FAKE, FAKE, FAKE, 16, L.DS_DTYPE_BF16, 1, 16, 1, 128, 1024, 1024, 1, FAKE,
+                                        1024, None) == L.DS_ERR_UNSUPPORTED
+    assert lib.ds_label_scores_positive(FAKE, FAKE, FAKE, 16, L.DS_DTYPE_BF16, 1, 8, 1, 128, 1024, 1024, 1, FAKE,
+                                        1022, None) == L.DS_ERR_INVALID_ARGUMENT
     # a valid call afterwards clears the message
     L.ds_decode_workspace_bytes(1, 1, 1, 128, 10, 1, 1)
     assert L.ds_last_error() == ""
