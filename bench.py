@@ -12,7 +12,9 @@ attended over its own length.  The threshold workload (--workload
 jenga_gqa_32k) runs ds_decode_sparse_attn_threshold: positive-only head
 aggregation, block max, and every block scoring at least tau kept (at most
 k_max); its kept-token count, and so its byte count, comes from the call's own
-counts.  Offline calibration is outside the step.  Steps rotate
+counts.  The offload workload (--workload offload_256k) keeps K and V in pinned
+host memory and runs ds_decode_sparse_attn_offload; its roofline is the host
+link, against a measured pinned-to-device copy.  Offline calibration is outside the step.  Steps rotate
 over N independent copies of the cache ("layers") so the per-step working set
 cannot be served from the 256 MB Infinity Cache.  K steps are captured into
 HIP graphs and replayed; the timed region is bracketed by device
@@ -187,7 +189,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=640)
     ap.add_argument("--warmup", type=int, default=64)
-    ap.add_argument("--workload", default=dsgen.HEADLINE, choices=dsgen.WORKLOAD_ORDER + dsgen.RAGGED_ORDER + dsgen.THRESHOLD_ORDER)
+    ap.add_argument("--workload", default=dsgen.HEADLINE, choices=dsgen.WORKLOAD_ORDER + dsgen.RAGGED_ORDER + dsgen.THRESHOLD_ORDER +
+                    dsgen.OFFLOAD_ORDER)
     ap.add_argument("--instances", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -250,10 +253,20 @@ def main():
     torch.cuda.synchronize()
     label_build_us = ev0.elapsed_time(ev1) * 1e3
 
+    if w.offload:
+        # K and V live in pinned host memory; the device keeps q, the label cache and the outputs.
+        def pinned_copy(t):
+            return torch.empty(t.shape, dtype=t.dtype, pin_memory=True).copy_(t)
+        K0, V0 = pinned_copy(K0), pinned_copy(V0)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
     inst = []
     for i in range(n_inst):
         if i == 0:
             qi, Ki, Vi, li = q0, K0, V0, lab0
+        elif w.offload:
+            qi, Ki, Vi, li = q0.clone(), pinned_copy(K0), pinned_copy(V0), lab0.clone()
         else:
             qi, Ki, Vi, li = q0.clone(), K0.clone(), V0.clone(), lab0.clone()
         ws = L.alloc_workspace(w.B, w.Hq, w.Hkv, w.d, w.T, w.block, w.k_units, dev)
@@ -275,6 +288,9 @@ def main():
             L.ds_decode_sparse_attn_threshold(it["q"], it["K"], it["V"], it["label"], chd, w.T, w.k_units, w.tau,
                                               w.block, out=it["out"], indices=it["idx"], counts=it["cnt"],
                                               workspace=it["ws"], t_append=w.T - 1)
+        elif w.offload:
+            L.ds_decode_sparse_attn_offload(it["q"], it["K"], it["V"], it["label"], chd, w.T, w.k_units, w.block,
+                                            out=it["out"], indices=it["idx"], workspace=it["ws"], t_append=w.T - 1)
         else:
             L.ds_decode_sparse_attn(it["q"], it["K"], it["V"], it["label"], chd, w.T, w.k_units, w.block,
                                     out=it["out"], indices=it["idx"], workspace=it["ws"], t_append=w.T - 1)
@@ -391,7 +407,7 @@ def main():
     # The decode step's two phases (its own kernels), then isolated stages for reference
     # (uniform-length top-k stages, so not for a ragged batch or the threshold rule).
     stages = [("decode_score", st_decode_score), ("decode_select_attend", st_decode_select_attend)]
-    if not w.ragged and w.tau is None:
+    if not w.ragged and w.tau is None and not w.offload:
         stages += [("label_append", st_append), ("scores", st_scores), ("select", st_select),
                    ("attention_from_indices", st_attn)]
     for name, fn in stages:
@@ -438,7 +454,8 @@ def main():
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "T": w.T, "r": w.r,
                    "block": w.block, "k_units": w.k_units, "instances": n_inst, "launch": "hip graph replay",
                    "parallelism": "single GPU", **({"seq_lens": lens.tolist()} if w.ragged else {}),
-                   **({"rule": "threshold", "tau": w.tau} if w.tau is not None else {})},
+                   **({"rule": "threshold", "tau": w.tau} if w.tau is not None else {}),
+                   **({"kv_location": "pinned host memory"} if w.offload else {})},
         "us_per_step": round(us_step, 3),
         "us_per_step_eager": round(us_step_eager, 3),
         "algorithmic_bytes_per_step": ab["step"],
@@ -450,6 +467,29 @@ def main():
                      "traffic": recorded_traffic(w.name, dominant),
                      "bytes_per_launch": stage_bytes[dominant], "avg_launch_us": round(kernel_us[dominant], 3)},
     }
+
+    if w.offload:
+        # The host link: kept K/V bytes per select-attend launch against a plain pinned-to-device copy.
+        src = torch.empty(2 ** 30, dtype=torch.uint8, pin_memory=True)
+        dst = torch.empty(2 ** 30, dtype=torch.uint8, device=dev)
+        with torch.cuda.stream(stream):
+            dst.copy_(src, non_blocking=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(5):
+                dst.copy_(src, non_blocking=True)
+            e1.record(stream)
+            torch.cuda.synchronize()
+        h2d_gbs = 5 * 2 ** 30 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del src, dst
+        link_gbs = ab["kv_gather"] / (kernel_us["decode_select_attend"] * 1e-6) / 1e9
+        result["host_link"] = {"kv_bytes_per_step": ab["kv_gather"], "achieved_gbs": round(link_gbs, 2),
+                               "pinned_to_device_copy_gbs": round(h2d_gbs, 2),
+                               "frac_of_copy": round(link_gbs / h2d_gbs, 4)}
+        result["roofline"].update({"bound": "host_link", "achieved": round(link_gbs, 2), "peak": round(h2d_gbs, 2),
+                                   "frac": round(link_gbs / h2d_gbs, 4), "traffic": None,
+                                   "peak_kind": "measured pinned-to-device copy (1 GiB)"})
+        log(f"host link: {link_gbs:.1f} GB/s of kept K/V rows; pinned-to-device copy {h2d_gbs:.1f} GB/s")
 
     if not args.no_cpu and args.cpu_seconds > 0:
         q, K, V = dsgen.gen_cache(w)

@@ -37,6 +37,7 @@ class Workload:
     n_calib: int = 256  # calibration queries per query head and keys per KV head
     ragged: bool = False   # True: sequence lengths drawn per sequence in [T // 16, T] (T is the longest)
     tau: float | None = None   # threshold rule (keep units scoring >= tau, at most k_units); None: top-k
+    offload: bool = False      # True: K and V live in pinned host memory
 
     @property
     def G(self) -> int:
@@ -100,6 +101,17 @@ THRESHOLD_WORKLOADS = {
 }
 WORKLOADS.update(THRESHOLD_WORKLOADS)
 THRESHOLD_ORDER = ["jenga_gqa_32k"]
+
+# Offloaded KV (Double Sparsity page, abstract: the method combines with
+# offloading; it reports its offloading result at 256K tokens): the shape of
+# block64_256k, with K and V in pinned host memory and only the label cache in
+# HBM, so each step reads the kept 64-token blocks across the host link.
+OFFLOAD_WORKLOADS = {
+    "offload_256k": Workload("offload_256k", "bf16", B=1, Hq=32, Hkv=32, d=128, T=262144, r=16, block=64,
+                             k_units=64, seed_base=5000, offload=True),
+}
+WORKLOADS.update(OFFLOAD_WORKLOADS)
+OFFLOAD_ORDER = ["offload_256k"]
 
 # The decode benchmark's headline workload: T=16K, 32 heads, bf16.
 HEADLINE = "llama7b_16k"

@@ -173,13 +173,35 @@ ds_status ds_decode_sparse_attn_ragged(const void* q, const void* K, const void*
                                        size_t workspace_bytes, void* stream);
 
 /*
+ * The decode step with K and V offloaded to host memory (GPU, async).
+ * Post-Training Sparse Attention with Double Sparsity, abstract: the method
+ * combines with offloading to cut GPU memory use.  Only the label cache (r of
+ * d channels), q, the outputs and the workspace stay in device memory; K and V
+ * stay in host memory, and each step moves only the kept rows (and the
+ * channels of the appended rows) across the host link, read in place by the
+ * kernels.  Same steps, kernels and results as ds_decode_sparse_attn.
+ *   K_host, V_host  [B, Hkv, T_cap, d] in pinned host memory that the device
+ *                   can access (hipHostMalloc, or a pinned torch tensor)
+ *   other arguments as for ds_decode_sparse_attn.
+ * Errors: as ds_decode_sparse_attn, plus DS_ERR_INVALID_ARGUMENT when K_host or
+ * V_host is not pinned host memory known to HIP.
+ */
+ds_status ds_decode_sparse_attn_offload(const void* q, const void* K_host, const void* V_host, void* label,
+                                        const int32_t* channels_dev, int32_t r, ds_dtype dt, int32_t B, int32_t Hq,
+                                        int32_t Hkv, int32_t d, int64_t T_cap, int64_t T, int64_t t_append,
+                                        int32_t block, int64_t k_units, float scale, float* out, int32_t* indices,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * ds_decode_sparse_attn in two phases through one workspace: ds_decode_score
  * runs steps 0 and 1 (label-row append and scoring) and leaves the scores and
  * their per-tile histograms in the workspace; ds_decode_select_attend runs
  * steps 2 and 3 from them.  Issued back to back on one stream with the same
  * shape and workspace, they launch exactly the kernels of
  * ds_decode_sparse_attn and give the same results; the split lets a caller
- * time or schedule the phases.  Arguments as for ds_decode_sparse_attn.
+ * time or schedule the phases.  Arguments as for ds_decode_sparse_attn; K and
+ * V may also be pinned host memory the device can access, which is how the
+ * phases of ds_decode_sparse_attn_offload are run on their own.
  */
 ds_status ds_decode_score(const void* q, const void* K, void* label, const int32_t* channels_dev, int32_t r,
                           ds_dtype dt, int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t T_cap, int64_t T,

@@ -60,6 +60,9 @@ _SIGNATURES = {
                                                    _c_vp, _c_vp, _c_size, _c_vp]),
     "ds_label_scores_positive": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64,
                                           _c_i64, _c_i32, _c_vp, _c_i64, _c_vp]),
+    "ds_decode_sparse_attn_offload": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32,
+                                               _c_i32, _c_i32, _c_i64, _c_i64, _c_i64, _c_i32, _c_i64, _c_f32, _c_vp,
+                                               _c_vp, _c_vp, _c_size, _c_vp]),
     "ds_select_attention": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i64,
                                      _c_i32, _c_i64, _c_vp, _c_i64, _c_f32, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
     "ds_label_scores": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i64,
@@ -135,6 +138,19 @@ def _dev(t, name):
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _host(t, name):
+    if t.device.type != "cpu" or not t.is_pinned():
+        raise ValueError(f"{name} must be a pinned host tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _kv(t, name):
+    """K or V: a device tensor, or a pinned host tensor (offloaded cache)."""
+    return _dev(t, name) if t.is_cuda else _host(t, name)
 
 
 def _stream(stream):
@@ -286,6 +302,33 @@ def ds_decode_select_attend_threshold(q, K, V, T: int, k_max: int, tau: float, w
     return out, indices, counts
 
 
+def ds_decode_sparse_attn_offload(q, K, V, label, channels, T: int, k_units: int, block: int = 1, scale: float = 0.0,
+                                  out=None, indices=None, workspace=None, stream=None, t_append: int | None = None):
+    """The decode step with K and V in pinned host memory (everything else on the device).
+    Returns (out fp32 [B, Hq, d], indices int32 [B, Hkv, k_units])."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    _, Hkv, T_cap, _ = K.shape
+    r = channels.shape[1]
+    dt = _dtype_code(q)
+    if K.dtype != q.dtype or V.dtype != q.dtype or label.dtype != q.dtype:
+        raise ValueError("q, K, V and label must share one dtype")
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if indices is None:
+        indices = torch.empty((B, Hkv, k_units), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(B, Hq, Hkv, d, T, block, k_units, q.device)
+    if t_append is None:
+        t_append = T
+    _check(lib().ds_decode_sparse_attn_offload(_dev(q, "q"), _host(K, "K"), _host(V, "V"), _dev(label, "label"),
+                                               _dev(channels, "channels"), r, dt, B, Hq, Hkv, d, T_cap, T, t_append,
+                                               block, k_units, scale, _dev(out, "out"), _dev(indices, "indices"),
+                                               _dev(workspace, "workspace"),
+                                               workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, indices
+
+
 def ds_decode_sparse_attn_ragged(q, K, V, label, channels, seq_lens, T_max: int, k_units: int, block: int = 1,
                                  n_append: int = 1, scale: float = 0.0, out=None, indices=None, workspace=None,
                                  stream=None):
@@ -324,7 +367,7 @@ def ds_decode_score(q, K, label, channels, T: int, k_units: int, block: int = 1,
         workspace = alloc_workspace(B, Hq, Hkv, d, T, block, k_units, q.device)
     if t_append is None:
         t_append = T
-    _check(lib().ds_decode_score(_dev(q, "q"), _dev(K, "K"), _dev(label, "label"), _dev(channels, "channels"), r,
+    _check(lib().ds_decode_score(_dev(q, "q"), _kv(K, "K"), _dev(label, "label"), _dev(channels, "channels"), r,
                                  _dtype_code(q), B, Hq, Hkv, d, T_cap, T, t_append, block, k_units,
                                  _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                                  _stream(stream)))
@@ -341,7 +384,7 @@ def ds_decode_select_attend(q, K, V, T: int, k_units: int, workspace, block: int
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
     if indices is None:
         indices = torch.empty((B, Hkv, k_units), dtype=torch.int32, device=q.device)
-    _check(lib().ds_decode_select_attend(_dev(q, "q"), _dev(K, "K"), _dev(V, "V"), _dtype_code(q), B, Hq, Hkv, d,
+    _check(lib().ds_decode_select_attend(_dev(q, "q"), _kv(K, "K"), _kv(V, "V"), _dtype_code(q), B, Hq, Hkv, d,
                                          T_cap, T, block, k_units, scale, _dev(out, "out"), _dev(indices, "indices"),
                                          _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                                          _stream(stream)))

@@ -410,6 +410,45 @@ ds_status ds_decode_select_attend_ragged(const void* q, const void* K, const voi
                              static_cast<char*>(workspace), static_cast<hipStream_t>(stream), seq_lens_dev);
 }
 
+// The device address of pinned host memory (allocated with hipHostMalloc or
+// registered by the runtime); fails for any other pointer.
+static ds_status host_pinned(const void* p, const char* name, const void*& dev) {
+  hipPointerAttribute_t at{};
+  const hipError_t e = hipPointerGetAttributes(&at, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();   // clear the sticky error of the failed query
+    return fail(DS_ERR_INVALID_ARGUMENT, "%s is not memory known to HIP (%s)", name, hipGetErrorString(e));
+  }
+  if (at.type != hipMemoryTypeHost) return fail(DS_ERR_INVALID_ARGUMENT, "%s must be pinned host memory", name);
+  dev = at.devicePointer ? at.devicePointer : p;
+  return DS_OK;
+}
+
+ds_status ds_decode_sparse_attn_offload(const void* q, const void* K_host, const void* V_host, void* label,
+                                        const int32_t* channels_dev, int32_t r, ds_dtype dt, int32_t B, int32_t Hq,
+                                        int32_t Hkv, int32_t d, int64_t T_cap, int64_t T, int64_t t_append,
+                                        int32_t block, int64_t k_units, float scale, float* out, int32_t* indices,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  ds::DecodePlan pl;
+  if (ds_status st = check_decode_call(q, K_host, V_host, label, channels_dev, r, dt, B, Hq, Hkv, d, T_cap, T,
+                                       t_append, block, k_units, out, indices, workspace, workspace_bytes, true, true,
+                                       pl))
+    return st;
+  const void* Kd = nullptr;
+  const void* Vd = nullptr;
+  if (ds_status st = host_pinned(K_host, "K", Kd)) return st;
+  if (ds_status st = host_pinned(V_host, "V", Vd)) return st;
+  if (!aligned(Kd, 16) || !aligned(Vd, 16)) return fail(DS_ERR_INVALID_ARGUMENT, "misaligned device address of K or V");
+  if (!(scale > 0.f)) scale = 1.0f / std::sqrt(float(d));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  if (ds_status st = decode_score_stage(q, Kd, label, channels_dev, r, dt, B, Hq, Hkv, T_cap, T, t_append, block, pl,
+                                        ws, s))
+    return st;
+  return decode_select_stage(q, Kd, Vd, dt, B, Hq, Hkv, T_cap, T, block, k_units, scale, pl, out, indices, ws, s);
+}
+
 ds_status ds_decode_score(const void* q, const void* K, void* label, const int32_t* channels_dev, int32_t r,
                           ds_dtype dt, int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t T_cap, int64_t T,
                           int64_t t_append, int32_t block, int64_t k_units, void* workspace, size_t workspace_bytes,

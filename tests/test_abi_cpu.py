@@ -155,6 +155,13 @@ def test_other_entry_points_validate_first():
                                         1024, None) == L.DS_ERR_UNSUPPORTED
     assert lib.ds_label_scores_positive(FAKE, FAKE, FAKE, 16, L.DS_DTYPE_BF16, 1, 8, 1, 128, 1024, 1024, 1, FAKE,
                                         1022, None) == L.DS_ERR_INVALID_ARGUMENT
+    # offloaded K/V: null pointers fail first; a pointer HIP does not know is rejected before any launch
+    oargs = (16, L.DS_DTYPE_BF16, 2, 4, 4, 128, 1000, 1000, 999, 1, 50, 0.0)
+    assert lib.ds_decode_sparse_attn_offload(FAKE, None, FAKE, FAKE, FAKE, *oargs, FAKE, FAKE, FAKE, ws, None) \
+        == L.DS_ERR_INVALID_ARGUMENT
+    assert lib.ds_decode_sparse_attn_offload(FAKE, FAKE, FAKE, FAKE, FAKE, *oargs, FAKE, FAKE, FAKE, ws, None) \
+        == L.DS_ERR_INVALID_ARGUMENT
+    assert "K" in L.ds_last_error()
     # a valid call afterwards clears the message
     L.ds_decode_workspace_bytes(1, 1, 1, 128, 10, 1, 1)
     assert L.ds_last_error() == ""
