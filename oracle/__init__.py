@@ -9,9 +9,9 @@ fixtures); none is "parity unpinned".
 from .ds_oracle import (calibrate_channels, label_rows, label_scores, block_scores, select_topk,
                         blocks_to_tokens, attention_weights, attend, attend_partial, merge_partials,
                         default_scale, decode_unit, tokens_of, label_scores_positive, select_threshold,
-                        decode_unit_threshold)
+                        decode_unit_threshold, group_token_scores, hip_search, spans_to_tokens, decode_unit_hip)
 
 __all__ = ["calibrate_channels", "label_rows", "label_scores", "block_scores", "select_topk",
            "blocks_to_tokens", "attention_weights", "attend", "attend_partial", "merge_partials",
            "default_scale", "decode_unit", "tokens_of", "label_scores_positive", "select_threshold",
-           "decode_unit_threshold"]
+           "decode_unit_threshold", "group_token_scores", "hip_search", "spans_to_tokens", "decode_unit_hip"]

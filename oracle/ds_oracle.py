@@ -262,3 +262,72 @@ def decode_unit_threshold(q_group, K, V, ch, k_max, tau, block=1, scale=None, T=
     if len(S) == 0:
         return np.zeros((np.asarray(q_group).shape[0], K.shape[1])), kept, scores
     return attend(q_group, K, V, S, scale), kept, scores
+
+
+# -- hierarchical span search (HiP page, abstract) ---------------------------
+
+def group_token_scores(q_group, K, tokens):
+    """Score of each listed key token for the query group: float32 of the float64
+    sum over the group's query heads of q_h . K_t (no scale; a positive scale
+    cannot change a ranking).  The search ranks these float32 values."""
+    qs = np.asarray(q_group, dtype=np.float64).sum(axis=0)        # [d]
+    s = np.asarray(K, dtype=np.float64)[np.asarray(tokens, dtype=np.int64)] @ qs
+    return s.astype(np.float32)
+
+
+def hip_search(q_group, K, T, k, span):
+    """Top-k key spans by hierarchical pruning, as (start, end) pairs ascending.
+
+    HiP page, abstract: nearby key tokens tend to have similar attention scores
+    ("attention locality"), so a tree-search-like procedure estimates the top-k
+    keys of a query on the fly in O(log T) rounds.  The page gives no further
+    detail; the procedure taken is a beam search over the binary halving tree:
+      * start from k spans splitting [0, T) evenly (span i is
+        [floor(i T / k), floor((i + 1) T / k)));
+      * each round, split every span longer than `span` tokens into a left half
+        of ceil(len / 2) tokens and a right half of the rest (shorter spans go
+        on whole), score every candidate by its first token, and keep the k
+        highest-scoring candidates (ties to the lower start);
+      * stop when no span is longer than `span` tokens.
+    Requires 1 <= k <= T and span >= 1.
+    """
+    if not (1 <= k <= T) or span < 1:
+        raise ValueError("need 1 <= k <= T and span >= 1")
+    spans = [(i * T // k, (i + 1) * T // k) for i in range(k)]
+    score = dict(zip([s for s, _ in spans], group_token_scores(q_group, K, [s for s, _ in spans])))
+    while any(e - s > span for s, e in spans):
+        cand = []
+        for s, e in spans:
+            if e - s > span:
+                m = s + (e - s + 1) // 2
+                cand += [(s, m), (m, e)]
+            else:
+                cand.append((s, e))
+        new = [c[0] for c in cand if c[0] not in score]
+        if new:
+            score.update(zip(new, group_token_scores(q_group, K, new)))
+        keys = np.array([score[s] for s, _ in cand], dtype=np.float32)
+        order = np.argsort(-keys.astype(np.float64), kind="stable")   # candidates are in start order
+        keep = np.sort(order[:k])
+        spans = [cand[i] for i in keep]
+    return spans
+
+
+def spans_to_tokens(spans):
+    """Token ids covered by the spans, ascending."""
+    return np.concatenate([np.arange(s, e, dtype=np.int64) for s, e in spans]) if spans else \
+        np.zeros(0, dtype=np.int64)
+
+
+def decode_unit_hip(q_group, K, V, k, span, scale=None, T=None):
+    """Decode for one unit with the hierarchical span search: attention over the
+    tokens of the k kept spans.  Returns (out [G, d], kept spans)."""
+    K = np.asarray(K, dtype=np.float64)
+    if T is None:
+        T = K.shape[0]
+    K = K[:T]
+    V = np.asarray(V, dtype=np.float64)[:T]
+    if scale is None:
+        scale = default_scale(K.shape[1])
+    spans = hip_search(q_group, K, T, k, span)
+    return attend(q_group, K, V, spans_to_tokens(spans), scale), spans

@@ -270,6 +270,49 @@ def check_golden_threshold_unit(ns):
             np.testing.assert_allclose(out, np.array(case["out"]), rtol=0, atol=1e-12, err_msg=case["why"])
 
 
+def _hip_K(case):
+    """K [T, 4] from the fixture's column formulas of the token position t."""
+    T = case["T"]
+    t = np.arange(T, dtype=np.float64)
+    forms = {"t": t, "-t": -t, "-2t": -2 * t, "-|t-37|": -np.abs(t - 37)}
+    K = np.zeros((T, 4))
+    for col, f in case["K_col"].items():
+        K[:, int(col)] = forms[f]
+    return K
+
+
+def check_golden_hip(ns):
+    with open(os.path.join(HERE, "golden", "hand_worked.json")) as f:
+        gold = json.load(f)["hierarchical"]
+    for case in gold["cases"]:
+        q = np.array(case["q"], dtype=np.float64)
+        got = [list(sp) for sp in ns.hip_search(q, _hip_K(case), case["T"], case["k"], case["span"])]
+        assert got == case["spans"], (case["why"], got)
+
+
+def check_hip_structure(ns, seed=13):
+    """Random inputs: k disjoint ascending spans, each inside one of the first even spans, none
+    longer than `span` (or the first spans themselves when no round runs), and rising scores
+    keep the k rightmost spans of the last level when T, k and span are powers of two."""
+    rng = np.random.default_rng(seed)
+    for T, k, span, G in ((97, 5, 3, 2), (1000, 16, 8, 1), (4096, 32, 16, 4), (64, 64, 1, 1)):
+        q = rng.standard_normal((G, 8))
+        K = rng.standard_normal((T, 8))
+        spans = ns.hip_search(q, K, T, k, span)
+        assert len(spans) == k
+        first = [(i * T // k, (i + 1) * T // k) for i in range(k)]
+        no_round = max(e - s for s, e in first) <= span
+        for i, (s, e) in enumerate(spans):
+            assert 0 <= s < e <= T and (i == 0 or spans[i - 1][1] <= s)
+            assert any(fs <= s and e <= fe for fs, fe in first)
+            assert (s, e) in first if no_round else e - s <= span
+    for T, k, span in ((256, 4, 8), (1024, 8, 4)):
+        K = np.zeros((T, 2))
+        K[:, 0] = np.cumsum(rng.random(T) + 0.1)   # strictly rising scores
+        spans = ns.hip_search(np.array([[1.0, 0.0]]), K, T, k, span)
+        assert spans == [(T - (k - i) * span, T - (k - i - 1) * span) for i in range(k)]
+
+
 # ---------------------------------------------------------------- pins
 
 def test_calibration_matches_all_pairs_brute_force():
@@ -482,6 +525,40 @@ def test_threshold_decode_reduces_to_topk_on_positive_scores():
                                    rtol=0, atol=1e-12)
 
 
+def test_hip_search_hand_worked_fixture():
+    check_golden_hip(O)
+
+
+def test_hip_search_structure_and_monotone_closed_form():
+    check_hip_structure(O)
+
+
+def check_group_scores(ns, seed=14):
+    """Group score = float32 of the exact sum over heads of q_h . K_t (brute force with fsum)."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((3, 16))
+    K = rng.standard_normal((40, 16))
+    toks = [0, 5, 39, 17]
+    got = ns.group_token_scores(q, K, toks)
+    want = [np.float32(math.fsum(float(q[h, c]) * float(K[t, c]) for h in range(3) for c in range(16))) for t in toks]
+    assert got.dtype == np.float32 and list(got) == want
+
+
+def test_hip_group_scores_are_float32_of_exact_dot():
+    check_group_scores(O)
+
+
+def test_hip_decode_without_rounds_is_dense_attention():
+    """When the first k spans are no longer than `span`, every token is kept: dense attention."""
+    rng = np.random.default_rng(15)
+    q = rng.standard_normal((2, 32))
+    K = rng.standard_normal((100, 32))
+    V = rng.standard_normal((100, 32))
+    out, spans = O.decode_unit_hip(q, K, V, 10, 10)
+    np.testing.assert_allclose(out, O.attend(q, K, V, np.arange(100), O.default_scale(32)), rtol=0, atol=1e-12)
+    assert list(O.spans_to_tokens(spans)) == list(range(100))
+
+
 # ---------------------------------------------------------------- planted mistakes
 
 def _mut_calib_sum_not_product(q_cal, k_cal, Hkv, r):
@@ -606,7 +683,38 @@ def _mut_unit_empty_nan(q_group, K, V, ch, k_max, tau, block=1, scale=None, T=No
     return out, kept, scores
 
 
+def _hip_variant(ties_high=False, floor_left=False, last_rep=False, extra=0, early_stop=False):
+    def search(q_group, K, T, k, span):
+        spans = [(i * T // k, (i + 1) * T // k) for i in range(k)]
+        rep = (lambda s, e: e - 1) if last_rep else (lambda s, e: s)
+        while any(e - s > (2 * span if early_stop else span) for s, e in spans):
+            cand = []
+            for s, e in spans:
+                if e - s > span:
+                    m = s + ((e - s) // 2 if floor_left else (e - s + 1) // 2)
+                    cand += [(s, m), (m, e)]
+                else:
+                    cand.append((s, e))
+            keys = O.group_token_scores(q_group, K, [rep(s, e) for s, e in cand]).astype(np.float64)
+            idx = np.arange(len(cand))
+            order = (idx[::-1][np.argsort(-keys[::-1], kind="stable")] if ties_high
+                     else np.argsort(-keys, kind="stable"))
+            spans = [cand[i] for i in np.sort(order[:k + extra])]
+        return spans
+    return search
+
+
+def _mut_hip_one_head(q_group, K, tokens):
+    return O.group_token_scores(np.asarray(q_group)[:1], K, tokens)
+
+
 MUTANTS = [
+    ("hip_search", _hip_variant(ties_high=True), check_golden_hip),
+    ("hip_search", _hip_variant(floor_left=True), check_golden_hip),
+    ("hip_search", _hip_variant(last_rep=True), check_golden_hip),
+    ("hip_search", _hip_variant(extra=1), check_hip_structure),
+    ("hip_search", _hip_variant(early_stop=True), check_hip_structure),
+    ("group_token_scores", _mut_hip_one_head, check_group_scores),
     ("label_scores_positive", _mut_pos_signed, check_positive_scores_brute),
     ("label_scores_positive", _mut_pos_clip_after_sum, check_positive_scores_brute),
     ("label_scores_positive", _mut_pos_abs, check_positive_scores_brute),
