@@ -12,7 +12,9 @@ attended over its own length.  The threshold workload (--workload
 jenga_gqa_32k) runs ds_decode_sparse_attn_threshold: positive-only head
 aggregation, block max, and every block scoring at least tau kept (at most
 k_max); its kept-token count, and so its byte count, comes from the call's own
-counts.  The offload workload (--workload offload_256k) keeps K and V in pinned
+counts.  The span-search workload (--workload hip_1m) runs ds_decode_hip_attn
+over one million tokens: the search phase is ds_hip_search, the attention phase
+ds_sparse_attn_from_indices over its token list.  The offload workload (--workload offload_256k) keeps K and V in pinned
 host memory and runs ds_decode_sparse_attn_offload; its roofline is the host
 link, against a measured pinned-to-device copy.  Offline calibration is outside the step.  Steps rotate
 over N independent copies of the cache ("layers") so the per-step working set
@@ -47,6 +49,8 @@ import dsgen  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 METRIC = "sparse decode attention µs/step + achieved HBM GB/s (T=16K, 32 heads, bf16)"
 MALL_BYTES = 256 * 2 ** 20
+# The two phases of the span-search step, timed through ds_hip_search and ds_sparse_attn_from_indices.
+PHASE_NAMES = {"decode_score": "hip_search", "decode_select_attend": "attention_from_indices"}
 
 
 def log(msg):
@@ -82,12 +86,28 @@ def recorded_traffic(workload: str, stage: str):
     return None
 
 
+def hip_rounds(w: dsgen.Workload) -> int:
+    """Rounds of the span search: halvings of ceil(T / k) until it is at most the final span length."""
+    n, r = -(-w.T // w.k_units), 0
+    while n > w.block:
+        n, r = -(-n // 2), r + 1
+    return r
+
+
 def algorithmic_bytes(w: dsgen.Workload, lens=None, kept=None) -> dict:
     """Bytes the method must move per step (score workspace, split partials and
     the label build are excluded).  lens: per-sequence lengths of a ragged batch.
     kept: (kept tokens, kept units) summed over the rows, for the threshold rule,
     whose kept counts depend on the data."""
     e = w.elem_bytes
+    if w.hip:
+        # kept = (kept tokens, representative tokens scored), summed over the rows
+        kept_tokens, scored = kept if kept is not None else (w.B * w.Hkv * w.k_units * w.block,
+                                                             w.B * w.Hkv * w.k_units * (1 + hip_rounds(w)))
+        parts = {"search_keys": scored * w.d * e, "kv_gather": 2 * kept_tokens * w.d * e,
+                 "q": w.B * w.Hq * w.d * e, "out": 4 * w.B * w.Hq * w.d, "spans": 8 * w.B * w.Hkv * w.k_units}
+        parts["step"] = sum(parts.values())
+        return parts
     if lens is None:
         lens = [w.T] * w.B
     tokens = sum(int(t) for t in lens)
@@ -136,7 +156,9 @@ def _oracle_init():
 def _oracle_task(i):
     import oracle as O
     qg, Kf, Vf, ch, k, block, T, tau = _ORACLE_UNITS[i]
-    if tau is None:
+    if ch is None:   # span search: k spans, final span length `block`
+        O.decode_unit_hip(qg, Kf, Vf, k, block, None, T)
+    elif tau is None:
         O.decode_unit(qg, Kf, Vf, ch, k, block, None, T)
     else:
         O.decode_unit_threshold(qg, Kf, Vf, ch, k, tau, block, None, T)
@@ -153,6 +175,8 @@ def cpu_baseline(w, q, K, V, ch, seconds: float, lens):
     if w.ragged:
         per = max(1, min(w.Hkv, 64 // w.B))
         sample = [(b, g) for b in range(w.B) for g in range(per)]
+    elif w.hip:
+        sample = units[:4]   # float64 copies of million-token rows: 2 GB per unit
     else:
         sample = units[:64]
     G = w.G
@@ -161,7 +185,8 @@ def cpu_baseline(w, q, K, V, ch, seconds: float, lens):
         Tb = int(lens[b])
         k_b = min(w.k_units, -(-Tb // w.block))
         return (dsgen.to_f64(q[b, g * G:(g + 1) * G], w.dtype), dsgen.to_f64(K[b, g, :Tb], w.dtype),
-                dsgen.to_f64(V[b, g, :Tb], w.dtype), ch[g], k_b, w.block, Tb, w.tau)
+                dsgen.to_f64(V[b, g, :Tb], w.dtype), None if w.hip else ch[g], w.k_units if w.hip else k_b,
+                w.block, Tb, w.tau)
 
     _ORACLE_UNITS = [unit(b, g) for b, g in sample]
     cores = max(1, min(16, len(os.sched_getaffinity(0)), len(sample)))
@@ -190,7 +215,7 @@ def main():
     ap.add_argument("--steps", type=int, default=640)
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--workload", default=dsgen.HEADLINE, choices=dsgen.WORKLOAD_ORDER + dsgen.RAGGED_ORDER + dsgen.THRESHOLD_ORDER +
-                    dsgen.OFFLOAD_ORDER)
+                    dsgen.OFFLOAD_ORDER + dsgen.HIP_ORDER)
     ap.add_argument("--instances", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -243,15 +268,17 @@ def main():
     q0, K0, V0 = up(q), up(K), up(V)
     chd = torch.from_numpy(ch).to(dev)
     seq = torch.from_numpy(lens).to(dev)
-    # full label build, timed on its own (prefill cost, not part of the step)
-    lab0 = L.ds_build_label_cache(K0, chd)
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    L.ds_build_label_cache(K0, chd, label=lab0)
-    ev1.record()
-    torch.cuda.synchronize()
-    label_build_us = ev0.elapsed_time(ev1) * 1e3
+    # full label build, timed on its own (prefill cost, not part of the step); the span search uses none
+    lab0, label_build_us = None, None
+    if not w.hip:
+        lab0 = L.ds_build_label_cache(K0, chd)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        L.ds_build_label_cache(K0, chd, label=lab0)
+        ev1.record()
+        torch.cuda.synchronize()
+        label_build_us = ev0.elapsed_time(ev1) * 1e3
 
     if w.offload:
         # K and V live in pinned host memory; the device keeps q, the label cache and the outputs.
@@ -268,19 +295,31 @@ def main():
         elif w.offload:
             qi, Ki, Vi, li = q0.clone(), pinned_copy(K0), pinned_copy(V0), lab0.clone()
         else:
-            qi, Ki, Vi, li = q0.clone(), K0.clone(), V0.clone(), lab0.clone()
-        ws = L.alloc_workspace(w.B, w.Hq, w.Hkv, w.d, w.T, w.block, w.k_units, dev)
+            qi, Ki, Vi, li = q0.clone(), K0.clone(), V0.clone(), (lab0.clone() if lab0 is not None else None)
+        extra = {}
+        if w.hip:
+            ws = torch.empty(L.lib().ds_hip_workspace_bytes(w.B, w.Hq, w.Hkv, w.d, w.T, w.k_units, w.block),
+                             dtype=torch.uint8, device=dev)
+            cap = L.ds_hip_token_capacity(w.T, w.k_units, w.block)
+            extra = dict(spans=torch.empty((w.B, w.Hkv, w.k_units, 2), dtype=torch.int32, device=dev),
+                         tokens=torch.empty((w.B, w.Hkv, cap), dtype=torch.int32, device=dev),
+                         ws_attn=L.alloc_workspace(w.B, w.Hq, w.Hkv, w.d, w.T, 1, cap, dev))
+        else:
+            ws = L.alloc_workspace(w.B, w.Hq, w.Hkv, w.d, w.T, w.block, w.k_units, dev)
         out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
         idx = torch.empty((w.B, w.Hkv, w.k_units), dtype=torch.int32, device=dev)
         cnt = torch.empty((w.B, w.Hkv), dtype=torch.int32, device=dev)
-        inst.append(dict(q=qi, K=Ki, V=Vi, label=li, ws=ws, out=out, idx=idx, cnt=cnt))
+        inst.append(dict(q=qi, K=Ki, V=Vi, label=li, ws=ws, out=out, idx=idx, cnt=cnt, **extra))
     del q, K, V
     torch.cuda.synchronize()
     log(f"{n_inst} instances resident ({torch.cuda.memory_allocated() / 2 ** 30:.1f} GiB)")
 
     def step(i):
         it = inst[i % n_inst]
-        if w.ragged:
+        if w.hip:
+            L.ds_decode_hip_attn(it["q"], it["K"], it["V"], w.T, w.k_units, w.block, out=it["out"],
+                                 spans=it["spans"], workspace=it["ws"])
+        elif w.ragged:
             L.ds_decode_sparse_attn_ragged(it["q"], it["K"], it["V"], it["label"], chd, seq, w.T, w.k_units,
                                            w.block, n_append=1, out=it["out"], indices=it["idx"],
                                            workspace=it["ws"])
@@ -297,6 +336,14 @@ def main():
 
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
+    if w.hip:
+        # Kept tokens from the call's own spans (the tests check them against the oracle).
+        step(0)
+        torch.cuda.synchronize()
+        sp = inst[0]["spans"].cpu().numpy()
+        kept_tokens = int((sp[..., 1] - sp[..., 0]).sum())
+        ab = algorithmic_bytes(w, None, (kept_tokens, w.B * w.Hkv * w.k_units * (1 + hip_rounds(w))))
+        log(f"span search: {hip_rounds(w)} rounds, {kept_tokens} tokens kept; algorithmic bytes/step {ab['step']}")
     if w.tau is not None:
         # The threshold rule keeps a data-dependent number of units: count the kept
         # tokens from the call's own output (the tests check it against the oracle).
@@ -372,7 +419,9 @@ def main():
 
     def st_decode_score(i):
         it = inst[i % n_inst]
-        if w.ragged:
+        if w.hip:
+            L.ds_hip_search(it["q"], it["K"], w.T, w.k_units, w.block, spans=it["spans"], tokens=it["tokens"])
+        elif w.ragged:
             L.ds_decode_score_ragged(it["q"], it["K"], it["label"], chd, seq, w.T, w.k_units, w.block, n_append=1,
                                      workspace=it["ws"])
         elif w.tau is not None:
@@ -384,7 +433,10 @@ def main():
 
     def st_decode_select_attend(i):
         it = inst[i % n_inst]
-        if w.ragged:
+        if w.hip:
+            L.ds_sparse_attn_from_indices(it["q"], it["K"], it["V"], it["tokens"], w.T, 1, out=it["out"],
+                                          workspace=it["ws_attn"])
+        elif w.ragged:
             L.ds_decode_select_attend_ragged(it["q"], it["K"], it["V"], seq, w.T, w.k_units, it["ws"], w.block,
                                              out=it["out"], indices=it["idx"])
         elif w.tau is not None:
@@ -407,7 +459,7 @@ def main():
     # The decode step's two phases (its own kernels), then isolated stages for reference
     # (uniform-length top-k stages, so not for a ragged batch or the threshold rule).
     stages = [("decode_score", st_decode_score), ("decode_select_attend", st_decode_select_attend)]
-    if not w.ragged and w.tau is None and not w.offload:
+    if not w.ragged and w.tau is None and not w.offload and not w.hip:
         stages += [("label_append", st_append), ("scores", st_scores), ("select", st_select),
                    ("attention_from_indices", st_attn)]
     for name, fn in stages:
@@ -424,15 +476,22 @@ def main():
         del g
     log("per-stage us: " + ", ".join(f"{k}={v:.2f}" for k, v in kernel_us.items()))
 
-    stage_bytes = {
-        "decode_score": ab["label_scan"] + ab["q"] + ab["label_append"] + ab.get("seq_lens", 0),
-        "decode_select_attend": ab["kv_gather"] + ab["q"] + ab["indices"] + ab["out"] + ab.get("seq_lens", 0) +
-        ab.get("counts", 0),
-        "label_append": ab["label_append"],
-        "scores": ab["label_scan"] + ab["q"],
-        "select": ab["indices"],
-        "attention_from_indices": ab["kv_gather"] + ab["q"] + ab["indices"] + ab["out"],
-    }
+    if w.hip:
+        # the search (representative K rows, q, spans) and the attention over the kept tokens (reading
+        # their int32 ids)
+        kept_tok = ab["kv_gather"] // (2 * w.d * w.elem_bytes)
+        stage_bytes = {"decode_score": ab["search_keys"] + ab["q"] + ab["spans"],
+                       "decode_select_attend": ab["kv_gather"] + ab["q"] + ab["out"] + 4 * kept_tok}
+    else:
+        stage_bytes = {
+            "decode_score": ab["label_scan"] + ab["q"] + ab["label_append"] + ab.get("seq_lens", 0),
+            "decode_select_attend": ab["kv_gather"] + ab["q"] + ab["indices"] + ab["out"] + ab.get("seq_lens", 0) +
+            ab.get("counts", 0),
+            "label_append": ab["label_append"],
+            "scores": ab["label_scan"] + ab["q"],
+            "select": ab["indices"],
+            "attention_from_indices": ab["kv_gather"] + ab["q"] + ab["indices"] + ab["out"],
+        }
     # the decode step's phases: the score pass and selection + attention
     dominant = max(("decode_score", "decode_select_attend"), key=lambda k: kernel_us[k])
     dom_gbs = stage_bytes[dominant] / (kernel_us[dominant] * 1e-6) / 1e9
@@ -455,14 +514,16 @@ def main():
                    "block": w.block, "k_units": w.k_units, "instances": n_inst, "launch": "hip graph replay",
                    "parallelism": "single GPU", **({"seq_lens": lens.tolist()} if w.ragged else {}),
                    **({"rule": "threshold", "tau": w.tau} if w.tau is not None else {}),
-                   **({"kv_location": "pinned host memory"} if w.offload else {})},
+                   **({"kv_location": "pinned host memory"} if w.offload else {}),
+                   **({"rule": "hierarchical span search", "k_spans": w.k_units, "span": w.block,
+                       "rounds": hip_rounds(w)} if w.hip else {})},
         "us_per_step": round(us_step, 3),
         "us_per_step_eager": round(us_step_eager, 3),
         "algorithmic_bytes_per_step": ab["step"],
         "step_roofline_frac": round(gbs / HBM_PEAK_GBS, 4),
-        "label_build_us": round(label_build_us, 2),
-        "stage_us": {k: round(v, 3) for k, v in kernel_us.items()},
-        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
+        "label_build_us": round(label_build_us, 2) if label_build_us is not None else None,
+        "stage_us": {PHASE_NAMES.get(k, k) if w.hip else k: round(v, 3) for k, v in kernel_us.items()},
+        "roofline": {"bound": "hbm", "kernel": PHASE_NAMES.get(dominant, dominant) if w.hip else dominant, "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(w.name, dominant),
                      "bytes_per_launch": stage_bytes[dominant], "avg_launch_us": round(kernel_us[dominant], 3)},

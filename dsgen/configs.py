@@ -38,6 +38,7 @@ class Workload:
     ragged: bool = False   # True: sequence lengths drawn per sequence in [T // 16, T] (T is the longest)
     tau: float | None = None   # threshold rule (keep units scoring >= tau, at most k_units); None: top-k
     offload: bool = False      # True: K and V live in pinned host memory
+    hip: bool = False          # True: hierarchical span search; k_units = spans kept, block = longest final span
 
     @property
     def G(self) -> int:
@@ -112,6 +113,17 @@ OFFLOAD_WORKLOADS = {
 }
 WORKLOADS.update(OFFLOAD_WORKLOADS)
 OFFLOAD_ORDER = ["offload_256k"]
+
+# Hierarchical span search (HiP page, abstract: O(log T) rounds, contexts of
+# millions of tokens): one million tokens, a 32/8 GQA group of a Llama-like
+# model, 64 spans of at most 64 tokens kept per KV head (4,096 of 1,048,576
+# tokens).  No label cache is used.
+HIP_WORKLOADS = {
+    "hip_1m": Workload("hip_1m", "bf16", B=2, Hq=32, Hkv=8, d=128, T=1 << 20, r=16, block=64, k_units=64,
+                       seed_base=8000, hip=True),
+}
+WORKLOADS.update(HIP_WORKLOADS)
+HIP_ORDER = ["hip_1m"]
 
 # The decode benchmark's headline workload: T=16K, 32 heads, bf16.
 HEADLINE = "llama7b_16k"

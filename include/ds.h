@@ -286,6 +286,51 @@ ds_status ds_decode_select_attend_threshold(const void* q, const void* K, const 
                                             size_t workspace_bytes, void* stream);
 
 /*
+ * Decode with a hierarchical span search instead of label scores (GPU, async).
+ * A Training-free Sub-quadratic Cost Transformer Model Serving Framework With
+ * Hierarchically Pruned Attention, abstract: nearby key tokens tend to have
+ * similar attention scores, so the top-k keys of a query can be estimated by a
+ * tree-search-like procedure in O(log T) rounds.  The page gives no algorithm;
+ * this library's, per row (sequence b, KV head g):
+ *   0. k_spans spans split [0, T) evenly: span i = [floor(i T / k), floor((i+1) T / k));
+ *   1. each round, every span longer than `span` tokens is cut into a left part
+ *      of ceil(len / 2) tokens and the rest (shorter spans go on whole); each
+ *      candidate is scored by its first token t, as the float32 of the exact
+ *      double sum over the group's query heads of q_h . K[b, g, t]; the
+ *      k_spans best candidates are kept, the lower start winning a tie;
+ *   2. the rounds stop when no span is longer than `span` tokens;
+ *   3. softmax attention (scale, 1/sqrt(d) when <= 0) over the tokens of the
+ *      kept spans.
+ *   k_spans  1 <= k_spans <= min(T, 1024)
+ *   span     >= 1: longest span the search ends with
+ *   out      device fp32 [B, Hq, d]
+ *   spans    device int32 [B, Hkv, k_spans, 2]: kept (start, end) pairs, ascending
+ *   workspace  ds_hip_workspace_bytes(...) bytes, 256-byte aligned
+ * No label cache is used.  Errors: DS_ERR_INVALID_ARGUMENT / UNSUPPORTED as
+ * for ds_decode_sparse_attn, DS_ERR_WORKSPACE_TOO_SMALL, DS_ERR_HIP.
+ */
+ds_status ds_decode_hip_attn(const void* q, const void* K, const void* V, ds_dtype dt, int32_t B, int32_t Hq,
+                             int32_t Hkv, int32_t d, int64_t T_cap, int64_t T, int32_t k_spans, int32_t span,
+                             float scale, float* out, int32_t* spans, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Workspace bytes of ds_decode_hip_attn, or 0 (ds_last_error set) for an invalid shape. */
+size_t ds_hip_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t T, int32_t k_spans,
+                              int32_t span);
+
+/* Tokens one row of the search can cover: k_spans * span when a round runs,
+ * else T (the first spans cover every token); 0 for invalid arguments. */
+int64_t ds_hip_token_capacity(int64_t T, int64_t k_spans, int64_t span);
+
+/* Steps 0-2 only: the kept spans [B, Hkv, k_spans, 2] and the covered token
+ * ids tokens [B, Hkv, capacity] (int32, ascending, -1 after the last), with
+ * capacity = ds_hip_token_capacity(T, k_spans, span).  Step 3 is then
+ * ds_sparse_attn_from_indices with block = 1 and k_units = capacity. */
+ds_status ds_hip_search(const void* q, const void* K, ds_dtype dt, int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
+                        int64_t T_cap, int64_t T, int32_t k_spans, int32_t span, int32_t* spans, int32_t* tokens,
+                        void* stream);
+
+/*
  * Stages of the decode step fed from caller buffers, so each can be checked in
  * isolation against independently computed inputs.
  */
@@ -319,7 +364,8 @@ ds_status ds_select_attention(const void* q, const void* K, const void* V, ds_dt
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Step 3 only: attention over the units listed in `indices` (as
- * ds_decode_sparse_attn writes them: ascending, distinct, each < ceil(T/block)).
+ * ds_decode_sparse_attn writes them: ascending, distinct, each < ceil(T/block);
+ * entries of -1 are skipped, as ds_hip_search pads its token lists).
  * Workspace as for ds_decode_sparse_attn. */
 ds_status ds_sparse_attn_from_indices(const void* q, const void* K, const void* V, ds_dtype dt, int32_t B,
                                       int32_t Hq, int32_t Hkv, int32_t d, int64_t T_cap, int64_t T,

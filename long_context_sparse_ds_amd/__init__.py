@@ -8,6 +8,8 @@ A thin Python binding over libdsparse.so (C ABI declared in include/ds.h):
 
 plus the decode step for sequences of unequal lengths (ds_decode_sparse_attn_ragged),
 the decode step with K and V in pinned host memory (ds_decode_sparse_attn_offload),
+decode with a hierarchical span search (ds_decode_hip_attn, its search ds_hip_search,
+ds_hip_workspace_bytes, ds_hip_token_capacity),
 the decode step in two phases (ds_decode_score, ds_decode_select_attend, and
 ds_decode_score_ragged, ds_decode_select_attend_ragged for unequal lengths),
 the decode step with the threshold rule (ds_decode_sparse_attn_threshold and its
@@ -22,7 +24,8 @@ from ._binding import (DS_OK, DS_ERR_INVALID_ARGUMENT, DS_ERR_UNSUPPORTED, DS_ER
                        alloc_workspace, ds_decode_sparse_attn, ds_decode_sparse_attn_ragged, ds_decode_score,
                        ds_decode_select_attend, ds_decode_score_ragged, ds_decode_select_attend_ragged,
                        ds_decode_sparse_attn_threshold, ds_decode_score_threshold, ds_decode_select_attend_threshold,
-                       ds_label_scores_positive, ds_decode_sparse_attn_offload,
+                       ds_label_scores_positive, ds_decode_sparse_attn_offload, ds_decode_hip_attn, ds_hip_search,
+                       ds_hip_token_capacity,
                        ds_label_scores, ds_topk_select, ds_select_attention, ds_sparse_attn_from_indices)
 
 __all__ = ["DS_OK", "DS_ERR_INVALID_ARGUMENT", "DS_ERR_UNSUPPORTED", "DS_ERR_WORKSPACE_TOO_SMALL", "DS_ERR_HIP",
@@ -31,5 +34,6 @@ __all__ = ["DS_OK", "DS_ERR_INVALID_ARGUMENT", "DS_ERR_UNSUPPORTED", "DS_ERR_WOR
            "alloc_workspace", "ds_decode_sparse_attn", "ds_decode_sparse_attn_ragged", "ds_decode_score",
            "ds_decode_select_attend", "ds_decode_score_ragged", "ds_decode_select_attend_ragged",
            "ds_decode_sparse_attn_threshold", "ds_decode_score_threshold", "ds_decode_select_attend_threshold",
-           "ds_label_scores_positive", "ds_decode_sparse_attn_offload", "ds_label_scores",
+           "ds_label_scores_positive", "ds_decode_sparse_attn_offload", "ds_decode_hip_attn", "ds_hip_search",
+           "ds_hip_token_capacity", "ds_label_scores",
            "ds_topk_select", "ds_select_attention", "ds_sparse_attn_from_indices"]

@@ -63,6 +63,12 @@ _SIGNATURES = {
     "ds_decode_sparse_attn_offload": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32,
                                                _c_i32, _c_i32, _c_i64, _c_i64, _c_i64, _c_i32, _c_i64, _c_f32, _c_vp,
                                                _c_vp, _c_vp, _c_size, _c_vp]),
+    "ds_decode_hip_attn": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i64,
+                                    _c_i32, _c_i32, _c_f32, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
+    "ds_hip_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32]),
+    "ds_hip_token_capacity": (_c_i64, [_c_i64, _c_i64, _c_i64]),
+    "ds_hip_search": (_c_i32, [_c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i64, _c_i32, _c_i32,
+                               _c_vp, _c_vp, _c_vp]),
     "ds_select_attention": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i64,
                                      _c_i32, _c_i64, _c_vp, _c_i64, _c_f32, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
     "ds_label_scores": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i64,
@@ -327,6 +333,52 @@ def ds_decode_sparse_attn_offload(q, K, V, label, channels, T: int, k_units: int
                                                _dev(workspace, "workspace"),
                                                workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, indices
+
+
+def ds_hip_token_capacity(T: int, k_spans: int, span: int) -> int:
+    cap = lib().ds_hip_token_capacity(T, k_spans, span)
+    if cap == 0:
+        raise DsError(DS_ERR_INVALID_ARGUMENT, ds_last_error())
+    return cap
+
+
+def ds_decode_hip_attn(q, K, V, T: int, k_spans: int, span: int, scale: float = 0.0, out=None, spans=None,
+                       workspace=None, stream=None):
+    """Decode with the hierarchical span search.  Returns (out fp32 [B, Hq, d], spans int32 [B, Hkv, k_spans, 2])."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    _, Hkv, T_cap, _ = K.shape
+    if K.dtype != q.dtype or V.dtype != q.dtype:
+        raise ValueError("q, K and V must share one dtype")
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if spans is None:
+        spans = torch.empty((B, Hkv, k_spans, 2), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        n = lib().ds_hip_workspace_bytes(B, Hq, Hkv, d, T, k_spans, span)
+        if n == 0:
+            raise DsError(DS_ERR_INVALID_ARGUMENT, ds_last_error())
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    _check(lib().ds_decode_hip_attn(_dev(q, "q"), _dev(K, "K"), _dev(V, "V"), _dtype_code(q), B, Hq, Hkv, d, T_cap,
+                                    T, k_spans, span, scale, _dev(out, "out"), _dev(spans, "spans"),
+                                    _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                    _stream(stream)))
+    return out, spans
+
+
+def ds_hip_search(q, K, T: int, k_spans: int, span: int, spans=None, tokens=None, stream=None):
+    """Steps 0-2 of ds_decode_hip_attn.  Returns (spans [B, Hkv, k_spans, 2], tokens [B, Hkv, capacity])."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    _, Hkv, T_cap, _ = K.shape
+    cap = ds_hip_token_capacity(T, k_spans, span)
+    if spans is None:
+        spans = torch.empty((B, Hkv, k_spans, 2), dtype=torch.int32, device=q.device)
+    if tokens is None:
+        tokens = torch.empty((B, Hkv, cap), dtype=torch.int32, device=q.device)
+    _check(lib().ds_hip_search(_dev(q, "q"), _dev(K, "K"), _dtype_code(q), B, Hq, Hkv, d, T_cap, T, k_spans, span,
+                               _dev(spans, "spans"), _dev(tokens, "tokens"), _stream(stream)))
+    return spans, tokens
 
 
 def ds_decode_sparse_attn_ragged(q, K, V, label, channels, seq_lens, T_max: int, k_units: int, block: int = 1,

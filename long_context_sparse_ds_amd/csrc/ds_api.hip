@@ -541,6 +541,108 @@ ds_status ds_decode_select_attend_threshold(const void* q, const void* K, const 
                              static_cast<char*>(workspace), static_cast<hipStream_t>(stream), nullptr, tau, counts);
 }
 
+// Hierarchical span search: rounds until no span is longer than `span`, and
+// the token capacity of a row (k * span, or T when no round runs, in which
+// case the first spans cover every token).
+static int hip_rounds(int64_t T, int64_t k, int64_t span) {
+  int64_t len = (T + k - 1) / k;
+  int rounds = 0;
+  while (len > span) {
+    len = (len + 1) / 2;
+    ++rounds;
+  }
+  return rounds;
+}
+
+static int64_t hip_capacity(int64_t T, int64_t k, int64_t span) {
+  return hip_rounds(T, k, span) > 0 ? k * span : T;
+}
+
+static ds_status check_hip_shape(int B, int Hq, int Hkv, int d, int64_t T_cap, int64_t T, int64_t k, int64_t span) {
+  if (ds_status st = check_decode_shape(B, Hq, Hkv, d, T_cap, T, 1, 1)) return st;
+  if (k < 1 || k > T || k > 1024)
+    return fail(DS_ERR_INVALID_ARGUMENT, "need 1 <= k_spans <= min(T, 1024) (got %lld)", (long long)k);
+  if (span < 1 || span > INT32_MAX) return fail(DS_ERR_INVALID_ARGUMENT, "span = %lld must be >= 1", (long long)span);
+  return DS_OK;
+}
+
+// Workspace of ds_decode_hip_attn: the token list, then the attention splits.
+static ds::DecodePlan plan_hip(int B, int Hq, int Hkv, int64_t T, int64_t k, int64_t span) {
+  ds::DecodePlan p{};
+  const int G = Hq / Hkv;
+  p.rows = int64_t(B) * Hkv;
+  p.n_units = T;
+  p.kv_virtual = hip_capacity(T, k, span);
+  p.sp = ds::plan_split(p.rows, G, p.kv_virtual, false);
+  p.sp_idx = p.sp;
+  size_t off = 0;
+  p.off_scores = off;   // token list [rows][capacity] int32
+  off += round256(size_t(p.rows) * size_t(p.kv_virtual) * sizeof(int32_t));
+  const int64_t bhs = int64_t(B) * Hq * p.sp.n_split;
+  p.off_acc = off;
+  off += round256(size_t(bhs) * ds::kHeadDim * sizeof(float));
+  p.off_ml = off;
+  off += round256(size_t(bhs) * 2 * sizeof(float));
+  p.total_bytes = off;
+  return p;
+}
+
+int64_t ds_hip_token_capacity(int64_t T, int64_t k_spans, int64_t span) {
+  g_err.clear();
+  if (T < 1 || k_spans < 1 || k_spans > T || span < 1) {
+    fail(DS_ERR_INVALID_ARGUMENT, "need T >= 1, 1 <= k_spans <= T, span >= 1");
+    return 0;
+  }
+  return hip_capacity(T, k_spans, span);
+}
+
+size_t ds_hip_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t T, int32_t k_spans,
+                              int32_t span) {
+  g_err.clear();
+  if (check_hip_shape(B, Hq, Hkv, d, T, T, k_spans, span) != DS_OK) return 0;
+  return plan_hip(B, Hq, Hkv, T, k_spans, span).total_bytes;
+}
+
+ds_status ds_hip_search(const void* q, const void* K, ds_dtype dt, int32_t B, int32_t Hq, int32_t Hkv, int32_t d,
+                        int64_t T_cap, int64_t T, int32_t k_spans, int32_t span, int32_t* spans, int32_t* tokens,
+                        void* stream) {
+  g_err.clear();
+  if (!q || !K || !spans || !tokens) return fail(DS_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (ds_status st = check_dtype(dt)) return st;
+  if (ds_status st = check_hip_shape(B, Hq, Hkv, d, T_cap, T, k_spans, span)) return st;
+  if (!aligned(q, 16) || !aligned(K, 16) || !aligned(spans, 4) || !aligned(tokens, 4))
+    return fail(DS_ERR_INVALID_ARGUMENT, "misaligned device pointer");
+  return hip_status(ds::launch_hip_search(q, K, dt == DS_DTYPE_BF16, B, Hq, Hkv, T_cap, T, k_spans, span,
+                                          hip_rounds(T, k_spans, span), spans, tokens,
+                                          hip_capacity(T, k_spans, span), static_cast<hipStream_t>(stream)),
+                    "search launch");
+}
+
+ds_status ds_decode_hip_attn(const void* q, const void* K, const void* V, ds_dtype dt, int32_t B, int32_t Hq,
+                             int32_t Hkv, int32_t d, int64_t T_cap, int64_t T, int32_t k_spans, int32_t span,
+                             float scale, float* out, int32_t* spans, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  g_err.clear();
+  if (!q || !K || !V || !out || !spans || !workspace) return fail(DS_ERR_INVALID_ARGUMENT, "null pointer argument");
+  if (ds_status st = check_dtype(dt)) return st;
+  if (ds_status st = check_hip_shape(B, Hq, Hkv, d, T_cap, T, k_spans, span)) return st;
+  if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(out, 16) || !aligned(spans, 4) ||
+      !aligned(workspace, 256))
+    return fail(DS_ERR_INVALID_ARGUMENT, "misaligned device pointer");
+  const ds::DecodePlan pl = plan_hip(B, Hq, Hkv, T, k_spans, span);
+  if (workspace_bytes < pl.total_bytes)
+    return fail(DS_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, pl.total_bytes);
+  if (!(scale > 0.f)) scale = 1.0f / std::sqrt(float(d));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* tokens = reinterpret_cast<int32_t*>(ws + pl.off_scores);
+  if (ds_status st = hip_status(ds::launch_hip_search(q, K, dt == DS_DTYPE_BF16, B, Hq, Hkv, T_cap, T, k_spans, span,
+                                                      hip_rounds(T, k_spans, span), spans, tokens, pl.kv_virtual, s),
+                                "search launch"))
+    return st;
+  return run_attention(q, K, V, dt, B, Hq, Hkv, T_cap, T, 1, pl.kv_virtual, tokens, scale, pl, pl.sp, out, ws, s);
+}
+
 ds_status ds_select_attention(const void* q, const void* K, const void* V, ds_dtype dt, int32_t B, int32_t Hq,
                               int32_t Hkv, int32_t d, int64_t T_cap, int64_t T, int32_t block, int64_t k_units,
                               const float* scores, int64_t ld, float scale, float* out, int32_t* indices,

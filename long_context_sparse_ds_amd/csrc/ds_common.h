@@ -91,6 +91,12 @@ hipError_t launch_select_attention(const void* q, const void* K, const void* V, 
 
 hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t s);
 
+// Hierarchical span search (rows of B * Hkv, k <= 1024 spans): writes the kept
+// spans [rows][k][2] and the covered token ids [rows][cap], ascending, -1 after.
+hipError_t launch_hip_search(const void* q, const void* K, int is_bf16, int B, int Hq, int Hkv, int64_t T_cap,
+                             int64_t T, int k, int span, int rounds, int32_t* spans, int32_t* tokens, int64_t cap,
+                             hipStream_t s);
+
 // Log-sum-exp merge of n_split partial states per (sequence, query head).
 hipError_t launch_merge(const float* part_acc, const float* part_ml, int64_t BH, int n_split, float* out,
                         hipStream_t s);

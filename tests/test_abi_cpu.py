@@ -162,6 +162,27 @@ def test_other_entry_points_validate_first():
     assert lib.ds_decode_sparse_attn_offload(FAKE, FAKE, FAKE, FAKE, FAKE, *oargs, FAKE, FAKE, FAKE, ws, None) \
         == L.DS_ERR_INVALID_ARGUMENT
     assert "K" in L.ds_last_error()
+    # hierarchical span search: capacity, workspace and argument checks on the host
+    assert lib.ds_hip_token_capacity(1 << 20, 64, 64) == 64 * 64
+    assert lib.ds_hip_token_capacity(1000, 20, 64) == 1000      # no round: every token
+    assert lib.ds_hip_token_capacity(10, 3, 2) == 6
+    assert lib.ds_hip_token_capacity(10, 0, 2) == 0 and lib.ds_hip_token_capacity(10, 11, 2) == 0
+    assert lib.ds_hip_workspace_bytes(1, 4, 4, 128, 1000, 2000, 8) == 0
+    assert lib.ds_hip_workspace_bytes(1, 4, 4, 96, 1000, 20, 8) == 0
+    hws = lib.ds_hip_workspace_bytes(1, 4, 4, 128, 1000, 20, 8)
+    assert hws > 0
+    hargs = (FAKE, FAKE, FAKE, L.DS_DTYPE_BF16, 1, 4, 4, 128, 1000, 1000)
+    assert lib.ds_decode_hip_attn(*hargs, 20, 8, 0.0, FAKE, None, FAKE, hws, None) == L.DS_ERR_INVALID_ARGUMENT
+    assert lib.ds_decode_hip_attn(*hargs, 1025, 8, 0.0, FAKE, FAKE, FAKE, hws, None) == L.DS_ERR_INVALID_ARGUMENT
+    assert lib.ds_decode_hip_attn(*hargs, 20, 0, 0.0, FAKE, FAKE, FAKE, hws, None) == L.DS_ERR_INVALID_ARGUMENT
+    assert lib.ds_decode_hip_attn(*hargs, 20, 8, 0.0, FAKE, FAKE, FAKE, hws - 1, None) \
+        == L.DS_ERR_WORKSPACE_TOO_SMALL
+    assert lib.ds_decode_hip_attn(FAKE, FAKE, FAKE, L.DS_DTYPE_BF16, 1, 4, 4, 64, 1000, 1000, 20, 8, 0.0, FAKE, FAKE,
+                                  FAKE, hws, None) == L.DS_ERR_UNSUPPORTED
+    assert lib.ds_hip_search(FAKE, FAKE, L.DS_DTYPE_BF16, 1, 4, 4, 128, 1000, 1000, 20, 8, FAKE, None, None) \
+        == L.DS_ERR_INVALID_ARGUMENT
+    assert lib.ds_hip_search(FAKE, FAKE, L.DS_DTYPE_BF16, 1, 4, 4, 128, 1000, 1001, 20, 8, FAKE, FAKE, None) \
+        == L.DS_ERR_INVALID_ARGUMENT
     # a valid call afterwards clears the message
     L.ds_decode_workspace_bytes(1, 1, 1, 128, 10, 1, 1)
     assert L.ds_last_error() == ""

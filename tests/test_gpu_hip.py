@@ -1,0 +1,107 @@
+"""GPU parity of the hierarchical span search (HiP page, abstract) against the CPU oracle.
+
+The search ranks float32 scores on both sides (the oracle rounds its float64 dot
+products to float32, the kernel rounds its double sums), so the kept spans must be
+identical; the attention output is compared with the oracle's attention over the
+GPU's spans.  Covered: bf16 and fp32, MHA and GQA groups, uneven spans (T not a
+multiple of k), a case with no round, k = 1 and k = 1024, span = 1, T_cap > T with
+NaN padding past T, the search stage against the one-call step, and the full-size
+one-million-token workload in the benchmark's launch configuration.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dsgen
+import long_context_sparse_ds_amd as L
+import oracle as O
+from dsgen import Workload
+from _helpers import OUT_TOL, to_device, unit_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    L.lib()   # raises if the HIP library is missing
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+# Workload.k_units is the number of spans k, Workload.block the longest final span.
+HIP_CASES = [
+    Workload("hip_mha", "bf16", B=2, Hq=4, Hkv=4, d=128, T=5000, r=16, block=8, k_units=32, seed_base=51000),
+    Workload("hip_gqa4", "bf16", B=1, Hq=16, Hkv=4, d=128, T=20000, r=16, block=16, k_units=64, seed_base=51100,
+             T_cap=20100),
+    Workload("hip_f32", "f32", B=1, Hq=2, Hkv=1, d=128, T=3001, r=16, block=4, k_units=40, seed_base=51200,
+             fixed_outliers=True),
+    Workload("hip_span1", "bf16", B=1, Hq=2, Hkv=2, d=128, T=777, r=16, block=1, k_units=50, seed_base=51300),
+    Workload("hip_k1", "bf16", B=1, Hq=8, Hkv=1, d=128, T=4096, r=16, block=64, k_units=1, seed_base=51400),
+    Workload("hip_k1024", "bf16", B=1, Hq=2, Hkv=1, d=128, T=65536, r=16, block=16, k_units=1024, seed_base=51500),
+    Workload("hip_no_round", "bf16", B=1, Hq=4, Hkv=2, d=128, T=1000, r=16, block=64, k_units=20, seed_base=51600),
+]
+
+
+def _run(w):
+    q, K, V = dsgen.gen_cache(w)
+    qd, Kd, Vd = to_device(q, w.dtype), to_device(K, w.dtype), to_device(V, w.dtype)
+    out, spans = L.ds_decode_hip_attn(qd, Kd, Vd, w.T, w.k_units, w.block)
+    torch.cuda.synchronize()
+    return q, K, V, qd, Kd, Vd, out.cpu().numpy(), spans.cpu().numpy()
+
+
+def _check_row(w, q, K, V, out, spans, b, g):
+    qg, Kf, Vf = unit_inputs(w, q, K, V, b, g)
+    want = O.hip_search(qg, Kf, w.T, w.k_units, w.block)
+    got = [tuple(int(x) for x in sp) for sp in spans[b, g]]
+    assert got == [tuple(sp) for sp in want], f"{w.name} row ({b},{g}): spans differ"
+    ref = O.attend(qg, Kf, Vf, O.spans_to_tokens(want), O.default_scale(w.d))
+    err = float(np.max(np.abs(out[b, g * w.G:(g + 1) * w.G] - ref)))
+    assert err <= OUT_TOL[w.dtype], f"{w.name} row ({b},{g}): max-abs error {err}"
+    return err
+
+
+@pytest.mark.parametrize("w", HIP_CASES, ids=[w.name for w in HIP_CASES])
+def test_hip_decode_all_rows(w):
+    _say(f"{w.name} T={w.T} k={w.k_units} span={w.block} G={w.G} {w.dtype}")
+    q, K, V, qd, Kd, Vd, out, spans = _run(w)
+    assert np.all(np.isfinite(out))
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            _check_row(w, q, K, V, out, spans, b, g)
+
+
+def test_hip_search_stage_matches_one_call():
+    """ds_hip_search's token list is the kept spans' tokens, ascending, -1 after them, and
+    attention from it (ds_sparse_attn_from_indices) gives the one call's output exactly."""
+    w = HIP_CASES[1]
+    q, K, V, qd, Kd, Vd, out, spans = _run(w)
+    sp2, toks = L.ds_hip_search(qd, Kd, w.T, w.k_units, w.block)
+    cap = L.ds_hip_token_capacity(w.T, w.k_units, w.block)
+    o2 = L.ds_sparse_attn_from_indices(qd, Kd, Vd, toks, w.T, 1)
+    torch.cuda.synchronize()
+    assert np.array_equal(sp2.cpu().numpy(), spans)
+    toks = toks.cpu().numpy()
+    assert toks.shape == (w.B, w.Hkv, cap)
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            want = O.spans_to_tokens([tuple(sp) for sp in spans[b, g]])
+            assert list(toks[b, g, :len(want)]) == list(want) and np.all(toks[b, g, len(want):] == -1)
+    assert np.array_equal(o2.cpu().numpy(), out)
+
+
+@pytest.mark.parametrize("name", dsgen.HIP_ORDER)
+def test_hip_full_size_workload(name):
+    """The one-million-token workload, called as the benchmark calls it: every row's spans
+    against the oracle, outputs of every row."""
+    w = dsgen.get(name)
+    _say(f"{name}: B={w.B} H={w.Hq}/{w.Hkv} T={w.T} k={w.k_units} span={w.block}")
+    q, K, V, qd, Kd, Vd, out, spans = _run(w)
+    errs = [_check_row(w, q, K, V, out, spans, b, g) for b in range(w.B) for g in range(w.Hkv)]
+    _say(f"{name}: max-abs err {max(errs):.3g}")
+    del q, K, V, qd, Kd, Vd
+    torch.cuda.empty_cache()
