@@ -220,6 +220,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--phases-only", action="store_true",
+                    help="time only the step's own two phases, not the isolated reference stages (for counter runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB ten times and exit (reference for "
                          "hardware byte counters)")
@@ -459,7 +461,7 @@ def main():
     # The decode step's two phases (its own kernels), then isolated stages for reference
     # (uniform-length top-k stages, so not for a ragged batch or the threshold rule).
     stages = [("decode_score", st_decode_score), ("decode_select_attend", st_decode_select_attend)]
-    if not w.ragged and w.tau is None and not w.offload and not w.hip:
+    if not w.ragged and w.tau is None and not w.offload and not w.hip and not args.phases_only:
         stages += [("label_append", st_append), ("scores", st_scores), ("select", st_select),
                    ("attention_from_indices", st_attn)]
     for name, fn in stages:
