@@ -94,10 +94,17 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t T, int block, int64_t k_u
   p.score_ld = (p.n_units + 63) / 64 * 64;
   p.kv_virtual = k_units * block;
   p.fused = p.n_units <= kFusedMaxUnits;
-  p.sp = plan_split(p.rows, G, p.kv_virtual, p.fused);
+  // Longer rows: the top k of each partition, then the fused kernel over the
+  // candidates, when those fit it.
+  const int64_t parts = (p.n_units + kPartUnits - 1) / kPartUnits;
+  p.partitioned = !p.fused && parts * k_units <= kFusedMaxUnits;
+  p.n_cand = p.partitioned ? parts * k_units : 0;
+  p.cand_ld = (p.n_cand + 63) / 64 * 64;
+  p.sp = plan_split(p.rows, G, p.kv_virtual, p.fused || p.partitioned);
   p.tiles = (T + kScoreTile - 1) / kScoreTile;
-  // The fused kernel then reads the row's top-digit histogram instead of building it.
-  p.tile_hist = p.fused && p.tiles <= kMaxHistTiles;
+  // The fused kernel then reads the row's top-digit histogram instead of building it
+  // (worth it for token-level rows; a tile of 64-token blocks holds only 32 units).
+  p.tile_hist = p.fused && p.tiles <= kMaxHistTiles && block <= 4;
   p.sp_idx = plan_split(p.rows, G, p.kv_virtual, false);
   const int max_split = p.sp.n_split > p.sp_idx.n_split ? p.sp.n_split : p.sp_idx.n_split;
   const int64_t bhs = int64_t(B) * Hq * max_split;
@@ -112,6 +119,10 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t T, int block, int64_t k_u
   off += round256(size_t(bhs) * 2 * sizeof(float));
   p.off_tickets = off;
   off += round256(size_t(p.rows) * p.sp.head_chunks * sizeof(unsigned));
+  p.off_cand_score = off;
+  off += round256(size_t(p.rows) * size_t(p.cand_ld) * sizeof(float));
+  p.off_cand_id = off;
+  off += round256(size_t(p.rows) * size_t(p.n_cand) * sizeof(int32_t));
   p.total_bytes = off;
   return p;
 }
@@ -142,16 +153,32 @@ ds_status run_select_attend(const void* q, const void* K, const void* V, ds_dtyp
                             const uint16_t* tile_hist, bool tickets_zeroed, float scale, const ds::DecodePlan& pl,
                             float* out, int32_t* indices, char* ws, hipStream_t s,
                             const int32_t* seq_lens = nullptr, float tau = 0.f, int32_t* counts = nullptr) {
-  if (pl.fused) {
+  if (pl.fused || pl.partitioned) {
     float* part_acc = reinterpret_cast<float*>(ws + pl.off_acc);
     float* part_ml = reinterpret_cast<float*>(ws + pl.off_ml);
     unsigned* tickets = reinterpret_cast<unsigned*>(ws + pl.off_tickets);
     if (!tickets_zeroed && pl.sp.n_split > 1)
       if (ds_status st = hip_status(ds::launch_zero_u32(tickets, pl.rows * pl.sp.head_chunks, s), "ticket reset"))
         return st;
+    if (pl.partitioned) {
+      // Top k of each partition, then the fused kernel over the candidates.
+      float* cand_score = reinterpret_cast<float*>(ws + pl.off_cand_score);
+      int32_t* cand_id = reinterpret_cast<int32_t*>(ws + pl.off_cand_id);
+      if (ds_status st = hip_status(ds::launch_partition_topk(scores, pl.rows, pl.n_units, ld, k_units, cand_score,
+                                                              pl.cand_ld, cand_id, s),
+                                    "partition select launch"))
+        return st;
+      ds::DecodePlan pc = pl;
+      pc.n_units = pl.n_cand;
+      pc.tile_hist = false;
+      return hip_status(ds::launch_select_attention(q, K, V, dt == DS_DTYPE_BF16, cand_score, pl.cand_ld, nullptr, Hq,
+                                                    Hkv, T_cap, T, block, k_units, scale, pc, indices, part_acc,
+                                                    part_ml, out, tickets, nullptr, 0.f, nullptr, cand_id, s),
+                        "select-attention launch");
+    }
     return hip_status(ds::launch_select_attention(q, K, V, dt == DS_DTYPE_BF16, scores, ld, tile_hist, Hq, Hkv, T_cap,
                                                   T, block, k_units, scale, pl, indices, part_acc, part_ml, out,
-                                                  tickets, seq_lens, tau, counts, s),
+                                                  tickets, seq_lens, tau, counts, nullptr, s),
                       "select-attention launch");
   }
   if (ds_status st = hip_status(ds::launch_select(scores, pl.rows, pl.n_units, ld, k_units, indices, s),
@@ -311,7 +338,7 @@ static ds_status decode_score_stage(const void* q, const void* K, void* label, c
                                     bool positive = false) {
   float* scores = reinterpret_cast<float*>(ws + pl.off_scores);
   uint16_t* tile_hist = pl.tile_hist ? reinterpret_cast<uint16_t*>(ws + pl.off_tile_hist) : nullptr;
-  unsigned* tickets = pl.fused ? reinterpret_cast<unsigned*>(ws + pl.off_tickets) : nullptr;
+  unsigned* tickets = pl.fused || pl.partitioned ? reinterpret_cast<unsigned*>(ws + pl.off_tickets) : nullptr;
   return hip_status(ds::launch_scores(q, label, K, channels_dev, r, dt == DS_DTYPE_BF16, B, Hq, Hkv, T_cap, T,
                                       t_append, block, scores, pl.score_ld, tile_hist, tickets, pl.sp.head_chunks,
                                       seq_lens, n_append, positive, s),

@@ -20,6 +20,10 @@ constexpr int64_t kScoreTile = 2048;
 constexpr int64_t kMaxHistTiles = 16;
 constexpr int kHistBins = 2048;   // top 11 bits of a score key
 
+// Units per partition of the two-stage selection of long rows (the top k of
+// each partition, then the top k of those candidates in the fused kernel).
+constexpr int64_t kPartUnits = 32768;
+
 // Query heads processed together by one attention workgroup (divides G).
 inline __host__ __device__ int head_chunk8(int G) { return G % 8 == 0 ? 8 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1; }
 inline __host__ __device__ int head_chunk4(int G) { return G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1; }
@@ -40,11 +44,14 @@ struct DecodePlan {
   int64_t score_ld;    // row stride of the score buffer, floats (multiple of 64)
   int64_t kv_virtual;  // k_units * block: attention positions per row (some may lie past T)
   bool fused;          // select and attention in one kernel
+  bool partitioned;    // longer rows: per-partition top k, then the fused kernel over the candidates
+  int64_t n_cand;      // partitioned: candidates per row (partitions * k_units)
+  int64_t cand_ld;     // partitioned: row stride of the candidate scores, floats (multiple of 64)
   bool tile_hist;      // the score kernel writes per-tile key histograms for the fused kernel
   int64_t tiles;       // score tiles per row
   SplitPlan sp;        // splits of the decode call
   SplitPlan sp_idx;    // splits of the attention-from-indices call
-  size_t off_scores, off_tile_hist, off_acc, off_ml, off_tickets, total_bytes;
+  size_t off_scores, off_tile_hist, off_acc, off_ml, off_tickets, off_cand_score, off_cand_id, total_bytes;
 };
 
 DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t T, int block, int64_t k_units);
@@ -70,6 +77,12 @@ hipError_t launch_scores(const void* q, void* label, const void* K, const int32_
 hipError_t launch_select(const float* scores, int64_t rows, int64_t n, int64_t ld, int64_t k, int32_t* idx,
                          hipStream_t s);
 
+// Per-partition top k of rows longer than kPartUnits: candidates [rows][parts * k]
+// (scores with row stride cand_ld, unit ids with row stride parts * k), in
+// ascending unit order; unused slots hold -inf and -1.
+hipError_t launch_partition_topk(const float* scores, int64_t rows, int64_t n, int64_t ld, int64_t k,
+                                 float* cand_score, int64_t cand_ld, int32_t* cand_id, hipStream_t s);
+
 // Attention over given kept units; writes out directly when sp.n_split == 1,
 // else partial states that launch_merge combines.
 hipError_t launch_attention(const void* q, const void* K, const void* V, int is_bf16, int B, int Hq, int Hkv,
@@ -83,11 +96,15 @@ hipError_t launch_attention(const void* q, const void* K, const void* V, int is_
 // seq_lens (may be null): device int32 [B]; sequence b holds seq_lens[b] tokens
 // (clamped to [1, T]), keeps min(k_units, its unit count) units, and its index
 // slots past that are set to -1.
+// unit_ids (may be null): the scores are candidates [rows][pl.n_units] whose
+// unit ids these are (ascending per row); kept candidates are written and
+// gathered as those units.
 hipError_t launch_select_attention(const void* q, const void* K, const void* V, int is_bf16, const float* scores,
                                    int64_t ld, const uint16_t* tile_hist, int Hq, int Hkv, int64_t T_cap, int64_t T,
                                    int block, int64_t k_units, float scale, const DecodePlan& pl, int32_t* indices,
                                    float* part_acc, float* part_ml, float* out, unsigned* tickets,
-                                   const int32_t* seq_lens, float tau, int32_t* counts, hipStream_t s);
+                                   const int32_t* seq_lens, float tau, int32_t* counts,
+                                   const int32_t* unit_ids, hipStream_t s);
 
 hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t s);
 

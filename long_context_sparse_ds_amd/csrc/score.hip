@@ -199,9 +199,10 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
 
   float u[kTPT];
   if constexpr (POS && R > 0) {
-    // Head-outer: one head's q values (LDS broadcast reads) against the label
-    // values of TCH tokens held in double.
-    constexpr int TCH = R <= 16 ? kTPT : 1;
+    // Head-outer: one head's q values (LDS broadcast reads) against one token's
+    // label values held in double (one token at a time keeps the kernel at
+    // 126 VGPRs for r = 16, two workgroups per CU).
+    constexpr int TCH = 1;
 #pragma unroll
     for (int c0 = 0; c0 < kTPT; c0 += TCH) {
       double lv[TCH][R];

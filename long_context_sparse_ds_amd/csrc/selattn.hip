@@ -204,6 +204,7 @@ struct FusedArgs {
   int32_t Hkv;
   float tau;                   // threshold rule: keep units scoring >= tau (at most k_units)
   int32_t* counts;             // threshold rule: kept units per row; null: plain top-k
+  const int32_t* unit_ids;     // the units are candidates with these unit ids [rows][n_units]; null: identity
 };
 
 // Scalar arguments, those of the first loads first: the first 14 dwords are
@@ -218,7 +219,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
     int32_t head_chunks_, int32_t n_units_, int32_t tiles_, int32_t k_units_, int32_t lb_, const void* K_,
     const void* V_, int32_t* indices_, float* part_acc_, float* part_ml_, float* out_, unsigned* tickets_,
     int64_t T_cap_, int32_t T_, int32_t kv_virtual_, int32_t chunk_, int32_t n_split_, float scale_,
-    const int32_t* seq_lens_, int32_t Hkv_, float tau_, int32_t* counts_) {
+    const int32_t* seq_lens_, int32_t Hkv_, float tau_, int32_t* counts_, const int32_t* unit_ids_) {
   FusedArgs a;
   a.q = q_;
   a.K = K_;
@@ -247,6 +248,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
   a.Hkv = Hkv_;
   a.tau = tau_;
   a.counts = counts_;
+  a.unit_ids = unit_ids_;
   using LN = Lanes<TE, NT>;
   constexpr int NW = LN::NW, EPL = LN::EPL, LPT = LN::LPT, GPW = LN::GPW, NG = LN::NG, KU = LN::KU;
   constexpr int BPT1 = 2048 / NT, BPT2 = 1024 / NT;
@@ -474,6 +476,13 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
     }
   }
   __syncthreads();
+  if (a.unit_ids != nullptr) {
+    // Candidates of a long row: their kept slots become the units they stand for.
+    const int32_t* ids = a.unit_ids + int64_t(row) * n_units;
+    for (int i = tid; i < u_hi - u_lo; i += NT)
+      if (u_lo + i < k_keep) sm.u.a.sel[i] = ids[sm.u.a.sel[i]];
+    __syncthreads();
+  }
   if (hchunk == 0) {
     int32_t* ridx = a.indices + int64_t(row) * k_units + u_lo;
     for (int i = tid; i < u_hi - u_lo; i += NT) ridx[i] = u_lo + i < k_keep ? sm.u.a.sel[i] : -1;
@@ -661,12 +670,12 @@ hipError_t launch_one(const FusedArgs& a, dim3 grid, hipStream_t s) {
     hipLaunchKernelGGL((selattn_kernel<TE, NT, ITEMS, HC, true>), grid, dim3(NT), 0, s, a.q, a.scores, a.tile_hist,
                        a.ld, a.G, a.head_chunks, a.n_units, a.tiles, a.k_units, a.lb, a.K, a.V, a.indices, a.part_acc,
                        a.part_ml, a.out, a.tickets, a.T_cap, a.T, a.kv_virtual, a.chunk, a.n_split, a.scale,
-                       a.seq_lens, a.Hkv, a.tau, a.counts);
+                       a.seq_lens, a.Hkv, a.tau, a.counts, a.unit_ids);
   else
     hipLaunchKernelGGL((selattn_kernel<TE, NT, ITEMS, HC, false>), grid, dim3(NT), 0, s, a.q, a.scores, a.tile_hist,
                        a.ld, a.G, a.head_chunks, a.n_units, a.tiles, a.k_units, a.lb, a.K, a.V, a.indices, a.part_acc,
                        a.part_ml, a.out, a.tickets, a.T_cap, a.T, a.kv_virtual, a.chunk, a.n_split, a.scale,
-                       nullptr, a.Hkv, a.tau, a.counts);
+                       nullptr, a.Hkv, a.tau, a.counts, a.unit_ids);
   return hipGetLastError();
 }
 
@@ -694,8 +703,10 @@ hipError_t launch_select_attention(const void* q, const void* K, const void* V, 
                                    int64_t ld, const uint16_t* tile_hist, int Hq, int Hkv, int64_t T_cap, int64_t T,
                                    int block, int64_t k_units, float scale, const DecodePlan& pl, int32_t* indices,
                                    float* part_acc, float* part_ml, float* out, unsigned* tickets,
-                                   const int32_t* seq_lens, float tau, int32_t* counts, hipStream_t s) {
+                                   const int32_t* seq_lens, float tau, int32_t* counts,
+                                   const int32_t* unit_ids, hipStream_t s) {
   FusedArgs a{};
+  a.unit_ids = unit_ids;
   a.seq_lens = seq_lens;
   a.tau = tau;
   a.counts = counts;

@@ -1,7 +1,9 @@
 // Per-row exact top-k selection as a kernel of its own.
 //
 // Used by the selection-only entry point and by decode rows longer than the
-// fused select+attention kernel holds (more than 32768 units).  One workgroup
+// fused select+attention kernel holds (more than 32768 units): either as the
+// first, per-partition stage of a two-stage selection (when the partitions'
+// candidates fit the fused kernel) or as a whole-row selection.  One workgroup
 // of 1024 threads per row.  Rows of up to 32768 keys are read once into
 // registers and selected with the shared radix routine; longer rows are
 // streamed from memory (L2-resident after the score kernel) once per radix
@@ -105,7 +107,53 @@ __global__ __launch_bounds__(kNT) void select_stream_kernel(const float* __restr
   }
 }
 
+// First stage of the exact top-k of a long row: the top k of each partition of
+// kPartUnits consecutive units (all of it when it holds fewer).  Every unit of
+// the row's top k is in its partition's top k under the same tie rule, so the
+// second stage, the top k of the candidates, is exact.  Candidates go out in
+// ascending unit order (partition by partition, each ascending), so a tie among
+// them still goes to the lower unit id: cand_score[row][p * k + i] and
+// cand_id[row][p * k + i]; the slots of a partition past its kept count hold
+// -inf and -1.
+__global__ __launch_bounds__(kNT) void partition_topk_kernel(const float* __restrict__ scores, int64_t n, int64_t ld,
+                                                             int64_t k, float* __restrict__ cand_score,
+                                                             int64_t cand_ld, int32_t* __restrict__ cand_id,
+                                                             int64_t n_cand) {
+  constexpr int ITEMS = int(kPartUnits / kNT);
+  __shared__ SelSmem<kNT> sm;
+  const int64_t p = blockIdx.x, row = blockIdx.y;
+  const int64_t base = p * kPartUnits;
+  const int64_t n_p = min(kPartUnits, n - base);
+  const int64_t k_p = min(k, n_p);
+  float* cs = cand_score + row * cand_ld + p * k;
+  int32_t* ci = cand_id + row * n_cand + p * k;
+  uint32_t key[ITEMS];
+  bool valid[ITEMS];
+  load_keys<ITEMS>(scores + row * ld + base, n_p, key, valid);
+  uint32_t kk, mask;
+  const uint32_t tau = select_threshold<kNT, ITEMS>(key, valid, uint32_t(k_p), sm, kk, mask, false, 0u, 0u);
+  const int64_t first = int64_t(threadIdx.x) * ITEMS;
+  for_each_kept<kNT, ITEMS>(key, valid, first, tau, mask, kk, sm, [&](int64_t unit, int64_t pos) {
+    if (pos < k_p) {
+      cs[pos] = key_to_float(key[unit - first]);
+      ci[pos] = int32_t(base + unit);
+    }
+  });
+  for (int64_t i = k_p + threadIdx.x; i < k; i += kNT) {
+    cs[i] = -INFINITY;
+    ci[i] = -1;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_partition_topk(const float* scores, int64_t rows, int64_t n, int64_t ld, int64_t k,
+                                 float* cand_score, int64_t cand_ld, int32_t* cand_id, hipStream_t s) {
+  const int64_t parts = (n + kPartUnits - 1) / kPartUnits;
+  hipLaunchKernelGGL(partition_topk_kernel, dim3(unsigned(parts), unsigned(rows)), dim3(kNT), 0, s, scores, n, ld, k,
+                     cand_score, cand_ld, cand_id, parts * k);
+  return hipGetLastError();
+}
 
 hipError_t launch_select(const float* scores, int64_t rows, int64_t n, int64_t ld, int64_t k, int32_t* idx,
                          hipStream_t s) {

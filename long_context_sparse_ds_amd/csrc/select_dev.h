@@ -285,6 +285,11 @@ __device__ __forceinline__ void for_each_kept(const uint32_t (&key)[ITEMS], cons
   }
 }
 
+// The float of a key (inverse of float_key for non-NaN floats; -0.0 comes back as +0.0).
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 // Load units [tid * ITEMS, tid * ITEMS + ITEMS) of a score row as keys.
 template <int ITEMS>
 __device__ __forceinline__ void load_keys(const float* s, int64_t n, uint32_t (&key)[ITEMS], bool (&valid)[ITEMS]) {

@@ -628,3 +628,50 @@ def test_decode_ragged_full_size_workload(name):
         assert err <= OUT_TOL[w.dtype], (w.name, b, g, err)
     del q, K, V
     torch.cuda.empty_cache()
+
+
+LONG_ADV_SHAPES = [(70000, 3000), (32868, 500), (65536, 16384)]
+
+
+@pytest.mark.parametrize("kind", ADV_KINDS)
+def test_long_rows_two_stage_selection_adversarial(kind):
+    """Rows longer than 32,768 units whose partitions' candidates fit the fused kernel
+    (a per-partition top k, then the fused kernel over the candidates): the adversarial
+    score rows again, with a last partition shorter than k (32,868 units, k = 500) and
+    the largest candidate set (two partitions of k = 16,384).  Kept ids bit-exact
+    against the oracle's selection of the same float32 values."""
+    for T, k in LONG_ADV_SHAPES:
+        w = Workload(f"long_{kind}_{T}", "bf16", B=1, Hq=4, Hkv=2, d=128, T=T, r=16, block=1, k_units=k,
+                     seed_base=28000 + T)
+        _say(f"{w.name} k={k}")
+        q, K, V = dsgen.gen_cache(w)
+        rng = np.random.default_rng(zlib.crc32(w.name.encode()))
+        ld = -(-T // 4) * 4
+        sc = np.zeros((1, 2, ld), np.float32)
+        for g in range(2):
+            sc[0, g, :T] = _adversarial_row(kind, T, rng)
+        out, idx = L.ds_select_attention(to_device(q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16"),
+                                         torch.from_numpy(sc).cuda(), T, k, 1)
+        torch.cuda.synchronize()
+        out, idx = out.cpu().numpy(), idx.cpu().numpy()
+        for g in range(2):
+            want = O.select_topk(sc[0, g, :T].astype(np.float64), k)
+            np.testing.assert_array_equal(idx[0, g], want, err_msg=f"{w.name} g={g}")
+            qg, Kf, Vf = unit_inputs(w, q, K, V, 0, g)
+            ref = O.attend(qg, Kf, Vf, want, O.default_scale(w.d))
+            err = float(np.max(np.abs(out[0, g * 2:(g + 1) * 2] - ref)))
+            assert err <= OUT_TOL["bf16"], (w.name, g, err)
+
+
+@pytest.mark.parametrize("w", [
+    Workload("long_gqa4", "bf16", B=1, Hq=8, Hkv=2, d=128, T=70000, r=8, block=1, k_units=2000, seed_base=29000),
+    Workload("long_blk2", "bf16", B=1, Hq=2, Hkv=2, d=128, T=2 * 40000 + 1, r=16, block=2, k_units=5000,
+             seed_base=29100),
+], ids=lambda w: w.name)
+def test_decode_long_rows_two_stage(w):
+    """The whole decode step on rows of more than 32,768 units (token-level with GQA, and
+    2-token blocks with a partial last block): every unit against the oracle."""
+    q, K, V, ch, out, idx = run_decode(w)
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            check_unit(w, q, K, V, ch, b, g, out, idx)
