@@ -104,7 +104,11 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t T, int block, int64_t k_u
   p.tiles = (T + kScoreTile - 1) / kScoreTile;
   // The fused kernel then reads the row's top-digit histogram instead of building it
   // (worth it for token-level rows; a tile of 64-token blocks holds only 32 units).
-  p.tile_hist = p.fused && p.tiles <= kMaxHistTiles && block <= 4;
+  // Token-level rows of the two-stage selection: the partitions sum their tiles'
+  // histograms too, and pass their candidates' histograms on (at most
+  // kMaxHistTiles partitions).
+  p.tile_hist = (p.fused && p.tiles <= kMaxHistTiles && block <= 4) || (p.partitioned && block == 1);
+  p.cand_hist = p.partitioned && block == 1 && parts <= kMaxHistTiles;
   p.sp_idx = plan_split(p.rows, G, p.kv_virtual, false);
   const int max_split = p.sp.n_split > p.sp_idx.n_split ? p.sp.n_split : p.sp_idx.n_split;
   const int64_t bhs = int64_t(B) * Hq * max_split;
@@ -123,6 +127,8 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t T, int block, int64_t k_u
   off += round256(size_t(p.rows) * size_t(p.cand_ld) * sizeof(float));
   p.off_cand_id = off;
   off += round256(size_t(p.rows) * size_t(p.n_cand) * sizeof(int32_t));
+  p.off_cand_hist = off;
+  if (p.cand_hist) off += round256(size_t(p.rows) * size_t(parts) * kHistBins * sizeof(uint16_t));
   p.total_bytes = off;
   return p;
 }
@@ -164,14 +170,17 @@ ds_status run_select_attend(const void* q, const void* K, const void* V, ds_dtyp
       // Top k of each partition, then the fused kernel over the candidates.
       float* cand_score = reinterpret_cast<float*>(ws + pl.off_cand_score);
       int32_t* cand_id = reinterpret_cast<int32_t*>(ws + pl.off_cand_id);
+      uint16_t* cand_hist = tile_hist != nullptr && pl.cand_hist ? reinterpret_cast<uint16_t*>(ws + pl.off_cand_hist)
+                                                                 : nullptr;
       if (ds_status st = hip_status(ds::launch_partition_topk(scores, pl.rows, pl.n_units, ld, k_units, cand_score,
-                                                              pl.cand_ld, cand_id, s),
+                                                              pl.cand_ld, cand_id, tile_hist, pl.tiles, cand_hist, s),
                                     "partition select launch"))
         return st;
       ds::DecodePlan pc = pl;
       pc.n_units = pl.n_cand;
-      pc.tile_hist = false;
-      return hip_status(ds::launch_select_attention(q, K, V, dt == DS_DTYPE_BF16, cand_score, pl.cand_ld, nullptr, Hq,
+      pc.tile_hist = cand_hist != nullptr;
+      pc.tiles = pl.n_cand / k_units;
+      return hip_status(ds::launch_select_attention(q, K, V, dt == DS_DTYPE_BF16, cand_score, pl.cand_ld, cand_hist, Hq,
                                                     Hkv, T_cap, T, block, k_units, scale, pc, indices, part_acc,
                                                     part_ml, out, tickets, nullptr, 0.f, nullptr, cand_id, s),
                         "select-attention launch");

@@ -19,6 +19,8 @@ constexpr int64_t kFusedMaxChunk = 4096;
 constexpr int64_t kScoreTile = 2048;
 constexpr int64_t kMaxHistTiles = 16;
 constexpr int kHistBins = 2048;   // top 11 bits of a score key
+// Units per score tile of token-level rows (the tile histograms' granularity).
+constexpr int64_t kHistTileUnits = kScoreTile;
 
 // Units per partition of the two-stage selection of long rows (the top k of
 // each partition, then the top k of those candidates in the fused kernel).
@@ -47,11 +49,13 @@ struct DecodePlan {
   bool partitioned;    // longer rows: per-partition top k, then the fused kernel over the candidates
   int64_t n_cand;      // partitioned: candidates per row (partitions * k_units)
   int64_t cand_ld;     // partitioned: row stride of the candidate scores, floats (multiple of 64)
+  bool cand_hist;      // partitioned: the first stage writes its candidates' top-digit histograms
   bool tile_hist;      // the score kernel writes per-tile key histograms for the fused kernel
   int64_t tiles;       // score tiles per row
   SplitPlan sp;        // splits of the decode call
   SplitPlan sp_idx;    // splits of the attention-from-indices call
-  size_t off_scores, off_tile_hist, off_acc, off_ml, off_tickets, off_cand_score, off_cand_id, total_bytes;
+  size_t off_scores, off_tile_hist, off_acc, off_ml, off_tickets, off_cand_score, off_cand_id, off_cand_hist,
+      total_bytes;
 };
 
 DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t T, int block, int64_t k_units);
@@ -80,8 +84,12 @@ hipError_t launch_select(const float* scores, int64_t rows, int64_t n, int64_t l
 // Per-partition top k of rows longer than kPartUnits: candidates [rows][parts * k]
 // (scores with row stride cand_ld, unit ids with row stride parts * k), in
 // ascending unit order; unused slots hold -inf and -1.
+// tile_hist (may be null): the score kernel's tile histograms (token-level rows,
+// tiles per row); cand_hist (may be null; needs tile_hist): the candidates'
+// top-digit histograms [rows][parts][2048] for the fused kernel.
 hipError_t launch_partition_topk(const float* scores, int64_t rows, int64_t n, int64_t ld, int64_t k,
-                                 float* cand_score, int64_t cand_ld, int32_t* cand_id, hipStream_t s);
+                                 float* cand_score, int64_t cand_ld, int32_t* cand_id, const uint16_t* tile_hist,
+                                 int64_t tiles, uint16_t* cand_hist, hipStream_t s);
 
 // Attention over given kept units; writes out directly when sp.n_split == 1,
 // else partial states that launch_merge combines.

@@ -115,12 +115,22 @@ __global__ __launch_bounds__(kNT) void select_stream_kernel(const float* __restr
 // them still goes to the lower unit id: cand_score[row][p * k + i] and
 // cand_id[row][p * k + i]; the slots of a partition past its kept count hold
 // -inf and -1.
+// tile_hist (may be null): the score kernel's top-digit histograms of the
+// row's tiles of kHistTileUnits units, tiles per row; a partition sums its
+// tiles' counts instead of building its histogram with LDS atomics (which
+// contend badly on the few digits that high scores share).  cand_hist (may be
+// null; needs tile_hist): the top-digit histogram of each partition's
+// candidates, [rows][parts][2048] uint16, for the fused kernel that selects
+// among them.
 __global__ __launch_bounds__(kNT) void partition_topk_kernel(const float* __restrict__ scores, int64_t n, int64_t ld,
                                                              int64_t k, float* __restrict__ cand_score,
                                                              int64_t cand_ld, int32_t* __restrict__ cand_id,
-                                                             int64_t n_cand) {
+                                                             int64_t n_cand, const uint16_t* __restrict__ tile_hist,
+                                                             int64_t tiles, uint16_t* __restrict__ cand_hist) {
   constexpr int ITEMS = int(kPartUnits / kNT);
-  __shared__ SelSmem<kNT> sm;
+  // k is often a quarter of the partition here, so the digit holding the k-th
+  // key can hold thousands of keys: room for 8192 candidates.
+  __shared__ SelSmem<kNT, 8192> sm;
   const int64_t p = blockIdx.x, row = blockIdx.y;
   const int64_t base = p * kPartUnits;
   const int64_t n_p = min(kPartUnits, n - base);
@@ -130,8 +140,43 @@ __global__ __launch_bounds__(kNT) void partition_topk_kernel(const float* __rest
   uint32_t key[ITEMS];
   bool valid[ITEMS];
   load_keys<ITEMS>(scores + row * ld + base, n_p, key, valid);
+  // This thread's two top-digit bins, 2047 - 2t (high half of word 1023 - t)
+  // and 2046 - 2t (low half), summed over the partition's tiles.
+  uint32_t hist_hi = 0u, hist_lo = 0u;
+  const bool have_hist = tile_hist != nullptr;
+  if (have_hist) {
+    constexpr int kPartTiles = int(kPartUnits / kHistTileUnits);
+    const uint32_t* th = reinterpret_cast<const uint32_t*>(tile_hist + row * tiles * kHistBins) +
+                         (kHistBins / 2 - 1 - int(threadIdx.x));
+    const int64_t t0 = p * kPartTiles;
+    uint32_t w[kPartTiles];
+#pragma unroll
+    for (int t = 0; t < kPartTiles; ++t) w[t] = th[(t0 + t < tiles ? t0 + t : t0) * (kHistBins / 2)];
+#pragma unroll
+    for (int t = 0; t < kPartTiles; ++t) {
+      if (t0 + t < tiles) {
+        hist_hi += w[t] >> 16;
+        hist_lo += w[t] & 0xFFFFu;
+      }
+    }
+  }
   uint32_t kk, mask;
-  const uint32_t tau = select_threshold<kNT, ITEMS>(key, valid, uint32_t(k_p), sm, kk, mask, false, 0u, 0u);
+  const uint32_t tau = select_threshold<kNT, ITEMS>(key, valid, uint32_t(k_p), sm, kk, mask, have_hist, hist_hi,
+                                                    hist_lo);
+  if (cand_hist != nullptr) {
+    // The candidates' histogram: every key in a digit above d0 is kept, k_p
+    // minus those in d0, none below.
+    const uint32_t d0 = tau >> 21;
+    const uint32_t bin_hi = 2047u - 2u * threadIdx.x, bin_lo = bin_hi - 1u;
+    uint32_t tot;
+    block_exclusive_scan1<kNT>((bin_hi > d0 ? hist_hi : 0u) + (bin_lo > d0 ? hist_lo : 0u), sm.wsum[2], tot);
+    const uint32_t in_d0 = uint32_t(k_p) - tot;
+    const uint32_t c_hi = bin_hi > d0 ? hist_hi : (bin_hi == d0 ? in_d0 : 0u);
+    const uint32_t c_lo = bin_lo > d0 ? hist_lo : (bin_lo == d0 ? in_d0 : 0u);
+    const int64_t parts = n_cand / k;
+    reinterpret_cast<uint32_t*>(cand_hist + (row * parts + p) * kHistBins)[kHistBins / 2 - 1 - threadIdx.x] =
+        (c_hi << 16) | c_lo;
+  }
   const int64_t first = int64_t(threadIdx.x) * ITEMS;
   for_each_kept<kNT, ITEMS>(key, valid, first, tau, mask, kk, sm, [&](int64_t unit, int64_t pos) {
     if (pos < k_p) {
@@ -148,10 +193,11 @@ __global__ __launch_bounds__(kNT) void partition_topk_kernel(const float* __rest
 }  // namespace
 
 hipError_t launch_partition_topk(const float* scores, int64_t rows, int64_t n, int64_t ld, int64_t k,
-                                 float* cand_score, int64_t cand_ld, int32_t* cand_id, hipStream_t s) {
+                                 float* cand_score, int64_t cand_ld, int32_t* cand_id, const uint16_t* tile_hist,
+                                 int64_t tiles, uint16_t* cand_hist, hipStream_t s) {
   const int64_t parts = (n + kPartUnits - 1) / kPartUnits;
   hipLaunchKernelGGL(partition_topk_kernel, dim3(unsigned(parts), unsigned(rows)), dim3(kNT), 0, s, scores, n, ld, k,
-                     cand_score, cand_ld, cand_id, parts * k);
+                     cand_score, cand_ld, cand_id, parts * k, tile_hist, tiles, cand_hist);
   return hipGetLastError();
 }
 

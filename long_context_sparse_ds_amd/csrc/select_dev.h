@@ -18,14 +18,15 @@
 namespace ds {
 
 // Candidates (keys sharing the k-th largest key's top 11 bits) gathered into
-// LDS for the remaining radix passes; more than this falls back to passes over
-// all the register-resident keys.
+// LDS for the remaining radix passes; more than this (a kernel may choose a
+// larger capacity) falls back to passes over all the register-resident keys.
 constexpr int kCandCap = 2048;
 
-template <int NT>
+template <int NT, int CAP = kCandCap>
 struct SelSmem {
+  static constexpr int kCap = CAP;
   uint32_t hist[2048];
-  uint32_t cand[kCandCap];
+  uint32_t cand[CAP];
   uint32_t wsum[3][NT / 64];   // one per scan use, so no scan needs a trailing barrier
   uint32_t digit, above, ncand, tau, kk;
 };
@@ -84,8 +85,8 @@ __device__ __forceinline__ int first_lane_reaching(uint32_t incl, uint32_t kk) {
 // lane-rotated so one step's reads fall in distinct LDS banks), a lane scan
 // finds the lane whose bins hold the kk-th key, then that lane's bins are
 // spread over the lanes and scanned again.
-template <int NT>
-__device__ __forceinline__ void pick_digit(SelSmem<NT>& sm, int nb, int shift, uint32_t& prefix, uint32_t& mask,
+template <int NT, int CAP>
+__device__ __forceinline__ void pick_digit(SelSmem<NT, CAP>& sm, int nb, int shift, uint32_t& prefix, uint32_t& mask,
                                            uint32_t& kk) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
@@ -138,15 +139,15 @@ __device__ __forceinline__ uint32_t block_exclusive_scan1(uint32_t v, uint32_t* 
 // `mask`, equal to `prefix`): histogram of the next digit, then the digit that
 // holds the kk-th largest.  Returns the number of candidates in that digit.
 // The histogram must be zeroed (and a barrier passed) on entry.
-template <int NT>
-__device__ __forceinline__ uint32_t candidate_pass(SelSmem<NT>& sm, int n, int shift, int nb, uint32_t& prefix,
+template <int NT, int CAP>
+__device__ __forceinline__ uint32_t candidate_pass(SelSmem<NT, CAP>& sm, int n, int shift, int nb, uint32_t& prefix,
                                                    uint32_t& mask, uint32_t& kk) {
   for (int i = threadIdx.x; i < n; i += NT) {
     const uint32_t c = sm.cand[i];
     if ((c & mask) == prefix) atomicAdd(&sm.hist[(c >> shift) & uint32_t(nb - 1)], 1u);
   }
   __syncthreads();
-  pick_digit<NT>(sm, nb, shift, prefix, mask, kk);
+  pick_digit(sm, nb, shift, prefix, mask, kk);
   const uint32_t count = sm.hist[sm.digit];
   __syncthreads();   // every thread holds the count before anyone clears the histogram
   return count;
@@ -160,9 +161,9 @@ __device__ __forceinline__ uint32_t candidate_pass(SelSmem<NT>& sm, int n, int s
 // their count).  hist_hi / hist_lo: when have_hist, the number of valid keys
 // whose top 11 bits are 2047 - 2t and 2046 - 2t for thread t (NT = 1024);
 // otherwise the histogram is built here.
-template <int NT, int ITEMS>
+template <int NT, int ITEMS, int CAP>
 __device__ __forceinline__ uint32_t select_threshold(const uint32_t (&key)[ITEMS], const bool (&valid)[ITEMS],
-                                                     uint32_t k, SelSmem<NT>& sm, uint32_t& kk_out,
+                                                     uint32_t k, SelSmem<NT, CAP>& sm, uint32_t& kk_out,
                                                      uint32_t& mask_out, bool have_hist, uint32_t hist_hi,
                                                      uint32_t hist_lo) {
   static_assert(NT * 2 == 2048, "two top-digit bins per thread");
@@ -203,20 +204,20 @@ __device__ __forceinline__ uint32_t select_threshold(const uint32_t (&key)[ITEMS
 #pragma unroll
   for (int j = 0; j < ITEMS; ++j)
     if (valid[j] && (key[j] >> 21) == digit) {
-      if (at < uint32_t(kCandCap)) sm.cand[at] = key[j];
+      if (at < uint32_t(CAP)) sm.cand[at] = key[j];
       ++at;
     }
   // Zero the histogram for the next pass while the candidates land.
   for (int i = tid; i < 2048; i += NT) sm.hist[i] = 0u;
   __syncthreads();
   const uint32_t ncand = sm.ncand;
-  if (ncand <= uint32_t(kCandCap)) {
+  if (ncand <= uint32_t(CAP)) {
     // Bits 20..10 of the candidates; when the chosen digit holds exactly the kk
     // keys still needed, all of them are kept and the selection is settled at
     // that precision (no tie can straddle it): return the 22-bit prefix as tau
     // with the mask, so the caller compares masked keys.
     uint32_t prefix = digit << 21, mask = 0xFFE00000u;
-    const uint32_t c1 = candidate_pass<NT>(sm, int(ncand), 10, 2048, prefix, mask, kk);
+    const uint32_t c1 = candidate_pass(sm, int(ncand), 10, 2048, prefix, mask, kk);
     if (c1 == kk) {
       kk_out = kk;
       mask_out = mask;
@@ -224,7 +225,7 @@ __device__ __forceinline__ uint32_t select_threshold(const uint32_t (&key)[ITEMS
     }
     for (int i = tid; i < 1024; i += NT) sm.hist[i] = 0u;
     __syncthreads();
-    candidate_pass<NT>(sm, int(ncand), 0, 1024, prefix, mask, kk);
+    candidate_pass(sm, int(ncand), 0, 1024, prefix, mask, kk);
     kk_out = kk;
     mask_out = 0xFFFFFFFFu;
     return prefix;
@@ -240,7 +241,7 @@ __device__ __forceinline__ uint32_t select_threshold(const uint32_t (&key)[ITEMS
     for (int j = 0; j < ITEMS; ++j)
       if (valid[j] && (key[j] & mask) == prefix) atomicAdd(&sm.hist[(key[j] >> shift) & uint32_t(nb - 1)], 1u);
     __syncthreads();
-    pick_digit<NT>(sm, nb, shift, prefix, mask, kk);
+    pick_digit(sm, nb, shift, prefix, mask, kk);
   }
   kk_out = kk;
   mask_out = 0xFFFFFFFFu;
@@ -254,9 +255,9 @@ __device__ __forceinline__ int radix_bins(int pass) { return pass < 2 ? 2048 : 1
 // [first, first + ITEMS), positions ascending with the unit index across the
 // whole row, for the threshold (tau, mask, kk) of select_threshold.  NT * ITEMS
 // must stay below 65536.
-template <int NT, int ITEMS, class F>
+template <int NT, int ITEMS, int CAP, class F>
 __device__ __forceinline__ void for_each_kept(const uint32_t (&key)[ITEMS], const bool (&valid)[ITEMS], int64_t first,
-                                              uint32_t tau, uint32_t mask, uint32_t kk, SelSmem<NT>& sm, F&& fn) {
+                                              uint32_t tau, uint32_t mask, uint32_t kk, SelSmem<NT, CAP>& sm, F&& fn) {
   static_assert(int64_t(NT) * ITEMS < 65536, "per-row counts must fit in 16 bits");
   uint32_t gt = 0u, eq = 0u;
 #pragma unroll
