@@ -1,0 +1,108 @@
+"""Host-side logic on the CPU: the benchmark's byte accounting for every kind of
+workload, the span search's round count (against the oracle's own stopping rule),
+the seeded generators, and the workspace sizes of the library's plans.  No GPU."""
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import dsgen
+import long_context_sparse_ds_amd as L
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_headline_bytes_match_the_definition():
+    """label scan + kept K/V rows + q + fp32 out + indices + the appended label row."""
+    w = dsgen.get("llama7b_16k")
+    ab = bench.algorithmic_bytes(w)
+    assert ab["label_scan"] == 32 * 16384 * 16 * 2
+    assert ab["kv_gather"] == 2 * 32 * 1024 * 128 * 2
+    assert ab["q"] == 32 * 128 * 2 and ab["out"] == 4 * 32 * 128 and ab["indices"] == 4 * 32 * 1024
+    assert ab["label_append"] == 2 * 32 * 16 * 2
+    assert ab["step"] == sum(v for k, v in ab.items() if k != "step") == 33_712_128
+
+
+def test_block_workload_bytes_count_whole_blocks():
+    w = dsgen.get("block64_256k")
+    ab = bench.algorithmic_bytes(w)
+    assert ab["kv_gather"] == 2 * 32 * 64 * 64 * 128 * 2
+    assert ab["indices"] == 4 * 32 * 64
+
+
+def test_ragged_bytes_use_each_sequence_length():
+    w = dsgen.get("ragged_16k")
+    lens = dsgen.seq_lengths(w)
+    ab = bench.algorithmic_bytes(w, lens)
+    assert ab["label_scan"] == w.Hkv * int(lens.sum()) * w.r * 2
+    assert ab["kv_gather"] == 2 * w.Hkv * sum(min(w.k_units, int(t)) for t in lens) * w.d * 2
+    assert ab["seq_lens"] == 4 * w.B
+    short = w.with_(T=5000)
+    ab2 = bench.algorithmic_bytes(short, np.array([5000, 300], dtype=np.int32))
+    assert ab2["kv_gather"] == 2 * short.Hkv * (1024 + 300) * short.d * 2   # a short sequence keeps all it has
+
+
+def test_threshold_bytes_follow_the_kept_counts():
+    w = dsgen.get("jenga_gqa_32k")
+    ab = bench.algorithmic_bytes(w, None, (123_264, 1_926))
+    assert ab["kv_gather"] == 2 * 123_264 * 128 * 2 and ab["indices"] == 4 * 1_926
+    assert ab["counts"] == 4 * w.B * w.Hkv
+
+
+@pytest.mark.parametrize("T,k,span", [(1 << 20, 64, 64), (1000, 20, 64), (10, 3, 2), (97, 5, 3), (4096, 32, 16),
+                                      (777, 50, 1), (65536, 1024, 16)])
+def test_span_search_round_count_matches_the_oracle(T, k, span):
+    """The host's round count (halvings of ceil(T / k) down to `span`) is at least the
+    number of rounds the oracle runs, and the extra rounds change nothing: running the
+    oracle's rule for exactly that many rounds ends with no span longer than `span`."""
+    w = dsgen.Workload("r", "bf16", B=1, Hq=1, Hkv=1, d=128, T=T, r=16, block=span, k_units=k, seed_base=1, hip=True)
+    rounds = bench.hip_rounds(w)
+    longest = max((i + 1) * T // k - i * T // k for i in range(k))
+    for _ in range(rounds):
+        longest = longest if longest <= span else -(-longest // 2)
+    assert longest <= span
+    cap = L.ds_hip_token_capacity(T, k, span)
+    assert cap == (k * span if rounds > 0 else T)
+    if rounds > 0:
+        assert k * span < T   # a round runs only when the spans cannot cover every token
+
+
+def test_span_search_oracle_never_needs_more_rounds_than_the_host():
+    rng = np.random.default_rng(3)
+    for T, k, span in ((97, 5, 3), (1000, 16, 8), (300, 7, 2)):
+        K = rng.standard_normal((T, 8))
+        q = rng.standard_normal((2, 8))
+        w = dsgen.Workload("r", "bf16", B=1, Hq=2, Hkv=1, d=8, T=T, r=4, block=span, k_units=k, seed_base=1)
+        spans = O.hip_search(q, K, T, k, span)
+        assert max(e - s for s, e in spans) <= span
+        assert bench.hip_rounds(w) >= math.ceil(math.log2(max(1, -(-T // k) / span)))
+
+
+def test_generators_are_deterministic_and_lengths_in_range():
+    w = dsgen.get("ragged_16k")
+    a, b = dsgen.seq_lengths(w), dsgen.seq_lengths(w)
+    assert np.array_equal(a, b) and a[0] == w.T and a.min() >= w.T // 16 and a.max() <= w.T
+    assert np.array_equal(dsgen.seq_lengths(dsgen.get("llama7b_16k")), [16384])
+    small = dsgen.Workload("g", "bf16", B=2, Hq=4, Hkv=2, d=128, T=300, r=16, block=1, k_units=10, seed_base=77,
+                           T_cap=320)
+    q1, K1, V1 = dsgen.gen_cache(small)
+    q2, K2, V2 = dsgen.gen_cache(small, threads=1)
+    assert np.array_equal(K1, K2) and np.array_equal(V1, V2) and np.array_equal(q1, q2)
+    assert np.all(K1[:, :, 300:] == np.uint16(0x7FC0))   # NaN padding past T
+
+
+def test_workspace_grows_with_the_two_stage_candidates():
+    """Rows over 32,768 units whose candidates fit the fused kernel reserve candidate
+    buffers; shapes beyond that fall back to the streaming path and still size cleanly."""
+    small = L.ds_decode_workspace_bytes(1, 4, 2, 128, 70000, 1, 2000)
+    assert small > 0
+    cand = 2 * (3 * 2000) * (4 + 4)   # scores and ids of 3 partitions x k per row, 2 rows
+    assert small >= cand
+    stream = L.ds_decode_workspace_bytes(1, 4, 2, 128, 70000, 1, 20000)   # 3 * 20000 > 32768
+    assert stream > 0
