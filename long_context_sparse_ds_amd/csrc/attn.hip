@@ -96,29 +96,39 @@ __global__ __launch_bounds__(kAT) void attn_kernel(const TE* __restrict__ q, con
   const TE* Vr = V + int64_t(row) * T_cap * kHeadDim + sub * EPL;
 
   for (int64_t base = p_begin; base < p_end; base += int64_t(NG) * kU) {
+    // Every load is issued unconditionally: positions past the slice read the
+    // slice's first index, and invalid slots read token 0 (always a real row)
+    // and are masked after the load.  A load inside a branch makes the
+    // compiler wait for it before the next one is issued.
     int64_t tok[kU];
     bool ok[kU];
+    int32_t unit[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int64_t p = base + int64_t(gid) * kU + u;
       ok[u] = p < p_end;
-      tok[u] = 0;
-      if (ok[u]) {
-        const int64_t unit = ridx[p >> lb];
-        tok[u] = (unit << lb) + (p & (block - 1));
-        ok[u] = unit >= 0 && tok[u] < T;
-      }
+      unit[u] = ridx[(ok[u] ? p : p_begin) >> lb];
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t p = base + int64_t(gid) * kU + u;
+      tok[u] = (int64_t(unit[u]) << lb) + (p & (block - 1));
+      ok[u] = ok[u] && unit[u] >= 0 && tok[u] < T;
+      if (!ok[u]) tok[u] = 0;
     }
     uint4 kr[kU], vr[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      if (ok[u]) {
-        kr[u] = *reinterpret_cast<const uint4*>(Kr + tok[u] * kHeadDim);
-        vr[u] = *reinterpret_cast<const uint4*>(Vr + tok[u] * kHeadDim);
-      } else {
-        kr[u] = make_uint4(0u, 0u, 0u, 0u);
-        vr[u] = make_uint4(0u, 0u, 0u, 0u);
-      }
+      kr[u] = *reinterpret_cast<const uint4*>(Kr + tok[u] * kHeadDim);
+      vr[u] = *reinterpret_cast<const uint4*>(Vr + tok[u] * kHeadDim);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {   // masked rows add nothing, whatever they hold (a bit mask, not a branch)
+      const uint32_t keep = ok[u] ? 0xFFFFFFFFu : 0u;
+      vr[u].x &= keep;
+      vr[u].y &= keep;
+      vr[u].z &= keep;
+      vr[u].w &= keep;
     }
     float kf[kU][EPL], vf[kU][EPL];
 #pragma unroll
@@ -205,26 +215,33 @@ __global__ __launch_bounds__(kAT) void attn_kernel(const TE* __restrict__ q, con
   }
 }
 
-// Log-sum-exp merge of the splits of one (sequence, query head): one thread per
-// channel, every split's values requested before any is used.
+// Log-sum-exp merge of the splits of one (sequence, query head).  kMergeSG
+// groups of one thread per channel each take every kMergeSG-th split, with all
+// of a batch's values requested before any is used, and the groups' partial
+// states are combined through LDS: 64 splits are one batch of loads.
 constexpr int kMergeBatch = 16;
+constexpr int kMergeSG = 4;
 
-__global__ __launch_bounds__(kHeadDim) void merge_kernel(const float* __restrict__ part_acc,
-                                                         const float* __restrict__ part_ml, int n_split,
-                                                         float* __restrict__ out) {
+__global__ __launch_bounds__(kHeadDim * kMergeSG) void merge_kernel(const float* __restrict__ part_acc,
+                                                                    const float* __restrict__ part_ml,
+                                                                    int n_split, float* __restrict__ out) {
+  __shared__ float sm_m[kMergeSG][kHeadDim], sm_l[kMergeSG][kHeadDim], sm_a[kMergeSG][kHeadDim];
   const int64_t bh = blockIdx.x;
-  const int c = threadIdx.x;
+  const int c = threadIdx.x % kHeadDim, sg = threadIdx.x / kHeadDim;
   const float* ml = part_ml + bh * n_split * 2;
   const float* pa = part_acc + bh * n_split * kHeadDim + c;
   float M = -INFINITY, L = 0.f, A = 0.f;
-  for (int s0 = 0; s0 < n_split; s0 += kMergeBatch) {
+  for (int s0 = sg; s0 < n_split; s0 += kMergeSG * kMergeBatch) {
     float a[kMergeBatch], m[kMergeBatch], l[kMergeBatch];
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
-      const bool ok = s0 + j < n_split;
-      a[j] = ok ? pa[int64_t(s0 + j) * kHeadDim] : 0.f;
-      m[j] = ok ? ml[2 * (s0 + j)] : -INFINITY;
-      l[j] = ok ? ml[2 * (s0 + j) + 1] : 0.f;
+      const int sp = s0 + j * kMergeSG;
+      const bool ok = sp < n_split;
+      const int sc = ok ? sp : sg;   // clamped: every load is issued, masked after
+      a[j] = pa[int64_t(sc) * kHeadDim];
+      m[j] = ml[2 * sc];
+      l[j] = ml[2 * sc + 1];
+      if (!ok) m[j] = -INFINITY;
     }
     float Mb = M;
 #pragma unroll
@@ -235,13 +252,29 @@ __global__ __launch_bounds__(kHeadDim) void merge_kernel(const float* __restrict
     A *= r;
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
-      const float f = __expf(m[j] - Mb);   // empty split (m = -inf): 0
+      const float f = __expf(m[j] - Mb);   // empty or masked split (m = -inf): 0
       L = fmaf(l[j], f, L);
       A = fmaf(a[j], f, A);
     }
     M = Mb;
   }
-  out[bh * kHeadDim + c] = A / L;
+  sm_m[sg][c] = M;
+  sm_l[sg][c] = L;
+  sm_a[sg][c] = A;
+  __syncthreads();
+  if (sg == 0) {
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < kMergeSG; ++g) Mt = fmaxf(Mt, sm_m[g][c]);
+    float Lt = 0.f, At = 0.f;
+#pragma unroll
+    for (int g = 0; g < kMergeSG; ++g) {
+      const float f = sm_m[g][c] == -INFINITY ? 0.f : __expf(sm_m[g][c] - Mt);
+      Lt = fmaf(sm_l[g][c], f, Lt);
+      At = fmaf(sm_a[g][c], f, At);
+    }
+    out[bh * kHeadDim + c] = At / Lt;
+  }
 }
 
 template <typename TE>
@@ -288,7 +321,8 @@ hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t s) {
 
 hipError_t launch_merge(const float* part_acc, const float* part_ml, int64_t BH, int n_split, float* out,
                         hipStream_t s) {
-  hipLaunchKernelGGL(merge_kernel, dim3(unsigned(BH)), dim3(kHeadDim), 0, s, part_acc, part_ml, n_split, out);
+  hipLaunchKernelGGL(merge_kernel, dim3(unsigned(BH)), dim3(kHeadDim * kMergeSG), 0, s, part_acc, part_ml, n_split,
+                     out);
   return hipGetLastError();
 }
 

@@ -56,6 +56,28 @@ __device__ __forceinline__ double lane_sum(double v, int lanes) {
   return v;
 }
 
+// A token's score from this lane's 16 bytes of its K row: the lane's products
+// accumulated in double, then summed over the lane group (the same order in
+// every kernel here, so every path ranks the same floats).
+template <typename TE>
+__device__ __forceinline__ float row_dot(const uint4& w, const double (&qbar)[SearchLanes<TE>::EPL]) {
+  double acc = 0.0;
+  if constexpr (sizeof(TE) == 2) {
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc = fma(qbar[2 * j], double(bf16_lo(u[j])), acc);
+      acc = fma(qbar[2 * j + 1], double(bf16_hi(u[j])), acc);
+    }
+  } else {
+    acc = fma(qbar[0], double(__uint_as_float(w.x)), acc);
+    acc = fma(qbar[1], double(__uint_as_float(w.y)), acc);
+    acc = fma(qbar[2], double(__uint_as_float(w.z)), acc);
+    acc = fma(qbar[3], double(__uint_as_float(w.w)), acc);
+  }
+  return float(lane_sum(acc, SearchLanes<TE>::LPT));
+}
+
 // Scores of the posted tokens req[0, k): one lane group per token and step.
 template <typename TE>
 __device__ __forceinline__ void score_posted(SearchSmem& sm, int k, const TE* __restrict__ Kr,
@@ -67,22 +89,8 @@ __device__ __forceinline__ void score_posted(SearchSmem& sm, int k, const TE* __
     const int t = sm.req[i];
     if (t < 0) continue;   // uniform over the lane group
     const uint4 w = *reinterpret_cast<const uint4*>(Kr + int64_t(t) * kHeadDim + sub * SL::EPL);
-    double acc = 0.0;
-    if constexpr (sizeof(TE) == 2) {
-      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc = fma(qbar[2 * j], double(bf16_lo(u[j])), acc);
-        acc = fma(qbar[2 * j + 1], double(bf16_hi(u[j])), acc);
-      }
-    } else {
-      acc = fma(qbar[0], double(__uint_as_float(w.x)), acc);
-      acc = fma(qbar[1], double(__uint_as_float(w.y)), acc);
-      acc = fma(qbar[2], double(__uint_as_float(w.z)), acc);
-      acc = fma(qbar[3], double(__uint_as_float(w.w)), acc);
-    }
-    acc = lane_sum(acc, SL::LPT);
-    if (sub == 0) sm.score[i] = float(acc);
+    const float sc = row_dot<TE>(w, qbar);
+    if (sub == 0) sm.score[i] = sc;
   }
 }
 
@@ -165,12 +173,280 @@ __global__ __launch_bounds__(kST) void hip_search_kernel(const TE* __restrict__ 
   for (int i = int(total) + tid; i < cap; i += kST) tr[i] = -1;
 }
 
+
+// ---------------------------------------------------------------------------
+// k <= 64 spans: the same search with one wavefront selecting and the other
+// fifteen scoring ahead.
+//
+// A round's candidates (at most 128) fit one wavefront, two per lane: wave 0
+// sorts their keys in registers (a bitonic network whose lane exchanges are
+// DPP permutations and the permlane swaps, no LDS and no barrier), reads the
+// k-th largest key, and keeps the keys above it plus, lowest candidate first,
+// as many keys equal to it as are still needed; ballots give every kept
+// candidate its ascending position.  Meanwhile waves 1-15 score the first
+// token of the right part of every candidate that will be split if it is
+// kept, so the next round's scores are ready when the selection ends and a
+// round costs one K-row read or one sort, whichever is longer, instead of
+// both.  The scores and the tie rule are those of the kernel above.
+
+constexpr int kWaveSpans = 64;
+constexpr int kWaveCand = 2 * kWaveSpans;
+
+struct WaveSearchSmem {
+  int32_t cs[kWaveCand], ce[kWaveCand];   // the round's candidates (start, end); unused slots: 0, 0, key 0
+  uint32_t ckey[kWaveCand];
+  float spec[kWaveCand];                  // score of candidate c's right part's first token
+  int32_t tok[kWaveCand];                 // first round: tokens to score
+  float tsc[kWaveCand];
+  int32_t ks[kWaveSpans], ke[kWaveSpans], kc[kWaveSpans];   // kept spans, ascending, and their candidate ids
+  uint32_t kkey[kWaveSpans];
+  uint32_t wsum[kST / 64];
+};
+
+// The value held by lane (lane ^ D) of the wavefront, D a power of two < 64.
+template <int D>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v, int lane) {
+  if constexpr (D == 1) {
+    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  } else if constexpr (D == 2) {
+    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  } else if constexpr (D == 4) {
+    // Mirror within each half row (lane i takes i ^ 7), then quad_perm
+    // [3,2,1,0] (i takes i ^ 3): i takes i ^ 4.
+    const int m = __builtin_amdgcn_update_dpp(0, int(v), 0x141, 0xF, 0xF, false);
+    return uint32_t(__builtin_amdgcn_update_dpp(0, m, 0x1B, 0xF, 0xF, false));
+  } else if constexpr (D == 8) {
+    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x128, 0xF, 0xF, false));  // rotate each row by 8
+  } else if constexpr (D == 16) {
+    // Rows 2p and 2p + 1 swap: the first result holds the even row's values
+    // in both rows, the second the odd row's.
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane & 16) ? r[0] : r[1];
+  } else {
+    static_assert(D == 32, "lane distance");
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (lane & 32) ? r[0] : r[1];
+  }
+}
+
+// Bitonic sort, descending, of the wavefront's 128 keys: element t * 64 + lane
+// is x[t] of that lane.
+template <int SIZE, int DIST>
+__device__ __forceinline__ void bitonic_merge(uint32_t (&x)[2], int lane) {
+  if constexpr (DIST == 64) {
+    const uint32_t hi = max(x[0], x[1]), lo = min(x[0], x[1]);
+    x[0] = hi;
+    x[1] = lo;
+  } else {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int j = t * 64 + lane;
+      const uint32_t p = lane_xor<DIST>(x[t], lane);
+      // The lower element of a pair takes the larger key in a descending run,
+      // the smaller in an ascending one.
+      const bool take_max = ((j & SIZE) == 0) == ((j & DIST) == 0);
+      x[t] = take_max ? max(x[t], p) : min(x[t], p);
+    }
+  }
+  if constexpr (DIST > 1) bitonic_merge<SIZE, DIST / 2>(x, lane);
+}
+
+template <int SIZE>
+__device__ __forceinline__ void bitonic_sort(uint32_t (&x)[2], int lane) {
+  if constexpr (SIZE > 2) bitonic_sort<SIZE / 2>(x, lane);
+  bitonic_merge<SIZE, SIZE / 2>(x, lane);
+}
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
+}
+
+// Wave 0: the k best of the round's candidates, in ascending order, to ks/ke/kkey/kc.
+__device__ __forceinline__ void wave_select(WaveSearchSmem& sm, int k, int lane) {
+  const int c0 = 2 * lane, c1 = c0 + 1;
+  const uint32_t o0 = sm.ckey[c0], o1 = sm.ckey[c1];
+  uint32_t x[2] = {o0, o1};
+  bitonic_sort<kWaveCand>(x, lane);
+  // Every span leaves at least one valid candidate, so k valid keys (all
+  // nonzero) exist and the k-th largest is one of them.
+  const uint32_t thr = __builtin_amdgcn_readlane(x[0], k - 1);
+  const uint32_t n_gt = uint32_t(__popcll(__ballot(o0 > thr))) + uint32_t(__popcll(__ballot(o1 > thr)));
+  const uint32_t eq_take = uint32_t(k) - n_gt;
+  const bool e0 = o0 == thr, e1 = o1 == thr;
+  const uint32_t eb0 = lanes_below(__ballot(e0)) + lanes_below(__ballot(e1));
+  const uint32_t eb1 = eb0 + uint32_t(e0);
+  const bool k0 = o0 > thr || (e0 && eb0 < eq_take);
+  const bool k1 = o1 > thr || (e1 && eb1 < eq_take);
+  const uint32_t p0 = lanes_below(__ballot(k0)) + lanes_below(__ballot(k1));
+  const uint32_t p1 = p0 + uint32_t(k0);
+  if (k0) {
+    sm.ks[p0] = sm.cs[c0];
+    sm.ke[p0] = sm.ce[c0];
+    sm.kkey[p0] = o0;
+    sm.kc[p0] = c0;
+  }
+  if (k1) {
+    sm.ks[p1] = sm.cs[c1];
+    sm.ke[p1] = sm.ce[c1];
+    sm.kkey[p1] = o1;
+    sm.kc[p1] = c1;
+  }
+}
+
+// Scores of the tokens t[u] (t < 0: none; token 0 is read in its place) of
+// this lane group, every K row requested before any is used.
+template <typename TE, int PER>
+__device__ __forceinline__ void score_tokens(const int32_t (&t)[PER], const TE* __restrict__ Kr, int sub,
+                                             const double (&qbar)[SearchLanes<TE>::EPL], float (&out)[PER]) {
+  using SL = SearchLanes<TE>;
+  uint4 w[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u)
+    w[u] = *reinterpret_cast<const uint4*>(Kr + int64_t(t[u] < 0 ? 0 : t[u]) * kHeadDim + sub * SL::EPL);
+#pragma unroll
+  for (int u = 0; u < PER; ++u) out[u] = row_dot<TE>(w[u], qbar);
+}
+
+template <typename TE>
+__global__ __launch_bounds__(kST) void hip_search_wave_kernel(const TE* __restrict__ q, const TE* __restrict__ K,
+                                                              int Hq, int Hkv, int64_t T_cap, int T, int k, int span,
+                                                              int rounds, int32_t* __restrict__ spans_out,
+                                                              int32_t* __restrict__ tokens, int cap) {
+  using SL = SearchLanes<TE>;
+  constexpr int NG = SL::NG;                        // lane groups of the workgroup
+  constexpr int NGS = SL::NG - 64 / SL::LPT;        // lane groups of waves 1-15
+  constexpr int PER0 = (kWaveCand + NG - 1) / NG;   // first round: tokens per lane group
+  constexpr int PERS = (kWaveCand + NGS - 1) / NGS; // later rounds
+  __shared__ WaveSearchSmem sm;
+  const uint32_t row = blockIdx.x;
+  const uint32_t b = row / uint32_t(Hkv), g = row - b * uint32_t(Hkv);
+  const int G = Hq / Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sub = lane % SL::LPT, gid = tid / SL::LPT;
+  const TE* Kr = K + int64_t(row) * T_cap * kHeadDim;
+
+  double qbar[SL::EPL];
+#pragma unroll
+  for (int e = 0; e < SL::EPL; ++e) qbar[e] = 0.0;
+  for (int h = 0; h < G; ++h) {
+    const TE* qh = q + (int64_t(b) * Hq + int64_t(g) * G + h) * kHeadDim + sub * SL::EPL;
+#pragma unroll
+    for (int e = 0; e < SL::EPL; ++e) qbar[e] += double(elem_to_f32(qh[e]));
+  }
+
+  const bool mine = tid < k;
+  const int s0 = mine ? int(int64_t(tid) * T / k) : 0;
+  const int e0 = mine ? int(int64_t(tid + 1) * T / k) : 0;
+  if (rounds == 0) {
+    if (mine) {
+      sm.ks[tid] = s0;
+      sm.ke[tid] = e0;
+    }
+  } else {
+    // First round: the first spans' first tokens and their right parts' first tokens.
+    const bool split0 = mine && e0 - s0 > span;
+    const int m0 = s0 + (e0 - s0 + 1) / 2;
+    if (tid < kWaveSpans) {
+      sm.tok[2 * tid] = mine ? s0 : -1;
+      sm.tok[2 * tid + 1] = split0 ? m0 : -1;
+    }
+    __syncthreads();
+    {
+      int32_t t[PER0];
+      float sc[PER0];
+#pragma unroll
+      for (int u = 0; u < PER0; ++u) {
+        const int c = gid + NG * u;
+        t[u] = c < kWaveCand ? sm.tok[c] : -1;
+      }
+      score_tokens<TE, PER0>(t, Kr, sub, qbar, sc);
+#pragma unroll
+      for (int u = 0; u < PER0; ++u)
+        if (sub == 0 && t[u] >= 0) sm.tsc[gid + NG * u] = sc[u];
+    }
+    __syncthreads();
+    if (tid < kWaveSpans) {
+      sm.cs[2 * tid] = s0;
+      sm.ce[2 * tid] = split0 ? m0 : e0;
+      sm.ckey[2 * tid] = mine ? float_key(sm.tsc[2 * tid]) : 0u;
+      sm.cs[2 * tid + 1] = split0 ? m0 : 0;
+      sm.ce[2 * tid + 1] = split0 ? e0 : 0;
+      sm.ckey[2 * tid + 1] = split0 ? float_key(sm.tsc[2 * tid + 1]) : 0u;
+    }
+    __syncthreads();
+
+    for (int r = 1; r <= rounds; ++r) {
+      if (wave == 0) {
+        wave_select(sm, k, lane);
+      } else if (r < rounds) {
+        // Speculative scores: every candidate that would be split next round.
+        const int gs = gid - 64 / SL::LPT;
+        int32_t t[PERS];
+        float sc[PERS];
+#pragma unroll
+        for (int u = 0; u < PERS; ++u) {
+          const int c = gs + NGS * u;
+          const int cc = c < kWaveCand ? c : 0;
+          const int len = sm.ce[cc] - sm.cs[cc];
+          t[u] = c < kWaveCand && len > span ? sm.cs[cc] + (len + 1) / 2 : -1;
+        }
+        score_tokens<TE, PERS>(t, Kr, sub, qbar, sc);
+#pragma unroll
+        for (int u = 0; u < PERS; ++u)
+          if (sub == 0 && t[u] >= 0) sm.spec[gs + NGS * u] = sc[u];
+      }
+      __syncthreads();
+      if (r == rounds) break;
+      if (mine) {
+        // Kept span tid becomes candidates 2 tid (left part, its score) and
+        // 2 tid + 1 (right part, scored ahead).
+        const int s = sm.ks[tid], e = sm.ke[tid];
+        const bool split = e - s > span;
+        const int m = s + (e - s + 1) / 2;
+        sm.cs[2 * tid] = s;
+        sm.ce[2 * tid] = split ? m : e;
+        sm.ckey[2 * tid] = sm.kkey[tid];
+        sm.cs[2 * tid + 1] = split ? m : 0;
+        sm.ce[2 * tid + 1] = split ? e : 0;
+        sm.ckey[2 * tid + 1] = split ? float_key(sm.spec[sm.kc[tid]]) : 0u;
+      }
+      __syncthreads();
+    }
+  }
+  if (rounds == 0) __syncthreads();
+
+  // Spans, then the covered tokens in ascending order, -1 after them.
+  const int s = mine ? sm.ks[tid] : 0, e = mine ? sm.ke[tid] : 0;
+  if (mine) {
+    int32_t* so = spans_out + (int64_t(row) * k + tid) * 2;
+    so[0] = s;
+    so[1] = e;
+  }
+  uint32_t total;
+  const uint32_t off = block_exclusive_scan1<kST>(mine ? uint32_t(e - s) : 0u, sm.wsum, total);
+  int32_t* tr = tokens + int64_t(row) * cap;
+  if (mine)
+    for (int t = s; t < e; ++t) tr[off + uint32_t(t - s)] = t;
+  for (int i = int(total) + tid; i < cap; i += kST) tr[i] = -1;
+}
+
 }  // namespace
 
 hipError_t launch_hip_search(const void* q, const void* K, int is_bf16, int B, int Hq, int Hkv, int64_t T_cap,
                              int64_t T, int k, int span, int rounds, int32_t* spans, int32_t* tokens, int64_t cap,
                              hipStream_t s) {
   const dim3 grid(unsigned(int64_t(B) * Hkv));
+  if (k <= kWaveSpans) {
+    if (is_bf16)
+      hipLaunchKernelGGL(hip_search_wave_kernel<uint16_t>, grid, dim3(kST), 0, s, static_cast<const uint16_t*>(q),
+                         static_cast<const uint16_t*>(K), Hq, Hkv, T_cap, int(T), k, span, rounds, spans, tokens,
+                         int(cap));
+    else
+      hipLaunchKernelGGL(hip_search_wave_kernel<float>, grid, dim3(kST), 0, s, static_cast<const float*>(q),
+                         static_cast<const float*>(K), Hq, Hkv, T_cap, int(T), k, span, rounds, spans, tokens,
+                         int(cap));
+    return hipGetLastError();
+  }
   if (is_bf16)
     hipLaunchKernelGGL(hip_search_kernel<uint16_t>, grid, dim3(kST), 0, s, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(K), Hq, Hkv, T_cap, int(T), k, span, rounds, spans, tokens,

@@ -4,8 +4,9 @@ The search ranks float32 scores on both sides (the oracle rounds its float64 dot
 products to float32, the kernel rounds its double sums), so the kept spans must be
 identical; the attention output is compared with the oracle's attention over the
 GPU's spans.  Covered: bf16 and fp32, MHA and GQA groups, uneven spans (T not a
-multiple of k), a case with no round, k = 1 and k = 1024, span = 1, T_cap > T with
-NaN padding past T, the search stage against the one-call step, and the full-size
+multiple of k), a case with no round, k = 1, 64, 65 and 1024 (both selection kernels and
+their boundary), span = 1, T_cap > T with NaN padding past T, exact score ties decided by
+the lower start, the search stage against the one-call step, and the full-size
 one-million-token workload in the benchmark's launch configuration.
 """
 import numpy as np
@@ -43,6 +44,9 @@ HIP_CASES = [
     Workload("hip_k1", "bf16", B=1, Hq=8, Hkv=1, d=128, T=4096, r=16, block=64, k_units=1, seed_base=51400),
     Workload("hip_k1024", "bf16", B=1, Hq=2, Hkv=1, d=128, T=65536, r=16, block=16, k_units=1024, seed_base=51500),
     Workload("hip_no_round", "bf16", B=1, Hq=4, Hkv=2, d=128, T=1000, r=16, block=64, k_units=20, seed_base=51600),
+    # k <= 64 runs the one-wavefront selection, larger k the block radix selection: both sides of the boundary.
+    Workload("hip_k65", "bf16", B=1, Hq=8, Hkv=2, d=128, T=30000, r=16, block=32, k_units=65, seed_base=51700),
+    Workload("hip_k64_f32", "f32", B=1, Hq=4, Hkv=2, d=128, T=12345, r=16, block=8, k_units=64, seed_base=51800),
 ]
 
 
@@ -70,6 +74,25 @@ def test_hip_decode_all_rows(w):
     _say(f"{w.name} T={w.T} k={w.k_units} span={w.block} G={w.G} {w.dtype}")
     q, K, V, qd, Kd, Vd, out, spans = _run(w)
     assert np.all(np.isfinite(out))
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            _check_row(w, q, K, V, out, spans, b, g)
+
+
+@pytest.mark.parametrize("k", [48, 96], ids=["k48_wave", "k96_block"])
+def test_hip_ties_go_to_the_lower_start(k):
+    """K rows repeat with period 5, so every candidate's score equals that of many others and
+    the lower start must win each tie (the oracle's rule), in both selection kernels."""
+    w = Workload(f"hip_ties_k{k}", "bf16", B=1, Hq=4, Hkv=2, d=128, T=9000, r=16, block=16, k_units=k,
+                 seed_base=51900 + k)
+    _say(f"{w.name} T={w.T} k={k} span={w.block} (periodic K rows)")
+    q, K, V = dsgen.gen_cache(w)
+    K = np.ascontiguousarray(K)
+    K[:, :, 5:w.T] = K[:, :, np.arange(5, w.T) % 5]
+    qd, Kd, Vd = to_device(q, w.dtype), to_device(K, w.dtype), to_device(V, w.dtype)
+    out, spans = L.ds_decode_hip_attn(qd, Kd, Vd, w.T, w.k_units, w.block)
+    torch.cuda.synchronize()
+    out, spans = out.cpu().numpy(), spans.cpu().numpy()
     for b in range(w.B):
         for g in range(w.Hkv):
             _check_row(w, q, K, V, out, spans, b, g)
