@@ -57,16 +57,20 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+# The sources that build the decode step's two kernels (score_kernel, selattn_kernel) and plan their launches.
+DECODE_STEP_SOURCES = ("ds_api.hip", "ds_common.h", "score.hip", "select_dev.h", "selattn.hip")
+
+
 def kernel_sources_digest() -> str:
-    """Digest of the HIP/C++ sources, to tell whether recorded counters still describe the kernels."""
+    """Digest of the sources of the decode step's kernels and their launch plan, to tell whether recorded
+    counters still describe those kernels (the other kernels' sources do not enter it)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "long_context_sparse_ds_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            h.update(name.encode())
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(f.read())
+    for name in DECODE_STEP_SOURCES:
+        h.update(name.encode())
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 

@@ -26,6 +26,8 @@ constexpr int kAT = 256;
 constexpr int kAW = kAT / 64;
 constexpr int kU = 4;   // kept rows per lane group per step
 
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+
 template <typename TE>
 struct Lanes {
   static constexpr int EPL = 16 / int(sizeof(TE));   // elements per lane: 8 (bf16), 4 (fp32)
@@ -71,13 +73,24 @@ __global__ __launch_bounds__(kAT) void attn_kernel(const TE* __restrict__ q, con
   const int grp = lane / LPT, sub = lane % LPT;
   const int gid = wave * GPW + grp;
 
+  // bf16: q stays packed and q.k runs on v_dot2_f32_bf16 (exact bf16 products,
+  // float32 sums), scaled after the lane-group sum; nothing of K is unpacked,
+  // which keeps the kernel at four workgroups per CU.  fp32: scaled floats.
+  constexpr bool kDot2 = sizeof(TE) == 2;
+  uint32_t qp[HC][4];
   float qv[HC][EPL];
 #pragma unroll
   for (int h = 0; h < HC; ++h) {
     const uint4 w = *reinterpret_cast<const uint4*>(q + (int64_t(b) * Hq + h0 + h) * kHeadDim + sub * EPL);
-    unpack(w, qv[h], TE());
+    qp[h][0] = w.x;
+    qp[h][1] = w.y;
+    qp[h][2] = w.z;
+    qp[h][3] = w.w;
+    if constexpr (!kDot2) {
+      unpack(w, qv[h], TE());
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) qv[h][e] *= scale;
+      for (int e = 0; e < EPL; ++e) qv[h][e] *= scale;
+    }
   }
 
   float m[HC], l[HC], acc[HC][EPL];
@@ -130,21 +143,29 @@ __global__ __launch_bounds__(kAT) void attn_kernel(const TE* __restrict__ q, con
       vr[u].z &= keep;
       vr[u].w &= keep;
     }
-    float kf[kU][EPL], vf[kU][EPL];
+    float vf[kU][EPL];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      unpack(kr[u], kf[u], TE());
-      unpack(vr[u], vf[u], TE());
-    }
+    for (int u = 0; u < kU; ++u) unpack(vr[u], vf[u], TE());
 #pragma unroll
     for (int h = 0; h < HC; ++h) {
       float z[kU];
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         float dsum = 0.f;
+        if constexpr (kDot2) {
+          const uint32_t kw[4] = {kr[u].x, kr[u].y, kr[u].z, kr[u].w};
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) dsum = fmaf(qv[h][e], kf[u][e], dsum);
-        dsum = group_sum<TE>(dsum);
+          for (int j = 0; j < 4; ++j)
+            dsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qp[h][j]),
+                                                   __builtin_bit_cast(bf16x2_t, kw[j]), dsum, false);
+          dsum = group_sum<TE>(dsum) * scale;
+        } else {
+          float kf[EPL];
+          unpack(kr[u], kf, TE());
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) dsum = fmaf(qv[h][e], kf[e], dsum);
+          dsum = group_sum<TE>(dsum);
+        }
         z[u] = ok[u] ? dsum : -INFINITY;
       }
       float mx = m[h];

@@ -69,11 +69,15 @@ void set_error(const char* msg) { g_err = msg; }
 SplitPlan plan_split(int64_t rows, int G, int64_t kv_virtual, bool fused) {
   SplitPlan sp{};
   // Fused workgroups are 1024 threads, one resident per CU, and aim at ~256 of
-  // them (each repeats the row's selection, so fewer is cheaper); separate
-  // attention workgroups are 256 threads and aim at ~2048.  Slices hold at
-  // least 64 kept positions, and a row is cut into at most 1024 splits.
+  // them (each repeats the row's selection, so fewer is cheaper, and a second
+  // round of workgroups would pay it twice); separate attention workgroups are
+  // 256 threads and aim at ~2048.  Every head chunk of a row is a workgroup of
+  // its own.  Slices hold at least 64 kept positions, and a row is cut into
+  // at most 1024 splits.
+  const int head_chunk = fused ? head_chunk4(G) : head_chunk8(G);
+  const int64_t head_chunks = G / head_chunk;
   const int64_t target = fused ? 256 : 2048;
-  int64_t chunk = (kv_virtual * rows + target - 1) / target;
+  int64_t chunk = (kv_virtual * rows * head_chunks + target - 1) / target;
   chunk = (chunk + 63) / 64 * 64;
   if (chunk < 64) chunk = 64;
   const int64_t min_for_cap = ((kv_virtual + 1023) / 1024 + 63) / 64 * 64;
@@ -81,8 +85,8 @@ SplitPlan plan_split(int64_t rows, int G, int64_t kv_virtual, bool fused) {
   if (fused && chunk > kFusedMaxChunk) chunk = kFusedMaxChunk;
   sp.chunk = chunk;
   sp.n_split = int((kv_virtual + chunk - 1) / chunk);
-  sp.head_chunk = fused ? head_chunk4(G) : head_chunk8(G);
-  sp.head_chunks = G / sp.head_chunk;
+  sp.head_chunk = head_chunk;
+  sp.head_chunks = int(head_chunks);
   return sp;
 }
 

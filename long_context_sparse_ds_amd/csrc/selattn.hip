@@ -205,10 +205,11 @@ struct FusedArgs {
   float tau;                   // threshold rule: keep units scoring >= tau (at most k_units)
   int32_t* counts;             // threshold rule: kept units per row; null: plain top-k
   const int32_t* unit_ids;     // the units are candidates with these unit ids [rows][n_units]; null: identity
+  int32_t xcd_rows;            // grid (8, n_split, rows * head_chunks / 8): row = 8 (z / head_chunks) + x
 };
 
-// Scalar arguments, those of the first loads first: the first 14 dwords are
-// preloaded into SGPRs at wave launch where the firmware supports it.
+// Scalar arguments, those of the first loads first: the first 15 dwords (up to
+// lb_) are preloaded into SGPRs at wave launch where the firmware supports it.
 // RAGGED: sequence b holds seq_lens[b] tokens (clamped to [1, T]) and keeps
 // min(k_units, its unit count) units; index slots past that are set to -1.
 // counts_ != null: the threshold rule with tau_ (index slots past a row's kept
@@ -216,7 +217,8 @@ struct FusedArgs {
 template <typename TE, int NT, int ITEMS, int HC, bool RAGGED>
 __global__ __launch_bounds__(NT) void selattn_kernel(
     const void* q_, const float* scores_, const uint16_t* tile_hist_, int64_t ld_, int32_t G_,
-    int32_t head_chunks_, int32_t n_units_, int32_t tiles_, int32_t k_units_, int32_t lb_, const void* K_,
+    int32_t head_chunks_, int32_t xcd_rows_, int32_t n_units_, int32_t tiles_, int32_t k_units_, int32_t lb_,
+    const void* K_,
     const void* V_, int32_t* indices_, float* part_acc_, float* part_ml_, float* out_, unsigned* tickets_,
     int64_t T_cap_, int32_t T_, int32_t kv_virtual_, int32_t chunk_, int32_t n_split_, float scale_,
     const int32_t* seq_lens_, int32_t Hkv_, float tau_, int32_t* counts_, const int32_t* unit_ids_) {
@@ -249,6 +251,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
   a.tau = tau_;
   a.counts = counts_;
   a.unit_ids = unit_ids_;
+  a.xcd_rows = xcd_rows_;
   using LN = Lanes<TE, NT>;
   constexpr int NW = LN::NW, EPL = LN::EPL, LPT = LN::LPT, GPW = LN::GPW, NG = LN::NG, KU = LN::KU;
   constexpr int BPT1 = 2048 / NT, BPT2 = 1024 / NT;
@@ -256,17 +259,26 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
   static_assert(BPT2 >= 1 && (BPT1 & 1) == 0, "two or more top-digit bins per thread");
   __shared__ FusedSmem<NT, ITEMS, HC> sm;
 
-  // Grid (8, n_split, n_rc / 8) when the (row, head chunk) count n_rc is a
-  // multiple of 8, else (1, n_split, n_rc).  Workgroups are dealt to the 8 XCDs
-  // round-robin by linear id (x fastest), so blockIdx.x is the XCD and every
-  // split of a (row, chunk) lands on the same one: the row's scores and
-  // histograms are fetched into that XCD's L2 once and shared.  No division:
-  // rc = 8 * z + x; queries of the row are heads row * G + [0, G).
+  // Grid (8, n_split, rows * head_chunks / 8) when the row count is a
+  // multiple of 8, else (rows * head_chunks, n_split, 1).  Workgroups are dealt
+  // to the 8 XCDs round-robin by linear id (x fastest), so in the first layout
+  // blockIdx.x is the XCD, row = 8 * (z / head_chunks) + x and the head chunk
+  // is z % head_chunks: every split and every head chunk of a row lands on the
+  // same XCD, whose L2 then serves the row's scores and histograms, and the
+  // K/V rows that the head chunks of a GQA group all read, once.  Queries of
+  // the row are heads row * G + [0, G).
   const uint32_t split = blockIdx.y;
-  const uint32_t rc = blockIdx.z * kXcds + blockIdx.x;   // (n_rc, n_split, 1) layout: z = 0
   const uint32_t hcs = uint32_t(a.head_chunks);
-  const uint32_t row = hcs == 1 ? rc : rc / hcs;
-  const uint32_t hchunk = rc - row * hcs;
+  uint32_t row, hchunk;
+  if (a.xcd_rows) {
+    const uint32_t zr = hcs == 1 ? blockIdx.z : blockIdx.z / hcs;
+    row = zr * kXcds + blockIdx.x;
+    hchunk = blockIdx.z - zr * hcs;
+  } else {
+    row = hcs == 1 ? blockIdx.x : blockIdx.x / hcs;
+    hchunk = blockIdx.x - row * hcs;
+  }
+  const uint32_t rc = row * hcs + hchunk;
   const int64_t bh0 = int64_t(row) * a.G + int64_t(hchunk) * HC;   // first (b, h) of this chunk
   const TE* __restrict__ q = static_cast<const TE*>(a.q);
   const TE* __restrict__ K = static_cast<const TE*>(a.K);
@@ -668,14 +680,14 @@ template <typename TE, int NT, int ITEMS, int HC>
 hipError_t launch_one(const FusedArgs& a, dim3 grid, hipStream_t s) {
   if (a.seq_lens != nullptr)
     hipLaunchKernelGGL((selattn_kernel<TE, NT, ITEMS, HC, true>), grid, dim3(NT), 0, s, a.q, a.scores, a.tile_hist,
-                       a.ld, a.G, a.head_chunks, a.n_units, a.tiles, a.k_units, a.lb, a.K, a.V, a.indices, a.part_acc,
-                       a.part_ml, a.out, a.tickets, a.T_cap, a.T, a.kv_virtual, a.chunk, a.n_split, a.scale,
-                       a.seq_lens, a.Hkv, a.tau, a.counts, a.unit_ids);
+                       a.ld, a.G, a.head_chunks, a.xcd_rows, a.n_units, a.tiles, a.k_units, a.lb, a.K, a.V, a.indices,
+                       a.part_acc, a.part_ml, a.out, a.tickets, a.T_cap, a.T, a.kv_virtual, a.chunk, a.n_split,
+                       a.scale, a.seq_lens, a.Hkv, a.tau, a.counts, a.unit_ids);
   else
     hipLaunchKernelGGL((selattn_kernel<TE, NT, ITEMS, HC, false>), grid, dim3(NT), 0, s, a.q, a.scores, a.tile_hist,
-                       a.ld, a.G, a.head_chunks, a.n_units, a.tiles, a.k_units, a.lb, a.K, a.V, a.indices, a.part_acc,
-                       a.part_ml, a.out, a.tickets, a.T_cap, a.T, a.kv_virtual, a.chunk, a.n_split, a.scale,
-                       nullptr, a.Hkv, a.tau, a.counts, a.unit_ids);
+                       a.ld, a.G, a.head_chunks, a.xcd_rows, a.n_units, a.tiles, a.k_units, a.lb, a.K, a.V, a.indices,
+                       a.part_acc, a.part_ml, a.out, a.tickets, a.T_cap, a.T, a.kv_virtual, a.chunk, a.n_split,
+                       a.scale, nullptr, a.Hkv, a.tau, a.counts, a.unit_ids);
   return hipGetLastError();
 }
 
@@ -734,10 +746,11 @@ hipError_t launch_select_attention(const void* q, const void* K, const void* V, 
   a.chunk = int32_t(pl.sp.chunk);
   a.n_split = pl.sp.n_split;
   a.scale = scale;
-  // XCD-grouped layout when it fits the grid limits, else (n_rc, n_split, 1):
-  // the kernel's rc = 8 z + x covers both.
+  // XCD-grouped layout when the rows come in eights and fit the grid limits,
+  // else (rows * head_chunks, n_split, 1).
   const unsigned n_rc = unsigned(pl.rows * pl.sp.head_chunks);
-  const bool grouped = n_rc % kXcds == 0 && n_rc / kXcds <= 65535u;
+  const bool grouped = pl.rows % kXcds == 0 && n_rc / kXcds <= 65535u;
+  a.xcd_rows = grouped ? 1 : 0;
   const dim3 grid = grouped ? dim3(unsigned(kXcds), unsigned(pl.sp.n_split), n_rc / kXcds)
                             : dim3(n_rc, unsigned(pl.sp.n_split), 1u);
   if (is_bf16) return dispatch<uint16_t>(a, pl.sp.head_chunk, grid, s);
