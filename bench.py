@@ -468,6 +468,9 @@ def main():
     if not w.ragged and w.tau is None and not w.offload and not w.hip and not args.phases_only:
         stages += [("label_append", st_append), ("scores", st_scores), ("select", st_select),
                    ("attention_from_indices", st_attn)]
+    elif w.tau is not None and not args.phases_only:
+        # The separate attention kernel over the step's own kept blocks (slots past a row's count are -1).
+        stages += [("attention_from_indices", st_attn)]
     for name, fn in stages:
         g = capture(n_inst, fn)
         with torch.cuda.stream(stream):

@@ -56,6 +56,40 @@ __device__ __forceinline__ double lane_sum(double v, int lanes) {
   return v;
 }
 
+// The group's summed q for this lane's channels (bf16 and fp32 sums are exact
+// in double), heads added in order; each head's 16 bytes are one load, eight
+// heads' loads issued before any is used.
+template <typename TE>
+__device__ __forceinline__ void group_qbar(const TE* __restrict__ q, int64_t h_first, int G, int sub,
+                                           double (&qbar)[SearchLanes<TE>::EPL]) {
+  using SL = SearchLanes<TE>;
+#pragma unroll
+  for (int e = 0; e < SL::EPL; ++e) qbar[e] = 0.0;
+  for (int h0 = 0; h0 < G; h0 += 8) {
+    uint4 w[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int h = min(h0 + j, G - 1);
+      w[j] = *reinterpret_cast<const uint4*>(q + (h_first + h) * kHeadDim + sub * SL::EPL);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (h0 + j >= G) break;
+      const uint32_t u[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
+      if constexpr (sizeof(TE) == 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          qbar[2 * i] += double(bf16_lo(u[i]));
+          qbar[2 * i + 1] += double(bf16_hi(u[i]));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qbar[i] += double(__uint_as_float(u[i]));
+      }
+    }
+  }
+}
+
 // A token's score from this lane's 16 bytes of its K row: the lane's products
 // accumulated in double, then summed over the lane group (the same order in
 // every kernel here, so every path ranks the same floats).
@@ -110,13 +144,7 @@ __global__ __launch_bounds__(kST) void hip_search_kernel(const TE* __restrict__ 
 
   // The group's summed q for this lane's channels (bf16 and fp32 sums are exact in double).
   double qbar[SL::EPL];
-#pragma unroll
-  for (int e = 0; e < SL::EPL; ++e) qbar[e] = 0.0;
-  for (int h = 0; h < G; ++h) {
-    const TE* qh = q + (int64_t(b) * Hq + int64_t(g) * G + h) * kHeadDim + sub * SL::EPL;
-#pragma unroll
-    for (int e = 0; e < SL::EPL; ++e) qbar[e] += double(elem_to_f32(qh[e]));
-  }
+  group_qbar<TE>(q, int64_t(b) * Hq + int64_t(g) * G, G, sub, qbar);
 
   // The first spans and their first tokens' scores.
   int s = 0, e = 0;
@@ -187,21 +215,38 @@ __global__ __launch_bounds__(kST) void hip_search_kernel(const TE* __restrict__ 
 // token of the right part of every candidate that will be split if it is
 // kept, so the next round's scores are ready when the selection ends and a
 // round costs one K-row read or one sort, whichever is longer, instead of
-// both.  The scores and the tie rule are those of the kernel above.
+// both.  A round's candidates are never stored: lane i of wave 0 derives the
+// two children of kept span i from the previous round's kept list, and the
+// scoring waves derive the same; the kept lists and the scores ahead are
+// double-buffered by round parity, so a round needs one barrier.  (Scoring two
+// levels ahead every other round, three K rows per candidate, measured slower:
+// the reads of one workgroup are not pure latency.)  The scores and the tie
+// rule are those of the kernel above.
 
 constexpr int kWaveSpans = 64;
 constexpr int kWaveCand = 2 * kWaveSpans;
 
+// Round r reads buffers (r - 1) & 1 and writes buffers r & 1.
 struct WaveSearchSmem {
-  int32_t cs[kWaveCand], ce[kWaveCand];   // the round's candidates (start, end); unused slots: 0, 0, key 0
-  uint32_t ckey[kWaveCand];
-  float spec[kWaveCand];                  // score of candidate c's right part's first token
-  int32_t tok[kWaveCand];                 // first round: tokens to score
+  int32_t ks[2][kWaveSpans], ke[2][kWaveSpans];   // kept spans (start, end), ascending
+  uint32_t kkey[2][kWaveSpans];                    // their keys (their first tokens' scores)
+  int32_t kc[2][kWaveSpans];                       // the candidate each was, in the round that kept it
+  float spec[2][kWaveCand];                        // score of candidate c's right part's first token
+  int32_t tok[kWaveCand];                          // first round: tokens to score
   float tsc[kWaveCand];
-  int32_t ks[kWaveSpans], ke[kWaveSpans], kc[kWaveSpans];   // kept spans, ascending, and their candidate ids
-  uint32_t kkey[kWaveSpans];
   uint32_t wsum[kST / 64];
 };
+
+// Child j (0: left, 1: right) of a kept span [s, e) in the next round: its
+// bounds, and whether it exists (a span no longer than `span` goes on whole
+// as its left child).
+__device__ __forceinline__ bool child_of(int s, int e, int j, int span, int& cs, int& ce) {
+  const bool split = e - s > span;
+  const int m = s + (e - s + 1) / 2;
+  cs = j == 0 ? s : m;
+  ce = j == 0 ? (split ? m : e) : e;
+  return j == 0 || split;
+}
 
 // The value held by lane (lane ^ D) of the wavefront, D a power of two < 64.
 template <int D>
@@ -261,35 +306,44 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
 }
 
-// Wave 0: the k best of the round's candidates, in ascending order, to ks/ke/kkey/kc.
-__device__ __forceinline__ void wave_select(WaveSearchSmem& sm, int k, int lane) {
-  const int c0 = 2 * lane, c1 = c0 + 1;
-  const uint32_t o0 = sm.ckey[c0], o1 = sm.ckey[c1];
-  uint32_t x[2] = {o0, o1};
+// Wave 0, round r: the k best children of the previous round's kept spans
+// (buffer rb), in ascending order, to buffer wb.  Lane i holds both children
+// of kept span i (candidates 2 i and 2 i + 1); lanes >= k hold none (key 0).
+__device__ __forceinline__ void wave_select(WaveSearchSmem& sm, int k, int span, int rb, int wb, int lane) {
+  int cs[2] = {0, 0}, ce[2] = {0, 0};
+  uint32_t o[2] = {0u, 0u};
+  if (lane < k) {
+    const int s = sm.ks[rb][lane], e = sm.ke[rb][lane];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (child_of(s, e, j, span, cs[j], ce[j]))
+        o[j] = j == 0 ? sm.kkey[rb][lane] : float_key(sm.spec[rb][sm.kc[rb][lane]]);
+  }
+  uint32_t x[2] = {o[0], o[1]};
   bitonic_sort<kWaveCand>(x, lane);
   // Every span leaves at least one valid candidate, so k valid keys (all
   // nonzero) exist and the k-th largest is one of them.
   const uint32_t thr = __builtin_amdgcn_readlane(x[0], k - 1);
-  const uint32_t n_gt = uint32_t(__popcll(__ballot(o0 > thr))) + uint32_t(__popcll(__ballot(o1 > thr)));
+  const uint32_t n_gt = uint32_t(__popcll(__ballot(o[0] > thr))) + uint32_t(__popcll(__ballot(o[1] > thr)));
   const uint32_t eq_take = uint32_t(k) - n_gt;
-  const bool e0 = o0 == thr, e1 = o1 == thr;
+  const bool e0 = o[0] == thr, e1 = o[1] == thr;
   const uint32_t eb0 = lanes_below(__ballot(e0)) + lanes_below(__ballot(e1));
   const uint32_t eb1 = eb0 + uint32_t(e0);
-  const bool k0 = o0 > thr || (e0 && eb0 < eq_take);
-  const bool k1 = o1 > thr || (e1 && eb1 < eq_take);
+  const bool k0 = o[0] > thr || (e0 && eb0 < eq_take);
+  const bool k1 = o[1] > thr || (e1 && eb1 < eq_take);
   const uint32_t p0 = lanes_below(__ballot(k0)) + lanes_below(__ballot(k1));
   const uint32_t p1 = p0 + uint32_t(k0);
   if (k0) {
-    sm.ks[p0] = sm.cs[c0];
-    sm.ke[p0] = sm.ce[c0];
-    sm.kkey[p0] = o0;
-    sm.kc[p0] = c0;
+    sm.ks[wb][p0] = cs[0];
+    sm.ke[wb][p0] = ce[0];
+    sm.kkey[wb][p0] = o[0];
+    sm.kc[wb][p0] = 2 * lane;
   }
   if (k1) {
-    sm.ks[p1] = sm.cs[c1];
-    sm.ke[p1] = sm.ce[c1];
-    sm.kkey[p1] = o1;
-    sm.kc[p1] = c1;
+    sm.ks[wb][p1] = cs[1];
+    sm.ke[wb][p1] = ce[1];
+    sm.kkey[wb][p1] = o[1];
+    sm.kc[wb][p1] = 2 * lane + 1;
   }
 }
 
@@ -326,29 +380,25 @@ __global__ __launch_bounds__(kST) void hip_search_wave_kernel(const TE* __restri
   const TE* Kr = K + int64_t(row) * T_cap * kHeadDim;
 
   double qbar[SL::EPL];
-#pragma unroll
-  for (int e = 0; e < SL::EPL; ++e) qbar[e] = 0.0;
-  for (int h = 0; h < G; ++h) {
-    const TE* qh = q + (int64_t(b) * Hq + int64_t(g) * G + h) * kHeadDim + sub * SL::EPL;
-#pragma unroll
-    for (int e = 0; e < SL::EPL; ++e) qbar[e] += double(elem_to_f32(qh[e]));
-  }
+  group_qbar<TE>(q, int64_t(b) * Hq + int64_t(g) * G, G, sub, qbar);
 
   const bool mine = tid < k;
   const int s0 = mine ? int(int64_t(tid) * T / k) : 0;
   const int e0 = mine ? int(int64_t(tid + 1) * T / k) : 0;
-  if (rounds == 0) {
-    if (mine) {
-      sm.ks[tid] = s0;
-      sm.ke[tid] = e0;
-    }
-  } else {
-    // First round: the first spans' first tokens and their right parts' first tokens.
+  // The first spans are the kept list of round 0 (buffer 0), each its own
+  // candidate tid; their first tokens' scores and their right parts' first
+  // tokens' scores are taken together.
+  if (mine) {
+    sm.ks[0][tid] = s0;
+    sm.ke[0][tid] = e0;
+    sm.kc[0][tid] = tid;
+  }
+  int fin = 0;   // buffer holding the final spans
+  if (rounds > 0) {
     const bool split0 = mine && e0 - s0 > span;
-    const int m0 = s0 + (e0 - s0 + 1) / 2;
     if (tid < kWaveSpans) {
       sm.tok[2 * tid] = mine ? s0 : -1;
-      sm.tok[2 * tid + 1] = split0 ? m0 : -1;
+      sm.tok[2 * tid + 1] = split0 ? s0 + (e0 - s0 + 1) / 2 : -1;
     }
     __syncthreads();
     {
@@ -365,58 +415,46 @@ __global__ __launch_bounds__(kST) void hip_search_wave_kernel(const TE* __restri
         if (sub == 0 && t[u] >= 0) sm.tsc[gid + NG * u] = sc[u];
     }
     __syncthreads();
-    if (tid < kWaveSpans) {
-      sm.cs[2 * tid] = s0;
-      sm.ce[2 * tid] = split0 ? m0 : e0;
-      sm.ckey[2 * tid] = mine ? float_key(sm.tsc[2 * tid]) : 0u;
-      sm.cs[2 * tid + 1] = split0 ? m0 : 0;
-      sm.ce[2 * tid + 1] = split0 ? e0 : 0;
-      sm.ckey[2 * tid + 1] = split0 ? float_key(sm.tsc[2 * tid + 1]) : 0u;
+    if (mine) {
+      sm.kkey[0][tid] = float_key(sm.tsc[2 * tid]);
+      if (split0) sm.spec[0][tid] = sm.tsc[2 * tid + 1];
     }
     __syncthreads();
 
     for (int r = 1; r <= rounds; ++r) {
+      const int rb = (r - 1) & 1, wb = r & 1;
       if (wave == 0) {
-        wave_select(sm, k, lane);
+        wave_select(sm, k, span, rb, wb, lane);
       } else if (r < rounds) {
-        // Speculative scores: every candidate that would be split next round.
+        // Scores ahead: the right part's first token of every candidate that
+        // would be split next round.
         const int gs = gid - 64 / SL::LPT;
         int32_t t[PERS];
         float sc[PERS];
 #pragma unroll
         for (int u = 0; u < PERS; ++u) {
           const int c = gs + NGS * u;
-          const int cc = c < kWaveCand ? c : 0;
-          const int len = sm.ce[cc] - sm.cs[cc];
-          t[u] = c < kWaveCand && len > span ? sm.cs[cc] + (len + 1) / 2 : -1;
+          t[u] = -1;
+          if (c < 2 * k) {
+            int cs, ce;
+            if (child_of(sm.ks[rb][c >> 1], sm.ke[rb][c >> 1], c & 1, span, cs, ce) && ce - cs > span)
+              t[u] = cs + (ce - cs + 1) / 2;
+          }
         }
         score_tokens<TE, PERS>(t, Kr, sub, qbar, sc);
 #pragma unroll
         for (int u = 0; u < PERS; ++u)
-          if (sub == 0 && t[u] >= 0) sm.spec[gs + NGS * u] = sc[u];
-      }
-      __syncthreads();
-      if (r == rounds) break;
-      if (mine) {
-        // Kept span tid becomes candidates 2 tid (left part, its score) and
-        // 2 tid + 1 (right part, scored ahead).
-        const int s = sm.ks[tid], e = sm.ke[tid];
-        const bool split = e - s > span;
-        const int m = s + (e - s + 1) / 2;
-        sm.cs[2 * tid] = s;
-        sm.ce[2 * tid] = split ? m : e;
-        sm.ckey[2 * tid] = sm.kkey[tid];
-        sm.cs[2 * tid + 1] = split ? m : 0;
-        sm.ce[2 * tid + 1] = split ? e : 0;
-        sm.ckey[2 * tid + 1] = split ? float_key(sm.spec[sm.kc[tid]]) : 0u;
+          if (sub == 0 && t[u] >= 0) sm.spec[wb][gs + NGS * u] = sc[u];
       }
       __syncthreads();
     }
+    fin = rounds & 1;
+  } else {
+    __syncthreads();
   }
-  if (rounds == 0) __syncthreads();
 
   // Spans, then the covered tokens in ascending order, -1 after them.
-  const int s = mine ? sm.ks[tid] : 0, e = mine ? sm.ke[tid] : 0;
+  const int s = mine ? sm.ks[fin][tid] : 0, e = mine ? sm.ke[fin][tid] : 0;
   if (mine) {
     int32_t* so = spans_out + (int64_t(row) * k + tid) * 2;
     so[0] = s;
