@@ -248,20 +248,27 @@ __device__ __forceinline__ bool child_of(int s, int e, int j, int span, int& cs,
   return j == 0 || split;
 }
 
+constexpr int kDppHalfMirror = 0x141;   // row_half_mirror: lane i of each 8-lane half takes lane 7 - i
+constexpr int kDppQuadRev = 0x1B;       // quad_perm [3,2,1,0]
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xF, 0xF, false));
+}
+
 // The value held by lane (lane ^ D) of the wavefront, D a power of two < 64.
 template <int D>
 __device__ __forceinline__ uint32_t lane_xor(uint32_t v, int lane) {
   if constexpr (D == 1) {
-    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+    return dpp_u32<kDppXor1>(v);
   } else if constexpr (D == 2) {
-    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+    return dpp_u32<kDppXor2>(v);
   } else if constexpr (D == 4) {
-    // Mirror within each half row (lane i takes i ^ 7), then quad_perm
-    // [3,2,1,0] (i takes i ^ 3): i takes i ^ 4.
-    const int m = __builtin_amdgcn_update_dpp(0, int(v), 0x141, 0xF, 0xF, false);
-    return uint32_t(__builtin_amdgcn_update_dpp(0, m, 0x1B, 0xF, 0xF, false));
+    // Mirror within each half row (lane i takes i ^ 7), then reverse each
+    // quad (i takes i ^ 3): i takes i ^ 4.
+    return dpp_u32<kDppQuadRev>(dpp_u32<kDppHalfMirror>(v));
   } else if constexpr (D == 8) {
-    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x128, 0xF, 0xF, false));  // rotate each row by 8
+    return dpp_u32<kDppRor8>(v);   // rotating a 16-lane row by 8 pairs i with i ^ 8
   } else if constexpr (D == 16) {
     // Rows 2p and 2p + 1 swap: the first result holds the even row's values
     // in both rows, the second the odd row's.

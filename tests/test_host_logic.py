@@ -1,6 +1,7 @@
 """Host-side logic on the CPU: the benchmark's byte accounting for every kind of
 workload, the span search's round count (against the oracle's own stopping rule),
-the seeded generators, and the workspace sizes of the library's plans.  No GPU."""
+the seeded generators, the workspace sizes of the library's plans, and a lane-by-lane
+model of the span search's one-wavefront selection network.  No GPU."""
 import math
 import os
 import sys
@@ -106,3 +107,85 @@ def test_workspace_grows_with_the_two_stage_candidates():
     assert small >= cand
     stream = L.ds_decode_workspace_bytes(1, 4, 2, 128, 70000, 1, 20000)   # 3 * 20000 > 32768
     assert stream > 0
+
+
+# ---------------------------------------------------------------------------
+# The span search's one-wavefront selection (k <= 64 spans), modelled lane by
+# lane: 64 lanes hold two keys each (element t * 64 + lane is item t), a bitonic
+# network sorts them in descending order (partner of element j at distance D is
+# j ^ D: in the lane at D = 64, across lanes below), the k-th largest key is
+# read from lane k - 1, and ballots (counts of lanes below) give the ties to
+# keep and every kept candidate's ascending position.  The model must keep the
+# k largest keys with ties to the lower candidate id, candidate c = 2 lane + item.
+
+def _wave_sort_desc(x):
+    size = 2
+    while size <= 128:
+        dist = size // 2
+        while dist > 0:
+            if dist == 64:
+                for ln in range(64):
+                    a, b = x[0][ln], x[1][ln]
+                    x[0][ln], x[1][ln] = max(a, b), min(a, b)
+            else:
+                new = [[0] * 64 for _ in range(2)]
+                for t in range(2):
+                    for ln in range(64):
+                        j = t * 64 + ln
+                        p = x[t][ln ^ dist]
+                        take_max = ((j & size) == 0) == ((j & dist) == 0)
+                        new[t][ln] = max(x[t][ln], p) if take_max else min(x[t][ln], p)
+                x = new
+            dist //= 2
+        size *= 2
+    return x
+
+
+def _wave_select(keys, k):
+    o = [[keys[2 * ln + t] for ln in range(64)] for t in range(2)]
+    x = _wave_sort_desc([row[:] for row in o])
+    flat = [x[j // 64][j % 64] for j in range(128)]
+    assert flat == sorted(flat, reverse=True)
+    thr = x[0][k - 1]
+
+    def below(mask, ln):
+        return bin(mask & ((1 << ln) - 1)).count("1")
+
+    def ballot(pred):
+        return sum(1 << ln for ln in range(64) if pred(ln))
+
+    n_gt = bin(ballot(lambda ln: o[0][ln] > thr)).count("1") + bin(ballot(lambda ln: o[1][ln] > thr)).count("1")
+    eq_take = k - n_gt
+    e = [ballot(lambda ln, t=t: o[t][ln] == thr) for t in range(2)]
+    kept = [[False] * 64 for _ in range(2)]
+    for ln in range(64):
+        eb0 = below(e[0], ln) + below(e[1], ln)
+        eb1 = eb0 + (o[0][ln] == thr)
+        kept[0][ln] = o[0][ln] > thr or (o[0][ln] == thr and eb0 < eq_take)
+        kept[1][ln] = o[1][ln] > thr or (o[1][ln] == thr and eb1 < eq_take)
+    p = [ballot(lambda ln, t=t: kept[t][ln]) for t in range(2)]
+    out = [None] * k
+    for ln in range(64):
+        p0 = below(p[0], ln) + below(p[1], ln)
+        if kept[0][ln]:
+            out[p0] = 2 * ln
+        if kept[1][ln]:
+            out[p0 + kept[0][ln]] = 2 * ln + 1
+    return out
+
+
+@pytest.mark.parametrize("mode", ["distinct", "few_values", "all_equal"])
+def test_one_wavefront_selection_model_keeps_the_top_k_ties_to_the_lower_id(mode):
+    rng = np.random.default_rng({"distinct": 1, "few_values": 2, "all_equal": 3}[mode])
+    for _ in range(300):
+        k = int(rng.integers(1, 65))
+        # every span has its left child (even id); some have a right child
+        valid = [c % 2 == 0 and c < 2 * k or (c % 2 == 1 and c < 2 * k and rng.random() < 0.7) for c in range(128)]
+        if mode == "distinct":
+            keys = [int(rng.integers(0x00800000, 0xFF7FFFFF)) if v else 0 for v in valid]
+        elif mode == "few_values":
+            keys = [0x40000000 + int(rng.integers(0, 6)) if v else 0 for v in valid]
+        else:
+            keys = [0x3F800000 if v else 0 for v in valid]
+        want = sorted(sorted((c for c in range(128) if valid[c]), key=lambda c: (-keys[c], c))[:k])
+        assert _wave_select(keys, k) == want
