@@ -251,11 +251,6 @@ __device__ __forceinline__ bool child_of(int s, int e, int j, int span, int& cs,
 constexpr int kDppHalfMirror = 0x141;   // row_half_mirror: lane i of each 8-lane half takes lane 7 - i
 constexpr int kDppQuadRev = 0x1B;       // quad_perm [3,2,1,0]
 
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xF, 0xF, false));
-}
-
 // The value held by lane (lane ^ D) of the wavefront, D a power of two < 64.
 template <int D>
 __device__ __forceinline__ uint32_t lane_xor(uint32_t v, int lane) {

@@ -177,13 +177,31 @@ __global__ __launch_bounds__(kNT) void partition_topk_kernel(const float* __rest
     reinterpret_cast<uint32_t*>(cand_hist + (row * parts + p) * kHistBins)[kHistBins / 2 - 1 - threadIdx.x] =
         (c_hi << 16) | c_lo;
   }
+  // The kept units go out in windows of the candidate buffer's size: the
+  // emission places each window's keys in that buffer (free once the
+  // threshold is known) and their partition-local ids beside them, at their
+  // final positions, and the window is then written with coalesced stores.
+  // Scattered 4-byte stores straight from the emission cost more than the
+  // selection itself.
+  constexpr int kWin = decltype(sm)::kCap;
+  __shared__ uint16_t kept_id[kWin];
+  static_assert(kPartUnits <= 65536, "partition-local ids fit 16 bits");
   const int64_t first = int64_t(threadIdx.x) * ITEMS;
-  for_each_kept<kNT, ITEMS>(key, valid, first, tau, mask, kk, sm, [&](int64_t unit, int64_t pos) {
-    if (pos < k_p) {
-      cs[pos] = key_to_float(key[unit - first]);
-      ci[pos] = int32_t(base + unit);
+  for (int64_t w0 = 0; w0 < k_p; w0 += kWin) {
+    const int64_t w1 = min(w0 + int64_t(kWin), k_p);
+    __syncthreads();   // the previous window (or the threshold search) is done with the buffers
+    for_each_kept<kNT, ITEMS>(key, valid, first, tau, mask, kk, sm, [&](int64_t unit, int64_t pos) {
+      if (pos >= w0 && pos < w1) {
+        sm.cand[pos - w0] = key[unit - first];
+        kept_id[pos - w0] = uint16_t(unit);
+      }
+    });
+    __syncthreads();
+    for (int64_t i = threadIdx.x; i < w1 - w0; i += kNT) {
+      cs[w0 + i] = key_to_float(sm.cand[i]);
+      ci[w0 + i] = int32_t(base + kept_id[i]);
     }
-  });
+  }
   for (int64_t i = k_p + threadIdx.x; i < k; i += kNT) {
     cs[i] = -INFINITY;
     ci[i] = -1;
