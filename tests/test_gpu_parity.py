@@ -71,6 +71,12 @@ SMALL = [
     Workload("r_eq_d", "bf16", B=1, Hq=2, Hkv=2, d=128, T=2000, r=128, block=1, k_units=125, seed_base=19000),
     Workload("select_multi_tile", "bf16", B=1, Hq=1, Hkv=1, d=128, T=70001, r=16, block=1, k_units=4000,
              seed_base=19500),
+    # Groups of 8 and 16 query heads: several 4-head chunks per row, each a workgroup of its own (fp32, a block
+    # variant, and G = 16 on 8 rows, which takes the XCD-grouped grid with four head chunks per row).
+    Workload("f32_gqa8", "f32", B=1, Hq=8, Hkv=1, d=128, T=1200, r=16, block=1, k_units=100, seed_base=19600,
+             fixed_outliers=True),
+    Workload("gqa8_block16", "bf16", B=1, Hq=16, Hkv=2, d=128, T=4000, r=16, block=16, k_units=25, seed_base=19700),
+    Workload("gqa16_rows8", "bf16", B=4, Hq=32, Hkv=2, d=128, T=3000, r=8, block=1, k_units=150, seed_base=19800),
 ]
 
 
@@ -512,6 +518,8 @@ RAGGED_CASES = [
               seed_base=27200), [64 * 40 + 5, 64 * 3 + 1, 10], 2),
     (Workload("ragged_f32", "f32", B=2, Hq=1, Hkv=1, d=128, T=1500, r=16, block=1, k_units=77, seed_base=27300,
               fixed_outliers=True), [1500, 64], 1),
+    (Workload("ragged_gqa8", "bf16", B=4, Hq=16, Hkv=2, d=128, T=6000, r=8, block=1, k_units=400, seed_base=27400),
+     [6000, 333, 4097, 1], 2),
 ]
 
 
