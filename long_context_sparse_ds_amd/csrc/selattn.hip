@@ -341,10 +341,16 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
       for (int i = 0; i < BPT1 / 2; ++i) hw[i] += t < tiles ? w[t][i] : 0u;
   }
 
-  // The scores go to LDS as well, for the candidate passes' indexed reads.
+  // The scores go to LDS as well, for the candidate passes' indexed reads of
+  // a thread's own units (a register array cannot be indexed at run time).
+  // Thread t's units 4v .. 4v + 3 sit in 16-byte slot v * NT + t, so a
+  // wavefront's stores cover consecutive slots: written at the thread's own
+  // 64-byte stride instead, all 64 lanes of a store hit the same few banks
+  // and the stores took ~6K clocks per workgroup.
+  const auto sc_at = [&](int j) -> float { return sm.u.sc[((j >> 2) * NT + tid) * 4 + (j & 3)]; };
 #pragma unroll
   for (int v = 0; v < ITEMS / 4; ++v)
-    *reinterpret_cast<float4*>(&sm.u.sc[first + 4 * v]) =
+    *reinterpret_cast<float4*>(&sm.u.sc[(v * NT + tid) * 4]) =
         make_float4(s[4 * v], s[4 * v + 1], s[4 * v + 2], s[4 * v + 3]);
   uint32_t c1[BPT1];
   if (a.tile_hist != nullptr) {
@@ -423,7 +429,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
     bool settled = kk == cnt0;   // every key of digit d0 is needed
     if (!settled) {
       for (uint32_t m = cm; m != 0u; m &= m - 1u) {
-        const uint32_t key = float_key(sm.u.sc[first + __builtin_ctz(m)]);
+        const uint32_t key = float_key(sc_at(__builtin_ctz(m)));
         atomicAdd(&sm.hist1[(key >> 10) & 2047u], 1u);
       }
       __syncthreads();
@@ -436,7 +442,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
       settled = kk == sm.pick[2];
       if (!settled) {
         for (uint32_t m = cm; m != 0u; m &= m - 1u) {
-          const uint32_t key = float_key(sm.u.sc[first + __builtin_ctz(m)]);
+          const uint32_t key = float_key(sc_at(__builtin_ctz(m)));
           if ((key & 0xFFFFFC00u) == thr) atomicAdd(&sm.hist2[key & 1023u], 1u);
         }
         __syncthreads();
@@ -460,7 +466,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
     } else {
       for (uint32_t m = cm; m != 0u; m &= m - 1u) {
         const int j = __builtin_ctz(m);
-        const uint32_t key = float_key(sm.u.sc[first + j]);
+        const uint32_t key = float_key(sc_at(j));
         if (key > thr || (all_eq && key == thr)) keepm |= 1u << j;
         else if (key == thr) eqm |= 1u << j;
       }
