@@ -23,6 +23,8 @@
 // per-step label-row append of the newest tokens, fused here so a decode step
 // is a single pass over the label cache); they are scored from the values just
 // gathered, summed in the same channel order.
+#include <type_traits>
+
 #include "ds_common.h"
 
 namespace ds {
@@ -86,8 +88,9 @@ __device__ __forceinline__ void label_values(const uint4 (&raw)[NV], double* lv,
 
 // R > 0: label width known at compile time and R * sizeof(TE) a multiple of 16 bytes.
 // R == 0: any width, element loads.
-// Label-row append of token t: gather its r channels from K into the label
-// cache and return its score.
+// Label-row append of token t: gather its r channels from its K row (a
+// staged copy in LDS, or global memory) into the label cache and return its
+// score.
 template <typename TE>
 __device__ __forceinline__ float append_row(const TE* __restrict__ Krow, TE* __restrict__ Lrow, const int* sch,
                                             const double* qs, int r) {
@@ -165,6 +168,22 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
   const int tx = int(threadIdx.x);
   const int jj = POS ? (tx < kQB * r ? tx % r : 0) : (tx < r ? tx : 0);
   const int cj = ch[g * r + jj];
+  // Label-row append: the K rows of this tile's first appended tokens, one
+  // whole row per wavefront, requested ahead of the label rows (their
+  // rebuild would otherwise wait on a second round trip after the scan).
+  // POS rebuilds its rows inside the scoring loop, from global memory: moving
+  // it out of the loop made the double-precision head loop measurably slower.
+  using RowWord = std::conditional_t<sizeof(TE) == 2, uint32_t, uint2>;   // a row is 64 of these
+  static_assert(kHeadDim * sizeof(TE) == 64 * sizeof(RowWord), "one row per wavefront, one word per lane");
+  constexpr int kPreRows = kThreads / 64;
+  __shared__ RowWord krow[kPreRows][64];
+  const int tile0 = int(blockIdx.x) * kTile;
+  const int a_lo = max(ta, tile0), a_hi = min(Ti, tile0 + kTile);   // appended tokens in this tile
+  const int wv = int(threadIdx.x) >> 6;
+  const bool pre = !POS && a_lo + wv < a_hi;   // uniform over the wavefront
+  RowWord kw{};
+  if (pre)
+    kw = reinterpret_cast<const RowWord*>(Kc + (int64_t(row) * T_cap + a_lo + wv) * kHeadDim)[threadIdx.x & 63];
   uint4 raw[kTPT][NV];
   if constexpr (R > 0) {
 #pragma unroll
@@ -177,6 +196,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
   }
   if (tile_hist != nullptr)
     for (int i = threadIdx.x; i < kHistBins; i += kThreads) h[i] = 0u;
+  if (pre) krow[wv][threadIdx.x & 63] = kw;
   if (threadIdx.x < kHeadDim) {
     if constexpr (POS) {
 #pragma unroll
@@ -197,6 +217,12 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
   if (threadIdx.x < r) sch[threadIdx.x] = cj;
   __syncthreads();
 
+  // An appended token's label row and score, from the staged K row when
+  // there is one (separate calls keep the LDS reads LDS reads).
+  const auto append = [&](int t, TE* Lrow) -> float {
+    if (t - a_lo < kPreRows) return append_row(reinterpret_cast<const TE*>(krow[t - a_lo]), Lrow, sch, qs, r);
+    return append_row(Kc + (int64_t(row) * T_cap + t) * kHeadDim, Lrow, sch, qs, r);
+  };
   float u[kTPT];
   if constexpr (POS && R > 0) {
     // Head-outer: one head's q values (LDS broadcast reads) against one token's
@@ -255,9 +281,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
 #pragma unroll
     for (int i = 0; i < kTPT; ++i) {
       const int t = t0 + i * kThreads;
-      if (t >= Ti) u[i] = -INFINITY;
-      else if (t >= ta) u[i] = append_row(Kc + (int64_t(row) * T_cap + t) * kHeadDim, L + int64_t(t) * R, sch, qs, R);
-      else u[i] = float(dot_label<NV>(raw[i], qr, TE()));
+      u[i] = t >= Ti ? -INFINITY : float(dot_label<NV>(raw[i], qr, TE()));
     }
   } else {
 #pragma unroll
@@ -266,9 +290,17 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
       double a = 0.0;
       if (t < Ti && t < ta)
         for (int j = 0; j < r; ++j) a = fma(qs[j], double(elem_to_f32(L[int64_t(t) * r + j])), a);
-      if (t >= Ti) u[i] = -INFINITY;
-      else if (t >= ta) u[i] = append_row(Kc + (int64_t(row) * T_cap + t) * kHeadDim, L + int64_t(t) * r, sch, qs, r);
-      else u[i] = float(a);
+      u[i] = t >= Ti ? -INFINITY : float(a);
+    }
+  }
+  // The appended tokens (the newest rows, in at most two tiles): their label
+  // rows are rebuilt and their scores replaced, apart from the loop above so
+  // that the common path carries none of this code.
+  if (!POS && a_lo < a_hi) {
+#pragma unroll
+    for (int i = 0; i < kTPT; ++i) {
+      const int t = t0 + i * kThreads;
+      if (t >= a_lo && t < a_hi) u[i] = append(t, L + int64_t(t) * r);
     }
   }
 

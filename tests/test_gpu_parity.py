@@ -303,11 +303,18 @@ def test_workspace_reuse_and_graph_replay_match_eager():
         assert torch.equal(o2.view(torch.int32), ref_o.view(torch.int32))
 
 
-@pytest.mark.parametrize("w", [SMALL[0], SMALL[4], SMALL[6]], ids=lambda w: w.name)
+APPEND_CASES = [SMALL[0], SMALL[4], SMALL[6],
+                # the 37 rebuilt rows straddle two 2048-token score tiles (17 + 20)
+                Workload("append_two_tiles", "bf16", B=1, Hq=4, Hkv=2, d=128, T=2068, r=16, block=1, k_units=150,
+                         seed_base=19900)]
+
+
+@pytest.mark.parametrize("w", APPEND_CASES, ids=lambda w: w.name)
 def test_decode_fused_label_append(w):
     """Label rows [t_append, T) are rebuilt from K inside the decode call: start from a
     cache whose newest rows hold garbage and check they come back bit-exact and the
-    step matches the oracle."""
+    step matches the oracle.  37 rows: more than the score kernel stages per tile, so
+    both the staged and the direct K reads are taken."""
     q, K, V = dsgen.gen_cache(w)
     qc, kc = dsgen.gen_calib(w)
     ch = L.ds_calibrate_channels(qc, kc, w.r)

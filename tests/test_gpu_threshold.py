@@ -107,6 +107,30 @@ def test_decode_threshold_all_units(w, quant):
     _say(f"{w.name} kept counts {counts}")
 
 
+@pytest.mark.parametrize("i", [0, 3, 5], ids=lambda i: THRESH_CASES[i][0].name)
+def test_decode_threshold_rebuilds_label_rows(i):
+    """The threshold step with the newest 37 label rows rebuilt inside the call, from a
+    cache whose rows there hold garbage: the rows come back bit-exact, and indices,
+    counts and outputs equal those of the same step on the intact cache (the rebuilt
+    rows are scored in the same channel order)."""
+    w, quant = THRESH_CASES[i]
+    q, K, V, ch, qd, Kd, Vd, chd, label = _setup(w)
+    tau = _tau_of(w, q, K, V, ch, quant)
+    ref = L.ds_decode_sparse_attn_threshold(qd, Kd, Vd, label, chd, w.T, w.k_units, tau, w.block)
+    torch.cuda.synchronize()
+    ref = [t.cpu() for t in ref]
+    t_app = w.T - 37
+    intact = label.clone()
+    raw = label.view(torch.int16) if w.dtype == "bf16" else label.view(torch.int32)
+    raw[:, :, t_app:w.T].fill_(0x3F00)   # garbage in the rows to be rebuilt
+    _say(f"{w.name} tau={tau:.6g} t_append={t_app}")
+    got = L.ds_decode_sparse_attn_threshold(qd, Kd, Vd, label, chd, w.T, w.k_units, tau, w.block, t_append=t_app)
+    torch.cuda.synchronize()
+    assert torch.equal(label.view(torch.uint8), intact.view(torch.uint8))
+    for a, b in zip(got, ref):
+        assert torch.equal(a.cpu().view(torch.int32), b.view(torch.int32))
+
+
 def test_decode_threshold_regimes_on_one_batch():
     """One batch whose rows fall in all three regimes at one tau: a row that keeps
     nothing, rows compacted below the cap, and a row at the cap."""
