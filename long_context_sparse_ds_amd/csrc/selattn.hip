@@ -363,12 +363,14 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
       c1[BPT1 - 2 - 2 * i] = hw[i] >> 16;
     }
   } else {
+    // The units of this sequence only (a short one's padding would pile onto one bin).
+    const int nu_hist = RAGGED ? ((T_row + block - 1) >> lb) : n_units;
 #pragma unroll
     for (int i = 0; i < BPT1; ++i) sm.hist1[i * NT + tid] = 0u;
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j)
-      if (first + j < n_units) atomicAdd(&sm.hist1[float_key(s[j]) >> 21], 1u);
+      if (first + j < nu_hist) atomicAdd(&sm.hist1[float_key(s[j]) >> 21], 1u);
     __syncthreads();
     read_bins<NT, 2048>(sm.hist1, c1);
     // Each bin is read by exactly one thread, which clears it for pass 1.

@@ -77,6 +77,9 @@ SMALL = [
              fixed_outliers=True),
     Workload("gqa8_block16", "bf16", B=1, Hq=16, Hkv=2, d=128, T=4000, r=16, block=16, k_units=25, seed_base=19700),
     Workload("gqa16_rows8", "bf16", B=4, Hq=32, Hkv=2, d=128, T=3000, r=8, block=1, k_units=150, seed_base=19800),
+    # 256 rows: one workgroup per row, which builds the row's top-digit histogram itself
+    Workload("rows256_one_split", "bf16", B=32, Hq=8, Hkv=8, d=128, T=2500, r=16, block=1, k_units=100,
+             seed_base=19950),
 ]
 
 
