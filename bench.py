@@ -24,7 +24,10 @@ synchronisation and HIP events on the replay stream.
 
 Per-kernel durations come from the stage entry points (same kernels), each
 replayed from its own graph over the rotating instances; the dominant one
-gives the roofline object.  The CPU baseline times the float64 oracle on a
+gives the roofline object.  A shape that the one-call step runs in one pass
+(ds_decode_is_one_pass: one kernel scores, selects and attends) has that
+kernel as its roofline, timed the same way; its phase entry points still run
+the two-kernel form and are reported beside it.  The CPU baseline times the float64 oracle on a
 bounded sample of the same workload with a process pool.
 
 Prints one JSON line.
@@ -58,7 +61,7 @@ def log(msg):
 
 
 # The sources that build the decode step's two kernels (score_kernel, selattn_kernel) and plan their launches.
-DECODE_STEP_SOURCES = ("ds_api.hip", "ds_common.h", "score.hip", "select_dev.h", "selattn.hip")
+DECODE_STEP_SOURCES = ("ds_api.hip", "ds_common.h", "label_dot.h", "score.hip", "select_dev.h", "selattn.hip")
 
 
 def kernel_sources_digest() -> str:
@@ -463,8 +466,13 @@ def main():
 
     kernel_us = {}
     # The decode step's two phases (its own kernels), then isolated stages for reference
-    # (uniform-length top-k stages, so not for a ragged batch or the threshold rule).
+    # (uniform-length top-k stages, so not for a ragged batch or the threshold rule).  A
+    # one-pass step is one kernel: the step itself is timed as its own stage.
+    one_pass = (not w.hip and w.tau is None and
+                L.ds_decode_is_one_pass(w.B, w.Hq, w.Hkv, w.d, w.T, w.block, w.k_units, w.r, w.dtype))
     stages = [("decode_score", st_decode_score), ("decode_select_attend", st_decode_select_attend)]
+    if one_pass:
+        stages = [("decode_step_one_pass", step)] + stages
     if not w.ragged and w.tau is None and not w.offload and not w.hip and not args.phases_only:
         stages += [("label_append", st_append), ("scores", st_scores), ("select", st_select),
                    ("attention_from_indices", st_attn)]
@@ -500,9 +508,11 @@ def main():
             "scores": ab["label_scan"] + ab["q"],
             "select": ab["indices"],
             "attention_from_indices": ab["kv_gather"] + ab["q"] + ab["indices"] + ab["out"],
+            "decode_step_one_pass": ab["step"],
         }
-    # the decode step's phases: the score pass and selection + attention
-    dominant = max(("decode_score", "decode_select_attend"), key=lambda k: kernel_us[k])
+    # the decode step's kernels: the one-pass kernel, or the score pass and selection + attention
+    dominant = ("decode_step_one_pass" if one_pass else
+                max(("decode_score", "decode_select_attend"), key=lambda k: kernel_us[k]))
     dom_gbs = stage_bytes[dominant] / (kernel_us[dominant] * 1e-6) / 1e9
 
     gbs = ab["step"] / (us_step * 1e-6) / 1e9
@@ -527,6 +537,7 @@ def main():
                    **({"rule": "hierarchical span search", "k_spans": w.k_units, "span": w.block,
                        "rounds": hip_rounds(w)} if w.hip else {})},
         "us_per_step": round(us_step, 3),
+        "one_pass": bool(one_pass),
         "us_per_step_eager": round(us_step_eager, 3),
         "algorithmic_bytes_per_step": ab["step"],
         "step_roofline_frac": round(gbs / HBM_PEAK_GBS, 4),

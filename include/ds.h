@@ -105,6 +105,21 @@ size_t ds_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, 
                                  int64_t k_units);
 
 /*
+ * Whether ds_decode_sparse_attn (and its ragged and offload forms) runs this
+ * shape in one pass: 1 when it launches a single kernel that scores each row
+ * from the label cache itself, then selects and attends, with no score buffer
+ * in memory; 0 when it launches the score kernel and then the fused
+ * select + attention kernel (the two phases below); -1 (with ds_last_error set)
+ * for an invalid shape.  One pass is taken for token-level rows (block = 1)
+ * that one fused workgroup handles alone (a single split of the kept set and
+ * at most 4 query heads per group, which holds once B * Hkv reaches about 256)
+ * with label rows of 16 or 32 bytes (r = 8 or 16 for bf16, 4 or 8 for fp32).
+ * Both forms give the same indices and outputs bit for bit.  Host only.
+ */
+int32_t ds_decode_is_one_pass(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t T, int32_t block,
+                              int64_t k_units, int32_t r, ds_dtype dt);
+
+/*
  * One Double Sparsity decode step for every (sequence b, KV head g) (GPU, async):
  *   0. label-row append: rows [t_append, T) of the label cache are rebuilt
  *      from K (as ds_build_label_cache would) before they are scored, so the
@@ -199,7 +214,9 @@ ds_status ds_decode_sparse_attn_offload(const void* q, const void* K_host, const
  * steps 2 and 3 from them.  Issued back to back on one stream with the same
  * shape and workspace, they launch exactly the kernels of
  * ds_decode_sparse_attn and give the same results; the split lets a caller
- * time or schedule the phases.  Arguments as for ds_decode_sparse_attn; K and
+ * time or schedule the phases.  For a shape that ds_decode_sparse_attn runs
+ * in one pass (ds_decode_is_one_pass), the phases still run the two kernels,
+ * with the same results bit for bit.  Arguments as for ds_decode_sparse_attn; K and
  * V may also be pinned host memory the device can access, which is how the
  * phases of ds_decode_sparse_attn_offload are run on their own.
  */

@@ -21,7 +21,7 @@ ds_decode_workspace_bytes.
 from ._binding import (DS_OK, DS_ERR_INVALID_ARGUMENT, DS_ERR_UNSUPPORTED, DS_ERR_WORKSPACE_TOO_SMALL, DS_ERR_HIP,
                        DS_DTYPE_F32, DS_DTYPE_BF16, DsError, LIB_PATH, lib, header_symbols, ds_last_error,
                        ds_version, ds_calibrate_channels, ds_build_label_cache, ds_decode_workspace_bytes,
-                       alloc_workspace, ds_decode_sparse_attn, ds_decode_sparse_attn_ragged, ds_decode_score,
+                       ds_decode_is_one_pass, alloc_workspace, ds_decode_sparse_attn, ds_decode_sparse_attn_ragged, ds_decode_score,
                        ds_decode_select_attend, ds_decode_score_ragged, ds_decode_select_attend_ragged,
                        ds_decode_sparse_attn_threshold, ds_decode_score_threshold, ds_decode_select_attend_threshold,
                        ds_label_scores_positive, ds_decode_sparse_attn_offload, ds_decode_hip_attn, ds_hip_search,
@@ -31,7 +31,7 @@ from ._binding import (DS_OK, DS_ERR_INVALID_ARGUMENT, DS_ERR_UNSUPPORTED, DS_ER
 __all__ = ["DS_OK", "DS_ERR_INVALID_ARGUMENT", "DS_ERR_UNSUPPORTED", "DS_ERR_WORKSPACE_TOO_SMALL", "DS_ERR_HIP",
            "DS_DTYPE_F32", "DS_DTYPE_BF16", "DsError", "LIB_PATH", "lib", "header_symbols", "ds_last_error",
            "ds_version", "ds_calibrate_channels", "ds_build_label_cache", "ds_decode_workspace_bytes",
-           "alloc_workspace", "ds_decode_sparse_attn", "ds_decode_sparse_attn_ragged", "ds_decode_score",
+           "ds_decode_is_one_pass", "alloc_workspace", "ds_decode_sparse_attn", "ds_decode_sparse_attn_ragged", "ds_decode_score",
            "ds_decode_select_attend", "ds_decode_score_ragged", "ds_decode_select_attend_ragged",
            "ds_decode_sparse_attn_threshold", "ds_decode_score_threshold", "ds_decode_select_attend_threshold",
            "ds_label_scores_positive", "ds_decode_sparse_attn_offload", "ds_decode_hip_attn", "ds_hip_search",

@@ -35,6 +35,7 @@ _SIGNATURES = {
     "ds_build_label_cache": (_c_i32, [_c_vp, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_vp, _c_i32, _c_i64, _c_i64,
                                       _c_vp, _c_vp]),
     "ds_decode_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_i64]),
+    "ds_decode_is_one_pass": (_c_i32, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_i64, _c_i32, _c_i32]),
     "ds_decode_sparse_attn": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                        _c_i32, _c_i64, _c_i64, _c_i64, _c_i32, _c_i64, _c_f32, _c_vp, _c_vp, _c_vp,
                                        _c_size, _c_vp]),
@@ -202,6 +203,16 @@ def ds_decode_workspace_bytes(B: int, Hq: int, Hkv: int, d: int, T: int, block: 
     if n == 0:
         raise DsError(DS_ERR_INVALID_ARGUMENT, ds_last_error())
     return n
+
+
+def ds_decode_is_one_pass(B: int, Hq: int, Hkv: int, d: int, T: int, block: int, k_units: int, r: int,
+                          dtype: str = "bf16") -> bool:
+    """Whether the one-call decode step runs this shape as a single kernel (host only)."""
+    v = lib().ds_decode_is_one_pass(B, Hq, Hkv, d, T, block, k_units, r,
+                                    DS_DTYPE_BF16 if dtype == "bf16" else DS_DTYPE_F32)
+    if v < 0:
+        raise DsError(DS_ERR_INVALID_ARGUMENT, ds_last_error())
+    return bool(v)
 
 
 def alloc_workspace(B, Hq, Hkv, d, T, block, k_units, device="cuda"):

@@ -373,6 +373,43 @@ static ds_status decode_select_stage(const void* q, const void* K, const void* V
                            scale, pl, out, indices, ws, s, seq_lens, tau, counts);
 }
 
+// The one-pass form of the decode step, one kernel instead of two: token-level
+// rows that one fused workgroup handles alone (one split, one head chunk),
+// with label rows of 16 or 32 bytes.  The kernel scores each row from the label
+// cache itself, so the scores never go through memory.
+static bool one_pass_ok(const ds::DecodePlan& pl, int32_t block, int32_t r, ds_dtype dt) {
+  const int row_bytes = r * (dt == DS_DTYPE_BF16 ? 2 : 4);
+  return pl.fused && block == 1 && pl.sp.n_split == 1 && pl.sp.head_chunks == 1 && !pl.tile_hist &&
+         (row_bytes == 16 || row_bytes == 32);
+}
+
+static ds_status decode_one_pass(const void* q, const void* K, const void* V, void* label,
+                                 const int32_t* channels_dev, int32_t r, ds_dtype dt, int32_t B, int32_t Hq,
+                                 int32_t Hkv, int64_t T_cap, int64_t T, int64_t t_append, int64_t k_units,
+                                 float scale, const ds::DecodePlan& pl, float* out, int32_t* indices, char* ws,
+                                 hipStream_t s, const int32_t* seq_lens = nullptr, int32_t n_append = 0) {
+  (void)B;
+  const ds::OnePass one{label, channels_dev, r, t_append, n_append};
+  return hip_status(
+      ds::launch_select_attention(q, K, V, dt == DS_DTYPE_BF16, nullptr, pl.score_ld, nullptr, Hq, Hkv, T_cap, T, 1,
+                                  k_units, scale, pl, indices, reinterpret_cast<float*>(ws + pl.off_acc),
+                                  reinterpret_cast<float*>(ws + pl.off_ml), out,
+                                  reinterpret_cast<unsigned*>(ws + pl.off_tickets), seq_lens, 0.f, nullptr, nullptr, s,
+                                  &one),
+      "one-pass decode launch");
+}
+
+int32_t ds_decode_is_one_pass(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t T, int32_t block,
+                              int64_t k_units, int32_t r, ds_dtype dt) {
+  g_err.clear();
+  if (check_dtype(dt) != DS_OK || check_decode_shape(B, Hq, Hkv, d, T, T, block, k_units) != DS_OK) return -1;
+  if (r < 1 || r > d) {
+    fail(DS_ERR_INVALID_ARGUMENT, "need 1 <= r <= d (r = %d)", r);
+    return -1;
+  }
+  return one_pass_ok(ds::plan_decode(B, Hq, Hkv, T, block, k_units), block, r, dt) ? 1 : 0;
+}
+
 ds_status ds_decode_sparse_attn(const void* q, const void* K, const void* V, void* label, const int32_t* channels_dev,
                                 int32_t r, ds_dtype dt, int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t T_cap,
                                 int64_t T, int64_t t_append, int32_t block, int64_t k_units, float scale, float* out,
@@ -385,6 +422,9 @@ ds_status ds_decode_sparse_attn(const void* q, const void* K, const void* V, voi
   if (!(scale > 0.f)) scale = 1.0f / std::sqrt(float(d));
   const hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
+  if (one_pass_ok(pl, block, r, dt))
+    return decode_one_pass(q, K, V, label, channels_dev, r, dt, B, Hq, Hkv, T_cap, T, t_append, k_units, scale, pl,
+                           out, indices, ws, s);
   if (ds_status st = decode_score_stage(q, K, label, channels_dev, r, dt, B, Hq, Hkv, T_cap, T, t_append, block, pl,
                                         ws, s))
     return st;
@@ -417,6 +457,9 @@ ds_status ds_decode_sparse_attn_ragged(const void* q, const void* K, const void*
   if (!(scale > 0.f)) scale = 1.0f / std::sqrt(float(d));
   const hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
+  if (one_pass_ok(pl, block, r, dt))
+    return decode_one_pass(q, K, V, label, channels_dev, r, dt, B, Hq, Hkv, T_cap, T_max, T_max, k_units, scale, pl,
+                           out, indices, ws, s, seq_lens_dev, n_append);
   if (ds_status st = decode_score_stage(q, K, label, channels_dev, r, dt, B, Hq, Hkv, T_cap, T_max, T_max, block, pl,
                                         ws, s, seq_lens_dev, n_append))
     return st;
@@ -487,6 +530,9 @@ ds_status ds_decode_sparse_attn_offload(const void* q, const void* K_host, const
   if (!(scale > 0.f)) scale = 1.0f / std::sqrt(float(d));
   const hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
+  if (one_pass_ok(pl, block, r, dt))
+    return decode_one_pass(q, Kd, Vd, label, channels_dev, r, dt, B, Hq, Hkv, T_cap, T, t_append, k_units, scale,
+                           pl, out, indices, ws, s);
   if (ds_status st = decode_score_stage(q, Kd, label, channels_dev, r, dt, B, Hq, Hkv, T_cap, T, t_append, block, pl,
                                         ws, s))
     return st;

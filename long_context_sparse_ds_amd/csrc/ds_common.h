@@ -107,12 +107,24 @@ hipError_t launch_attention(const void* q, const void* K, const void* V, int is_
 // unit_ids (may be null): the scores are candidates [rows][pl.n_units] whose
 // unit ids these are (ascending per row); kept candidates are written and
 // gathered as those units.
+// one (may be null): the one-pass form, for token-level rows that one
+// workgroup handles alone (pl.sp.n_split == 1, pl.sp.head_chunks == 1) and
+// label rows of 16 or 32 bytes: the kernel scores each row from the label
+// cache itself (rebuilding rows [t_append, T), or the last n_append of each
+// sequence, from K first) and scores / tile_hist are not read.
+struct OnePass {
+  void* label;        // [B, Hkv, T_cap, r]
+  const int32_t* ch;  // [Hkv, r]
+  int r;
+  int64_t t_append;
+  int n_append;
+};
 hipError_t launch_select_attention(const void* q, const void* K, const void* V, int is_bf16, const float* scores,
                                    int64_t ld, const uint16_t* tile_hist, int Hq, int Hkv, int64_t T_cap, int64_t T,
                                    int block, int64_t k_units, float scale, const DecodePlan& pl, int32_t* indices,
                                    float* part_acc, float* part_ml, float* out, unsigned* tickets,
                                    const int32_t* seq_lens, float tau, int32_t* counts,
-                                   const int32_t* unit_ids, hipStream_t s);
+                                   const int32_t* unit_ids, hipStream_t s, const OnePass* one = nullptr);
 
 hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t s);
 

@@ -1,0 +1,71 @@
+// The approximate score of one token from its label row, shared by the score
+// kernel and the fused kernel's one-pass form so that both give the same
+// float32 value bit for bit.
+//
+// Double Sparsity page, method details: the score of token t for KV head g is
+// sum_j qs[j] * label[t, j], with qs[j] the group's q summed over its heads at
+// channel ch[g, j].  A bf16 x bf16 or fp32 x fp32 product is exact in double,
+// and the r products are accumulated in double in channel order, so the score
+// is the exact value rounded once to float32 (up to the double rounding of the
+// running sum).
+#pragma once
+
+#include "ds_common.h"
+
+namespace ds {
+
+// qs at channel c: the group's q summed in head order from +0.0, which is the
+// score kernel's sum for groups of up to eight heads (it adds any heads past
+// the eighth first).
+template <typename TE>
+__device__ __forceinline__ double group_q_sum(const TE* __restrict__ qg, int G, int c) {
+  double s = 0.0;
+  for (int h = 0; h < G; ++h) s += double(elem_to_f32(qg[int64_t(h) * kHeadDim + c]));
+  return s;
+}
+
+// NV 16-byte words of one label row against qr[0 .. 8 NV) (bf16) or
+// qr[0 .. 4 NV) (fp32), in channel order.
+template <int NV>
+__device__ __forceinline__ double dot_label(const uint4 (&raw)[NV], const double* qr, uint16_t) {
+  double a = 0.0;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const uint32_t w[4] = {raw[v].x, raw[v].y, raw[v].z, raw[v].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      a = fma(qr[v * 8 + 2 * k], double(bf16_lo(w[k])), a);
+      a = fma(qr[v * 8 + 2 * k + 1], double(bf16_hi(w[k])), a);
+    }
+  }
+  return a;
+}
+
+template <int NV>
+__device__ __forceinline__ double dot_label(const uint4 (&raw)[NV], const double* qr, float) {
+  double a = 0.0;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const uint32_t w[4] = {raw[v].x, raw[v].y, raw[v].z, raw[v].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a = fma(qr[v * 4 + k], double(__uint_as_float(w[k])), a);
+  }
+  return a;
+}
+
+// Label-row append of token t: gather its r channels from its K row (a staged
+// copy in LDS, or global memory) into the label cache and return its score,
+// accumulated in the same channel order as dot_label.
+template <typename TE>
+__device__ __forceinline__ float append_row(const TE* __restrict__ Krow, TE* __restrict__ Lrow, const int* sch,
+                                            const double* qs, int r) {
+  double a = 0.0;
+  for (int j = 0; j < r; ++j) {
+    const TE v = Krow[sch[j]];
+    Lrow[j] = v;
+    a = fma(qs[j], double(elem_to_f32(v)), a);
+  }
+  return float(a);
+}
+
+}  // namespace ds

@@ -25,7 +25,7 @@
 // gathered, summed in the same channel order.
 #include <type_traits>
 
-#include "ds_common.h"
+#include "label_dot.h"
 
 namespace ds {
 namespace {
@@ -34,33 +34,6 @@ constexpr int kThreads = 512;
 constexpr int kTPT = 4;                     // tokens per thread
 constexpr int kTile = kThreads * kTPT;      // tokens per workgroup
 static_assert(kTile == kScoreTile, "tile size shared with the fused kernel's histogram reader");
-
-template <int NV>
-__device__ __forceinline__ double dot_label(const uint4 (&raw)[NV], const double* qr, uint16_t) {
-  double a = 0.0;
-#pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    const uint32_t w[4] = {raw[v].x, raw[v].y, raw[v].z, raw[v].w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      a = fma(qr[v * 8 + 2 * k], double(bf16_lo(w[k])), a);
-      a = fma(qr[v * 8 + 2 * k + 1], double(bf16_hi(w[k])), a);
-    }
-  }
-  return a;
-}
-
-template <int NV>
-__device__ __forceinline__ double dot_label(const uint4 (&raw)[NV], const double* qr, float) {
-  double a = 0.0;
-#pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    const uint32_t w[4] = {raw[v].x, raw[v].y, raw[v].z, raw[v].w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) a = fma(qr[v * 4 + k], double(__uint_as_float(w[k])), a);
-  }
-  return a;
-}
 
 // Unpack NV 16-byte words of label values into doubles.
 template <int NV>
@@ -88,22 +61,7 @@ __device__ __forceinline__ void label_values(const uint4 (&raw)[NV], double* lv,
 
 // R > 0: label width known at compile time and R * sizeof(TE) a multiple of 16 bytes.
 // R == 0: any width, element loads.
-// Label-row append of token t: gather its r channels from its K row (a
-// staged copy in LDS, or global memory) into the label cache and return its
-// score.
-template <typename TE>
-__device__ __forceinline__ float append_row(const TE* __restrict__ Krow, TE* __restrict__ Lrow, const int* sch,
-                                            const double* qs, int r) {
-  double a = 0.0;
-  for (int j = 0; j < r; ++j) {
-    const TE v = Krow[sch[j]];
-    Lrow[j] = v;
-    a = fma(qs[j], double(elem_to_f32(v)), a);
-  }
-  return float(a);
-}
-
-// The same with positive-only head aggregation; qh holds q[h, ch[j]] at h * r + j.
+// append_row (label_dot.h) with positive-only head aggregation; qh holds q[h, ch[j]] at h * r + j.
 template <typename TE>
 __device__ __forceinline__ float append_row_pos(const TE* __restrict__ Krow, TE* __restrict__ Lrow, const int* sch,
                                                 const double* qh, int r, int G) {

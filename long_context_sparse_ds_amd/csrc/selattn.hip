@@ -41,6 +41,7 @@
 // kept set is exactly the passing units, so the radix passes are skipped and
 // the prefix sum over the pass masks alone places them.  Otherwise the top-k
 // search runs as usual and every unit it keeps passes.
+#include "label_dot.h"
 #include "select_dev.h"
 
 namespace ds {
@@ -206,6 +207,12 @@ struct FusedArgs {
   int32_t* counts;             // threshold rule: kept units per row; null: plain top-k
   const int32_t* unit_ids;     // the units are candidates with these unit ids [rows][n_units]; null: identity
   int32_t xcd_rows;            // grid (8, n_split, rows * head_chunks / 8): row = 8 (z / head_chunks) + x
+  // One pass (scores null): the kernel scores the row from its label rows
+  // [rows][T_cap][r] with channels ch [Hkv][r], rebuilding rows [t_append, T)
+  // (ragged: the last n_append of each sequence) from K first.
+  void* label;
+  const int32_t* ch;
+  int32_t r, t_append, n_append;
 };
 
 // Scalar arguments, those of the first loads first: the first 15 dwords (up to
@@ -214,15 +221,25 @@ struct FusedArgs {
 // min(k_units, its unit count) units; index slots past that are set to -1.
 // counts_ != null: the threshold rule with tau_ (index slots past a row's kept
 // count are -1; a row that keeps nothing gets a zero output).
-template <typename TE, int NT, int ITEMS, int HC, bool RAGGED>
+// LNV > 0: one pass, for token-level rows that one workgroup handles alone (a
+// single split and head chunk): the row's scores are computed here from its
+// label rows of LNV 16-byte words, with the score kernel's arithmetic, instead
+// of being read from scores_; no tile histograms.
+template <typename TE, int NT, int ITEMS, int HC, bool RAGGED, int LNV>
 __global__ __launch_bounds__(NT) void selattn_kernel(
     const void* q_, const float* scores_, const uint16_t* tile_hist_, int64_t ld_, int32_t G_,
     int32_t head_chunks_, int32_t xcd_rows_, int32_t n_units_, int32_t tiles_, int32_t k_units_, int32_t lb_,
     const void* K_,
     const void* V_, int32_t* indices_, float* part_acc_, float* part_ml_, float* out_, unsigned* tickets_,
     int64_t T_cap_, int32_t T_, int32_t kv_virtual_, int32_t chunk_, int32_t n_split_, float scale_,
-    const int32_t* seq_lens_, int32_t Hkv_, float tau_, int32_t* counts_, const int32_t* unit_ids_) {
+    const int32_t* seq_lens_, int32_t Hkv_, float tau_, int32_t* counts_, const int32_t* unit_ids_, void* label_,
+    const int32_t* ch_, int32_t r_, int32_t t_append_, int32_t n_append_) {
   FusedArgs a;
+  a.label = label_;
+  a.ch = ch_;
+  a.r = r_;
+  a.t_append = t_append_;
+  a.n_append = n_append_;
   a.q = q_;
   a.K = K_;
   a.V = V_;
@@ -304,9 +321,53 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
   for (int h = 0; h < HC; ++h)
     qraw[h] = *reinterpret_cast<const uint4*>(q + (bh0 + h) * kHeadDim + sub * EPL);
   const int first = tid * ITEMS;
-  const float* srow = a.scores + int64_t(row) * a.ld;   // 16-byte aligned: ld is a multiple of 4
   float s[ITEMS];
-  if (first + ITEMS <= n_units) {
+  if constexpr (LNV > 0) {
+    // One pass: score the row here.  Pass c covers units c * NT + tid (a
+    // wavefront reads 64 consecutive label rows per load), each score going
+    // to the LDS slot of its owner thread; the owners read them back below.
+    constexpr int R = LNV * 16 / int(sizeof(TE));   // label channels
+    constexpr int CB = LNV == 1 ? 8 : 4;            // passes whose label rows are requested together
+    __shared__ double qs_l[R];
+    __shared__ int ch_l[R];
+    const int g = int(row % uint32_t(a.Hkv));
+    if (tid < R) {
+      const int cj = a.ch[g * R + tid];
+      qs_l[tid] = group_q_sum(q + int64_t(row) * a.G * kHeadDim, a.G, cj);
+      ch_l[tid] = cj;
+    }
+    TE* lab = static_cast<TE*>(a.label) + int64_t(row) * a.T_cap * R;
+    const int ta = RAGGED ? max(T_row - a.n_append, 0) : a.t_append;   // rows rebuilt from K
+    __syncthreads();
+    double qr[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) qr[j] = qs_l[j];
+    for (int c0 = 0; c0 < ITEMS; c0 += CB) {
+      uint4 raw[CB][LNV];
+#pragma unroll
+      for (int i = 0; i < CB; ++i) {
+        const int u = (c0 + i) * NT + tid;
+        const uint4* p = reinterpret_cast<const uint4*>(lab + int64_t(u < T_row ? u : 0) * R);   // row 0 exists
+#pragma unroll
+        for (int v = 0; v < LNV; ++v) raw[i][v] = p[v];
+      }
+#pragma unroll
+      for (int i = 0; i < CB; ++i) {
+        const int u = (c0 + i) * NT + tid;
+        float sv;
+        if (u >= T_row) sv = -INFINITY;   // past the sequence (and the row's units)
+        else if (u >= ta)
+          sv = append_row(K + (int64_t(row) * a.T_cap + u) * kHeadDim, lab + int64_t(u) * R, ch_l, qs_l, R);
+        else sv = float(dot_label<LNV>(raw[i], qr, TE()));
+        const int ut = u / ITEMS, uj = u % ITEMS;
+        sm.u.sc[((uj >> 2) * NT + ut) * 4 + (uj & 3)] = sv;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) s[j] = sm.u.sc[((j >> 2) * NT + tid) * 4 + (j & 3)];
+  } else if (first + ITEMS <= n_units) {
+    const float* srow = a.scores + int64_t(row) * a.ld;   // 16-byte aligned: ld is a multiple of 4
 #pragma unroll
     for (int v = 0; v < ITEMS / 4; ++v) {
       const float4 f = *reinterpret_cast<const float4*>(srow + first + 4 * v);
@@ -316,6 +377,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
       s[4 * v + 3] = f.w;
     }
   } else {
+    const float* srow = a.scores + int64_t(row) * a.ld;
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) s[j] = first + j < n_units ? srow[first + j] : -INFINITY;
   }
@@ -347,11 +409,14 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
   // wavefront's stores cover consecutive slots: written at the thread's own
   // 64-byte stride instead, all 64 lanes of a store hit the same few banks
   // and the stores took ~6K clocks per workgroup.
+  // (One pass: they are there already.)
   const auto sc_at = [&](int j) -> float { return sm.u.sc[((j >> 2) * NT + tid) * 4 + (j & 3)]; };
+  if constexpr (LNV == 0) {
 #pragma unroll
-  for (int v = 0; v < ITEMS / 4; ++v)
-    *reinterpret_cast<float4*>(&sm.u.sc[(v * NT + tid) * 4]) =
-        make_float4(s[4 * v], s[4 * v + 1], s[4 * v + 2], s[4 * v + 3]);
+    for (int v = 0; v < ITEMS / 4; ++v)
+      *reinterpret_cast<float4*>(&sm.u.sc[(v * NT + tid) * 4]) =
+          make_float4(s[4 * v], s[4 * v + 1], s[4 * v + 2], s[4 * v + 3]);
+  }
   uint32_t c1[BPT1];
   if (a.tile_hist != nullptr) {
 #pragma unroll
@@ -684,19 +749,28 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
   if (tid == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+template <typename TE, int NT, int ITEMS, int HC, bool RAGGED, int LNV>
+hipError_t launch_kernel(const FusedArgs& a, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((selattn_kernel<TE, NT, ITEMS, HC, RAGGED, LNV>), grid, dim3(NT), 0, s, a.q, a.scores,
+                     a.tile_hist, a.ld, a.G, a.head_chunks, a.xcd_rows, a.n_units, a.tiles, a.k_units, a.lb, a.K, a.V,
+                     a.indices, a.part_acc, a.part_ml, a.out, a.tickets, a.T_cap, a.T, a.kv_virtual, a.chunk,
+                     a.n_split, a.scale, a.seq_lens, a.Hkv, a.tau, a.counts, a.unit_ids, a.label, a.ch, a.r,
+                     a.t_append, a.n_append);
+  return hipGetLastError();
+}
+
+// One pass when a label cache is given: LNV 16-byte words per label row.
 template <typename TE, int NT, int ITEMS, int HC>
 hipError_t launch_one(const FusedArgs& a, dim3 grid, hipStream_t s) {
-  if (a.seq_lens != nullptr)
-    hipLaunchKernelGGL((selattn_kernel<TE, NT, ITEMS, HC, true>), grid, dim3(NT), 0, s, a.q, a.scores, a.tile_hist,
-                       a.ld, a.G, a.head_chunks, a.xcd_rows, a.n_units, a.tiles, a.k_units, a.lb, a.K, a.V, a.indices,
-                       a.part_acc, a.part_ml, a.out, a.tickets, a.T_cap, a.T, a.kv_virtual, a.chunk, a.n_split,
-                       a.scale, a.seq_lens, a.Hkv, a.tau, a.counts, a.unit_ids);
-  else
-    hipLaunchKernelGGL((selattn_kernel<TE, NT, ITEMS, HC, false>), grid, dim3(NT), 0, s, a.q, a.scores, a.tile_hist,
-                       a.ld, a.G, a.head_chunks, a.xcd_rows, a.n_units, a.tiles, a.k_units, a.lb, a.K, a.V, a.indices,
-                       a.part_acc, a.part_ml, a.out, a.tickets, a.T_cap, a.T, a.kv_virtual, a.chunk, a.n_split,
-                       a.scale, nullptr, a.Hkv, a.tau, a.counts, a.unit_ids);
-  return hipGetLastError();
+  const int lnv = a.label == nullptr ? 0 : a.r * int(sizeof(TE)) / 16;
+  if (a.seq_lens != nullptr) {
+    if (lnv == 1) return launch_kernel<TE, NT, ITEMS, HC, true, 1>(a, grid, s);
+    if (lnv == 2) return launch_kernel<TE, NT, ITEMS, HC, true, 2>(a, grid, s);
+    return launch_kernel<TE, NT, ITEMS, HC, true, 0>(a, grid, s);
+  }
+  if (lnv == 1) return launch_kernel<TE, NT, ITEMS, HC, false, 1>(a, grid, s);
+  if (lnv == 2) return launch_kernel<TE, NT, ITEMS, HC, false, 2>(a, grid, s);
+  return launch_kernel<TE, NT, ITEMS, HC, false, 0>(a, grid, s);
 }
 
 template <typename TE, int HC>
@@ -724,8 +798,15 @@ hipError_t launch_select_attention(const void* q, const void* K, const void* V, 
                                    int block, int64_t k_units, float scale, const DecodePlan& pl, int32_t* indices,
                                    float* part_acc, float* part_ml, float* out, unsigned* tickets,
                                    const int32_t* seq_lens, float tau, int32_t* counts,
-                                   const int32_t* unit_ids, hipStream_t s) {
+                                   const int32_t* unit_ids, hipStream_t s, const OnePass* one) {
   FusedArgs a{};
+  if (one != nullptr) {
+    a.label = one->label;
+    a.ch = one->ch;
+    a.r = one->r;
+    a.t_append = int32_t(one->t_append);
+    a.n_append = one->n_append;
+  }
   a.unit_ids = unit_ids;
   a.seq_lens = seq_lens;
   a.tau = tau;

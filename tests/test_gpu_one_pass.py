@@ -1,0 +1,98 @@
+"""The one-pass decode step against the two-kernel form, bit for bit.
+
+Token-level rows that one fused workgroup handles alone (a single split and head
+chunk: at least 256 row-chunks) are decoded by one kernel that scores each row from
+its label rows itself.  The two phase calls still run the score kernel and then the
+fused kernel from the stored scores.  Both accumulate each score the same way, so on
+the same inputs the one-call step must give the same indices, outputs and rebuilt
+label rows as the two phases, bit for bit.  The cases cover both label-row widths
+(16 and 32 bytes) in both element types, groups of 1, 2 and 4 query heads, every
+per-thread item count of the fused kernel, rows rebuilt from K, and a ragged batch.
+The oracle checks the one-pass path on its own in the 256-row case of the parity
+suite and at full size (batched_32k, ragged_16k).
+"""
+import pytest
+import torch
+
+import long_context_sparse_ds_amd as L
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    L.lib()   # raises if the HIP library is missing
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+# (name, dtype, B, Hq, Hkv, T, r, k, rows rebuilt, ragged); B * Hkv >= 256 rows, groups <= 4 heads
+CASES = [
+    ("bf16_r8_items32", "bf16", 64, 4, 4, 20000, 8, 700, 3, False),
+    ("bf16_r16_g4_items16", "bf16", 64, 16, 4, 9000, 16, 300, 1, False),
+    ("bf16_r16_g2_items4", "bf16", 128, 4, 2, 3000, 16, 120, 40, False),
+    ("f32_r4_items8", "f32", 128, 2, 2, 5000, 4, 200, 2, False),
+    ("f32_r8_items4", "f32", 256, 1, 1, 3000, 8, 100, 1, False),
+    ("bf16_r8_ragged", "bf16", 64, 4, 4, 12000, 8, 400, 2, True),
+    ("bf16_r16_ragged_g2", "bf16", 128, 4, 2, 6000, 16, 250, 1, True),
+]
+
+
+def _inputs(dt, B, Hq, Hkv, T, r, seed):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    q = torch.randn((B, Hq, 128), generator=g, device="cuda").to(tdt)
+    K = torch.randn((B, Hkv, T, 128), generator=g, device="cuda").to(tdt)
+    V = torch.randn((B, Hkv, T, 128), generator=g, device="cuda").to(tdt)
+    ch = torch.stack([torch.randperm(128, generator=g, device="cuda")[:r].sort().values for _ in range(Hkv)])
+    ch = ch.to(torch.int32).contiguous()
+    return q, K, V, ch
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_one_pass_matches_two_kernels(case):
+    name, dt, B, Hq, Hkv, T, r, k, n_new, ragged = case
+    _say(f"{name}: B={B} Hq={Hq} Hkv={Hkv} T={T} r={r} k={k} rebuilt={n_new} ragged={ragged}")
+    q, K, V, ch = _inputs(dt, B, Hq, Hkv, T, r, seed=sum(map(ord, name)))
+    label = L.ds_build_label_cache(K, ch)
+    torch.cuda.synchronize()
+    raw = label.view(torch.int16) if dt == "bf16" else label.view(torch.int32)
+    ws1 = L.alloc_workspace(B, Hq, Hkv, 128, T, 1, k)
+    ws2 = L.alloc_workspace(B, Hq, Hkv, 128, T, 1, k)
+    if ragged:
+        g = torch.Generator().manual_seed(7)
+        lens = torch.randint(1, T + 1, (B,), generator=g, dtype=torch.int32)
+        lens[0], lens[1] = T, 1
+        seq = lens.cuda()
+        lab1, lab2 = label.clone(), label.clone()
+        for b in range(B):   # garbage where each sequence's rows are rebuilt
+            t0 = max(int(lens[b]) - n_new, 0)
+            for lab in (lab1, lab2):
+                (lab.view(torch.int16) if dt == "bf16" else lab.view(torch.int32))[b, :, t0:int(lens[b])].fill_(0x3F00)
+        o1, i1 = L.ds_decode_sparse_attn_ragged(q, K, V, lab1, ch, seq, T, k, n_append=n_new, workspace=ws1)
+        L.ds_decode_score_ragged(q, K, lab2, ch, seq, T, k, n_append=n_new, workspace=ws2)
+        o2, i2 = L.ds_decode_select_attend_ragged(q, K, V, seq, T, k, ws2)
+    else:
+        raw[:, :, T - n_new:T].fill_(0x3F00)   # garbage in the rows to be rebuilt
+        lab1, lab2 = label.clone(), label.clone()
+        o1, i1 = L.ds_decode_sparse_attn(q, K, V, lab1, ch, T, k, workspace=ws1, t_append=T - n_new)
+        L.ds_decode_score(q, K, lab2, ch, T, k, workspace=ws2, t_append=T - n_new)
+        o2, i2 = L.ds_decode_select_attend(q, K, V, T, k, ws2)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2), f"{name}: indices differ in {(i1 != i2).sum().item()} slots"
+    assert torch.equal(o1.view(torch.int32), o2.view(torch.int32)), f"{name}: outputs differ"
+    assert torch.equal(lab1.view(torch.uint8), lab2.view(torch.uint8)), f"{name}: rebuilt label rows differ"
+    want = L.ds_build_label_cache(K, ch)   # the rebuilt rows are K's channels
+    torch.cuda.synchronize()
+    if not ragged:
+        assert torch.equal(lab1.view(torch.uint8), want.view(torch.uint8))
+    ii = i1.view(-1, k)
+    valid = ii >= 0   # index slots past a short sequence's kept count are -1
+    assert valid[:, 0].all() and ((ii[:, 1:] > ii[:, :-1]) | ~valid[:, 1:]).all()
+    _say(f"{name}: identical; first row kept {int(valid[0].sum())}")
+    del q, K, V, label, lab1, lab2, ws1, ws2
+    torch.cuda.empty_cache()

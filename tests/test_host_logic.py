@@ -189,3 +189,19 @@ def test_one_wavefront_selection_model_keeps_the_top_k_ties_to_the_lower_id(mode
             keys = [0x3F800000 if v else 0 for v in valid]
         want = sorted(sorted((c for c in range(128) if valid[c]), key=lambda c: (-keys[c], c))[:k])
         assert _wave_select(keys, k) == want
+
+
+def test_one_pass_is_taken_exactly_for_rows_one_workgroup_handles_alone():
+    """The one-call decode step runs as one kernel for token-level rows with a single
+    split and head chunk and 16- or 32-byte label rows, and as two kernels otherwise."""
+    assert L.ds_decode_is_one_pass(16, 32, 32, 128, 32768, 1, 2048, 8)            # batched_32k: 512 rows
+    assert L.ds_decode_is_one_pass(256, 32, 32, 128, 16384, 1, 1024, 16)          # 8,192 rows, r = 16
+    assert L.ds_decode_is_one_pass(64, 256, 64, 128, 4096, 1, 200, 8)             # groups of 4: one chunk
+    assert L.ds_decode_is_one_pass(128, 2, 2, 128, 5000, 1, 200, 4, "f32")        # fp32, 16-byte rows
+    assert not L.ds_decode_is_one_pass(1, 32, 32, 128, 16384, 1, 1024, 16)        # 32 rows: eight splits each
+    assert not L.ds_decode_is_one_pass(16, 32, 32, 128, 32768, 64, 32, 8)         # blocks
+    assert not L.ds_decode_is_one_pass(16, 32, 32, 128, 32768, 1, 2048, 12)       # 24-byte label rows
+    assert not L.ds_decode_is_one_pass(64, 512, 64, 128, 4096, 1, 100, 8)         # groups of 8: two head chunks
+    assert not L.ds_decode_is_one_pass(64, 32, 32, 128, 131072, 1, 2048, 8)       # past the fused kernel's rows
+    with pytest.raises(L.DsError):
+        L.ds_decode_is_one_pass(1, 32, 32, 128, 16384, 1, 1024, 0)
