@@ -2,9 +2,9 @@
 
 The benchmark times graph-replayed steps, and the split merge relies on tickets that
 the kernels reset themselves, so each path (unequal lengths, the threshold rule, the
-two-stage selection of long rows, the span search, offloaded K/V) is captured once and
-replayed several times, with eager calls and synchronisation in between, each replay
-checked against the eager call on the same inputs.
+two-stage selection of long rows, the span search, offloaded K/V, the one-pass kernel) is
+captured once and replayed several times, with eager calls and synchronisation in between,
+each replay checked against the eager call on the same inputs.
 """
 import numpy as np
 import pytest
@@ -91,10 +91,19 @@ def _path(name):
         return (lambda o: L.ds_decode_sparse_attn_offload(qd, Kh, Vh, lab, chd, w.T, w.k_units, w.block,
                                                           out=o["out"], indices=o["idx"], workspace=o["ws"],
                                                           t_append=w.T - 1)), outs
+    if name == "one_pass":
+        w = Workload("g_one", "bf16", B=64, Hq=4, Hkv=4, d=128, T=2500, r=16, block=1, k_units=100, seed_base=61500)
+        assert L.ds_decode_is_one_pass(w.B, w.Hq, w.Hkv, w.d, w.T, w.block, w.k_units, w.r)
+        qd, Kd, Vd, chd, lab = _inputs(w)
+        outs = dict(out=torch.empty((w.B, w.Hq, w.d), device="cuda"),
+                    idx=torch.empty((w.B, w.Hkv, w.k_units), dtype=torch.int32, device="cuda"),
+                    ws=L.alloc_workspace(w.B, w.Hq, w.Hkv, w.d, w.T, w.block, w.k_units))
+        return (lambda o: L.ds_decode_sparse_attn(qd, Kd, Vd, lab, chd, w.T, w.k_units, w.block, out=o["out"],
+                                                  indices=o["idx"], workspace=o["ws"], t_append=w.T - 1)), outs
     raise ValueError(name)
 
 
-PATHS = ["ragged", "threshold", "long_rows", "span_search", "offload"]
+PATHS = ["ragged", "threshold", "long_rows", "span_search", "offload", "one_pass"]
 
 
 @pytest.mark.parametrize("name", PATHS)

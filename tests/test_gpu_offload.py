@@ -4,8 +4,9 @@ ds_decode_sparse_attn_offload runs the kernels of ds_decode_sparse_attn with K a
 read across the host link, so its indices and outputs must equal, bit for bit, those
 of the same call on device-resident K and V; the oracle checks a sample of units too.
 Covered: the fused path (token-level and 64-token blocks, GQA, T_cap > T, appended
-label rows read from host K) and the separate path for rows of more than 32,768
-units, the full-size offload workload, and the rejection of device-resident K/V.
+label rows read from host K), its one-pass form (256 one-split rows), the separate path
+for rows of more than 32,768 units, the full-size offload workload, and the rejection
+of device-resident K/V.
 """
 import ctypes
 
@@ -53,6 +54,8 @@ OFFLOAD_CASES = [
              fixed_outliers=True),
     Workload("off_long_rows", "bf16", B=1, Hq=2, Hkv=2, d=128, T=40000, r=16, block=1, k_units=600,
              seed_base=41300),
+    # 256 rows of one split each: the one-pass kernel, reading K (for the rebuilt rows) and V from the host
+    Workload("off_one_pass", "bf16", B=64, Hq=4, Hkv=4, d=128, T=1500, r=8, block=1, k_units=60, seed_base=41400),
 ]
 
 
