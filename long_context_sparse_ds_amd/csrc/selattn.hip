@@ -327,7 +327,10 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
     // wavefront reads 64 consecutive label rows per load), each score going
     // to the LDS slot of its owner thread; the owners read them back below.
     constexpr int R = LNV * 16 / int(sizeof(TE));   // label channels
-    constexpr int CB = LNV == 1 ? 8 : 4;            // passes whose label rows are requested together
+    // Passes whose label rows are requested together, never more than the
+    // ITEMS passes there are: a unit of a pass past ITEMS would have no slot.
+    constexpr int CB = (LNV == 1 ? 8 : 4) < ITEMS ? (LNV == 1 ? 8 : 4) : ITEMS;
+    static_assert(ITEMS % CB == 0, "whole batches of passes");
     __shared__ double qs_l[R];
     __shared__ int ch_l[R];
     const int g = int(row % uint32_t(a.Hkv));
@@ -338,6 +341,10 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
     }
     TE* lab = static_cast<TE*>(a.label) + int64_t(row) * a.T_cap * R;
     const int ta = RAGGED ? max(T_row - a.n_append, 0) : a.t_append;   // rows rebuilt from K
+    // The top-digit histogram is built as the scores come in, its LDS atomics
+    // overlapping the next passes' label loads.
+#pragma unroll
+    for (int i = 0; i < BPT1; ++i) sm.hist1[i * NT + tid] = 0u;
     __syncthreads();
     double qr[R];
 #pragma unroll
@@ -359,6 +366,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
         else if (u >= ta)
           sv = append_row(K + (int64_t(row) * a.T_cap + u) * kHeadDim, lab + int64_t(u) * R, ch_l, qs_l, R);
         else sv = float(dot_label<LNV>(raw[i], qr, TE()));
+        if (u < T_row) atomicAdd(&sm.hist1[float_key(sv) >> 21], 1u);   // the sequence's units only
         const int ut = u / ITEMS, uj = u % ITEMS;
         sm.u.sc[((uj >> 2) * NT + ut) * 4 + (uj & 3)] = sv;
       }
@@ -428,15 +436,17 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
       c1[BPT1 - 2 - 2 * i] = hw[i] >> 16;
     }
   } else {
-    // The units of this sequence only (a short one's padding would pile onto one bin).
-    const int nu_hist = RAGGED ? ((T_row + block - 1) >> lb) : n_units;
+    if constexpr (LNV == 0) {   // (one pass: built while scoring)
+      // The units of this sequence only (a short one's padding would pile onto one bin).
+      const int nu_hist = RAGGED ? ((T_row + block - 1) >> lb) : n_units;
 #pragma unroll
-    for (int i = 0; i < BPT1; ++i) sm.hist1[i * NT + tid] = 0u;
-    __syncthreads();
+      for (int i = 0; i < BPT1; ++i) sm.hist1[i * NT + tid] = 0u;
+      __syncthreads();
 #pragma unroll
-    for (int j = 0; j < ITEMS; ++j)
-      if (first + j < nu_hist) atomicAdd(&sm.hist1[float_key(s[j]) >> 21], 1u);
-    __syncthreads();
+      for (int j = 0; j < ITEMS; ++j)
+        if (first + j < nu_hist) atomicAdd(&sm.hist1[float_key(s[j]) >> 21], 1u);
+      __syncthreads();
+    }
     read_bins<NT, 2048>(sm.hist1, c1);
     // Each bin is read by exactly one thread, which clears it for pass 1.
     const int lo = 2048 - BPT1 * (tid + 1);
