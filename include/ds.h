@@ -111,9 +111,10 @@ size_t ds_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, 
  * in memory; 0 when it launches the score kernel and then the fused
  * select + attention kernel (the two phases below); -1 (with ds_last_error set)
  * for an invalid shape.  One pass is taken for token-level rows (block = 1)
- * that one fused workgroup handles alone (a single split of the kept set and
- * at most 4 query heads per group, which holds once B * Hkv reaches about 256)
- * with label rows of 16 or 32 bytes (r = 8 or 16 for bf16, 4 or 8 for fp32).
+ * of at most 32,768 tokens that one fused workgroup handles alone: a single
+ * split of the kept set (which holds once B * Hkv reaches about 256) and
+ * groups of 1, 2 or 4 query heads, with label rows of 16 or 32 bytes (r = 8
+ * or 16 for bf16, 4 or 8 for fp32).
  * Both forms give the same indices and outputs bit for bit.  Host only.
  */
 int32_t ds_decode_is_one_pass(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t T, int32_t block,

@@ -205,3 +205,9 @@ def test_one_pass_is_taken_exactly_for_rows_one_workgroup_handles_alone():
     assert not L.ds_decode_is_one_pass(64, 32, 32, 128, 131072, 1, 2048, 8)       # past the fused kernel's rows
     with pytest.raises(L.DsError):
         L.ds_decode_is_one_pass(1, 32, 32, 128, 16384, 1, 1024, 0)
+
+
+def test_one_pass_needs_groups_of_one_two_or_four_heads():
+    """Groups of 3 heads run as three one-head chunks, so they keep the two kernels."""
+    assert L.ds_decode_is_one_pass(128, 8, 4, 128, 4096, 1, 100, 8)       # G = 2
+    assert not L.ds_decode_is_one_pass(128, 12, 4, 128, 4096, 1, 100, 8)  # G = 3
