@@ -384,11 +384,10 @@ static bool one_pass_ok(const ds::DecodePlan& pl, int32_t block, int32_t r, ds_d
 }
 
 static ds_status decode_one_pass(const void* q, const void* K, const void* V, void* label,
-                                 const int32_t* channels_dev, int32_t r, ds_dtype dt, int32_t B, int32_t Hq,
-                                 int32_t Hkv, int64_t T_cap, int64_t T, int64_t t_append, int64_t k_units,
-                                 float scale, const ds::DecodePlan& pl, float* out, int32_t* indices, char* ws,
-                                 hipStream_t s, const int32_t* seq_lens = nullptr, int32_t n_append = 0) {
-  (void)B;
+                                 const int32_t* channels_dev, int32_t r, ds_dtype dt, int32_t Hq, int32_t Hkv,
+                                 int64_t T_cap, int64_t T, int64_t t_append, int64_t k_units, float scale,
+                                 const ds::DecodePlan& pl, float* out, int32_t* indices, char* ws, hipStream_t s,
+                                 const int32_t* seq_lens = nullptr, int32_t n_append = 0) {
   const ds::OnePass one{label, channels_dev, r, t_append, n_append};
   return hip_status(
       ds::launch_select_attention(q, K, V, dt == DS_DTYPE_BF16, nullptr, pl.score_ld, nullptr, Hq, Hkv, T_cap, T, 1,
@@ -423,7 +422,7 @@ ds_status ds_decode_sparse_attn(const void* q, const void* K, const void* V, voi
   const hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   if (one_pass_ok(pl, block, r, dt))
-    return decode_one_pass(q, K, V, label, channels_dev, r, dt, B, Hq, Hkv, T_cap, T, t_append, k_units, scale, pl,
+    return decode_one_pass(q, K, V, label, channels_dev, r, dt, Hq, Hkv, T_cap, T, t_append, k_units, scale, pl,
                            out, indices, ws, s);
   if (ds_status st = decode_score_stage(q, K, label, channels_dev, r, dt, B, Hq, Hkv, T_cap, T, t_append, block, pl,
                                         ws, s))
@@ -458,7 +457,7 @@ ds_status ds_decode_sparse_attn_ragged(const void* q, const void* K, const void*
   const hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   if (one_pass_ok(pl, block, r, dt))
-    return decode_one_pass(q, K, V, label, channels_dev, r, dt, B, Hq, Hkv, T_cap, T_max, T_max, k_units, scale, pl,
+    return decode_one_pass(q, K, V, label, channels_dev, r, dt, Hq, Hkv, T_cap, T_max, T_max, k_units, scale, pl,
                            out, indices, ws, s, seq_lens_dev, n_append);
   if (ds_status st = decode_score_stage(q, K, label, channels_dev, r, dt, B, Hq, Hkv, T_cap, T_max, T_max, block, pl,
                                         ws, s, seq_lens_dev, n_append))
@@ -531,7 +530,7 @@ ds_status ds_decode_sparse_attn_offload(const void* q, const void* K_host, const
   const hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   if (one_pass_ok(pl, block, r, dt))
-    return decode_one_pass(q, Kd, Vd, label, channels_dev, r, dt, B, Hq, Hkv, T_cap, T, t_append, k_units, scale,
+    return decode_one_pass(q, Kd, Vd, label, channels_dev, r, dt, Hq, Hkv, T_cap, T, t_append, k_units, scale,
                            pl, out, indices, ws, s);
   if (ds_status st = decode_score_stage(q, Kd, label, channels_dev, r, dt, B, Hq, Hkv, T_cap, T, t_append, block, pl,
                                         ws, s))
