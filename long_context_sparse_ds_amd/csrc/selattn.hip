@@ -327,9 +327,11 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
     // wavefront reads 64 consecutive label rows per load), each score going
     // to the LDS slot of its owner thread; the owners read them back below.
     constexpr int R = LNV * 16 / int(sizeof(TE));   // label channels
-    // Passes whose label rows are requested together, never more than the
-    // ITEMS passes there are: a unit of a pass past ITEMS would have no slot.
-    constexpr int CB = (LNV == 1 ? 8 : 4) < ITEMS ? (LNV == 1 ? 8 : 4) : ITEMS;
+    // Passes whose label rows are requested together (64 bytes per thread:
+    // measured faster than 128 or 32, the other wavefronts covering the
+    // latency), never more than the ITEMS passes there are: a unit of a pass
+    // past ITEMS would have no slot.
+    constexpr int CB = (LNV == 1 ? 4 : 2) < ITEMS ? (LNV == 1 ? 4 : 2) : ITEMS;
     static_assert(ITEMS % CB == 0, "whole batches of passes");
     __shared__ double qs_l[R];
     __shared__ int ch_l[R];
