@@ -40,6 +40,9 @@ CASES = [
     # 16-byte rows with fewer passes (4) than a batch of label requests (8)
     ("bf16_r8_items4", "bf16", 128, 2, 2, 3000, 8, 100, 2, False),
     ("f32_r4_items4", "f32", 256, 1, 1, 2000, 4, 64, 1, False),
+    # edge shapes: rows of 5 tokens with 3 of them rebuilt, and every token kept (k = T)
+    ("bf16_r8_T5", "bf16", 64, 4, 4, 5, 8, 3, 3, False),
+    ("f32_r4_dense", "f32", 256, 1, 1, 40, 4, 40, 1, False),
     ("bf16_r8_ragged", "bf16", 64, 4, 4, 12000, 8, 400, 2, True),
     ("bf16_r16_ragged_g2", "bf16", 128, 4, 2, 6000, 16, 250, 1, True),
 ]
