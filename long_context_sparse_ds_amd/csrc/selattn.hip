@@ -1,4 +1,7 @@
 // Fused top-k selection and sparse attention, one launch per decode step.
+// In its one-pass form (LNV > 0) the same kernel also scores the row from the
+// label cache first, so that a step whose rows each fit one workgroup is a
+// single launch with no score buffer in memory.
 //
 // Double Sparsity page, method details and abstract: keep the tokens with the
 // highest approximate scores, then compute self-attention over those tokens
