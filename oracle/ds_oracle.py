@@ -267,12 +267,11 @@ def decode_unit_threshold(q_group, K, V, ch, k_max, tau, block=1, scale=None, T=
 # -- hierarchical span search (HiP page, abstract) ---------------------------
 
 def group_token_scores(q_group, K, tokens):
-    """Score of each listed key token for the query group: float32 of the float64
-    sum over the group's query heads of q_h . K_t (no scale; a positive scale
-    cannot change a ranking).  The search ranks these float32 values."""
+    """Score of each listed key token for the query group: the float64 sum over
+    the group's query heads of q_h . K_t (no scale; a positive scale cannot
+    change a ranking).  The search ranks these float64 values."""
     qs = np.asarray(q_group, dtype=np.float64).sum(axis=0)        # [d]
-    s = np.asarray(K, dtype=np.float64)[np.asarray(tokens, dtype=np.int64)] @ qs
-    return s.astype(np.float32)
+    return np.asarray(K, dtype=np.float64)[np.asarray(tokens, dtype=np.int64)] @ qs
 
 
 def hip_search(q_group, K, T, k, span):
@@ -306,8 +305,8 @@ def hip_search(q_group, K, T, k, span):
         new = [c[0] for c in cand if c[0] not in score]
         if new:
             score.update(zip(new, group_token_scores(q_group, K, new)))
-        keys = np.array([score[s] for s, _ in cand], dtype=np.float32)
-        order = np.argsort(-keys.astype(np.float64), kind="stable")   # candidates are in start order
+        keys = np.array([score[s] for s, _ in cand], dtype=np.float64)
+        order = np.argsort(-keys, kind="stable")   # candidates are in start order: ties keep the lower start
         keep = np.sort(order[:k])
         spans = [cand[i] for i in keep]
     return spans

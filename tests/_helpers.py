@@ -50,21 +50,31 @@ def unit_inputs(w: dsgen.Workload, q, K, V, b, g):
             dsgen.to_f64(V[b, g, :w.T], w.dtype))
 
 
-def check_unit(w, q, K, V, ch, b, g, gpu_out, gpu_idx, scale=None):
-    """Full parity of one unit: kept indices by the index rule, output vs the oracle's
-    attention over the GPU's kept set.  Returns the number of legal tie swaps."""
-    qg, Kf, Vf = unit_inputs(w, q, K, V, b, g)
+def check_row(qg, Kf, Vf, ch_g, k, block, T, gpu_out_g, gpu_idx_g, dtype, what, scale=None):
+    """Full parity of one (sequence, KV head) row from float64 inputs (qg [G, d], Kf and Vf
+    [>= T, d]): the first k index slots by the index rule, any slots after them -1, and the
+    output against the oracle's attention over the GPU's kept set.  Returns (tie swaps, error)."""
     if scale is None:
-        scale = O.default_scale(w.d)
-    out_ref, kept_ref, scores = O.decode_unit(qg, Kf, Vf, ch[g], w.k_units, w.block, scale, w.T)
-    swaps = check_index_parity(gpu_idx[b, g], scores, w.k_units, what=f"unit b={b} g={g}")
-    S = O.tokens_of(gpu_idx[b, g], w.block, w.T)
+        scale = O.default_scale(Kf.shape[1])
+    out_ref, kept_ref, scores = O.decode_unit(qg, Kf, Vf, ch_g, k, block, scale, T)
+    idx = np.asarray(gpu_idx_g)
+    assert np.all(idx[k:] == -1), f"{what}: index slots past the kept count are not -1"
+    swaps = check_index_parity(idx[:k], scores, k, what=what)
+    S = O.tokens_of(idx[:k], block, T)
     ref = O.attend(qg, Kf, Vf, S, scale)
-    err = float(np.max(np.abs(gpu_out[b, g * w.G:(g + 1) * w.G] - ref)))
-    assert err <= OUT_TOL[w.dtype], f"unit b={b} g={g}: max-abs error {err} > {OUT_TOL[w.dtype]}"
+    err = float(np.max(np.abs(np.asarray(gpu_out_g) - ref)))
+    assert err <= OUT_TOL[dtype], f"{what}: max-abs error {err} > {OUT_TOL[dtype]}"
     if swaps == 0:
         assert float(np.max(np.abs(ref - out_ref))) == 0.0
     return swaps, err
+
+
+def check_unit(w, q, K, V, ch, b, g, gpu_out, gpu_idx, scale=None):
+    """Full parity of one unit of a workload: kept indices by the index rule, output vs the
+    oracle's attention over the GPU's kept set.  Returns (tie swaps, max-abs error)."""
+    qg, Kf, Vf = unit_inputs(w, q, K, V, b, g)
+    return check_row(qg, Kf, Vf, ch[g], w.k_units, w.block, w.T, gpu_out[b, g * w.G:(g + 1) * w.G],
+                     gpu_idx[b, g], w.dtype, f"unit b={b} g={g}", scale)
 
 
 def check_threshold_parity(gpu_idx, gpu_count, u_oracle, tau, k_max, what=""):

@@ -1,20 +1,30 @@
-"""The one-pass decode step against the two-kernel form, bit for bit.
+"""The one-pass decode step: against the oracle on every row, and against the two-kernel
+form bit for bit.
 
 Token-level rows that one fused workgroup handles alone (a single split and head
 chunk: at least 256 row-chunks) are decoded by one kernel that scores each row from
-its label rows itself.  The two phase calls still run the score kernel and then the
-fused kernel from the stored scores.  Both accumulate each score the same way, so on
-the same inputs the one-call step must give the same indices, outputs and rebuilt
-label rows as the two phases, bit for bit.  The cases cover both label-row widths
-(16 and 32 bytes) in both element types, groups of 1, 2 and 4 query heads, every
-per-thread item count of the fused kernel, rows rebuilt from K, and a ragged batch.
-The oracle checks the one-pass path on its own in the 256-row case of the parity
-suite and at full size (batched_32k, ragged_16k).
+its label rows itself.  Every case first asserts that the shape takes that path
+(ds_decode_is_one_pass).  Every row of the one-call result is then checked against
+the float64 oracle on float64 copies of the same inputs: kept set by the index rule
+(boundary ties within 1e-6 relative of the oracle's k-th score), index slots past a
+short sequence's kept count -1, and output within 2e-3 (bf16) or 1e-5 (fp32) of the
+oracle's attention over the kept set.  The two phase calls still run the score kernel
+and then the fused kernel from the stored scores; both accumulate each score the same
+way, so on the same inputs the one-call step must give the same indices, outputs and
+rebuilt label rows as the two phases, bit for bit.  The cases cover both label-row
+widths (16 and 32 bytes) in both element types, groups of 1, 2 and 4 query heads,
+every per-thread item count of the fused kernel, rows rebuilt from K, and ragged
+batches.
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
 import pytest
 import torch
 
 import long_context_sparse_ds_amd as L
+from _helpers import check_row
 
 pytestmark = pytest.mark.gpu
 
@@ -59,11 +69,33 @@ def _inputs(dt, B, Hq, Hkv, T, r, seed):
     return q, K, V, ch
 
 
+def _check_against_oracle(dt, q, K, V, ch, lens, k, out, idx, name):
+    """Every (sequence, KV head) row of the one-call result against the oracle, on float64 copies
+    of the device inputs: row b keeps min(k, lens[b]) tokens of its first lens[b]."""
+    B, Hkv = K.shape[0], K.shape[1]
+    G = q.shape[1] // Hkv
+    qh, Kh, Vh = (t.float().cpu().numpy() for t in (q, K, V))
+    chh, outh, idxh = ch.cpu().numpy(), out.cpu().numpy(), idx.cpu().numpy()
+
+    def row(u):
+        b, g = divmod(u, Hkv)
+        Tb = int(lens[b])
+        return check_row(qh[b, g * G:(g + 1) * G].astype(np.float64), Kh[b, g, :Tb].astype(np.float64),
+                         Vh[b, g, :Tb].astype(np.float64), chh[g], min(k, Tb), 1, Tb,
+                         outh[b, g * G:(g + 1) * G], idxh[b, g], dt, f"{name} row ({b},{g})")
+
+    n = max(1, min(16, len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(n) as ex:
+        res = list(ex.map(row, range(B * Hkv)))
+    return sum(r[0] for r in res), max(r[1] for r in res)
+
+
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_one_pass_matches_two_kernels(case):
     name, dt, B, Hq, Hkv, T, r, k, n_new, ragged = case
     _say(f"{name}: B={B} Hq={Hq} Hkv={Hkv} T={T} r={r} k={k} rebuilt={n_new} ragged={ragged}")
     q, K, V, ch = _inputs(dt, B, Hq, Hkv, T, r, seed=sum(map(ord, name)))
+    assert L.ds_decode_is_one_pass(B, Hq, Hkv, 128, T, 1, k, r, dt), f"{name}: not a one-pass shape"
     label = L.ds_build_label_cache(K, ch)
     torch.cuda.synchronize()
     raw = label.view(torch.int16) if dt == "bf16" else label.view(torch.int32)
@@ -99,6 +131,9 @@ def test_one_pass_matches_two_kernels(case):
     ii = i1.view(-1, k)
     valid = ii >= 0   # index slots past a short sequence's kept count are -1
     assert valid[:, 0].all() and ((ii[:, 1:] > ii[:, :-1]) | ~valid[:, 1:]).all()
-    _say(f"{name}: identical; first row kept {int(valid[0].sum())}")
+    lens_h = lens.tolist() if ragged else [T] * B
+    swaps, err = _check_against_oracle(dt, q, K, V, ch, lens_h, k, o1, i1, name)
+    _say(f"{name}: identical to the two phases; every row matches the oracle "
+         f"(tie swaps {swaps}, max-abs err {err:.3g}); first row kept {int(valid[0].sum())}")
     del q, K, V, label, lab1, lab2, ws1, ws2
     torch.cuda.empty_cache()

@@ -533,18 +533,34 @@ def test_hip_search_structure_and_monotone_closed_form():
     check_hip_structure(O)
 
 
+def check_hip_near_tie(ns):
+    """Two first tokens scoring 2^24 and 2^24 + 1 (equal once rounded to float32): the search ranks
+    the exact scores, so the higher one wins although the other starts lower."""
+    K = np.zeros((4, 4))
+    K[0, 0], K[2, 0] = 2.0 ** 24, 2.0 ** 24 + 1
+    assert [tuple(sp) for sp in ns.hip_search(np.array([[1.0, 0.0, 0.0, 0.0]]), K, 4, 1, 2)] == [(2, 4)]
+
+
+def test_hip_search_ranks_exact_scores():
+    check_hip_near_tie(O)
+
+
 def check_group_scores(ns, seed=14):
-    """Group score = float32 of the exact sum over heads of q_h . K_t (brute force with fsum)."""
+    """Group score = the sum over heads of q_h . K_t in float64, within a few float64 roundings of
+    the exact sum (brute force with fsum)."""
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((3, 16))
     K = rng.standard_normal((40, 16))
     toks = [0, 5, 39, 17]
-    got = ns.group_token_scores(q, K, toks)
-    want = [np.float32(math.fsum(float(q[h, c]) * float(K[t, c]) for h in range(3) for c in range(16))) for t in toks]
-    assert got.dtype == np.float32 and list(got) == want
+    got = np.asarray(ns.group_token_scores(q, K, toks))
+    assert got.dtype == np.float64
+    for t, v in zip(toks, got):
+        terms = [float(q[h, c]) * float(K[t, c]) for h in range(3) for c in range(16)]
+        bound = 64 * 2.0 ** -53 * math.fsum(abs(x) for x in terms)
+        assert abs(float(v) - math.fsum(terms)) <= bound, (t, v)
 
 
-def test_hip_group_scores_are_float32_of_exact_dot():
+def test_hip_group_scores_are_the_float64_dot():
     check_group_scores(O)
 
 
@@ -683,7 +699,7 @@ def _mut_unit_empty_nan(q_group, K, V, ch, k_max, tau, block=1, scale=None, T=No
     return out, kept, scores
 
 
-def _hip_variant(ties_high=False, floor_left=False, last_rep=False, extra=0, early_stop=False):
+def _hip_variant(ties_high=False, floor_left=False, last_rep=False, extra=0, early_stop=False, f32=False):
     def search(q_group, K, T, k, span):
         spans = [(i * T // k, (i + 1) * T // k) for i in range(k)]
         rep = (lambda s, e: e - 1) if last_rep else (lambda s, e: s)
@@ -695,7 +711,8 @@ def _hip_variant(ties_high=False, floor_left=False, last_rep=False, extra=0, ear
                     cand += [(s, m), (m, e)]
                 else:
                     cand.append((s, e))
-            keys = O.group_token_scores(q_group, K, [rep(s, e) for s, e in cand]).astype(np.float64)
+            keys = np.asarray(O.group_token_scores(q_group, K, [rep(s, e) for s, e in cand]),
+                              dtype=np.float32 if f32 else np.float64).astype(np.float64)
             idx = np.arange(len(cand))
             order = (idx[::-1][np.argsort(-keys[::-1], kind="stable")] if ties_high
                      else np.argsort(-keys, kind="stable"))
@@ -714,6 +731,7 @@ MUTANTS = [
     ("hip_search", _hip_variant(last_rep=True), check_golden_hip),
     ("hip_search", _hip_variant(extra=1), check_hip_structure),
     ("hip_search", _hip_variant(early_stop=True), check_hip_structure),
+    ("hip_search", _hip_variant(f32=True), check_hip_near_tie),
     ("group_token_scores", _mut_hip_one_head, check_group_scores),
     ("label_scores_positive", _mut_pos_signed, check_positive_scores_brute),
     ("label_scores_positive", _mut_pos_clip_after_sum, check_positive_scores_brute),
