@@ -161,6 +161,34 @@ ds_status ds_decode_sparse_attn(const void* q, const void* K, const void* V, voi
                                 int64_t T, int64_t t_append, int32_t block, int64_t k_units, float scale, float* out,
                                 int32_t* indices, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the static device scratch behind ds_decode_sparse_attn_noalloc. */
+#define DS_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * ds_decode_sparse_attn for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, and harnesses that forbid
+ * hipMalloc.  Same steps, kernels, arguments and results as
+ * ds_decode_sparse_attn, without the workspace arguments: the workspace is a
+ * static device array of DS_NOALLOC_SCRATCH_BYTES bytes inside the library,
+ * one copy per GPU, allocated when the library's device code is loaded onto
+ * that GPU and held until the process ends.  The call itself allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine); its first
+ * call on a device looks up that device's copy once (hipGetSymbolAddress,
+ * with the device current).  Shapes whose workspace
+ * (ds_decode_workspace_bytes) exceeds DS_NOALLOC_SCRATCH_BYTES are rejected
+ * with DS_ERR_WORKSPACE_TOO_SMALL before any HIP call.  Every call on a GPU
+ * shares that GPU's scratch and leaves its contents behind (the kernels clear
+ * what must start at zero), so calls that overlap on one GPU, on different
+ * streams or threads, race; calls in order on one stream do not.
+ * Errors: as ds_decode_sparse_attn, plus DS_ERR_HIP if the scratch cannot be
+ * found on the current device.
+ */
+ds_status ds_decode_sparse_attn_noalloc(const void* q, const void* K, const void* V, void* label,
+                                        const int32_t* channels_dev, int32_t r, ds_dtype dt, int32_t B, int32_t Hq,
+                                        int32_t Hkv, int32_t d, int64_t T_cap, int64_t T, int64_t t_append,
+                                        int32_t block, int64_t k_units, float scale, float* out, int32_t* indices,
+                                        void* stream);
+
 /*
  * The decode step for a batch of sequences of unequal lengths (GPU, async): the
  * incremental decode loop of serving, where the Double Sparsity page's online

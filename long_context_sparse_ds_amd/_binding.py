@@ -39,6 +39,9 @@ _SIGNATURES = {
     "ds_decode_sparse_attn": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                        _c_i32, _c_i64, _c_i64, _c_i64, _c_i32, _c_i64, _c_f32, _c_vp, _c_vp, _c_vp,
                                        _c_size, _c_vp]),
+    "ds_decode_sparse_attn_noalloc": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32,
+                                               _c_i32, _c_i32, _c_i64, _c_i64, _c_i64, _c_i32, _c_i64, _c_f32, _c_vp,
+                                               _c_vp, _c_vp]),
     "ds_decode_sparse_attn_ragged": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32,
                                               _c_i32, _c_i32, _c_i64, _c_i64, _c_vp, _c_i32, _c_i32, _c_i64, _c_f32,
                                               _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
@@ -245,6 +248,34 @@ def ds_decode_sparse_attn(q, K, V, label, channels, T: int, k_units: int, block:
                                        k_units, scale, _dev(out, "out"), _dev(indices, "indices"),
                                        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                                        _stream(stream)))
+    return out, indices
+
+
+DS_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def ds_decode_sparse_attn_noalloc(q, K, V, label, channels, T: int, k_units: int, block: int = 1, scale: float = 0.0,
+                                  out=None, indices=None, stream=None, t_append: int | None = None):
+    """ds_decode_sparse_attn with the library's static device scratch as its workspace (the call
+    allocates nothing on the device; pass out and indices to allocate nothing here either).
+    Returns (out fp32 [B, Hq, d], indices int32 [B, Hkv, k_units])."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    _, Hkv, T_cap, _ = K.shape
+    r = channels.shape[1]
+    dt = _dtype_code(q)
+    if K.dtype != q.dtype or V.dtype != q.dtype or label.dtype != q.dtype:
+        raise ValueError("q, K, V and label must share one dtype")
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if indices is None:
+        indices = torch.empty((B, Hkv, k_units), dtype=torch.int32, device=q.device)
+    if t_append is None:
+        t_append = T
+    _check(lib().ds_decode_sparse_attn_noalloc(_dev(q, "q"), _dev(K, "K"), _dev(V, "V"), _dev(label, "label"),
+                                               _dev(channels, "channels"), r, dt, B, Hq, Hkv, d, T_cap, T, t_append,
+                                               block, k_units, scale, _dev(out, "out"), _dev(indices, "indices"),
+                                               _stream(stream)))
     return out, indices
 
 

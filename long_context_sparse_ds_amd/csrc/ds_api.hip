@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "ds.h"
@@ -52,6 +53,36 @@ ds_status check_decode_shape(int B, int Hq, int Hkv, int d, int64_t T_cap, int64
                 (long long)n_units, (long long)k_units);
   if (int64_t(B) * Hkv > 65535)
     return fail(DS_ERR_UNSUPPORTED, "B * Hkv = %lld exceeds 65535 rows", (long long)(int64_t(B) * Hkv));
+  return DS_OK;
+}
+
+// Device scratch of ds_decode_sparse_attn_noalloc, for callers that cannot
+// allocate: one copy per GPU, held until the process ends.  Host code never
+// uses the array's name as an address: each device's copy is found once with
+// hipGetSymbolAddress (with that device current) and that pointer is used.
+// Every call on a GPU shares its copy, so calls that overlap on one GPU race.
+constexpr size_t kScratchBytes = size_t(DS_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+char* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+ds_status scratch_for_current_device(char*& ptr) {
+  int dev = -1;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess)
+    return fail(DS_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(DS_ERR_UNSUPPORTED, "device %d: the static scratch supports devices 0..%d", dev, kMaxDevices - 1);
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? static_cast<char*>(p) : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr)
+    return fail(DS_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                hipGetErrorString(g_scratch_err[dev]));
+  ptr = g_scratch_ptr[dev];
   return DS_OK;
 }
 
@@ -409,6 +440,21 @@ int32_t ds_decode_is_one_pass(int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int
   return one_pass_ok(ds::plan_decode(B, Hq, Hkv, T, block, k_units), block, r, dt) ? 1 : 0;
 }
 
+// The decode step's launches, once the call has been validated and planned.
+static ds_status decode_step(const void* q, const void* K, const void* V, void* label, const int32_t* channels_dev,
+                             int32_t r, ds_dtype dt, int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t T_cap,
+                             int64_t T, int64_t t_append, int32_t block, int64_t k_units, float scale, float* out,
+                             int32_t* indices, char* ws, const ds::DecodePlan& pl, hipStream_t s) {
+  if (!(scale > 0.f)) scale = 1.0f / std::sqrt(float(d));
+  if (one_pass_ok(pl, block, r, dt))
+    return decode_one_pass(q, K, V, label, channels_dev, r, dt, Hq, Hkv, T_cap, T, t_append, k_units, scale, pl,
+                           out, indices, ws, s);
+  if (ds_status st = decode_score_stage(q, K, label, channels_dev, r, dt, B, Hq, Hkv, T_cap, T, t_append, block, pl,
+                                        ws, s))
+    return st;
+  return decode_select_stage(q, K, V, dt, B, Hq, Hkv, T_cap, T, block, k_units, scale, pl, out, indices, ws, s);
+}
+
 ds_status ds_decode_sparse_attn(const void* q, const void* K, const void* V, void* label, const int32_t* channels_dev,
                                 int32_t r, ds_dtype dt, int32_t B, int32_t Hq, int32_t Hkv, int32_t d, int64_t T_cap,
                                 int64_t T, int64_t t_append, int32_t block, int64_t k_units, float scale, float* out,
@@ -418,16 +464,34 @@ ds_status ds_decode_sparse_attn(const void* q, const void* K, const void* V, voi
   if (ds_status st = check_decode_call(q, K, V, label, channels_dev, r, dt, B, Hq, Hkv, d, T_cap, T, t_append, block,
                                        k_units, out, indices, workspace, workspace_bytes, true, true, pl))
     return st;
-  if (!(scale > 0.f)) scale = 1.0f / std::sqrt(float(d));
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  if (one_pass_ok(pl, block, r, dt))
-    return decode_one_pass(q, K, V, label, channels_dev, r, dt, Hq, Hkv, T_cap, T, t_append, k_units, scale, pl,
-                           out, indices, ws, s);
-  if (ds_status st = decode_score_stage(q, K, label, channels_dev, r, dt, B, Hq, Hkv, T_cap, T, t_append, block, pl,
-                                        ws, s))
+  return decode_step(q, K, V, label, channels_dev, r, dt, B, Hq, Hkv, d, T_cap, T, t_append, block, k_units, scale,
+                     out, indices, static_cast<char*>(workspace), pl, static_cast<hipStream_t>(stream));
+}
+
+ds_status ds_decode_sparse_attn_noalloc(const void* q, const void* K, const void* V, void* label,
+                                        const int32_t* channels_dev, int32_t r, ds_dtype dt, int32_t B, int32_t Hq,
+                                        int32_t Hkv, int32_t d, int64_t T_cap, int64_t T, int64_t t_append,
+                                        int32_t block, int64_t k_units, float scale, float* out, int32_t* indices,
+                                        void* stream) {
+  g_err.clear();
+  // The shape's workspace must fit the scratch.  The placeholder workspace
+  // pointer passed to the shared checks is only tested for null and alignment.
+  if (ds_status st = check_decode_shape(B, Hq, Hkv, d, T_cap, T, block, k_units)) return st;
+  const size_t need = ds::plan_decode(B, Hq, Hkv, T, block, k_units).total_bytes;
+  if (need > kScratchBytes)
+    return fail(DS_ERR_WORKSPACE_TOO_SMALL,
+                "this shape needs %zu bytes of workspace, more than the %zu-byte static device scratch of the "
+                "no-allocation entry point; call ds_decode_sparse_attn with a workspace instead",
+                need, kScratchBytes);
+  ds::DecodePlan pl;
+  if (ds_status st = check_decode_call(q, K, V, label, channels_dev, r, dt, B, Hq, Hkv, d, T_cap, T, t_append, block,
+                                       k_units, out, indices, reinterpret_cast<void*>(uintptr_t(256)), kScratchBytes,
+                                       true, true, pl))
     return st;
-  return decode_select_stage(q, K, V, dt, B, Hq, Hkv, T_cap, T, block, k_units, scale, pl, out, indices, ws, s);
+  char* ws = nullptr;
+  if (ds_status st = scratch_for_current_device(ws)) return st;
+  return decode_step(q, K, V, label, channels_dev, r, dt, B, Hq, Hkv, d, T_cap, T, t_append, block, k_units, scale,
+                     out, indices, ws, pl, static_cast<hipStream_t>(stream));
 }
 
 // Validation shared by the ragged-length calls, after check_decode_call.

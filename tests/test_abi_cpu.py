@@ -216,3 +216,27 @@ def test_calibrate_matches_oracle_on_ties_and_small_shapes():
         kc = rng.integers(-2, 3, size=(Hkv, n_k, d)).astype(np.float32)
         for r in sorted({1, d // 3 + 1, d}):
             np.testing.assert_array_equal(L.ds_calibrate_channels(qc, kc, r), O.calibrate_channels(qc, kc, Hkv, r))
+
+
+def _noalloc(B=1, Hq=32, Hkv=32, T=16384, k=1024, block=1, q=FAKE):
+    return L.lib().ds_decode_sparse_attn_noalloc(q, FAKE, FAKE, FAKE, FAKE, 16, L.DS_DTYPE_BF16, B, Hq, Hkv, 128, T, T,
+                                                 T, block, k, 0.0, FAKE, FAKE, None)
+
+
+def test_noalloc_scratch_size_matches_header():
+    import re
+    with open(L._binding.HEADER) as f:
+        m = re.search(r"#define\s+DS_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", f.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == L.DS_NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch_before_any_hip_call():
+    # 512 rows of 32,768 scores need 64 MiB of workspace: more than the static scratch.
+    assert L.ds_decode_workspace_bytes(16, 32, 32, 128, 32768, 1, 2048) > L.DS_NOALLOC_SCRATCH_BYTES
+    assert _noalloc(B=16, T=32768, k=2048) == L.DS_ERR_WORKSPACE_TOO_SMALL
+    assert "static device scratch" in L.ds_last_error()
+    # argument checks come first, as for the workspace form
+    assert _noalloc(q=None) == L.DS_ERR_INVALID_ARGUMENT
+    assert _noalloc(k=0) == L.DS_ERR_INVALID_ARGUMENT
+    # the headline shape fits
+    assert L.ds_decode_workspace_bytes(1, 32, 32, 128, 16384, 1, 1024) <= L.DS_NOALLOC_SCRATCH_BYTES
