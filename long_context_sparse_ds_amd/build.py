@@ -22,7 +22,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdsparse.so")
 
-HIP_SOURCES = ["ds_api.hip", "pack.hip", "score.hip", "select.hip", "selattn.hip", "attn.hip", "hip_search.hip"]
+HIP_SOURCES = ["ds_api.hip", "pack.hip", "score.hip", "select.hip", "selattn.hip", "bucket.hip", "attn.hip",
+               "hip_search.hip"]
 CPP_SOURCES = ["calibrate.cpp"]
 ARCH = "gfx950"
 

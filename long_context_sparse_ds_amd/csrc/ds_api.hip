@@ -148,6 +148,10 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t T, int block, int64_t k_u
   p.tile_hist = (p.fused && p.tiles <= kMaxHistTiles && block <= 4 && p.sp.n_split * p.sp.head_chunks > 1) ||
                 (p.partitioned && block == 1);
   p.cand_hist = p.partitioned && block == 1 && parts <= kMaxHistTiles;
+  // Token-level rows over several fused workgroups take the sorted tile lists
+  // and the bucket kernel: a split then reads the tiles' prefixes, its share of
+  // the kept ids and the boundary digit's candidates instead of the row.
+  p.bucketed = p.fused && block == 1 && p.tile_hist;
   p.sp_idx = plan_split(p.rows, G, p.kv_virtual, false);
   const int max_split = p.sp.n_split > p.sp_idx.n_split ? p.sp.n_split : p.sp_idx.n_split;
   const int64_t bhs = int64_t(B) * Hq * max_split;
@@ -387,9 +391,12 @@ static ds_status decode_score_stage(const void* q, const void* K, void* label, c
   float* scores = reinterpret_cast<float*>(ws + pl.off_scores);
   uint16_t* tile_hist = pl.tile_hist ? reinterpret_cast<uint16_t*>(ws + pl.off_tile_hist) : nullptr;
   unsigned* tickets = pl.fused || pl.partitioned ? reinterpret_cast<unsigned*>(ws + pl.off_tickets) : nullptr;
+  // The plain top-k step of bucketed shapes writes sorted tile lists; ragged and
+  // threshold calls keep the unit-order scores and histograms.
+  const bool sorted = pl.bucketed && seq_lens == nullptr && !positive;
   return hip_status(ds::launch_scores(q, label, K, channels_dev, r, dt == DS_DTYPE_BF16, B, Hq, Hkv, T_cap, T,
                                       t_append, block, scores, pl.score_ld, tile_hist, tickets, pl.sp.head_chunks,
-                                      seq_lens, n_append, positive, s),
+                                      seq_lens, n_append, positive, s, sorted),
                     "score launch");
 }
 
@@ -400,6 +407,12 @@ static ds_status decode_select_stage(const void* q, const void* K, const void* V
                                      int32_t* counts = nullptr) {
   const float* scores = reinterpret_cast<const float*>(ws + pl.off_scores);
   const uint16_t* tile_hist = pl.tile_hist ? reinterpret_cast<const uint16_t*>(ws + pl.off_tile_hist) : nullptr;
+  if (pl.bucketed && seq_lens == nullptr && counts == nullptr)
+    return hip_status(
+        ds::launch_bucket_attention(q, K, V, dt == DS_DTYPE_BF16, reinterpret_cast<const uint32_t*>(scores), tile_hist, Hq, Hkv, T_cap, k_units, scale, pl, indices,
+                                    reinterpret_cast<float*>(ws + pl.off_acc), reinterpret_cast<float*>(ws + pl.off_ml),
+                                    out, reinterpret_cast<unsigned*>(ws + pl.off_tickets), s),
+        "bucket select-attention launch");
   return run_select_attend(q, K, V, dt, B, Hq, Hkv, T_cap, T, block, k_units, scores, pl.score_ld, tile_hist, true,
                            scale, pl, out, indices, ws, s, seq_lens, tau, counts);
 }

@@ -8,6 +8,9 @@
 namespace ds {
 
 constexpr int kHeadDim = 128;
+// MI355X: 8 XCDs, each with its own L2.  Workgroups are dealt to the XCDs
+// round-robin by linear id, so in a grid (8, Y, Z) blockIdx.x is the XCD.
+constexpr int kXcds = 8;
 
 // Rows of up to this many units take the fused select+attention kernel, whose
 // workgroups (1024 threads) hold a whole score row in registers.
@@ -51,11 +54,14 @@ struct DecodePlan {
   int64_t cand_ld;     // partitioned: row stride of the candidate scores, floats (multiple of 64)
   bool cand_hist;      // partitioned: the first stage writes its candidates' top-digit histograms
   bool tile_hist;      // the score kernel writes per-tile key histograms for the fused kernel
+  bool bucketed;       // token-level rows over several fused workgroups: sorted tile lists and the
+                       // bucket kernel (for the plain top-k step; ragged and threshold calls keep the
+                       // histogram form)
   int64_t tiles;       // score tiles per row
   SplitPlan sp;        // splits of the decode call
   SplitPlan sp_idx;    // splits of the attention-from-indices call
-  size_t off_scores, off_tile_hist, off_acc, off_ml, off_tickets, off_cand_score, off_cand_id, off_cand_hist,
-      total_bytes;
+  size_t off_scores, off_tile_hist, off_acc, off_ml, off_tickets, off_cand_score, off_cand_id,
+      off_cand_hist, total_bytes;
 };
 
 DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t T, int block, int64_t k_units);
@@ -73,10 +79,17 @@ hipError_t launch_pack(const void* K, int is_bf16, int B, int Hkv, int64_t T_cap
 // seq_lens (may be null): device int32 [B]; sequence b then holds seq_lens[b]
 // tokens (clamped to [1, T]), its last n_append rows are rebuilt (t_append is
 // ignored), and its scores past its length are written as -inf up to T.
+// sorted (token-level rows, not ragged or positive, tile_hist given): the
+// sorted-list form.  Tile i of a row writes its units in descending order of
+// top score digit, as 32-bit words (score key bits 20..0 above the 11-bit
+// tile-local id) at ((uint32_t*)scores)[row * ld + 2048 i + e]; tile_hist then
+// holds each tile's exclusive descending prefix P[b] (units whose top digit
+// exceeds b) instead of counts.
 hipError_t launch_scores(const void* q, void* label, const void* K, const int32_t* ch, int r, int is_bf16, int B,
                          int Hq, int Hkv, int64_t T_cap, int64_t T, int64_t t_append, int block, float* scores,
                          int64_t ld, uint16_t* tile_hist, unsigned* tickets, int tickets_per_row,
-                         const int32_t* seq_lens, int n_append, bool positive, hipStream_t s);
+                         const int32_t* seq_lens, int n_append, bool positive, hipStream_t s,
+                         bool sorted = false);
 
 hipError_t launch_select(const float* scores, int64_t rows, int64_t n, int64_t ld, int64_t k, int32_t* idx,
                          hipStream_t s);
@@ -125,6 +138,17 @@ hipError_t launch_select_attention(const void* q, const void* K, const void* V, 
                                    float* part_acc, float* part_ml, float* out, unsigned* tickets,
                                    const int32_t* seq_lens, float tau, int32_t* counts,
                                    const int32_t* unit_ids, hipStream_t s, const OnePass* one = nullptr);
+
+// Selection + attention of token-level rows from the score kernel's sorted
+// tile lists (pl.bucketed): per (row, head chunk, split), the top digit from
+// the tiles' prefixes, the boundary digit's candidates refined to the exact
+// threshold, this split's share of the kept tokens gathered and attended, its
+// tiles' slices of the ascending index list written, and the splits merged.
+// tickets: rows * head_chunks merge tickets, zero on entry (left zero).
+hipError_t launch_bucket_attention(const void* q, const void* K, const void* V, int is_bf16, const uint32_t* slist,
+                                   const uint16_t* tprefix, int Hq, int Hkv, int64_t T_cap,
+                                   int64_t k_units, float scale, const DecodePlan& pl, int32_t* indices,
+                                   float* part_acc, float* part_ml, float* out, unsigned* tickets, hipStream_t s);
 
 hipError_t launch_zero_u32(unsigned* p, int64_t n, hipStream_t s);
 

@@ -19,6 +19,16 @@
 // heads are accumulated in double, so here too the float32 result is the
 // exact value rounded once (up to double rounding of the sums).
 //
+// SORT (token-level rows split over several workgroups of the fused kernel):
+// instead of the scores in unit order and a histogram, each tile writes its
+// units in descending order of the top 11 bits of their score keys (a counting
+// sort: the histogram's LDS atomics return each unit's rank within its bin),
+// one 32-bit word per unit: the key's low 21 bits above the 11-bit tile-local
+// id (the top 11 bits are the digit, known from the unit's place in the list);
+// plus the tile's exclusive descending prefix P[b] = number of units whose top
+// digit exceeds b.  The selection kernel then finds any digit's units of a
+// tile at a known offset without reading the rest of the row.
+//
 // Tokens in [t_append, T) first get their label rows rebuilt from K (the
 // per-step label-row append of the newest tokens, fused here so a decode step
 // is a single pass over the label cache); they are scored from the values just
@@ -26,6 +36,7 @@
 #include <type_traits>
 
 #include "label_dot.h"
+#include "select_dev.h"
 
 namespace ds {
 namespace {
@@ -82,20 +93,35 @@ __device__ __forceinline__ float append_row_pos(const TE* __restrict__ Krow, TE*
 // n_append rows are rebuilt, and its scores past its length are written as
 // -inf up to T, so a row's score buffer is always T entries long.
 // POS: positive-only head aggregation (G <= 8, checked on the host).
-template <typename TE, int R, bool RAGGED, bool POS>
+// Grid: (8, tiles, rows / 8) when xcd_rows (row = 8 z + x, tile = y: every
+// tile of a row runs on the XCD of the fused kernel's splits of that row, whose
+// L2 then holds what this kernel wrote), else (tiles, Hkv, B).
+// SORT: sorted-list output (block == 1, tile_hist given), in the score buffer.
+template <typename TE, int R, bool RAGGED, bool POS, bool SORT>
 __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ q, TE* __restrict__ label,
                                                          const int32_t* __restrict__ ch, int64_t T_cap, int T,
                                                          int t_append, int G, int Hkv, int r, int block,
                                                          const TE* __restrict__ Kc, float* __restrict__ scores,
                                                          int64_t ld, uint16_t* __restrict__ tile_hist,
                                                          unsigned* __restrict__ tickets, int tickets_per_row,
-                                                         const int32_t* __restrict__ seq_lens, int n_append) {
+                                                         const int32_t* __restrict__ seq_lens, int n_append,
+                                                         int xcd_rows, int n_tiles) {
   // 32-bit index math throughout (T < 2^31 is checked on the host); 64-bit
-  // only for element offsets.  Grid (tiles, Hkv, B): no division to find the row.
-  const uint32_t g = blockIdx.y, b = blockIdx.z;
-  const uint32_t row = b * uint32_t(Hkv) + g;
+  // only for element offsets.
+  uint32_t row, tile, g, b;
+  if (xcd_rows) {
+    row = blockIdx.z * uint32_t(kXcds) + blockIdx.x;
+    tile = blockIdx.y;
+    b = row / uint32_t(Hkv);
+    g = row - b * uint32_t(Hkv);
+  } else {
+    tile = blockIdx.x;
+    g = blockIdx.y;
+    b = blockIdx.z;
+    row = b * uint32_t(Hkv) + g;
+  }
   TE* L = label + int64_t(row) * T_cap * r;
-  const int t0 = int(blockIdx.x) * kTile + int(threadIdx.x);
+  const int t0 = int(tile) * kTile + int(threadIdx.x);
   int Ti = T, ta = t_append;
   if constexpr (RAGGED) {
     Ti = min(max(seq_lens[b], 1), T);
@@ -135,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
   static_assert(kHeadDim * sizeof(TE) == 64 * sizeof(RowWord), "one row per wavefront, one word per lane");
   constexpr int kPreRows = kThreads / 64;
   __shared__ RowWord krow[kPreRows][64];
-  const int tile0 = int(blockIdx.x) * kTile;
+  const int tile0 = int(tile) * kTile;
   const int a_lo = max(ta, tile0), a_hi = min(Ti, tile0 + kTile);   // appended tokens in this tile
   const int wv = int(threadIdx.x) >> 6;
   const bool pre = !POS && a_lo + wv < a_hi;   // uniform over the wavefront
@@ -272,7 +298,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
       const int t = t0 + i * kThreads;
       uv[i] = u[i];
       has[i] = t < Ti;
-      if (t < T) out[t] = u[i];   // -inf past this sequence's length
+      if (!SORT && t < T) out[t] = u[i];   // -inf past this sequence's length
     }
   } else {
     // 64 consecutive tokens per wavefront, 64-aligned: blocks of `block` lanes.
@@ -287,7 +313,56 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
       if (t < T && (t & (block - 1)) == 0) out[t >> lb] = v;   // -inf past this sequence's length
     }
   }
-  if (tile_hist != nullptr) {
+  constexpr int per = kHistBins / kThreads;   // 4 bins per thread: one 8-byte store
+  static_assert(per == 4, "one uint2 of packed 16-bit counts per thread");
+  if constexpr (SORT) {
+    // Counting sort of the tile's units by top digit, highest digit first.
+    // The histogram's atomics return each unit's rank within its bin (any
+    // order: the selection kernel orders equal keys by unit id itself).
+    uint32_t bin[kTPT], rk[kTPT];
+#pragma unroll
+    for (int i = 0; i < kTPT; ++i) {
+      bin[i] = float_key(uv[i]) >> 21;
+      rk[i] = has[i] ? atomicAdd(&h[bin[i]], 1u) : 0u;
+    }
+    __syncthreads();
+    // Thread t owns bins 2047 - 4t down to 2044 - 4t, so thread order is
+    // descending digit order and one prefix sum gives every bin's start.
+    const int hb = kHistBins - 1 - per * int(threadIdx.x);
+    uint32_t c[per], sum = 0u;
+#pragma unroll
+    for (int j = 0; j < per; ++j) {
+      c[j] = h[hb - j];
+      sum += c[j];
+    }
+    __shared__ uint32_t wsum[kThreads / 64];
+    uint32_t tot;
+    uint32_t p = block_exclusive_scan<kThreads>(sum, wsum, tot);   // ends with a barrier
+    uint32_t P[per];
+#pragma unroll
+    for (int j = 0; j < per; ++j) {
+      P[j] = p;   // units of this tile whose top digit exceeds bin hb - j
+      h[hb - j] = p;
+      p += c[j];
+    }
+    uint16_t* dst = tile_hist + (int64_t(row) * n_tiles + tile) * kHistBins + (hb - (per - 1));
+    *reinterpret_cast<uint2*>(dst) = make_uint2(P[3] | (P[2] << 16), P[1] | (P[0] << 16));
+    __syncthreads();
+    __shared__ __align__(16) uint32_t sent[SORT ? kTile : 1];
+#pragma unroll
+    for (int i = 0; i < kTPT; ++i)
+      if (has[i])
+        sent[h[bin[i]] + rk[i]] = ((float_key(uv[i]) & 0x1FFFFFu) << 11) | uint32_t(threadIdx.x + i * kThreads);
+    __syncthreads();
+    const int n_tile = min(kTile, Ti - tile0);
+    uint32_t* sl = reinterpret_cast<uint32_t*>(out) + tile0;
+    if (n_tile == kTile) {
+      const int e = int(threadIdx.x) * kTPT;
+      *reinterpret_cast<uint4*>(sl + e) = *reinterpret_cast<const uint4*>(&sent[e]);
+    } else {
+      for (int e = threadIdx.x; e < n_tile; e += kThreads) sl[e] = sent[e];
+    }
+  } else if (tile_hist != nullptr) {
     // Dense histogram of the top 11 key bits of this tile's units (cleared
     // above, before the barriers), every bin written, so the buffer needs no
     // clearing between calls.
@@ -295,28 +370,31 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
     for (int i = 0; i < kTPT; ++i)
       if (has[i]) atomicAdd(&h[float_key(uv[i]) >> 21], 1u);
     __syncthreads();
-    constexpr int per = kHistBins / kThreads;   // 4 bins per thread: one 8-byte store
-    static_assert(per == 4, "one uint2 of packed 16-bit counts per thread");
     const int b0 = threadIdx.x * per;
-    uint16_t* dst = tile_hist + (int64_t(row) * gridDim.x + blockIdx.x) * kHistBins + b0;
+    uint16_t* dst = tile_hist + (int64_t(row) * n_tiles + tile) * kHistBins + b0;
     *reinterpret_cast<uint2*>(dst) = make_uint2(h[b0] | (h[b0 + 1] << 16), h[b0 + 2] | (h[b0 + 3] << 16));
   }
   // The row's merge tickets for the fused kernel that follows start at zero.
-  if (tickets != nullptr && blockIdx.x == 0)
+  if (tickets != nullptr && tile == 0)
     for (int i = threadIdx.x; i < tickets_per_row; i += kThreads) tickets[int64_t(row) * tickets_per_row + i] = 0u;
 }
 
-template <typename TE, bool RAGGED, bool POS>
+template <typename TE, bool RAGGED, bool POS, bool SORT>
 hipError_t dispatch_r(const TE* q, TE* label, const TE* Kc, const int32_t* ch, int r, int B, int Hq, int Hkv,
                       int64_t T_cap, int64_t T, int64_t t_append, int block, float* scores, int64_t ld,
                       uint16_t* tile_hist, unsigned* tickets, int tickets_per_row, const int32_t* seq_lens,
                       int n_append, hipStream_t s) {
-  const dim3 grid(unsigned((T + kTile - 1) / kTile), unsigned(Hkv), unsigned(B));
+  const unsigned tiles = unsigned((T + kTile - 1) / kTile);
+  const unsigned rows = unsigned(B) * unsigned(Hkv);
+  // A row's tiles spread over the XCDs (tile = blockIdx.x): measured faster for
+  // the label stream than keeping a row's tiles on one XCD.
+  const int xcd = 0;
+  const dim3 grid = xcd ? dim3(unsigned(kXcds), tiles, rows / kXcds) : dim3(tiles, unsigned(Hkv), unsigned(B));
   const bool vec = (int64_t(r) * sizeof(TE)) % 16 == 0;
 #define DS_SCORE(RR)                                                                                               \
-  hipLaunchKernelGGL((score_kernel<TE, RR, RAGGED, POS>), grid, dim3(kThreads), 0, s, q, label, ch, T_cap, int(T),     \
-                     int(t_append), Hq / Hkv, Hkv, r, block, Kc, scores, ld, tile_hist, tickets, tickets_per_row,  \
-                     seq_lens, n_append)
+  hipLaunchKernelGGL((score_kernel<TE, RR, RAGGED, POS, SORT>), grid, dim3(kThreads), 0, s, q, label, ch, T_cap,     \
+                     int(T), int(t_append), Hq / Hkv, Hkv, r, block, Kc, scores, ld, tile_hist, tickets,           \
+                     tickets_per_row, seq_lens, n_append, xcd, int(tiles))
   if (vec && r == 8) DS_SCORE(8);
   else if (vec && r == 16) DS_SCORE(16);
   else if (vec && r == 32) DS_SCORE(32);
@@ -329,15 +407,18 @@ template <typename TE>
 hipError_t dispatch(const TE* q, TE* label, const TE* Kc, const int32_t* ch, int r, int B, int Hq, int Hkv,
                     int64_t T_cap, int64_t T, int64_t t_append, int block, float* scores, int64_t ld,
                     uint16_t* tile_hist, unsigned* tickets, int tickets_per_row, const int32_t* seq_lens,
-                    int n_append, bool positive, hipStream_t s) {
+                    int n_append, bool positive, bool sorted, hipStream_t s) {
   if (positive)
-    return dispatch_r<TE, false, true>(q, label, Kc, ch, r, B, Hq, Hkv, T_cap, T, t_append, block, scores, ld,
-                                       tile_hist, tickets, tickets_per_row, nullptr, 0, s);
+    return dispatch_r<TE, false, true, false>(q, label, Kc, ch, r, B, Hq, Hkv, T_cap, T, t_append, block, scores,
+                                              ld, tile_hist, tickets, tickets_per_row, nullptr, 0, s);
   if (seq_lens != nullptr)
-    return dispatch_r<TE, true, false>(q, label, Kc, ch, r, B, Hq, Hkv, T_cap, T, t_append, block, scores, ld,
-                                       tile_hist, tickets, tickets_per_row, seq_lens, n_append, s);
-  return dispatch_r<TE, false, false>(q, label, Kc, ch, r, B, Hq, Hkv, T_cap, T, t_append, block, scores, ld,
-                                      tile_hist, tickets, tickets_per_row, nullptr, 0, s);
+    return dispatch_r<TE, true, false, false>(q, label, Kc, ch, r, B, Hq, Hkv, T_cap, T, t_append, block, scores,
+                                              ld, tile_hist, tickets, tickets_per_row, seq_lens, n_append, s);
+  if (sorted)
+    return dispatch_r<TE, false, false, true>(q, label, Kc, ch, r, B, Hq, Hkv, T_cap, T, t_append, block, scores,
+                                              ld, tile_hist, tickets, tickets_per_row, nullptr, 0, s);
+  return dispatch_r<TE, false, false, false>(q, label, Kc, ch, r, B, Hq, Hkv, T_cap, T, t_append, block, scores,
+                                             ld, tile_hist, tickets, tickets_per_row, nullptr, 0, s);
 }
 
 }  // namespace
@@ -345,14 +426,14 @@ hipError_t dispatch(const TE* q, TE* label, const TE* Kc, const int32_t* ch, int
 hipError_t launch_scores(const void* q, void* label, const void* K, const int32_t* ch, int r, int is_bf16, int B,
                          int Hq, int Hkv, int64_t T_cap, int64_t T, int64_t t_append, int block, float* scores,
                          int64_t ld, uint16_t* tile_hist, unsigned* tickets, int tickets_per_row,
-                         const int32_t* seq_lens, int n_append, bool positive, hipStream_t s) {
+                         const int32_t* seq_lens, int n_append, bool positive, hipStream_t s, bool sorted) {
   if (is_bf16)
     return dispatch(static_cast<const uint16_t*>(q), static_cast<uint16_t*>(label), static_cast<const uint16_t*>(K),
                     ch, r, B, Hq, Hkv, T_cap, T, t_append, block, scores, ld, tile_hist, tickets, tickets_per_row,
-                    seq_lens, n_append, positive, s);
+                    seq_lens, n_append, positive, sorted, s);
   return dispatch(static_cast<const float*>(q), static_cast<float*>(label), static_cast<const float*>(K), ch, r, B,
                   Hq, Hkv, T_cap, T, t_append, block, scores, ld, tile_hist, tickets, tickets_per_row, seq_lens,
-                  n_append, positive, s);
+                  n_append, positive, sorted, s);
 }
 
 }  // namespace ds

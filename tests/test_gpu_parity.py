@@ -697,3 +697,71 @@ def test_decode_long_rows_two_stage(w):
     for b in range(w.B):
         for g in range(w.Hkv):
             check_unit(w, q, K, V, ch, b, g, out, idx)
+
+
+BUCKET_ADV_SHAPES = [(3000, 1000), (16384, 1024), (30000, 9000)]
+
+
+def _bf16_adversarial_column(kind, n, rng):
+    """bf16 bit patterns for one K column (the tokens' scores, up to a factor of 2)."""
+    if kind == "one_digit":     # every score in one top digit: all are candidates
+        return dsgen.f32_to_bf16_bits((1.0 + rng.random(n) * 0.2).astype(np.float32))
+    if kind == "equal":         # one value: the k lowest ids are kept
+        return np.full(n, dsgen.f32_to_bf16_bits(np.float32([-2.75]))[0], np.uint16)
+    if kind == "zeros":         # +0.0 / -0.0 are one key; a few positives above them
+        bits = np.where(rng.random(n) < 0.5, 0x8000, 0x0000).astype(np.uint16)
+        bits[::97] = 0x3F80     # 1.0
+        return bits
+    if kind == "denormal":      # bf16 subnormals of both signs (exponent field 0)
+        return (rng.integers(1, 128, size=n) | np.where(rng.random(n) < 0.5, 0x8000, 0)).astype(np.uint16)
+    if kind == "boundaries":    # powers of two and their bf16 neighbours: values on the 11-bit digit edges
+        sign = np.where(rng.random(n) < 0.3, 0x8000, 0).astype(np.int64)
+        expo = rng.integers(124, 131, size=n).astype(np.int64)   # 2^-3 .. 2^3
+        base = sign | (expo << 7)
+        step = rng.integers(-1, 2, size=n)
+        return np.clip(base + step, 0, 0xFFFF).astype(np.uint16)
+    if kind == "ints":          # heavy exact ties everywhere, also at the k-th score
+        return dsgen.f32_to_bf16_bits(rng.integers(-6, 7, size=n).astype(np.float32))
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind", ["one_digit", "equal", "zeros", "denormal", "boundaries", "ints"])
+def test_decode_bucketed_adversarial_scores(kind):
+    """The whole decode step of rows split over several workgroups (the score kernel's
+    sorted tile lists, then the selection from them) on scores built to stress it: q is
+    the first unit vector in every head and the label channels are 0..r-1, so a token's
+    score is G times K[t, 0], which is set to a bf16 pattern of the given kind (all in one
+    top digit, all equal, signed zeros, subnormals, values on digit edges, small
+    integers).  Kept ids must equal the oracle's exactly (ties to the lower id), outputs
+    within 2e-3."""
+    Hq, Hkv, r = 4, 2, 16
+    G = Hq // Hkv
+    for T, k in BUCKET_ADV_SHAPES:
+        rng = np.random.default_rng(zlib.crc32(f"{kind}{T}".encode()))
+        w = Workload(f"badv_{kind}_{T}", "bf16", B=1, Hq=Hq, Hkv=Hkv, d=128, T=T, r=r, block=1, k_units=k,
+                     seed_base=28000 + T)
+        assert L.ds_decode_workspace_bytes(1, Hq, Hkv, 128, T, 1, k) > 0
+        _say(f"{w.name} k={k}")
+        _, K, V = dsgen.gen_cache(w)
+        K = np.ascontiguousarray(K)
+        for g in range(Hkv):
+            K[0, g, :T, 0] = _bf16_adversarial_column(kind, T, rng)
+        qf = np.zeros((1, Hq, 128), np.float32)
+        qf[:, :, 0] = 1.0
+        q = dsgen.f32_to_bf16_bits(qf)
+        ch = np.tile(np.arange(r, dtype=np.int32), (Hkv, 1))
+        qd, Kd, Vd = to_device(q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16")
+        chd = torch.from_numpy(ch).cuda()
+        label = L.ds_build_label_cache(Kd, chd)
+        out, idx = L.ds_decode_sparse_attn(qd, Kd, Vd, label, chd, T, k, 1)
+        torch.cuda.synchronize()
+        out, idx = out.cpu().numpy(), idx.cpu().numpy()
+        for g in range(Hkv):
+            qg, Kg, Vg = unit_inputs(w, q, K, V, 0, g)
+            u = O.label_scores(qg, O.label_rows(Kg, ch[g]), ch[g])
+            np.testing.assert_array_equal(u, G * Kg[:, 0])   # the construction above
+            want = O.select_topk(u, k)
+            np.testing.assert_array_equal(idx[0, g], want, err_msg=f"{w.name} g={g}")
+            ref = O.attend(qg, Kg, Vg, want, O.default_scale(128))
+            err = float(np.max(np.abs(out[0, g * G:(g + 1) * G] - ref)))
+            assert err <= OUT_TOL["bf16"], (w.name, g, err)
