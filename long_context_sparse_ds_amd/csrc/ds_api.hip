@@ -419,12 +419,12 @@ static ds_status decode_select_stage(const void* q, const void* K, const void* V
 
 // The one-pass form of the decode step, one kernel instead of two: token-level
 // rows that one fused workgroup handles alone (one split, one head chunk),
-// with label rows of 16 or 32 bytes.  The kernel scores each row from the label
+// with label rows of 16 or 32 bytes (or 64 in fp32).  The kernel scores each row from the label
 // cache itself, so the scores never go through memory.
 static bool one_pass_ok(const ds::DecodePlan& pl, int32_t block, int32_t r, ds_dtype dt) {
   const int row_bytes = r * (dt == DS_DTYPE_BF16 ? 2 : 4);
   return pl.fused && block == 1 && pl.sp.n_split == 1 && pl.sp.head_chunks == 1 && !pl.tile_hist &&
-         (row_bytes == 16 || row_bytes == 32);
+         (row_bytes == 16 || row_bytes == 32 || (row_bytes == 64 && dt == DS_DTYPE_F32));
 }
 
 static ds_status decode_one_pass(const void* q, const void* K, const void* V, void* label,

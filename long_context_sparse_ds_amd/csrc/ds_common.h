@@ -122,7 +122,7 @@ hipError_t launch_attention(const void* q, const void* K, const void* V, int is_
 // gathered as those units.
 // one (may be null): the one-pass form, for token-level rows that one
 // workgroup handles alone (pl.sp.n_split == 1, pl.sp.head_chunks == 1) and
-// label rows of 16 or 32 bytes: the kernel scores each row from the label
+// label rows of 16 or 32 bytes (64 for fp32): the kernel scores each row from the label
 // cache itself (rebuilding rows [t_append, T), or the last n_append of each
 // sequence, from K first) and scores / tile_hist are not read.
 struct OnePass {

@@ -219,7 +219,8 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
     // measured faster than 128 or 32, the other wavefronts covering the
     // latency), never more than the ITEMS passes there are: a unit of a pass
     // past ITEMS would have no slot.
-    constexpr int CB = (LNV == 1 ? 4 : 2) < ITEMS ? (LNV == 1 ? 4 : 2) : ITEMS;
+    constexpr int CB0 = LNV == 1 ? 4 : LNV == 2 ? 2 : 1;
+    constexpr int CB = CB0 < ITEMS ? CB0 : ITEMS;
     static_assert(ITEMS % CB == 0, "whole batches of passes");
     __shared__ double qs_l[R];
     __shared__ int ch_l[R];
@@ -659,17 +660,22 @@ hipError_t launch_kernel(const FusedArgs& a, dim3 grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-// One pass when a label cache is given: LNV 16-byte words per label row.
+// One pass when a label cache is given: LNV 16-byte words per label row (1 or
+// 2; 4 for fp32).
 template <typename TE, int NT, int ITEMS, int HC>
 hipError_t launch_one(const FusedArgs& a, dim3 grid, hipStream_t s) {
   const int lnv = a.label == nullptr ? 0 : a.r * int(sizeof(TE)) / 16;
   if (a.seq_lens != nullptr) {
     if (lnv == 1) return launch_kernel<TE, NT, ITEMS, HC, true, 1>(a, grid, s);
     if (lnv == 2) return launch_kernel<TE, NT, ITEMS, HC, true, 2>(a, grid, s);
+    if constexpr (sizeof(TE) == 4)   // 64-byte rows (fp32, r = 16); in bf16 (r = 32) the kernel would spill
+      if (lnv == 4) return launch_kernel<TE, NT, ITEMS, HC, true, 4>(a, grid, s);
     return launch_kernel<TE, NT, ITEMS, HC, true, 0>(a, grid, s);
   }
   if (lnv == 1) return launch_kernel<TE, NT, ITEMS, HC, false, 1>(a, grid, s);
   if (lnv == 2) return launch_kernel<TE, NT, ITEMS, HC, false, 2>(a, grid, s);
+  if constexpr (sizeof(TE) == 4)
+    if (lnv == 4) return launch_kernel<TE, NT, ITEMS, HC, false, 4>(a, grid, s);
   return launch_kernel<TE, NT, ITEMS, HC, false, 0>(a, grid, s);
 }
 

@@ -12,7 +12,7 @@ oracle's attention over the kept set.  The two phase calls still run the score k
 and then the fused kernel from the stored scores; both accumulate each score the same
 way, so on the same inputs the one-call step must give the same indices, outputs and
 rebuilt label rows as the two phases, bit for bit.  The cases cover both label-row
-widths (16 and 32 bytes) in both element types, groups of 1, 2 and 4 query heads,
+widths (16 and 32 bytes) in both element types and 64-byte fp32 rows, groups of 1, 2 and 4 query heads,
 every per-thread item count of the fused kernel, rows rebuilt from K, and ragged
 batches.
 """
@@ -40,7 +40,8 @@ def _say(msg):
     print(f"[case] {msg}", flush=True)
 
 
-# (name, dtype, B, Hq, Hkv, T, r, k, rows rebuilt, ragged); B * Hkv >= 256 rows, groups <= 4 heads
+# (name, dtype, B, Hq, Hkv, T, r, k, rows rebuilt, ragged); one split per row (B * Hkv >= 256 rows, or
+# k <= 64), groups <= 4 heads
 CASES = [
     ("bf16_r8_items32", "bf16", 64, 4, 4, 20000, 8, 700, 3, False),
     ("bf16_r16_g4_items16", "bf16", 64, 16, 4, 9000, 16, 300, 1, False),
@@ -53,6 +54,15 @@ CASES = [
     # edge shapes: rows of 5 tokens with 3 of them rebuilt, and every token kept (k = T)
     ("bf16_r8_T5", "bf16", 64, 4, 4, 5, 8, 3, 3, False),
     ("f32_r4_dense", "f32", 256, 1, 1, 40, 4, 40, 1, False),
+    # 64-byte label rows (fp32, r = 16), and the single tiny row whose 64 kept tokens make one split
+    ("f32_r16_items4", "f32", 256, 1, 1, 3000, 16, 100, 1, False),
+    ("f32_r16_g2_items8", "f32", 128, 4, 2, 6000, 16, 200, 2, False),
+    ("f32_r16_one_row", "f32", 1, 1, 1, 1024, 16, 64, 1, False),
+    # short rows: a group of 4, 16-byte rows at T < 1024, a ragged fp32 batch
+    ("bf16_r8_small_g4", "bf16", 64, 16, 4, 1000, 8, 60, 2, False),
+    ("bf16_r16_small", "bf16", 256, 1, 1, 777, 16, 50, 1, False),
+    ("f32_r4_small_ragged", "f32", 256, 2, 2, 1024, 4, 64, 1, True),
+    ("f32_r16_ragged", "f32", 256, 2, 2, 4000, 16, 150, 1, True),
     ("bf16_r8_ragged", "bf16", 64, 4, 4, 12000, 8, 400, 2, True),
     ("bf16_r16_ragged_g2", "bf16", 128, 4, 2, 6000, 16, 250, 1, True),
 ]
