@@ -60,17 +60,25 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-# The sources that build the decode step's two kernels (score_kernel, selattn_kernel) and plan their launches.
-DECODE_STEP_SOURCES = ("ds_api.hip", "ds_common.h", "label_dot.h", "score.hip", "select_dev.h", "selattn.hip")
+# The sources that build each timed stage's kernels and plan their launches: a recorded counter reading stays
+# valid while these files are unchanged (the other kernels' sources do not enter its digest).
+STAGE_SOURCES = {
+    "decode_score": ("ds_api.hip", "ds_common.h", "label_dot.h", "score.hip"),
+    "decode_select_attend": ("ds_api.hip", "ds_common.h", "select_dev.h", "fused_dev.h", "select.hip", "selattn.hip",
+                             "bucket.hip", "attn.hip"),
+    "decode_step_one_pass": ("ds_api.hip", "ds_common.h", "label_dot.h", "select_dev.h", "fused_dev.h",
+                             "selattn.hip"),
+    "hip_search": ("ds_api.hip", "ds_common.h", "hip_search.hip"),
+    "attention_from_indices": ("ds_api.hip", "ds_common.h", "attn.hip"),
+}
 
 
-def kernel_sources_digest() -> str:
-    """Digest of the sources of the decode step's kernels and their launch plan, to tell whether recorded
-    counters still describe those kernels (the other kernels' sources do not enter it)."""
+def kernel_sources_digest(stage: str) -> str:
+    """Digest of the sources of one stage's kernels and their launch plan."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "long_context_sparse_ds_amd", "csrc")
-    for name in DECODE_STEP_SOURCES:
+    for name in STAGE_SOURCES[stage]:
         h.update(name.encode())
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
@@ -79,11 +87,11 @@ def kernel_sources_digest() -> str:
 
 def recorded_traffic(workload: str, stage: str):
     """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by a copy kernel) and
-    recorded in profiles/, or None when no record matches the current kernel sources."""
+    recorded in profiles/, or None when no record matches the current sources of that stage's kernels."""
     path = os.path.join(ROOT, "profiles", f"decode_{workload}_hbm_traffic.md")
-    if not os.path.exists(path):
+    if not os.path.exists(path) or stage not in STAGE_SOURCES:
         return None
-    digest = kernel_sources_digest()
+    digest = kernel_sources_digest(stage)
     with open(path) as f:
         for line in f:
             if line.startswith("traffic-record:"):
@@ -229,10 +237,15 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--phases-only", action="store_true",
                     help="time only the step's own two phases, not the isolated reference stages (for counter runs)")
+    ap.add_argument("--sources-digest", choices=sorted(STAGE_SOURCES),
+                    help="print the source digest of one stage's kernels (the key of its traffic records) and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB ten times and exit (reference for "
                          "hardware byte counters)")
     args = ap.parse_args()
+    if args.sources_digest:
+        print(kernel_sources_digest(args.sources_digest))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this single-GPU build has no multi-GPU path "
@@ -545,7 +558,7 @@ def main():
         "stage_us": {PHASE_NAMES.get(k, k) if w.hip else k: round(v, 3) for k, v in kernel_us.items()},
         "roofline": {"bound": "hbm", "kernel": PHASE_NAMES.get(dominant, dominant) if w.hip else dominant, "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(w.name, dominant),
+                     "traffic": recorded_traffic(w.name, PHASE_NAMES.get(dominant, dominant) if w.hip else dominant),
                      "bytes_per_launch": stage_bytes[dominant], "avg_launch_us": round(kernel_us[dominant], 3)},
     }
 
@@ -581,7 +594,8 @@ def main():
             "cores": cb["cores"], "kind": "oracle",
             "sample": (f"float64 numpy oracle decode of {cb['sample_units']} of {cb['units']} (sequence, KV head) "
                        f"units, {cb['reps']} repetitions in {cb['elapsed_s']:.1f}s over a pool of {cb['cores']} "
-                       f"single-threaded workers; scaled to the whole step")}
+                       f"single-threaded workers (the pool is capped at 16 workers, one per host core the "
+                       f"process may use, and at the sample's unit count); scaled to the whole step")}
         result["gpu_over_cpu"] = round(cpu_us / us_step, 1)
     print(json.dumps(result), flush=True)
 
