@@ -52,7 +52,11 @@ typedef enum {
   DS_ERR_HIP = 4
 } ds_status;
 
-typedef enum { DS_DTYPE_F32 = 0, DS_DTYPE_BF16 = 1 } ds_dtype;
+/* Element type of q, K, V and the label cache.  A plain 32-bit integer rather
+ * than an enum type, so that any value a caller passes is a valid argument
+ * (values other than these two are rejected with DS_ERR_INVALID_ARGUMENT). */
+typedef int32_t ds_dtype;
+enum { DS_DTYPE_F32 = 0, DS_DTYPE_BF16 = 1 };
 
 /* Message of the last failed call on this thread ("" if none).  Valid until the
  * next ds_* call on the same thread. */

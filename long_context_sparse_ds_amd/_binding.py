@@ -14,7 +14,8 @@ import re
 import numpy as np
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libdsparse.so")
+# DSPARSE_LIB selects another build of the same library (the host-sanitizer build of build.py).
+LIB_PATH = os.environ.get("DSPARSE_LIB") or os.path.join(PKG, "libdsparse.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "ds.h")
 
 DS_OK = 0

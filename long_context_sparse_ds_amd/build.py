@@ -6,6 +6,14 @@ Every HIP source is compiled with hipcc for gfx950 only; the CPU calibration
 file with g++.  Packed-fp32 instruction selection is disabled for all device
 code, and kernel arguments are preloaded into SGPRs where supported.  Objects go to long_context_sparse_ds_amd/_build/, the shared library
 next to this file.
+
+    python -m long_context_sparse_ds_amd.build --sanitize-host
+
+builds libdsparse_hostsan.so under _build/: the host code of the boundary
+(argument checks, workspace planning, launch set-up in ds_api.hip, and the CPU
+calibration) instrumented with AddressSanitizer and UndefinedBehaviorSanitizer,
+linked with the ordinary kernel objects.  Device code is never instrumented.
+Load it with clang's ASan runtime preloaded and DSPARSE_LIB pointing at it.
 """
 from __future__ import annotations
 
@@ -21,6 +29,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdsparse.so")
+LIB_HOSTSAN = os.path.join(BUILD, "libdsparse_hostsan.so")
 
 HIP_SOURCES = ["ds_api.hip", "pack.hip", "score.hip", "select.hip", "selattn.hip", "bucket.hip", "attn.hip",
                "hip_search.hip"]
@@ -76,6 +85,60 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Sanitizers for the host pass only (each flag after -Xarch_host), so no device code is instrumented.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+CXX_SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"]
+
+
+def _llvm_clangxx() -> str:
+    for cand in ("/opt/rocm/llvm/bin/clang++", shutil.which("amdclang++")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("clang++ of the ROCm toolchain not found")
+
+
+def asan_runtime() -> str:
+    """Path of the shared ASan runtime (with UBSan) of the toolchain that builds the sanitized library."""
+    out = subprocess.run([_llvm_clangxx(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                         text=True).stdout.strip()
+    if not out or not os.path.exists(out):
+        raise RuntimeError("libclang_rt.asan-x86_64.so not found")
+    return out
+
+
+def _objects_current() -> bool:
+    """Whether build()'s objects exist and are newer than every source and header."""
+    objs = [os.path.join(BUILD, src.replace(".hip", ".o")) for src in HIP_SOURCES]
+    if not all(os.path.exists(o) for o in objs):
+        return False
+    srcs = [os.path.join(CSRC, f) for f in os.listdir(CSRC)] + [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE)]
+    return min(os.path.getmtime(o) for o in objs) >= max(os.path.getmtime(f) for f in srcs)
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """The library with its host boundary code under ASan + UBSan (kernel objects from build(), rebuilt first
+    if they are missing or older than the sources)."""
+    if not _objects_current():
+        build(verbose)
+    san = os.path.join(BUILD, "hostsan")
+    os.makedirs(san, exist_ok=True)
+    api = os.path.join(san, "ds_api.o")
+    cal = os.path.join(san, "calibrate.o")
+    flags = [f for f in hip_flags() if f != "-O3"] + ["-O1", "-g"]
+    _run([_hipcc(), "-x", "hip", "-c", *flags, *HOST_SANITIZE, os.path.join(CSRC, "ds_api.hip"), "-o", api], verbose)
+    _run([_llvm_clangxx(), "-O1", "-g", "-std=c++17", "-fPIC", *CXX_SANITIZE, f"-I{INCLUDE}", "-c",
+          os.path.join(CSRC, "calibrate.cpp"), "-o", cal], verbose)
+    kernels = [os.path.join(BUILD, src.replace(".hip", ".o")) for src in HIP_SOURCES if src != "ds_api.hip"]
+    tmp = LIB_HOSTSAN + ".tmp"
+    _run([_hipcc(), "-shared", f"--offload-arch={ARCH}", "-shared-libsan", *HOST_SANITIZE, "-o", tmp, api, cal,
+          *kernels], verbose)
+    os.replace(tmp, LIB_HOSTSAN)
+    return LIB_HOSTSAN
+
+
 if __name__ == "__main__":
-    path = build(verbose="-v" in sys.argv)
-    print(path)
+    if "--sanitize-host" in sys.argv:
+        print(build_host_sanitized(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))
