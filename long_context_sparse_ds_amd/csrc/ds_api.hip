@@ -97,15 +97,17 @@ namespace ds {
 
 void set_error(const char* msg) { g_err = msg; }
 
-SplitPlan plan_split(int64_t rows, int G, int64_t kv_virtual, bool fused) {
+SplitPlan plan_split(int64_t rows, int G, int64_t kv_virtual, bool fused, bool wide = false) {
   SplitPlan sp{};
   // Fused workgroups are 1024 threads, one resident per CU, and aim at ~256 of
   // them (each repeats the row's selection, so fewer is cheaper, and a second
   // round of workgroups would pay it twice); separate attention workgroups are
   // 256 threads and aim at ~2048.  Every head chunk of a row is a workgroup of
   // its own.  Slices hold at least 64 kept positions, and a row is cut into
-  // at most 1024 splits.
-  const int head_chunk = fused ? head_chunk4(G) : head_chunk8(G);
+  // at most 1024 splits.  Fused workgroups take up to four heads, or up to
+  // eight when `wide` (the long rows of the two-stage selection, whose kept
+  // K/V rows the eight-head form reads once per group instead of twice).
+  const int head_chunk = fused ? (wide ? head_chunk8(G) : head_chunk4(G)) : head_chunk8(G);
   const int64_t head_chunks = G / head_chunk;
   const int64_t target = fused ? 256 : 2048;
   int64_t chunk = (kv_virtual * rows * head_chunks + target - 1) / target;
@@ -135,18 +137,19 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t T, int block, int64_t k_u
   p.partitioned = !p.fused && parts * k_units <= kFusedMaxUnits;
   p.n_cand = p.partitioned ? parts * k_units : 0;
   p.cand_ld = (p.n_cand + 63) / 64 * 64;
-  p.sp = plan_split(p.rows, G, p.kv_virtual, p.fused || p.partitioned);
+  p.sp = plan_split(p.rows, G, p.kv_virtual, p.fused || p.partitioned, p.partitioned);
   p.tiles = (T + kScoreTile - 1) / kScoreTile;
   // The fused kernel then reads the row's top-digit histogram instead of building it
   // (worth it for token-level rows; a tile of 64-token blocks holds only 32 units),
   // when several of its workgroups would each build it: a row that one workgroup
   // handles alone builds it once, for less than the histograms cost to write and
   // read back (batched_32k: 208.9 -> 201.4 us per step).
-  // Token-level rows of the two-stage selection: the partitions sum their tiles'
-  // histograms too, and pass their candidates' histograms on (at most
-  // kMaxHistTiles partitions).
-  p.tile_hist = (p.fused && p.tiles <= kMaxHistTiles && block <= 4 && p.sp.n_split * p.sp.head_chunks > 1) ||
-                (p.partitioned && block == 1);
+  // Token-level rows of the two-stage selection score their partitions from
+  // the label cache inside the first stage (no score buffer, no tile
+  // histograms; each partition builds its own histogram) and pass their
+  // candidates' histograms on (at most kMaxHistTiles partitions).
+  p.part_onepass = p.partitioned && block == 1;
+  p.tile_hist = p.fused && p.tiles <= kMaxHistTiles && block <= 4 && p.sp.n_split * p.sp.head_chunks > 1;
   p.cand_hist = p.partitioned && block == 1 && parts <= kMaxHistTiles;
   // Token-level rows over several fused workgroups take the sorted tile lists
   // and the bucket kernel: a split then reads the tiles' prefixes, its share of
@@ -157,7 +160,7 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int64_t T, int block, int64_t k_u
   const int64_t bhs = int64_t(B) * Hq * max_split;
   size_t off = 0;
   p.off_scores = off;
-  off += round256(size_t(p.rows) * size_t(p.score_ld) * sizeof(float));
+  if (!p.part_onepass) off += round256(size_t(p.rows) * size_t(p.score_ld) * sizeof(float));
   p.off_tile_hist = off;
   if (p.tile_hist) off += round256(size_t(p.rows) * size_t(p.tiles) * kHistBins * sizeof(uint16_t));
   p.off_acc = off;
@@ -201,7 +204,8 @@ ds_status run_select_attend(const void* q, const void* K, const void* V, ds_dtyp
                             int64_t T_cap, int64_t T, int block, int64_t k_units, const float* scores, int64_t ld,
                             const uint16_t* tile_hist, bool tickets_zeroed, float scale, const ds::DecodePlan& pl,
                             float* out, int32_t* indices, char* ws, hipStream_t s,
-                            const int32_t* seq_lens = nullptr, float tau = 0.f, int32_t* counts = nullptr) {
+                            const int32_t* seq_lens = nullptr, float tau = 0.f, int32_t* counts = nullptr,
+                            bool cand_ready = false) {
   if (pl.fused || pl.partitioned) {
     float* part_acc = reinterpret_cast<float*>(ws + pl.off_acc);
     float* part_ml = reinterpret_cast<float*>(ws + pl.off_ml);
@@ -213,12 +217,15 @@ ds_status run_select_attend(const void* q, const void* K, const void* V, ds_dtyp
       // Top k of each partition, then the fused kernel over the candidates.
       float* cand_score = reinterpret_cast<float*>(ws + pl.off_cand_score);
       int32_t* cand_id = reinterpret_cast<int32_t*>(ws + pl.off_cand_id);
-      uint16_t* cand_hist = tile_hist != nullptr && pl.cand_hist ? reinterpret_cast<uint16_t*>(ws + pl.off_cand_hist)
-                                                                 : nullptr;
-      if (ds_status st = hip_status(ds::launch_partition_topk(scores, pl.rows, pl.n_units, ld, k_units, cand_score,
-                                                              pl.cand_ld, cand_id, tile_hist, pl.tiles, cand_hist, s),
-                                    "partition select launch"))
-        return st;
+      // cand_ready: the score phase's one-pass first stage already wrote the candidates.
+      uint16_t* cand_hist = (tile_hist != nullptr || cand_ready) && pl.cand_hist
+                                ? reinterpret_cast<uint16_t*>(ws + pl.off_cand_hist)
+                                : nullptr;
+      if (!cand_ready)
+        if (ds_status st = hip_status(ds::launch_partition_topk(scores, pl.rows, pl.n_units, ld, k_units, cand_score,
+                                                                pl.cand_ld, cand_id, tile_hist, pl.tiles, cand_hist, s),
+                                      "partition select launch"))
+          return st;
       ds::DecodePlan pc = pl;
       pc.n_units = pl.n_cand;
       pc.tile_hist = cand_hist != nullptr;
@@ -391,6 +398,15 @@ static ds_status decode_score_stage(const void* q, const void* K, void* label, c
   float* scores = reinterpret_cast<float*>(ws + pl.off_scores);
   uint16_t* tile_hist = pl.tile_hist ? reinterpret_cast<uint16_t*>(ws + pl.off_tile_hist) : nullptr;
   unsigned* tickets = pl.fused || pl.partitioned ? reinterpret_cast<unsigned*>(ws + pl.off_tickets) : nullptr;
+  if (pl.part_onepass && seq_lens == nullptr && !positive)
+    return hip_status(ds::launch_partition_onepass(
+                          q, label, K, channels_dev, r, dt == DS_DTYPE_BF16, B, Hq, Hkv, T_cap, T, t_append,
+                          pl.n_cand / ((pl.n_units + ds::kPartUnits - 1) / ds::kPartUnits),
+                          reinterpret_cast<float*>(ws + pl.off_cand_score), pl.cand_ld,
+                          reinterpret_cast<int32_t*>(ws + pl.off_cand_id),
+                          pl.cand_hist ? reinterpret_cast<uint16_t*>(ws + pl.off_cand_hist) : nullptr, tickets,
+                          pl.sp.head_chunks, s),
+                      "one-pass partition launch");
   // The plain top-k step of bucketed shapes writes sorted tile lists; ragged and
   // threshold calls keep the unit-order scores and histograms.
   const bool sorted = pl.bucketed && seq_lens == nullptr && !positive;
@@ -414,7 +430,8 @@ static ds_status decode_select_stage(const void* q, const void* K, const void* V
                                     out, reinterpret_cast<unsigned*>(ws + pl.off_tickets), s),
         "bucket select-attention launch");
   return run_select_attend(q, K, V, dt, B, Hq, Hkv, T_cap, T, block, k_units, scores, pl.score_ld, tile_hist, true,
-                           scale, pl, out, indices, ws, s, seq_lens, tau, counts);
+                           scale, pl, out, indices, ws, s, seq_lens, tau, counts,
+                           pl.part_onepass && seq_lens == nullptr && counts == nullptr);
 }
 
 // The one-pass form of the decode step, one kernel instead of two: token-level

@@ -53,6 +53,8 @@ struct DecodePlan {
   int64_t n_cand;      // partitioned: candidates per row (partitions * k_units)
   int64_t cand_ld;     // partitioned: row stride of the candidate scores, floats (multiple of 64)
   bool cand_hist;      // partitioned: the first stage writes its candidates' top-digit histograms
+  bool part_onepass;   // partitioned token-level rows: the first stage scores the label cache itself (the
+                       // decode step's score phase), so no score buffer or tile histograms are written
   bool tile_hist;      // the score kernel writes per-tile key histograms for the fused kernel
   bool bucketed;       // token-level rows over several fused workgroups: sorted tile lists and the
                        // bucket kernel (for the plain top-k step; ragged and threshold calls keep the
@@ -103,6 +105,17 @@ hipError_t launch_select(const float* scores, int64_t rows, int64_t n, int64_t l
 hipError_t launch_partition_topk(const float* scores, int64_t rows, int64_t n, int64_t ld, int64_t k,
                                  float* cand_score, int64_t cand_ld, int32_t* cand_id, const uint16_t* tile_hist,
                                  int64_t tiles, uint16_t* cand_hist, hipStream_t s);
+
+// The same first stage in one pass over the label cache, for token-level rows
+// (block 1): each partition is scored from its label rows (rows [t_append, T)
+// rebuilt from K first), with the score kernel's arithmetic, and its top k and
+// the candidates' top-digit histogram (cand_hist, may be null) written as by
+// launch_partition_topk.  No score buffer is written.  tickets (may be null):
+// tickets_per_row merge tickets per row, zeroed for the fused kernel that follows.
+hipError_t launch_partition_onepass(const void* q, void* label, const void* K, const int32_t* ch, int r, int is_bf16,
+                                    int B, int Hq, int Hkv, int64_t T_cap, int64_t T, int64_t t_append, int64_t k,
+                                    float* cand_score, int64_t cand_ld, int32_t* cand_id, uint16_t* cand_hist,
+                                    unsigned* tickets, int tickets_per_row, hipStream_t s);
 
 // Attention over given kept units; writes out directly when sp.n_split == 1,
 // else partial states that launch_merge combines.

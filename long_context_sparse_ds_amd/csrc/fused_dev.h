@@ -8,6 +8,10 @@
 namespace ds {
 namespace {
 
+// Operand and accumulator types of the matrix-core instructions.
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
 template <typename TE, int NT>
 struct Lanes {
   static constexpr int NW = NT / 64;                  // wavefronts

@@ -24,6 +24,17 @@ __device__ __forceinline__ double group_q_sum(const TE* __restrict__ qg, int G, 
   return s;
 }
 
+// qs at channel c in the score kernel's own order for any group size: the
+// heads past the eighth first, then heads 0 .. 7 (equal to group_q_sum for
+// groups of up to eight heads).
+template <typename TE>
+__device__ __forceinline__ double score_q_sum(const TE* __restrict__ qg, int G, int c) {
+  double s = 0.0;
+  for (int h = 8; h < G; ++h) s += double(elem_to_f32(qg[int64_t(h) * kHeadDim + c]));
+  for (int h = 0; h < 8 && h < G; ++h) s += double(elem_to_f32(qg[int64_t(h) * kHeadDim + c]));
+  return s;
+}
+
 // NV 16-byte words of one label row against qr[0 .. 8 NV) (bf16) or
 // qr[0 .. 4 NV) (fp32), in channel order.
 template <int NV>

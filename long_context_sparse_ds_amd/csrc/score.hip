@@ -337,7 +337,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
     }
     __shared__ uint32_t wsum[kThreads / 64];
     uint32_t tot;
-    uint32_t p = block_exclusive_scan<kThreads>(sum, wsum, tot);   // ends with a barrier
+    uint32_t p = block_exclusive_scan1<kThreads>(sum, wsum, tot);   // one barrier; wsum is not used again
     uint32_t P[per];
 #pragma unroll
     for (int j = 0; j < per; ++j) {

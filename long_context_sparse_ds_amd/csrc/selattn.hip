@@ -44,6 +44,17 @@
 // kept set is exactly the passing units, so the radix passes are skipped and
 // the prefix sum over the pass masks alone places them.  Otherwise the top-k
 // search runs as usual and every unit it keeps passes.
+//
+// Eight query heads per workgroup (GQA groups of 8 in bf16, the long rows of
+// the two-stage selection): the attention runs on the matrix cores, so each
+// kept K/V row is read once for all eight heads.  A wavefront takes 16 kept
+// tokens per step.  S^T = K q^T (16 tokens x 16 head slots, eight used) comes
+// from four v_mfma_f32_16x16x32_bf16 over the 128 channels, taken in an order
+// in which every lane's share of a K row is 32 contiguous channels; the online
+// softmax runs on that tile (a head's 16 tokens lie in one lane column of
+// four lanes); O^T += V^T P^T is 32 v_mfma_f32_16x16x4_f32 with P in fp32
+// (each lane's share of a V row is 8 contiguous channels, the output channels
+// permuted to match).  The state then takes the lane path's way to LDS.
 #include "fused_dev.h"
 #include "label_dot.h"
 
@@ -203,11 +214,26 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
   const int gid = wave * GPW + grp;
 
   // Loads first: q (consumed only after the selection), the thread's scores,
-  // and the tile histograms of its top-digit bins.
-  uint4 qraw[HC];
+  // and the tile histograms of its top-digit bins.  The matrix-core path holds
+  // q as the B operand of S^T = K q^T: lane (16 g + j) has channels
+  // [32 g, 32 g + 32) of head j (zero for the padding heads j >= HC).
+  constexpr bool kMfma = HC == 8 && sizeof(TE) == 2;
+  constexpr int NQ = kMfma ? 4 : HC;
+  uint4 qraw[NQ];
+  if constexpr (kMfma) {
+    const int hq = (lane & 15) < HC ? (lane & 15) : 0;
 #pragma unroll
-  for (int h = 0; h < HC; ++h)
-    qraw[h] = *reinterpret_cast<const uint4*>(q + (bh0 + h) * kHeadDim + sub * EPL);
+    for (int i = 0; i < 4; ++i)
+      qraw[i] = *reinterpret_cast<const uint4*>(q + (bh0 + hq) * kHeadDim + 32 * (lane >> 4) + 8 * i);
+    if ((lane & 15) >= HC) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qraw[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < HC; ++h)
+      qraw[h] = *reinterpret_cast<const uint4*>(q + (bh0 + h) * kHeadDim + sub * EPL);
+  }
   const int first = tid * ITEMS;
   float s[ITEMS];
   if constexpr (LNV > 0) {
@@ -476,100 +502,186 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
   }
 
   // Attention over the split's kept rows.
-  float qv[HC][EPL];
-#pragma unroll
-  for (int h = 0; h < HC; ++h) {
-    unpack(qraw[h], qv[h], TE());
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) qv[h][e] *= a.scale;
-  }
-  float m[HC], l[HC], acc[HC][EPL];
-#pragma unroll
-  for (int h = 0; h < HC; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
-  }
-  const TE* Kr = K + int64_t(row) * a.T_cap * kHeadDim + sub * EPL;
-  const TE* Vr = V + int64_t(row) * a.T_cap * kHeadDim + sub * EPL;
-  for (int base = p_begin; base < p_end; base += NG * KU) {
-    // Loads are unconditional: a position past the split or an invalid entry
-    // reads token 0 of the row (which exists) and is masked out of the
-    // softmax; a load inside a branch would make the compiler wait for it
-    // where the branches join.
-    int64_t tok[KU];
-    bool ok[KU];
-#pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const int p = base + gid * KU + u;
+  if constexpr (kMfma) {
+    // Kept position p of this split: its token, and whether it is one.
+    const auto token_at = [&](int p, bool& ok) -> int64_t {
       const bool in = p < p_end;
       const int rel = in ? p - p_begin : 0;
       const int unit = in ? sm.u.a.sel[rel >> lb] : 0;
       const int64_t t = (int64_t(unit) << lb) + (rel & (block - 1));
-      ok[u] = in && unit >= 0 && t < T_row;   // always true for p < p_end when the kept list is whole
-      tok[u] = ok[u] ? t : 0;
-    }
-    uint4 kr[KU], vr[KU];
+      ok = in && unit >= 0 && t < T_row;
+      return ok ? t : 0;
+    };
+    const int g = lane >> 4, j = lane & 15;
+    bf16x8_t qb[4];
 #pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      kr[u] = *reinterpret_cast<const uint4*>(Kr + tok[u] * kHeadDim);
-      vr[u] = *reinterpret_cast<const uint4*>(Vr + tok[u] * kHeadDim);
-    }
-    float kf[KU][EPL], vf[KU][EPL];
+    for (int i = 0; i < 4; ++i) qb[i] = __builtin_bit_cast(bf16x8_t, qraw[i]);
+    const TE* Kb = K + int64_t(row) * a.T_cap * kHeadDim;
+    const TE* Vb = V + int64_t(row) * a.T_cap * kHeadDim;
+    float M = -INFINITY, L = 0.f;   // head j's running maximum and denominator
+    f32x4_t o[8];                   // O^T rows 4 g + r of channel tile c: channel 8 (4 g + r) + c, head j
 #pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      unpack(kr[u], kf[u], TE());
-      unpack(vr[u], vf[u], TE());
-    }
+    for (int c = 0; c < 8; ++c) o[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int base = p_begin; base < p_end; base += NW * 16) {
+      const int pw = base + wave * 16;   // this wavefront's 16 positions
+      bool okk, okv[4];
+      const int64_t tk = token_at(pw + j, okk);   // K row of slot j
+      int64_t tv[4];
 #pragma unroll
+      for (int i = 0; i < 4; ++i) tv[i] = token_at(pw + 4 * g + i, okv[i]);   // V rows of slots 4 g + i
+      // Unconditional loads (a slot that is not kept reads token 0 and is masked).
+      uint4 kq[4], vq[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kq[i] = *reinterpret_cast<const uint4*>(Kb + tk * kHeadDim + 32 * g + 8 * i);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vq[i] = *reinterpret_cast<const uint4*>(Vb + tv[i] * kHeadDim + 8 * j);
+      f32x4_t d = {0.f, 0.f, 0.f, 0.f};   // S^T rows 4 g + r (slots), column j (head)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kq[i]), qb[i], d, 0, 0, 0);
+      float z[4], mt = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        z[r] = okv[r] ? d[r] * a.scale : -INFINITY;
+        mt = fmaxf(mt, z[r]);
+      }
+      float m16, m32;
+      pair_values<16>(mt, m16, m32);
+      mt = fmaxf(m16, m32);
+      pair_values<32>(mt, m16, m32);
+      mt = fmaxf(m16, m32);   // head j's maximum over the 16 slots
+      const float Mn = fmaxf(M, mt);
+      const float alpha = Mn == -INFINITY ? 1.f : __expf(M - Mn);
+      float pr[4], ps = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pr[r] = z[r] == -INFINITY ? 0.f : __expf(z[r] - Mn);
+        ps += pr[r];
+      }
+      float s16, s32;
+      pair_values<16>(ps, s16, s32);
+      ps = s16 + s32;
+      pair_values<32>(ps, s16, s32);
+      ps = s16 + s32;
+      L = L * alpha + ps;
+      M = Mn;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) o[c] *= alpha;
+      // O^T += V^T P^T over slots 4 g + i (k index g of the i-th product).
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float vf[8];
+        unpack(vq[i], vf, TE());
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[c], pr[i], o[c], 0, 0, 0);
+      }
+    }
+    if (j < HC) {
+      if (g == 0) {
+        sm.wm[wave][j] = M;
+        sm.wl[wave][j] = L;
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm.u.a.wacc[wave][j][8 * (4 * g + r) + c] = o[c][r];
+    }
+  } else {
+    float qv[HC][EPL];
+  #pragma unroll
     for (int h = 0; h < HC; ++h) {
-      float z[KU];
-#pragma unroll
-      for (int u = 0; u < KU; ++u) {
-        float d = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) d = fmaf(qv[h][e], kf[u][e], d);
-        d = group_sum<TE, NT>(d);
-        z[u] = ok[u] ? d : -INFINITY;
-      }
-      float mx = m[h];
-#pragma unroll
-      for (int u = 0; u < KU; ++u) mx = fmaxf(mx, z[u]);
-      if (mx == -INFINITY) continue;   // uniform across the lane group
-      const float alpha = __expf(m[h] - mx);
-      float p[KU], psum = 0.f;
-#pragma unroll
-      for (int u = 0; u < KU; ++u) {
-        p[u] = __expf(z[u] - mx);
-        psum += p[u];
-      }
-      l[h] = l[h] * alpha + psum;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        float a = acc[h][e] * alpha;
-#pragma unroll
-        for (int u = 0; u < KU; ++u) a = fmaf(p[u], vf[u][e], a);
-        acc[h][e] = a;
-      }
-      m[h] = mx;
+      unpack(qraw[h], qv[h], TE());
+  #pragma unroll
+      for (int e = 0; e < EPL; ++e) qv[h][e] *= a.scale;
     }
-  }
+    float m[HC], l[HC], acc[HC][EPL];
+  #pragma unroll
+    for (int h = 0; h < HC; ++h) {
+      m[h] = -INFINITY;
+      l[h] = 0.f;
+  #pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+    }
+    const TE* Kr = K + int64_t(row) * a.T_cap * kHeadDim + sub * EPL;
+    const TE* Vr = V + int64_t(row) * a.T_cap * kHeadDim + sub * EPL;
+    for (int base = p_begin; base < p_end; base += NG * KU) {
+      // Loads are unconditional: a position past the split or an invalid entry
+      // reads token 0 of the row (which exists) and is masked out of the
+      // softmax; a load inside a branch would make the compiler wait for it
+      // where the branches join.
+      int64_t tok[KU];
+      bool ok[KU];
+  #pragma unroll
+      for (int u = 0; u < KU; ++u) {
+        const int p = base + gid * KU + u;
+        const bool in = p < p_end;
+        const int rel = in ? p - p_begin : 0;
+        const int unit = in ? sm.u.a.sel[rel >> lb] : 0;
+        const int64_t t = (int64_t(unit) << lb) + (rel & (block - 1));
+        ok[u] = in && unit >= 0 && t < T_row;   // always true for p < p_end when the kept list is whole
+        tok[u] = ok[u] ? t : 0;
+      }
+      uint4 kr[KU], vr[KU];
+  #pragma unroll
+      for (int u = 0; u < KU; ++u) {
+        kr[u] = *reinterpret_cast<const uint4*>(Kr + tok[u] * kHeadDim);
+        vr[u] = *reinterpret_cast<const uint4*>(Vr + tok[u] * kHeadDim);
+      }
+      float kf[KU][EPL], vf[KU][EPL];
+  #pragma unroll
+      for (int u = 0; u < KU; ++u) {
+        unpack(kr[u], kf[u], TE());
+        unpack(vr[u], vf[u], TE());
+      }
+  #pragma unroll
+      for (int h = 0; h < HC; ++h) {
+        float z[KU];
+  #pragma unroll
+        for (int u = 0; u < KU; ++u) {
+          float d = 0.f;
+  #pragma unroll
+          for (int e = 0; e < EPL; ++e) d = fmaf(qv[h][e], kf[u][e], d);
+          d = group_sum<TE, NT>(d);
+          z[u] = ok[u] ? d : -INFINITY;
+        }
+        float mx = m[h];
+  #pragma unroll
+        for (int u = 0; u < KU; ++u) mx = fmaxf(mx, z[u]);
+        if (mx == -INFINITY) continue;   // uniform across the lane group
+        const float alpha = __expf(m[h] - mx);
+        float p[KU], psum = 0.f;
+  #pragma unroll
+        for (int u = 0; u < KU; ++u) {
+          p[u] = __expf(z[u] - mx);
+          psum += p[u];
+        }
+        l[h] = l[h] * alpha + psum;
+  #pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          float a = acc[h][e] * alpha;
+  #pragma unroll
+          for (int u = 0; u < KU; ++u) a = fmaf(p[u], vf[u][e], a);
+          acc[h][e] = a;
+        }
+        m[h] = mx;
+      }
+    }
 
-  // Merge the lane groups of each wavefront (pairwise lane swaps), then the
-  // wavefronts through LDS: every output channel combines the NW wavefront
-  // states itself, so one barrier suffices.
-  if constexpr (LPT == 16) merge_pairs<16, HC, EPL>(m, l, acc);
-  merge_pairs<32, HC, EPL>(m, l, acc);
-  if (grp == 0) {
-#pragma unroll
-    for (int h = 0; h < HC; ++h) {
-      if (sub == 0) {
-        sm.wm[wave][h] = m[h];
-        sm.wl[wave][h] = l[h];
+    // Merge the lane groups of each wavefront (pairwise lane swaps), then the
+    // wavefronts through LDS: every output channel combines the NW wavefront
+    // states itself, so one barrier suffices.
+    if constexpr (LPT == 16) merge_pairs<16, HC, EPL>(m, l, acc);
+    merge_pairs<32, HC, EPL>(m, l, acc);
+    if (grp == 0) {
+  #pragma unroll
+      for (int h = 0; h < HC; ++h) {
+        if (sub == 0) {
+          sm.wm[wave][h] = m[h];
+          sm.wl[wave][h] = l[h];
+        }
+  #pragma unroll
+        for (int e = 0; e < EPL; ++e) sm.u.a.wacc[wave][h][sub * EPL + e] = acc[h][e];
       }
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) sm.u.a.wacc[wave][h][sub * EPL + e] = acc[h][e];
     }
   }
   __syncthreads();
@@ -688,9 +800,22 @@ hipError_t dispatch_items(const FusedArgs& a, dim3 grid, hipStream_t s) {
   return launch_one<TE, 1024, 32, HC>(a, grid, s);
 }
 
+// Eight heads per workgroup: only the long rows of the two-stage selection
+// (never ragged, one pass or the threshold rule).
+template <typename TE>
+hipError_t dispatch_wide(const FusedArgs& a, dim3 grid, hipStream_t s) {
+  if (a.seq_lens != nullptr || a.label != nullptr || a.counts != nullptr) return hipErrorInvalidValue;
+  const int n = a.n_units;
+  if (n <= 1024 * 4) return launch_kernel<TE, 1024, 4, 8, false, 0>(a, grid, s);
+  if (n <= 1024 * 8) return launch_kernel<TE, 1024, 8, 8, false, 0>(a, grid, s);
+  if (n <= 1024 * 16) return launch_kernel<TE, 1024, 16, 8, false, 0>(a, grid, s);
+  return launch_kernel<TE, 1024, 32, 8, false, 0>(a, grid, s);
+}
+
 template <typename TE>
 hipError_t dispatch(const FusedArgs& a, int head_chunk, dim3 grid, hipStream_t s) {
   switch (head_chunk) {
+    case 8: return dispatch_wide<TE>(a, grid, s);
     case 4: return dispatch_items<TE, 4>(a, grid, s);
     case 2: return dispatch_items<TE, 2>(a, grid, s);
     default: return dispatch_items<TE, 1>(a, grid, s);

@@ -9,6 +9,7 @@
 // streamed from memory (L2-resident after the score kernel) once per radix
 // pass, eight independent loads in flight per thread, and compacted in
 // ordered tiles.
+#include "label_dot.h"
 #include "select_dev.h"
 
 namespace ds {
@@ -115,51 +116,22 @@ __global__ __launch_bounds__(kNT) void select_stream_kernel(const float* __restr
 // them still goes to the lower unit id: cand_score[row][p * k + i] and
 // cand_id[row][p * k + i]; the slots of a partition past its kept count hold
 // -inf and -1.
-// tile_hist (may be null): the score kernel's top-digit histograms of the
-// row's tiles of kHistTileUnits units, tiles per row; a partition sums its
-// tiles' counts instead of building its histogram with LDS atomics (which
-// contend badly on the few digits that high scores share).  cand_hist (may be
-// null; needs tile_hist): the top-digit histogram of each partition's
-// candidates, [rows][parts][2048] uint16, for the fused kernel that selects
-// among them.
-__global__ __launch_bounds__(kNT) void partition_topk_kernel(const float* __restrict__ scores, int64_t n, int64_t ld,
-                                                             int64_t k, float* __restrict__ cand_score,
-                                                             int64_t cand_ld, int32_t* __restrict__ cand_id,
-                                                             int64_t n_cand, const uint16_t* __restrict__ tile_hist,
-                                                             int64_t tiles, uint16_t* __restrict__ cand_hist) {
-  constexpr int ITEMS = int(kPartUnits / kNT);
-  // k is often a quarter of the partition here, so the digit holding the k-th
-  // key can hold thousands of keys: room for 8192 candidates.
-  __shared__ SelSmem<kNT, 8192> sm;
-  const int64_t p = blockIdx.x, row = blockIdx.y;
-  const int64_t base = p * kPartUnits;
-  const int64_t n_p = min(kPartUnits, n - base);
-  const int64_t k_p = min(k, n_p);
+// cand_hist (may be null; needs the partition's top-digit histogram): the
+// top-digit histogram of each partition's candidates, [rows][parts][2048]
+// uint16, for the fused kernel that selects among them.
+//
+// The end common to both forms below, once thread t holds the keys of units
+// [t ITEMS, (t + 1) ITEMS) of the partition (and, when have_hist, the
+// partition's counts of its two top-digit bins 2047 - 2t and 2046 - 2t).
+template <int ITEMS, int CAP>
+__device__ __forceinline__ void partition_finish(const uint32_t (&key)[ITEMS], const bool (&valid)[ITEMS],
+                                                 SelSmem<kNT, CAP>& sm, uint16_t* kept_id, bool have_hist,
+                                                 uint32_t hist_hi, uint32_t hist_lo, int64_t row, int64_t p,
+                                                 int64_t base, int64_t k_p, int64_t k, float* __restrict__ cand_score,
+                                                 int64_t cand_ld, int32_t* __restrict__ cand_id, int64_t n_cand,
+                                                 uint16_t* __restrict__ cand_hist) {
   float* cs = cand_score + row * cand_ld + p * k;
   int32_t* ci = cand_id + row * n_cand + p * k;
-  uint32_t key[ITEMS];
-  bool valid[ITEMS];
-  load_keys<ITEMS>(scores + row * ld + base, n_p, key, valid);
-  // This thread's two top-digit bins, 2047 - 2t (high half of word 1023 - t)
-  // and 2046 - 2t (low half), summed over the partition's tiles.
-  uint32_t hist_hi = 0u, hist_lo = 0u;
-  const bool have_hist = tile_hist != nullptr;
-  if (have_hist) {
-    constexpr int kPartTiles = int(kPartUnits / kHistTileUnits);
-    const uint32_t* th = reinterpret_cast<const uint32_t*>(tile_hist + row * tiles * kHistBins) +
-                         (kHistBins / 2 - 1 - int(threadIdx.x));
-    const int64_t t0 = p * kPartTiles;
-    uint32_t w[kPartTiles];
-#pragma unroll
-    for (int t = 0; t < kPartTiles; ++t) w[t] = th[(t0 + t < tiles ? t0 + t : t0) * (kHistBins / 2)];
-#pragma unroll
-    for (int t = 0; t < kPartTiles; ++t) {
-      if (t0 + t < tiles) {
-        hist_hi += w[t] >> 16;
-        hist_lo += w[t] & 0xFFFFu;
-      }
-    }
-  }
   uint32_t kk, mask;
   const uint32_t tau = select_threshold<kNT, ITEMS>(key, valid, uint32_t(k_p), sm, kk, mask, have_hist, hist_hi,
                                                     hist_lo);
@@ -183,8 +155,7 @@ __global__ __launch_bounds__(kNT) void partition_topk_kernel(const float* __rest
   // final positions, and the window is then written with coalesced stores.
   // Scattered 4-byte stores straight from the emission cost more than the
   // selection itself.
-  constexpr int kWin = decltype(sm)::kCap;
-  __shared__ uint16_t kept_id[kWin];
+  constexpr int kWin = CAP;
   static_assert(kPartUnits <= 65536, "partition-local ids fit 16 bits");
   const int64_t first = int64_t(threadIdx.x) * ITEMS;
   for (int64_t w0 = 0; w0 < k_p; w0 += kWin) {
@@ -208,6 +179,158 @@ __global__ __launch_bounds__(kNT) void partition_topk_kernel(const float* __rest
   }
 }
 
+constexpr int kPartItems = int(kPartUnits / kNT);
+// k is often a quarter of the partition here, so the digit holding the k-th
+// key can hold thousands of keys: room for 8192 candidates.
+constexpr int kPartCap = 8192;
+
+// The first stage from a score buffer.  tile_hist (may be null): the score
+// kernel's top-digit histograms of the row's tiles of kHistTileUnits units,
+// tiles per row; a partition sums its tiles' counts instead of building its
+// histogram with LDS atomics (which contend badly on the few digits that high
+// scores share).
+__global__ __launch_bounds__(kNT) void partition_topk_kernel(const float* __restrict__ scores, int64_t n, int64_t ld,
+                                                             int64_t k, float* __restrict__ cand_score,
+                                                             int64_t cand_ld, int32_t* __restrict__ cand_id,
+                                                             int64_t n_cand, const uint16_t* __restrict__ tile_hist,
+                                                             int64_t tiles, uint16_t* __restrict__ cand_hist) {
+  constexpr int ITEMS = kPartItems;
+  __shared__ SelSmem<kNT, kPartCap> sm;
+  __shared__ uint16_t kept_id[kPartCap];
+  const int64_t p = blockIdx.x, row = blockIdx.y;
+  const int64_t base = p * kPartUnits;
+  const int64_t n_p = min(kPartUnits, n - base);
+  const int64_t k_p = min(k, n_p);
+  uint32_t key[ITEMS];
+  bool valid[ITEMS];
+  load_keys<ITEMS>(scores + row * ld + base, n_p, key, valid);
+  // This thread's two top-digit bins, 2047 - 2t (high half of word 1023 - t)
+  // and 2046 - 2t (low half), summed over the partition's tiles.
+  uint32_t hist_hi = 0u, hist_lo = 0u;
+  const bool have_hist = tile_hist != nullptr;
+  if (have_hist) {
+    constexpr int kPartTiles = int(kPartUnits / kHistTileUnits);
+    const uint32_t* th = reinterpret_cast<const uint32_t*>(tile_hist + row * tiles * kHistBins) +
+                         (kHistBins / 2 - 1 - int(threadIdx.x));
+    const int64_t t0 = p * kPartTiles;
+    uint32_t w[kPartTiles];
+#pragma unroll
+    for (int t = 0; t < kPartTiles; ++t) w[t] = th[(t0 + t < tiles ? t0 + t : t0) * (kHistBins / 2)];
+#pragma unroll
+    for (int t = 0; t < kPartTiles; ++t) {
+      if (t0 + t < tiles) {
+        hist_hi += w[t] >> 16;
+        hist_lo += w[t] & 0xFFFFu;
+      }
+    }
+  }
+  partition_finish<ITEMS>(key, valid, sm, kept_id, have_hist, hist_hi, hist_lo, row, p, base, k_p, k, cand_score,
+                          cand_ld, cand_id, n_cand, cand_hist);
+}
+
+// The first stage in one pass over the label cache, for token-level rows: the
+// partition's scores are computed here (Double Sparsity page, method details:
+// the label channels' dot product with the group's q, as in the score kernel,
+// with the same float64 arithmetic, so the scores equal the score kernel's bit
+// for bit), with rows [t_append, n) rebuilt from K first (the label-row
+// append).  No score buffer goes to memory.  Pass c covers tokens c NT + tid
+// of the partition, so a wavefront reads 64 consecutive label rows per load;
+// each score goes to the LDS slot of the thread that owns its token in the
+// selection, and into the partition's top-digit histogram.  R: label channels
+// (LNV 16-byte words per row), or R = 0 for any width (element loads, r at
+// run time).  Partition 0 of a row also zeroes the row's merge tickets for the
+// fused kernel that follows.
+template <typename TE, int R, int LNV>
+__global__ __launch_bounds__(kNT) void partition_onepass_kernel(
+    const TE* __restrict__ q, TE* __restrict__ label, const TE* __restrict__ Kc, const int32_t* __restrict__ ch,
+    int32_t r_rt, int32_t G, int32_t Hkv, int64_t T_cap, int64_t n, int64_t t_append, int64_t k,
+    float* __restrict__ cand_score, int64_t cand_ld, int32_t* __restrict__ cand_id, int64_t n_cand,
+    uint16_t* __restrict__ cand_hist, unsigned* __restrict__ tickets, int32_t tickets_per_row) {
+  constexpr int ITEMS = kPartItems;
+  constexpr int RMAX = R > 0 ? R : kHeadDim;
+  // Label rows requested together per thread (64 bytes), as in the one-pass
+  // fused kernel.
+  constexpr int CB = R == 0 ? 4 : (LNV == 1 ? 4 : LNV == 2 ? 2 : 1);
+  static_assert(ITEMS % CB == 0, "whole batches of passes");
+  __shared__ union {
+    float sc[kPartUnits];   // the partition's scores, in the owners' layout
+    struct {
+      SelSmem<kNT, kPartCap> sel;
+      uint16_t kept_id[kPartCap];
+    } b;
+  } u;
+  __shared__ uint32_t hist1[kHistBins];
+  __shared__ double qs_l[RMAX];
+  __shared__ int ch_l[RMAX];
+  const int r = R > 0 ? R : r_rt;
+  const int64_t p = blockIdx.x, row = blockIdx.y;
+  const int tid = int(threadIdx.x);
+  const int64_t base = p * kPartUnits;
+  const int64_t n_p = min(kPartUnits, n - base);
+  const int64_t k_p = min(k, n_p);
+  const int g = int(row % Hkv);
+  if (tid < r) {
+    const int cj = ch[g * r + tid];
+    qs_l[tid] = score_q_sum(q + row * G * kHeadDim, G, cj);
+    ch_l[tid] = cj;
+  }
+  for (int i = tid; i < kHistBins; i += kNT) hist1[i] = 0u;
+  if (tickets != nullptr && p == 0)
+    for (int i = tid; i < tickets_per_row; i += kNT) tickets[row * tickets_per_row + i] = 0u;
+  __syncthreads();
+  TE* lab = label + row * T_cap * r;
+  double qr[RMAX];
+  if constexpr (R > 0) {
+#pragma unroll
+    for (int j = 0; j < R; ++j) qr[j] = qs_l[j];
+  }
+  for (int c0 = 0; c0 < ITEMS; c0 += CB) {
+    uint4 raw[CB][LNV > 0 ? LNV : 1];
+    if constexpr (R > 0) {
+#pragma unroll
+      for (int i = 0; i < CB; ++i) {
+        const int64_t t = base + (c0 + i) * kNT + tid;
+        const uint4* pr = reinterpret_cast<const uint4*>(lab + (t < n ? t : 0) * R);   // row 0 exists
+#pragma unroll
+        for (int v = 0; v < LNV; ++v) raw[i][v] = pr[v];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < CB; ++i) {
+      const int uloc = (c0 + i) * kNT + tid;
+      const int64_t t = base + uloc;
+      float sv;
+      if (t >= n) {
+        sv = -INFINITY;
+      } else if (t >= t_append) {
+        sv = append_row(Kc + (row * T_cap + t) * kHeadDim, lab + t * r, ch_l, qs_l, r);
+      } else if constexpr (R > 0) {
+        sv = float(dot_label<LNV>(raw[i], qr, TE()));
+      } else {
+        double a = 0.0;
+        for (int j = 0; j < r; ++j) a = fma(qs_l[j], double(elem_to_f32(lab[t * r + j])), a);
+        sv = float(a);
+      }
+      if (t < n) atomicAdd(&hist1[float_key(sv) >> 21], 1u);
+      const int ut = uloc / ITEMS, uj = uloc % ITEMS;
+      u.sc[((uj >> 2) * kNT + ut) * 4 + (uj & 3)] = sv;
+    }
+  }
+  __syncthreads();
+  uint32_t key[ITEMS];
+  bool valid[ITEMS];
+  const int64_t first = int64_t(tid) * ITEMS;
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) {
+    valid[j] = first + j < n_p;
+    key[j] = valid[j] ? float_key(u.sc[((j >> 2) * kNT + tid) * 4 + (j & 3)]) : 0u;
+  }
+  const uint32_t hist_hi = hist1[2047 - 2 * tid], hist_lo = hist1[2046 - 2 * tid];
+  __syncthreads();   // the scores are in registers: the selection's buffers overlay them
+  partition_finish<ITEMS>(key, valid, u.b.sel, u.b.kept_id, true, hist_hi, hist_lo, row, p, base, k_p, k,
+                          cand_score, cand_ld, cand_id, n_cand, cand_hist);
+}
+
 }  // namespace
 
 hipError_t launch_partition_topk(const float* scores, int64_t rows, int64_t n, int64_t ld, int64_t k,
@@ -217,6 +340,42 @@ hipError_t launch_partition_topk(const float* scores, int64_t rows, int64_t n, i
   hipLaunchKernelGGL(partition_topk_kernel, dim3(unsigned(parts), unsigned(rows)), dim3(kNT), 0, s, scores, n, ld, k,
                      cand_score, cand_ld, cand_id, parts * k, tile_hist, tiles, cand_hist);
   return hipGetLastError();
+}
+
+namespace {
+template <typename TE, int R, int LNV>
+hipError_t launch_onepass_t(const void* q, void* label, const void* K, const int32_t* ch, int r, int G, int Hkv,
+                            int64_t rows, int64_t T_cap, int64_t T, int64_t t_append, int64_t k, float* cand_score,
+                            int64_t cand_ld, int32_t* cand_id, uint16_t* cand_hist, unsigned* tickets,
+                            int tickets_per_row, hipStream_t s) {
+  const int64_t parts = (T + kPartUnits - 1) / kPartUnits;
+  hipLaunchKernelGGL((partition_onepass_kernel<TE, R, LNV>), dim3(unsigned(parts), unsigned(rows)), dim3(kNT), 0, s,
+                     static_cast<const TE*>(q), static_cast<TE*>(label), static_cast<const TE*>(K), ch, r, G, Hkv,
+                     T_cap, T, t_append, k, cand_score, cand_ld, cand_id, parts * k, cand_hist, tickets,
+                     tickets_per_row);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_partition_onepass(const void* q, void* label, const void* K, const int32_t* ch, int r, int is_bf16,
+                                    int B, int Hq, int Hkv, int64_t T_cap, int64_t T, int64_t t_append, int64_t k,
+                                    float* cand_score, int64_t cand_ld, int32_t* cand_id, uint16_t* cand_hist,
+                                    unsigned* tickets, int tickets_per_row, hipStream_t s) {
+  const int G = Hq / Hkv;
+  const int64_t rows = int64_t(B) * Hkv;
+#define DS_ONEPASS(TE, R, LNV)                                                                                     \
+  return launch_onepass_t<TE, R, LNV>(q, label, K, ch, r, G, Hkv, rows, T_cap, T, t_append, k, cand_score, cand_ld, \
+                                      cand_id, cand_hist, tickets, tickets_per_row, s)
+  if (is_bf16) {
+    if (r == 8) DS_ONEPASS(uint16_t, 8, 1);
+    if (r == 16) DS_ONEPASS(uint16_t, 16, 2);
+    DS_ONEPASS(uint16_t, 0, 0);
+  }
+  if (r == 4) DS_ONEPASS(float, 4, 1);
+  if (r == 8) DS_ONEPASS(float, 8, 2);
+  if (r == 16) DS_ONEPASS(float, 16, 4);
+  DS_ONEPASS(float, 0, 0);
+#undef DS_ONEPASS
 }
 
 hipError_t launch_select(const float* scores, int64_t rows, int64_t n, int64_t ld, int64_t k, int32_t* idx,

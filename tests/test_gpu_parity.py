@@ -411,7 +411,9 @@ def test_alternating_inputs_through_one_workspace():
         assert torch.equal(o.view(torch.int32), ro.view(torch.int32)), rep
 
 
-@pytest.mark.parametrize("w", [SMALL[0], SMALL[1], SMALL[4], SMALL[6], SMALL[13]], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [SMALL[0], SMALL[1], SMALL[4], SMALL[6], SMALL[13],
+                               Workload("two_stage_gqa8", "bf16", B=1, Hq=16, Hkv=2, d=128, T=40001, r=8, block=1,
+                                        k_units=900, seed_base=29500)], ids=lambda w: w.name)
 def test_two_phase_decode_equals_single_call(w):
     """ds_decode_score then ds_decode_select_attend through one workspace must give exactly
     the results of ds_decode_sparse_attn (same kernels), including the fused label append."""
@@ -689,10 +691,15 @@ def test_long_rows_two_stage_selection_adversarial(kind):
     Workload("long_gqa4", "bf16", B=1, Hq=8, Hkv=2, d=128, T=70000, r=8, block=1, k_units=2000, seed_base=29000),
     Workload("long_blk2", "bf16", B=1, Hq=2, Hkv=2, d=128, T=2 * 40000 + 1, r=16, block=2, k_units=5000,
              seed_base=29100),
+    # groups of 8 and 16 query heads: eight heads per workgroup (matrix cores in bf16, the lane path in fp32)
+    Workload("long_gqa8", "bf16", B=2, Hq=16, Hkv=2, d=128, T=70001, r=8, block=1, k_units=2001, seed_base=29200),
+    Workload("long_gqa16", "bf16", B=1, Hq=32, Hkv=2, d=128, T=40000, r=8, block=1, k_units=1500, seed_base=29300),
+    Workload("long_gqa8_f32", "f32", B=1, Hq=8, Hkv=1, d=128, T=40000, r=16, block=1, k_units=700,
+             seed_base=29400),
 ], ids=lambda w: w.name)
 def test_decode_long_rows_two_stage(w):
-    """The whole decode step on rows of more than 32,768 units (token-level with GQA, and
-    2-token blocks with a partial last block): every unit against the oracle."""
+    """The whole decode step on rows of more than 32,768 units (token-level with GQA groups of 4, 8
+    and 16, and 2-token blocks with a partial last block): every unit against the oracle."""
     q, K, V, ch, out, idx = run_decode(w)
     for b in range(w.B):
         for g in range(w.Hkv):
