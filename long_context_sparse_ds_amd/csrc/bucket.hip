@@ -87,6 +87,8 @@ struct BucketSmem {
     } a;
   } u;
   float wm[kNW][HC], wl[kNW][HC];
+  __align__(16) float wf[HC][kNW];   // each wavefront's weight in the combined state, per head
+  float hm[HC], hl[HC];              // the combined maximum and denominator, per head
   unsigned ticket;
 };
 
@@ -467,8 +469,8 @@ __global__ __launch_bounds__(kNT) void bucket_attn_kernel(
     }
   }
 
-  // Lane groups of each wavefront (pairwise lane swaps), then the wavefronts
-  // through LDS: every output channel combines the wavefront states itself.
+  // Lane groups of each wavefront (pairwise lane swaps); the wavefronts'
+  // states then go through LDS.
   if constexpr (LPT == 16) merge_pairs<16, HC, EPL>(m, l, acc);
   merge_pairs<32, HC, EPL>(m, l, acc);
   if (grp == 0) {
@@ -483,18 +485,34 @@ __global__ __launch_bounds__(kNT) void bucket_attn_kernel(
     }
   }
   __syncthreads();
+  // Each wavefront's weight in the combined state, once per head: lane
+  // 16 (h % 4) + w of wavefront h / 4 (one 16-lane row per head).  Then every
+  // output channel sums the weighted wavefront states (independent LDS reads);
+  // the same arithmetic as the fused kernel's, so both give equal outputs.
+  static_assert(kNW == 16, "one 16-lane row per head");
+  if (wave < (HC + 3) / 4) {
+    const int hh = wave * 4 + lane / 16, w = lane % 16;
+    const bool in = hh < HC;
+    const int h = in ? hh : 0;
+    const float mw = in ? sm.wm[w][h] : -INFINITY;
+    const float M = row16_max(mw);
+    const float f = M == -INFINITY ? 0.f : __expf(mw - M);   // empty wavefronts: 0
+    const float Ls = row16_sum(in ? sm.wl[w][h] * f : 0.f);
+    if (in) {
+      sm.wf[h][w] = f;
+      if (w == 0) {
+        sm.hm[h] = M;
+        sm.hl[h] = Ls;
+      }
+    }
+  }
+  __syncthreads();
   for (int i = tid; i < HC * kHeadDim; i += kNT) {
     const int h = i / kHeadDim, c = i % kHeadDim;
-    float M = -INFINITY;
+    float Acc = 0.f;
 #pragma unroll
-    for (int w = 0; w < kNW; ++w) M = fmaxf(M, sm.wm[w][h]);
-    float Ls = 0.f, Acc = 0.f;
-#pragma unroll
-    for (int w = 0; w < kNW; ++w) {
-      const float f = M == -INFINITY ? 0.f : __expf(sm.wm[w][h] - M);   // empty wavefronts: 0
-      Ls = fmaf(sm.wl[w][h], f, Ls);
-      Acc = fmaf(sm.u.a.wacc[w][h][c], f, Acc);
-    }
+    for (int w = 0; w < kNW; ++w) Acc = fmaf(sm.u.a.wacc[w][h][c], sm.wf[h][w], Acc);
+    const float M = sm.hm[h], Ls = sm.hl[h];
     const int64_t bh = bh0 + h;
     if (n_split == 1) {
       out_[bh * kHeadDim + c] = Acc / Ls;

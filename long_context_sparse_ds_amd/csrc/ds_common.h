@@ -215,5 +215,14 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// Maximum over the 16 lanes of a DPP row; every lane of the row receives it.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f32<kDppXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppRor4>(v));
+  v = fmaxf(v, dpp_f32<kDppRor8>(v));
+  return v;
+}
+
 }  // namespace ds
 #endif

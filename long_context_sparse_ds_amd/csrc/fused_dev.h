@@ -10,7 +10,15 @@ namespace {
 
 // Operand and accumulator types of the matrix-core instructions.
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) short bf16x4_t;   // four bf16 bit patterns
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+// A float rounded to the nearest bf16, ties to even, as its 16-bit pattern in
+// the low half (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
 
 template <typename TE, int NT>
 struct Lanes {

@@ -52,9 +52,9 @@
 // from four v_mfma_f32_16x16x32_bf16 over the 128 channels, taken in an order
 // in which every lane's share of a K row is 32 contiguous channels; the online
 // softmax runs on that tile (a head's 16 tokens lie in one lane column of
-// four lanes); O^T += V^T P^T is 32 v_mfma_f32_16x16x4_f32 with P in fp32
-// (each lane's share of a V row is 8 contiguous channels, the output channels
-// permuted to match).  The state then takes the lane path's way to LDS.
+// four lanes); O^T += V^T P^T is 16 v_mfma_f32_16x16x16_bf16 with P split
+// into a bf16 head and remainder (each lane's share of a V row is 8
+// contiguous channels, the output channels permuted to match).  The state then takes the lane path's way to LDS.
 #include "fused_dev.h"
 #include "label_dot.h"
 
@@ -77,6 +77,8 @@ struct FusedSmem {
   uint32_t hist2[1024];     // bits 9..0
   uint32_t wsum[4][NW];     // one per prefix sum, so none needs a trailing barrier
   float wm[NW][HC], wl[NW][HC];
+  __align__(16) float wf[HC][NW];   // each wavefront's weight in the combined state, per head
+  float hm[HC], hl[HC];             // the combined maximum and denominator, per head
   uint32_t pick[3];         // digit, count above it, count in it
   unsigned ticket;
 };
@@ -567,13 +569,33 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
       M = Mn;
 #pragma unroll
       for (int c = 0; c < 8; ++c) o[c] *= alpha;
-      // O^T += V^T P^T over slots 4 g + i (k index g of the i-th product).
+      // O^T += V^T P^T over the 16 slots: per channel tile c, A = V^T (lane
+      // 16 g + j: channel 8 j + c of slots 4 g .. 4 g + 3, exact in bf16) and
+      // B = P^T (the lane's own four slots of head j), P being split into a
+      // bf16 head and a bf16 remainder (P = hi + lo to about 2^-16 relative),
+      // so two bf16 products give P V in fp32 accumulation.
+      uint32_t phi[2], plo[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float vf[8];
-        unpack(vq[i], vf, TE());
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const uint32_t a = bf16_rne(pr[2 * h2]), b = bf16_rne(pr[2 * h2 + 1]);
+        phi[h2] = a | (b << 16);
+        const uint32_t ra = bf16_rne(pr[2 * h2] - __uint_as_float(a << 16));
+        const uint32_t rb = bf16_rne(pr[2 * h2 + 1] - __uint_as_float(b << 16));
+        plo[h2] = ra | (rb << 16);
+      }
+      const bf16x4_t bh = __builtin_bit_cast(bf16x4_t, make_uint2(phi[0], phi[1]));
+      const bf16x4_t bl = __builtin_bit_cast(bf16x4_t, make_uint2(plo[0], plo[1]));
+      const uint32_t vw[4][4] = {{vq[0].x, vq[0].y, vq[0].z, vq[0].w}, {vq[1].x, vq[1].y, vq[1].z, vq[1].w},
+                                 {vq[2].x, vq[2].y, vq[2].z, vq[2].w}, {vq[3].x, vq[3].y, vq[3].z, vq[3].w}};
 #pragma unroll
-        for (int c = 0; c < 8; ++c) o[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[c], pr[i], o[c], 0, 0, 0);
+      for (int c = 0; c < 8; ++c) {
+        // bf16 element c of each slot's 8 channels: half (c & 1) of word c / 2.
+        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t lo = __builtin_amdgcn_perm(vw[1][c >> 1], vw[0][c >> 1], sel);
+        const uint32_t hi = __builtin_amdgcn_perm(vw[3][c >> 1], vw[2][c >> 1], sel);
+        const bf16x4_t av = __builtin_bit_cast(bf16x4_t, make_uint2(lo, hi));
+        o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bh, o[c], 0, 0, 0);
+        o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bl, o[c], 0, 0, 0);
       }
     }
     if (j < HC) {
@@ -667,9 +689,8 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
       }
     }
 
-    // Merge the lane groups of each wavefront (pairwise lane swaps), then the
-    // wavefronts through LDS: every output channel combines the NW wavefront
-    // states itself, so one barrier suffices.
+    // Merge the lane groups of each wavefront (pairwise lane swaps); the
+    // wavefronts' states then go through LDS.
     if constexpr (LPT == 16) merge_pairs<16, HC, EPL>(m, l, acc);
     merge_pairs<32, HC, EPL>(m, l, acc);
     if (grp == 0) {
@@ -685,18 +706,33 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
     }
   }
   __syncthreads();
+  // Each wavefront's weight in the combined state, once per head: lane
+  // 16 (h % 4) + w of wavefront h / 4 (one 16-lane row per head).  Then every
+  // output channel sums the weighted wavefront states (independent LDS reads).
+  static_assert(NW == 16, "one 16-lane row per head");
+  if (wave < (HC + 3) / 4) {
+    const int hh = wave * 4 + lane / 16, w = lane % 16;
+    const bool in = hh < HC;
+    const int h = in ? hh : 0;
+    const float mw = in ? sm.wm[w][h] : -INFINITY;
+    const float M = row16_max(mw);
+    const float f = M == -INFINITY ? 0.f : __expf(mw - M);   // empty wavefronts: 0
+    const float Ls = row16_sum(in ? sm.wl[w][h] * f : 0.f);
+    if (in) {
+      sm.wf[h][w] = f;
+      if (w == 0) {
+        sm.hm[h] = M;
+        sm.hl[h] = Ls;
+      }
+    }
+  }
+  __syncthreads();
   for (int i = tid; i < HC * kHeadDim; i += NT) {
     const int h = i / kHeadDim, c = i % kHeadDim;
-    float M = -INFINITY;
+    float A = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.wm[w][h]);
-    float Ls = 0.f, A = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float f = M == -INFINITY ? 0.f : __expf(sm.wm[w][h] - M);   // empty wavefronts: 0
-      Ls = fmaf(sm.wl[w][h], f, Ls);
-      A = fmaf(sm.u.a.wacc[w][h][c], f, A);
-    }
+    for (int w = 0; w < NW; ++w) A = fmaf(sm.u.a.wacc[w][h][c], sm.wf[h][w], A);
+    const float M = sm.hm[h], Ls = sm.hl[h];
     const int64_t bh = bh0 + h;
     if (n_split == 1) {
       a.out[bh * kHeadDim + c] = Ls > 0.f ? A / Ls : 0.f;   // nothing kept (threshold rule): zero
