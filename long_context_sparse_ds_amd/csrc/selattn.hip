@@ -269,6 +269,15 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
 #pragma unroll
     for (int j = 0; j < R; ++j) qr[j] = qs_l[j];
     for (int c0 = 0; c0 < ITEMS; c0 += CB) {
+      if (c0 * NT >= T_row) {   // (uniform) passes wholly past the sequence: no loads, -inf scores
+#pragma unroll
+        for (int i = 0; i < CB; ++i) {
+          const int u = (c0 + i) * NT + tid;
+          const int ut = u / ITEMS, uj = u % ITEMS;
+          sm.u.sc[((uj >> 2) * NT + ut) * 4 + (uj & 3)] = -INFINITY;
+        }
+        continue;
+      }
       uint4 raw[CB][LNV];
 #pragma unroll
       for (int i = 0; i < CB; ++i) {
