@@ -317,13 +317,18 @@ __global__ __launch_bounds__(kNT) void partition_onepass_kernel(
     }
   }
   __syncthreads();
+  // Units past the partition get key 0, below every finite score's key (at
+  // least 0x00800000, so their top digit is below any digit the selection can
+  // reach): they are never counted, gathered or kept, as k_p never exceeds the
+  // partition's units.  So no per-unit validity is carried (a bool array of
+  // ITEMS flags lives in scalar lane masks, which spill at this register count).
   uint32_t key[ITEMS];
   bool valid[ITEMS];
-  const int64_t first = int64_t(tid) * ITEMS;
+  const int first = tid * ITEMS;
 #pragma unroll
   for (int j = 0; j < ITEMS; ++j) {
-    valid[j] = first + j < n_p;
-    key[j] = valid[j] ? float_key(u.sc[((j >> 2) * kNT + tid) * 4 + (j & 3)]) : 0u;
+    valid[j] = true;
+    key[j] = first + j < int(n_p) ? float_key(u.sc[((j >> 2) * kNT + tid) * 4 + (j & 3)]) : 0u;
   }
   const uint32_t hist_hi = hist1[2047 - 2 * tid], hist_lo = hist1[2046 - 2 * tid];
   __syncthreads();   // the scores are in registers: the selection's buffers overlay them
