@@ -248,9 +248,10 @@ __global__ __launch_bounds__(kNT) void partition_onepass_kernel(
     uint16_t* __restrict__ cand_hist, unsigned* __restrict__ tickets, int32_t tickets_per_row) {
   constexpr int ITEMS = kPartItems;
   constexpr int RMAX = R > 0 ? R : kHeadDim;
-  // Label rows requested together per thread (64 bytes), as in the one-pass
-  // fused kernel.
-  constexpr int CB = R == 0 ? 4 : (LNV == 1 ? 4 : LNV == 2 ? 2 : 1);
+  // Label rows requested together per thread: 64 bytes of 16-byte rows, one
+  // row otherwise (two 32-byte rows with their sixteen double channel weights
+  // need more than the 128 VGPRs of a 1024-thread workgroup).
+  constexpr int CB = R == 0 ? 4 : (LNV == 1 ? 4 : 1);
   static_assert(ITEMS % CB == 0, "whole batches of passes");
   __shared__ union {
     float sc[kPartUnits];   // the partition's scores, in the owners' layout
