@@ -449,14 +449,12 @@ __global__ __launch_bounds__(kNT) void bucket_attn_kernel(
       float mx = m[h];
 #pragma unroll
       for (int u = 0; u < KU; ++u) mx = fmaxf(mx, z[u]);
-      // A lane group with no kept row so far takes no branch (the compiler would
-      // then issue the V loads only after the scores): ms = 0 makes its weights 0.
-      const float ms = mx == -INFINITY ? 0.f : mx;
-      const float alpha = __expf(m[h] - ms);
+      if (mx == -INFINITY) continue;   // uniform across the lane group
+      const float alpha = __expf(m[h] - mx);
       float p[KU], psum = 0.f;
 #pragma unroll
       for (int u = 0; u < KU; ++u) {
-        p[u] = __expf(z[u] - ms);
+        p[u] = __expf(z[u] - mx);
         psum += p[u];
       }
       l[h] = l[h] * alpha + psum;
