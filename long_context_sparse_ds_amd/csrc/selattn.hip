@@ -488,13 +488,18 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
   {
     uint32_t eq_seen = ex & 0xFFFFu;
     int pos = int(ex >> 16) + int(min(eq_seen, eq_take));
-    for (uint32_t m = keepm | eqm; m != 0u; m &= m - 1u) {
-      const int j = __builtin_ctz(m);
-      bool take = true;
-      if (eqm & (1u << j)) take = eq_seen++ < eq_take;
-      if (take) {
-        if (pos >= u_lo && pos < u_hi) sm.u.a.sel[pos - u_lo] = first + j;
-        ++pos;
+    // This thread's kept units take positions [pos, pos + n_take): only a
+    // thread whose range meets this split's slots walks its masks.
+    const int n_take = __popc(keepm) + int(min(uint32_t(__popc(eqm)), eq_take > eq_seen ? eq_take - eq_seen : 0u));
+    if (pos < u_hi && pos + n_take > u_lo) {
+      for (uint32_t m = keepm | eqm; m != 0u; m &= m - 1u) {
+        const int j = __builtin_ctz(m);
+        bool take = true;
+        if (eqm & (1u << j)) take = eq_seen++ < eq_take;
+        if (take) {
+          if (pos >= u_lo && pos < u_hi) sm.u.a.sel[pos - u_lo] = first + j;
+          ++pos;
+        }
       }
     }
   }
