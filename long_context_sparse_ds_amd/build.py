@@ -14,6 +14,14 @@ builds libdsparse_hostsan.so under _build/: the host code of the boundary
 calibration) instrumented with AddressSanitizer and UndefinedBehaviorSanitizer,
 linked with the ordinary kernel objects.  Device code is never instrumented.
 Load it with clang's ASan runtime preloaded and DSPARSE_LIB pointing at it.
+
+    python -m long_context_sparse_ds_amd.build --stamps
+
+builds libdsparse_stamps.so beside the library: every kernel source compiled with
+DS_STAMPS, so the score, bucket, fused and first-stage kernels record clock
+stamps at their phase boundaries (csrc/stamps.h); python -m
+long_context_sparse_ds_amd.stamps runs a workload through it and prints the
+per-phase timeline.  The ordinary library is built without them.
 """
 from __future__ import annotations
 
@@ -30,6 +38,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdsparse.so")
 LIB_HOSTSAN = os.path.join(BUILD, "libdsparse_hostsan.so")
+LIB_STAMPS = os.path.join(PKG, "libdsparse_stamps.so")
 
 HIP_SOURCES = ["ds_api.hip", "pack.hip", "score.hip", "select.hip", "selattn.hip", "bucket.hip", "attn.hip",
                "hip_search.hip"]
@@ -137,8 +146,33 @@ def build_host_sanitized(verbose: bool = False) -> str:
     return LIB_HOSTSAN
 
 
+def build_stamped(verbose: bool = False) -> str:
+    """The library with the kernels' clock stamps compiled in (-DDS_STAMPS), beside libdsparse.so."""
+    out = os.path.join(BUILD, "stamps")
+    os.makedirs(out, exist_ok=True)
+    hipcc = _hipcc()
+    jobs, objs = [], []
+    for src in HIP_SOURCES:
+        obj = os.path.join(out, src.replace(".hip", ".o"))
+        objs.append(obj)
+        jobs.append([hipcc, "-x", "hip", "-c", *hip_flags(), "-DDS_STAMPS", os.path.join(CSRC, src), "-o", obj])
+    for src in CPP_SOURCES:
+        obj = os.path.join(out, src.replace(".cpp", ".o"))
+        objs.append(obj)
+        jobs.append(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", "-c",
+                     os.path.join(CSRC, src), "-o", obj])
+    with ThreadPoolExecutor(min(8, len(jobs))) as ex:
+        list(ex.map(lambda c: _run(c, verbose), jobs))
+    tmp = LIB_STAMPS + ".tmp"
+    _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-Wl,--no-undefined", "-o", tmp, *objs], verbose)
+    os.replace(tmp, LIB_STAMPS)
+    return LIB_STAMPS
+
+
 if __name__ == "__main__":
     if "--sanitize-host" in sys.argv:
         print(build_host_sanitized(verbose="-v" in sys.argv))
+    elif "--stamps" in sys.argv:
+        print(build_stamped(verbose="-v" in sys.argv))
     else:
         print(build(verbose="-v" in sys.argv))

@@ -57,6 +57,8 @@
 // 3 us slower per step on the 16K-token, 32-head shape.
 #include "fused_dev.h"
 
+DS_STAMP_BUFFER(bucket)
+
 namespace ds {
 namespace {
 
@@ -147,6 +149,7 @@ __global__ __launch_bounds__(kNT) void bucket_attn_kernel(
   using LN = Lanes<TE, kNT>;
   constexpr int EPL = LN::EPL, LPT = LN::LPT, GPW = LN::GPW, NG = LN::NG, KU = LN::KU;
   __shared__ BucketSmem<HC> sm;
+  DS_STAMP_START(bucket);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane / LPT, sub = lane % LPT;
@@ -208,6 +211,7 @@ __global__ __launch_bounds__(kNT) void bucket_attn_kernel(
   }
   sm.rhi[tid] = R_hi;
   __syncthreads();
+  DS_STAMP(bucket, 2);   // prefix words and list heads in
 
   // B. d0: R[d0] < k <= R[d0 - 1] (R[-1] = every unit); R[b_lo - 1] is the next thread's R[b_hi].
   {
@@ -224,6 +228,7 @@ __global__ __launch_bounds__(kNT) void bucket_attn_kernel(
     }
   }
   __syncthreads();
+  DS_STAMP(bucket, 3);   // d0
   // (Counts are bounded by the row's units, so that lists inconsistent with
   // their prefixes cannot send a loop or an access out of range.)
   const uint32_t d0 = sm.info[0], A = min(sm.info[1], k), cnt0 = min(sm.info[2], uint32_t(n_units));
@@ -252,6 +257,7 @@ __global__ __launch_bounds__(kNT) void bucket_attn_kernel(
     }
   }
   __syncthreads();
+  DS_STAMP(bucket, 4);   // the tiles' slices
   // A tile-local id read from a list, as a token of tile t (masked into the tile).
   const auto token_of = [&](int t, uint32_t id) -> int { return t * kTileU + int(min(id, tile_count(t) - 1u)); };
   const auto mark = [&](uint32_t* m, int tok) { atomicOr(&m[uint32_t(tok) >> 5], 1u << (tok & 31)); };
@@ -311,6 +317,7 @@ __global__ __launch_bounds__(kNT) void bucket_attn_kernel(
     }
   };
   __syncthreads();
+  DS_STAMP(bucket, 5);   // candidates classified
 
   // D. Narrow the threshold inside d0: thr is a key, eq_take the number of keys
   // equal to thr to keep (lowest token ids first), all_eq when that is all of them.
@@ -372,6 +379,7 @@ __global__ __launch_bounds__(kNT) void bucket_attn_kernel(
     if (keep) mark(sm.map, tok);
   });
   __syncthreads();
+  DS_STAMP(bucket, 6);   // radix passes and join
 
   // Ascending positions: thread w holds map word w.  Split s takes positions
   // [p0, p1): it writes those indices (one head chunk does) and keeps their tokens.
@@ -381,6 +389,7 @@ __global__ __launch_bounds__(kNT) void bucket_attn_kernel(
   uint32_t pos = block_exclusive_scan1<kNT>(cnt, sm.wsum, total);   // total = k
   const uint32_t p0 = split * uint32_t(chunk_), p1 = min(p0 + uint32_t(chunk_), k);
   const int n_sel = p0 < p1 ? int(p1 - p0) : 0;
+  DS_STAMP(bucket, 7);   // position scan
   if (pos < p1 && pos + cnt > p0) {
     int32_t* ridx = indices_ + int64_t(row) * k_units_;
     for (uint32_t w = word; w != 0u; w &= w - 1u, ++pos) {
@@ -391,6 +400,7 @@ __global__ __launch_bounds__(kNT) void bucket_attn_kernel(
     }
   }
   __syncthreads();
+  DS_STAMP(bucket, 8);   // the split's indices written
 
   // E. Attention over the split's kept rows.
   const TE* __restrict__ K = static_cast<const TE*>(K_);
@@ -473,6 +483,7 @@ __global__ __launch_bounds__(kNT) void bucket_attn_kernel(
   // states then go through LDS.
   if constexpr (LPT == 16) merge_pairs<16, HC, EPL>(m, l, acc);
   merge_pairs<32, HC, EPL>(m, l, acc);
+  DS_STAMP(bucket, 9);   // wavefront 0's gather and lane-group merge
   if (grp == 0) {
 #pragma unroll
     for (int h = 0; h < HC; ++h) {
@@ -485,6 +496,7 @@ __global__ __launch_bounds__(kNT) void bucket_attn_kernel(
     }
   }
   __syncthreads();
+  DS_STAMP(bucket, 10);   // every wavefront's state in LDS
   // Each wavefront's weight in the combined state, once per head: lane
   // 16 (h % 4) + w of wavefront h / 4 (one 16-lane row per head).  Then every
   // output channel sums the weighted wavefront states (independent LDS reads);
@@ -507,6 +519,7 @@ __global__ __launch_bounds__(kNT) void bucket_attn_kernel(
     }
   }
   __syncthreads();
+  DS_STAMP(bucket, 11);   // combine weights
   for (int i = tid; i < HC * kHeadDim; i += kNT) {
     const int h = i / kHeadDim, c = i % kHeadDim;
     float Acc = 0.f;
@@ -526,15 +539,24 @@ __global__ __launch_bounds__(kNT) void bucket_attn_kernel(
       }
     }
   }
-  if (n_split == 1) return;
+  DS_STAMP(bucket, 12);   // output or split state stored
+  if (n_split == 1) {
+    DS_STAMP_END(bucket);
+    return;
+  }
 
   // The row's last workgroup merges the splits (ordering: see the file header).
   __builtin_amdgcn_s_waitcnt(0);   // this wavefront's state stores have completed
+  DS_STAMP(bucket, 13);   // the stores completed
   __syncthreads();
   unsigned* ticket = tickets_ + rc;
   if (tid == 0) sm.ticket = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  if (sm.ticket != unsigned(n_split - 1)) return;
+  DS_STAMP(bucket, 14);   // ticket
+  if (sm.ticket != unsigned(n_split - 1)) {
+    DS_STAMP_END(bucket);
+    return;
+  }
   constexpr int kBatch = 8;   // splits whose states are requested together
   for (int i = tid; i < HC * kHeadDim; i += kNT) {
     const int h = i / kHeadDim, c = i % kHeadDim;
@@ -575,6 +597,8 @@ __global__ __launch_bounds__(kNT) void bucket_attn_kernel(
     out_[bh * kHeadDim + c] = Acc / Ls;
   }
   if (tid == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  DS_STAMP(bucket, 15);   // splits merged
+  DS_STAMP_END(bucket);
 }
 
 template <typename TE, int HC>

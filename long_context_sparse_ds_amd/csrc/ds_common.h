@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "stamps.h"
+
 namespace ds {
 
 constexpr int kHeadDim = 128;

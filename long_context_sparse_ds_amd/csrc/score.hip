@@ -38,6 +38,8 @@
 #include "label_dot.h"
 #include "select_dev.h"
 
+DS_STAMP_BUFFER(score)
+
 namespace ds {
 namespace {
 
@@ -121,6 +123,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
     row = b * uint32_t(Hkv) + g;
   }
   TE* L = label + int64_t(row) * T_cap * r;
+  DS_STAMP_START(score);
   const int t0 = int(tile) * kTile + int(threadIdx.x);
   int Ti = T, ta = t_append;
   if constexpr (RAGGED) {
@@ -200,6 +203,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
   }
   if (threadIdx.x < r) sch[threadIdx.x] = cj;
   __syncthreads();
+  DS_STAMP(score, 2);   // q and the channel table in
 
   // An appended token's label row and score, from the staged K row when
   // there is one (separate calls keep the LDS reads LDS reads).
@@ -288,6 +292,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
     }
   }
 
+  DS_STAMP(score, 3);   // wavefront 0's label rows in and scored
   float* out = scores + int64_t(row) * ld;
   // Each unit score this thread writes: value and whether it exists.
   float uv[kTPT];
@@ -326,6 +331,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
       rk[i] = has[i] ? atomicAdd(&h[bin[i]], 1u) : 0u;
     }
     __syncthreads();
+    DS_STAMP(score, 4);   // the tile's top-digit histogram
     // Thread t owns bins 2047 - 4t down to 2044 - 4t, so thread order is
     // descending digit order and one prefix sum gives every bin's start.
     const int hb = kHistBins - 1 - per * int(threadIdx.x);
@@ -338,6 +344,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
     __shared__ uint32_t wsum[kThreads / 64];
     uint32_t tot;
     uint32_t p = block_exclusive_scan1<kThreads>(sum, wsum, tot);   // one barrier; wsum is not used again
+    DS_STAMP(score, 5);   // bin starts
     uint32_t P[per];
 #pragma unroll
     for (int j = 0; j < per; ++j) {
@@ -348,12 +355,14 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
     uint16_t* dst = tile_hist + (int64_t(row) * n_tiles + tile) * kHistBins + (hb - (per - 1));
     *reinterpret_cast<uint2*>(dst) = make_uint2(P[3] | (P[2] << 16), P[1] | (P[0] << 16));
     __syncthreads();
+    DS_STAMP(score, 6);   // descending prefix stored
     __shared__ __align__(16) uint32_t sent[SORT ? kTile : 1];
 #pragma unroll
     for (int i = 0; i < kTPT; ++i)
       if (has[i])
         sent[h[bin[i]] + rk[i]] = ((float_key(uv[i]) & 0x1FFFFFu) << 11) | uint32_t(threadIdx.x + i * kThreads);
     __syncthreads();
+    DS_STAMP(score, 7);   // the tile sorted in LDS
     const int n_tile = min(kTile, Ti - tile0);
     uint32_t* sl = reinterpret_cast<uint32_t*>(out) + tile0;
     if (n_tile == kTile) {
@@ -377,6 +386,8 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ 
   // The row's merge tickets for the fused kernel that follows start at zero.
   if (tickets != nullptr && tile == 0)
     for (int i = threadIdx.x; i < tickets_per_row; i += kThreads) tickets[int64_t(row) * tickets_per_row + i] = 0u;
+  DS_STAMP(score, 8);   // stores issued
+  DS_STAMP_END(score);
 }
 
 template <typename TE, bool RAGGED, bool POS, bool SORT>

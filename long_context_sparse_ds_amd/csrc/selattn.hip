@@ -58,6 +58,8 @@
 #include "fused_dev.h"
 #include "label_dot.h"
 
+DS_STAMP_BUFFER(selattn)
+
 namespace ds {
 namespace {
 
@@ -171,6 +173,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
   a.unit_ids = unit_ids_;
   a.xcd_rows = xcd_rows_;
   using LN = Lanes<TE, NT>;
+  DS_STAMP_START(selattn);
   constexpr int NW = LN::NW, EPL = LN::EPL, LPT = LN::LPT, GPW = LN::GPW, NG = LN::NG, KU = LN::KU;
   constexpr int BPT1 = 2048 / NT, BPT2 = 1024 / NT;
   static_assert(ITEMS % 4 == 0 && ITEMS <= 32, "per-thread masks are 32 bits");
@@ -300,6 +303,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
       }
     }
     __syncthreads();
+    DS_STAMP(selattn, 16);   // one pass: the row's label rows scored
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) s[j] = sm.u.sc[((j >> 2) * NT + tid) * 4 + (j & 3)];
   } else if (first + ITEMS <= n_units) {
@@ -386,6 +390,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
 
   // Threshold rule: this thread's units scoring at least tau (-inf padding and
   // units past a short sequence never count).
+  DS_STAMP(selattn, 2);   // scores and top-digit counts in
   const bool thresh = a.counts != nullptr;
   uint32_t passm = 0u;
   if (thresh) {
@@ -399,6 +404,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
   const uint32_t k = uint32_t(k_row);
   const uint32_t n_pass = pick_bin<NT, 2048>(c1, k, sm.wsum[0], sm.pick, uint32_t(__popc(passm)));
   __syncthreads();
+  DS_STAMP(selattn, 3);   // d0
   // Kept units of the row; with the threshold rule, when no more than k pass,
   // they are exactly the passing ones and the search below is skipped.
   int k_keep = k_row;
@@ -429,6 +435,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
 
     // Narrow the threshold inside d0: thr is a key, eq_take the number of keys
     // equal to thr to keep (lowest unit ids first), all_eq when that is all of them.
+    DS_STAMP(selattn, 4);   // units classified against d0
     uint32_t thr = d0 << 21;
     bool all_eq = true;
     bool settled = kk == cnt0;   // every key of digit d0 is needed
@@ -440,6 +447,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
       __syncthreads();
       uint32_t c[BPT1];
       read_bins<NT, 2048>(sm.hist1, c);
+      DS_STAMP(selattn, 5);   // first candidate pass's histogram
       pick_bin<NT, 2048>(c, kk, sm.wsum[1], sm.pick);
       __syncthreads();
       thr |= sm.pick[0] << 10;
@@ -453,6 +461,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
         __syncthreads();
         uint32_t c2[BPT2];
         read_bins<NT, 1024>(sm.hist2, c2);
+        DS_STAMP(selattn, 6);   // second candidate pass's histogram
         pick_bin<NT, 1024>(c2, kk, sm.wsum[2], sm.pick);
         __syncthreads();
         thr |= sm.pick[0];
@@ -465,6 +474,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
     // Kept units of this thread: above d0, plus candidates at or above thr (when
     // all keys equal to a full-precision thr are kept), or above thr and the
     // first eq_take equal ones in unit order.
+    DS_STAMP(selattn, 7);   // exact threshold
     keepm = gtm;
     if (thr == (d0 << 21) && all_eq) {
       keepm |= cm;
@@ -477,6 +487,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
       }
     }
   }   // !compact
+  DS_STAMP(selattn, 8);   // kept units classified
   uint32_t tot;
   const uint32_t ex = block_exclusive_scan1<NT>((uint32_t(__popc(keepm)) << 16) | uint32_t(__popc(eqm)),
                                                 sm.wsum[3], tot);
@@ -504,6 +515,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
     }
   }
   __syncthreads();
+  DS_STAMP(selattn, 9);   // the split's kept list in LDS
   if (a.unit_ids != nullptr) {
     // Candidates of a long row: their kept slots become the units they stand for.
     const int32_t* ids = a.unit_ids + int64_t(row) * n_units;
@@ -511,12 +523,14 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
       if (u_lo + i < k_keep) sm.u.a.sel[i] = ids[sm.u.a.sel[i]];
     __syncthreads();
   }
+  DS_STAMP(selattn, 10);   // candidate slots mapped to units
   if (hchunk == 0) {
     int32_t* ridx = a.indices + int64_t(row) * k_units + u_lo;
     for (int i = tid; i < u_hi - u_lo; i += NT) ridx[i] = u_lo + i < k_keep ? sm.u.a.sel[i] : -1;
     if (thresh && split == 0 && tid == 0) a.counts[row] = k_keep;
   }
 
+  DS_STAMP(selattn, 11);   // indices written
   // Attention over the split's kept rows.
   if constexpr (kMfma) {
     // Kept position p of this split: its token, and whether it is one.
@@ -612,6 +626,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
         o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bl, o[c], 0, 0, 0);
       }
     }
+    DS_STAMP(selattn, 12);   // wavefront 0's gather
     if (j < HC) {
       if (g == 0) {
         sm.wm[wave][j] = M;
@@ -703,6 +718,7 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
       }
     }
 
+    DS_STAMP(selattn, 12);   // wavefront 0's gather
     // Merge the lane groups of each wavefront (pairwise lane swaps); the
     // wavefronts' states then go through LDS.
     if constexpr (LPT == 16) merge_pairs<16, HC, EPL>(m, l, acc);
@@ -761,7 +777,11 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
       }
     }
   }
-  if (n_split == 1) return;
+  DS_STAMP(selattn, 13);   // output or split state stored
+  if (n_split == 1) {
+    DS_STAMP_END(selattn);
+    return;
+  }
 
   // The row's last workgroup merges the splits.
   __builtin_amdgcn_s_waitcnt(0);   // this thread's state stores have completed
@@ -769,7 +789,11 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
   unsigned* ticket = a.tickets + rc;
   if (tid == 0) sm.ticket = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  if (sm.ticket != unsigned(n_split - 1)) return;
+  DS_STAMP(selattn, 14);   // ticket
+  if (sm.ticket != unsigned(n_split - 1)) {
+    DS_STAMP_END(selattn);
+    return;
+  }
   constexpr int kBatch = 8;   // splits whose states are requested together
   for (int i = tid; i < HC * kHeadDim; i += NT) {
     const int h = i / kHeadDim, c = i % kHeadDim;
@@ -810,6 +834,8 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
     a.out[bh * kHeadDim + c] = L > 0.f ? A / L : 0.f;   // nothing kept (threshold rule): zero
   }
   if (tid == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  DS_STAMP(selattn, 15);   // splits merged
+  DS_STAMP_END(selattn);
 }
 
 template <typename TE, int NT, int ITEMS, int HC, bool RAGGED, int LNV>

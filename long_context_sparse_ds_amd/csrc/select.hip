@@ -12,6 +12,8 @@
 #include "label_dot.h"
 #include "select_dev.h"
 
+DS_STAMP_BUFFER(select)
+
 namespace ds {
 namespace {
 
@@ -135,6 +137,7 @@ __device__ __forceinline__ void partition_finish(const uint32_t (&key)[ITEMS], c
   uint32_t kk, mask;
   const uint32_t tau = select_threshold<kNT, ITEMS>(key, valid, uint32_t(k_p), sm, kk, mask, have_hist, hist_hi,
                                                     hist_lo);
+  DS_STAMP(select, 3);   // the partition's threshold
   if (cand_hist != nullptr) {
     // The candidates' histogram: every key in a digit above d0 is kept, k_p
     // minus those in d0, none below.
@@ -155,6 +158,7 @@ __device__ __forceinline__ void partition_finish(const uint32_t (&key)[ITEMS], c
   // final positions, and the window is then written with coalesced stores.
   // Scattered 4-byte stores straight from the emission cost more than the
   // selection itself.
+  DS_STAMP(select, 4);   // candidates' histogram stored
   constexpr int kWin = CAP;
   static_assert(kPartUnits <= 65536, "partition-local ids fit 16 bits");
   const int64_t first = int64_t(threadIdx.x) * ITEMS;
@@ -177,6 +181,8 @@ __device__ __forceinline__ void partition_finish(const uint32_t (&key)[ITEMS], c
     cs[i] = -INFINITY;
     ci[i] = -1;
   }
+  DS_STAMP(select, 5);   // candidates emitted (stores issued)
+  DS_STAMP_END(select);
 }
 
 constexpr int kPartItems = int(kPartUnits / kNT);
@@ -253,6 +259,7 @@ __global__ __launch_bounds__(kNT) void partition_onepass_kernel(
   // need more than the 128 VGPRs of a 1024-thread workgroup).
   constexpr int CB = R == 0 ? 4 : (LNV == 1 ? 4 : 1);
   static_assert(ITEMS % CB == 0, "whole batches of passes");
+  DS_STAMP_START(select);
   __shared__ union {
     float sc[kPartUnits];   // the partition's scores, in the owners' layout
     struct {
@@ -318,6 +325,7 @@ __global__ __launch_bounds__(kNT) void partition_onepass_kernel(
     }
   }
   __syncthreads();
+  DS_STAMP(select, 2);   // the partition scored
   // Units past the partition get key 0, below every finite score's key (at
   // least 0x00800000, so their top digit is below any digit the selection can
   // reach): they are never counted, gathered or kept, as k_p never exceeds the
