@@ -63,13 +63,14 @@ def log(msg):
 # The sources that build each timed stage's kernels and plan their launches: a recorded counter reading stays
 # valid while these files are unchanged (the other kernels' sources do not enter its digest).
 STAGE_SOURCES = {
-    "decode_score": ("ds_api.hip", "ds_common.h", "label_dot.h", "score.hip", "select_dev.h", "select.hip"),
-    "decode_select_attend": ("ds_api.hip", "ds_common.h", "label_dot.h", "select_dev.h", "fused_dev.h", "select.hip",
-                             "selattn.hip", "bucket.hip", "attn.hip"),
-    "decode_step_one_pass": ("ds_api.hip", "ds_common.h", "label_dot.h", "select_dev.h", "fused_dev.h",
+    "decode_score": ("ds_api.hip", "ds_common.h", "stamps.h", "label_dot.h", "score.hip", "select_dev.h",
+                     "select.hip"),
+    "decode_select_attend": ("ds_api.hip", "ds_common.h", "stamps.h", "label_dot.h", "select_dev.h", "fused_dev.h",
+                             "select.hip", "selattn.hip", "bucket.hip", "attn.hip"),
+    "decode_step_one_pass": ("ds_api.hip", "ds_common.h", "stamps.h", "label_dot.h", "select_dev.h", "fused_dev.h",
                              "selattn.hip"),
-    "hip_search": ("ds_api.hip", "ds_common.h", "hip_search.hip"),
-    "attention_from_indices": ("ds_api.hip", "ds_common.h", "attn.hip"),
+    "hip_search": ("ds_api.hip", "ds_common.h", "stamps.h", "hip_search.hip"),
+    "attention_from_indices": ("ds_api.hip", "ds_common.h", "stamps.h", "attn.hip"),
 }
 
 

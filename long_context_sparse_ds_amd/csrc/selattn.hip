@@ -497,22 +497,23 @@ __global__ __launch_bounds__(NT) void selattn_kernel(
   const int u_lo = p_begin >> lb;
   const int u_hi = (min(p_begin + a.chunk, a.kv_virtual) + block - 1) >> lb;   // kept-list slots of this split
   {
-    uint32_t eq_seen = ex & 0xFFFFu;
+    // This thread's kept units: keepm, plus its first n_eq units equal to the
+    // threshold (the tied units kept go lowest unit first across the row).
+    // They take positions [pos, pos + popc(takem)) in unit order; only a thread
+    // whose range meets this split's slots walks them.
+    const uint32_t eq_seen = ex & 0xFFFFu;
     int pos = int(ex >> 16) + int(min(eq_seen, eq_take));
-    // This thread's kept units take positions [pos, pos + n_take): only a
-    // thread whose range meets this split's slots walks its masks.
-    const int n_take = __popc(keepm) + int(min(uint32_t(__popc(eqm)), eq_take > eq_seen ? eq_take - eq_seen : 0u));
-    if (pos < u_hi && pos + n_take > u_lo) {
-      for (uint32_t m = keepm | eqm; m != 0u; m &= m - 1u) {
-        const int j = __builtin_ctz(m);
-        bool take = true;
-        if (eqm & (1u << j)) take = eq_seen++ < eq_take;
-        if (take) {
-          if (pos >= u_lo && pos < u_hi) sm.u.a.sel[pos - u_lo] = first + j;
-          ++pos;
-        }
-      }
+    const uint32_t n_eq = min(uint32_t(__popc(eqm)), eq_take > eq_seen ? eq_take - eq_seen : 0u);
+    uint32_t takem = keepm;
+    if (n_eq == uint32_t(__popc(eqm))) {
+      takem |= eqm;
+    } else {
+      uint32_t m = eqm;
+      for (uint32_t i = 0; i < n_eq; ++i, m &= m - 1u) takem |= m & (0u - m);
     }
+    if (pos < u_hi && pos + __popc(takem) > u_lo)
+      for (uint32_t m = takem; m != 0u; m &= m - 1u, ++pos)
+        if (pos >= u_lo && pos < u_hi) sm.u.a.sel[pos - u_lo] = first + __builtin_ctz(m);
   }
   __syncthreads();
   DS_STAMP(selattn, 9);   // the split's kept list in LDS
