@@ -35,6 +35,30 @@ __device__ __forceinline__ double score_q_sum(const TE* __restrict__ qg, int G, 
   return s;
 }
 
+// The same sums in two steps, so that other requests can go out between the
+// loads and the additions: q_load8 requests the first eight heads' values
+// (a loop over a run-time head count would wait for each); q_add8 adds them
+// in score_q_sum's order (kScoreOrder) or group_q_sum's, the heads past the
+// eighth read there.
+template <typename TE>
+__device__ __forceinline__ void q_load8(const TE* __restrict__ qg, int G, int c, float (&v)[8]) {
+#pragma unroll
+  for (int h = 0; h < 8; ++h) v[h] = elem_to_f32(qg[int64_t(h < G ? h : 0) * kHeadDim + c]);
+}
+
+template <bool kScoreOrder, typename TE>
+__device__ __forceinline__ double q_add8(const float (&v)[8], const TE* __restrict__ qg, int G, int c) {
+  double s = 0.0;
+  if (kScoreOrder)
+    for (int h = 8; h < G; ++h) s += double(elem_to_f32(qg[int64_t(h) * kHeadDim + c]));
+#pragma unroll
+  for (int h = 0; h < 8; ++h)
+    if (h < G) s += double(v[h]);
+  if (!kScoreOrder)
+    for (int h = 8; h < G; ++h) s += double(elem_to_f32(qg[int64_t(h) * kHeadDim + c]));
+  return s;
+}
+
 // NV 16-byte words of one label row against qr[0 .. 8 NV) (bf16) or
 // qr[0 .. 4 NV) (fp32), in channel order.
 template <int NV>
@@ -75,6 +99,23 @@ __device__ __forceinline__ float append_row(const TE* __restrict__ Krow, TE* __r
     const TE v = Krow[sch[j]];
     Lrow[j] = v;
     a = fma(qs[j], double(elem_to_f32(v)), a);
+  }
+  return float(a);
+}
+
+// append_row for a label width R known at compile time: every channel is
+// requested before any is used (one round trip), with the same arithmetic.
+template <int R, typename TE>
+__device__ __forceinline__ float append_row_n(const TE* __restrict__ Krow, TE* __restrict__ Lrow, const int* sch,
+                                              const double* qs) {
+  TE v[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) v[j] = Krow[sch[j]];
+  double a = 0.0;
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    Lrow[j] = v[j];
+    a = fma(qs[j], double(elem_to_f32(v[j])), a);
   }
   return float(a);
 }

@@ -268,6 +268,7 @@ __global__ __launch_bounds__(kNT) void partition_onepass_kernel(
     } b;
   } u;
   __shared__ uint32_t hist1[kHistBins];
+  __shared__ double qall[kHeadDim];   // the group's q summed over its heads, every channel
   __shared__ double qs_l[RMAX];
   __shared__ int ch_l[RMAX];
   const int r = R > 0 ? R : r_rt;
@@ -277,23 +278,18 @@ __global__ __launch_bounds__(kNT) void partition_onepass_kernel(
   const int64_t n_p = min(kPartUnits, n - base);
   const int64_t k_p = min(k, n_p);
   const int g = int(row % Hkv);
-  if (tid < r) {
-    const int cj = ch[g * r + tid];
-    qs_l[tid] = score_q_sum(q + row * G * kHeadDim, G, cj);
-    ch_l[tid] = cj;
-  }
-  for (int i = tid; i < kHistBins; i += kNT) hist1[i] = 0u;
-  if (tickets != nullptr && p == 0)
-    for (int i = tid; i < tickets_per_row; i += kNT) tickets[row * tickets_per_row + i] = 0u;
-  __syncthreads();
+  // Loads that do not wait on each other: the q sums of all 128 channels
+  // (so that none waits for the channel table), the channel table, and the
+  // first pass's label rows; the label channels' sums are picked after them.
+  // (The loads are unconditional, only the stores below are not: a load in a
+  // branch is waited for where the branch ends, before the label rows' requests.)
+  const TE* qg = q + row * G * kHeadDim;
+  float qv8[8];
+  q_load8(qg, G, tid & (kHeadDim - 1), qv8);
+  const int cj = ch[g * r + (tid < r ? tid : 0)];
   TE* lab = label + row * T_cap * r;
-  double qr[RMAX];
-  if constexpr (R > 0) {
-#pragma unroll
-    for (int j = 0; j < R; ++j) qr[j] = qs_l[j];
-  }
-  for (int c0 = 0; c0 < ITEMS; c0 += CB) {
-    uint4 raw[CB][LNV > 0 ? LNV : 1];
+  uint4 raw[CB][LNV > 0 ? LNV : 1];
+  const auto load_pass = [&](int c0) {
     if constexpr (R > 0) {
 #pragma unroll
       for (int i = 0; i < CB; ++i) {
@@ -303,6 +299,24 @@ __global__ __launch_bounds__(kNT) void partition_onepass_kernel(
         for (int v = 0; v < LNV; ++v) raw[i][v] = pr[v];
       }
     }
+  };
+  load_pass(0);
+  const double qsum = q_add8<true>(qv8, qg, G, tid & (kHeadDim - 1));
+  if (tid < kHeadDim) qall[tid] = qsum;
+  if (tid < r) ch_l[tid] = cj;
+  for (int i = tid; i < kHistBins; i += kNT) hist1[i] = 0u;
+  if (tickets != nullptr && p == 0)
+    for (int i = tid; i < tickets_per_row; i += kNT) tickets[row * tickets_per_row + i] = 0u;
+  __syncthreads();
+  if (tid < r) qs_l[tid] = qall[ch_l[tid]];
+  __syncthreads();
+  double qr[RMAX];
+  if constexpr (R > 0) {
+#pragma unroll
+    for (int j = 0; j < R; ++j) qr[j] = qs_l[j];
+  }
+  for (int c0 = 0; c0 < ITEMS; c0 += CB) {
+    if (c0 > 0) load_pass(c0);
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
       const int uloc = (c0 + i) * kNT + tid;
@@ -311,7 +325,8 @@ __global__ __launch_bounds__(kNT) void partition_onepass_kernel(
       if (t >= n) {
         sv = -INFINITY;
       } else if (t >= t_append) {
-        sv = append_row(Kc + (row * T_cap + t) * kHeadDim, lab + t * r, ch_l, qs_l, r);
+        if constexpr (R > 0) sv = append_row_n<R>(Kc + (row * T_cap + t) * kHeadDim, lab + t * R, ch_l, qs_l);
+        else sv = append_row(Kc + (row * T_cap + t) * kHeadDim, lab + t * r, ch_l, qs_l, r);
       } else if constexpr (R > 0) {
         sv = float(dot_label<LNV>(raw[i], qr, TE()));
       } else {
