@@ -24,38 +24,25 @@ __device__ __forceinline__ double group_q_sum(const TE* __restrict__ qg, int G, 
   return s;
 }
 
-// qs at channel c in the score kernel's own order for any group size: the
-// heads past the eighth first, then heads 0 .. 7 (equal to group_q_sum for
-// groups of up to eight heads).
-template <typename TE>
-__device__ __forceinline__ double score_q_sum(const TE* __restrict__ qg, int G, int c) {
-  double s = 0.0;
-  for (int h = 8; h < G; ++h) s += double(elem_to_f32(qg[int64_t(h) * kHeadDim + c]));
-  for (int h = 0; h < 8 && h < G; ++h) s += double(elem_to_f32(qg[int64_t(h) * kHeadDim + c]));
-  return s;
-}
-
-// The same sums in two steps, so that other requests can go out between the
-// loads and the additions: q_load8 requests the first eight heads' values
-// (a loop over a run-time head count would wait for each); q_add8 adds them
-// in score_q_sum's order (kScoreOrder) or group_q_sum's, the heads past the
-// eighth read there.
+// qs at channel c in the score kernel's own order for any group size (the
+// heads past the eighth first, then heads 0 .. 7: group_q_sum's result for
+// groups of up to eight heads), in two steps so that other requests can go
+// out between the loads and the additions: q_load8 requests the first eight
+// heads' values together (a loop over a run-time head count would wait for
+// each), q_score_sum adds them, reading any further heads itself.
 template <typename TE>
 __device__ __forceinline__ void q_load8(const TE* __restrict__ qg, int G, int c, float (&v)[8]) {
 #pragma unroll
   for (int h = 0; h < 8; ++h) v[h] = elem_to_f32(qg[int64_t(h < G ? h : 0) * kHeadDim + c]);
 }
 
-template <bool kScoreOrder, typename TE>
-__device__ __forceinline__ double q_add8(const float (&v)[8], const TE* __restrict__ qg, int G, int c) {
+template <typename TE>
+__device__ __forceinline__ double q_score_sum(const float (&v)[8], const TE* __restrict__ qg, int G, int c) {
   double s = 0.0;
-  if (kScoreOrder)
-    for (int h = 8; h < G; ++h) s += double(elem_to_f32(qg[int64_t(h) * kHeadDim + c]));
+  for (int h = 8; h < G; ++h) s += double(elem_to_f32(qg[int64_t(h) * kHeadDim + c]));
 #pragma unroll
   for (int h = 0; h < 8; ++h)
     if (h < G) s += double(v[h]);
-  if (!kScoreOrder)
-    for (int h = 8; h < G; ++h) s += double(elem_to_f32(qg[int64_t(h) * kHeadDim + c]));
   return s;
 }
 

@@ -99,8 +99,13 @@ __device__ __forceinline__ float append_row_pos(const TE* __restrict__ Krow, TE*
 // tile of a row runs on the XCD of the fused kernel's splits of that row, whose
 // L2 then holds what this kernel wrote), else (tiles, Hkv, B).
 // SORT: sorted-list output (block == 1, tile_hist given), in the score buffer.
+// The unsorted bf16 instance for 16 label channels is held to 80 VGPRs (six
+// wavefronts per SIMD: three workgroups per CU instead of two, for more label
+// rows in flight on long streams); it fits without spilling, where the other
+// instances would spill.
 template <typename TE, int R, bool RAGGED, bool POS, bool SORT>
-__global__ __launch_bounds__(kThreads) void score_kernel(const TE* __restrict__ q, TE* __restrict__ label,
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(sizeof(TE) == 2 && R == 16 && !RAGGED && !POS && !SORT ? 6 : 1))) void score_kernel(const TE* __restrict__ q, TE* __restrict__ label,
                                                          const int32_t* __restrict__ ch, int64_t T_cap, int T,
                                                          int t_append, int G, int Hkv, int r, int block,
                                                          const TE* __restrict__ Kc, float* __restrict__ scores,

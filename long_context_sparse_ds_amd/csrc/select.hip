@@ -278,11 +278,11 @@ __global__ __launch_bounds__(kNT) void partition_onepass_kernel(
   const int64_t n_p = min(kPartUnits, n - base);
   const int64_t k_p = min(k, n_p);
   const int g = int(row % Hkv);
-  // Loads that do not wait on each other: the q sums of all 128 channels
-  // (so that none waits for the channel table), the channel table, and the
-  // first pass's label rows; the label channels' sums are picked after them.
-  // (The loads are unconditional, only the stores below are not: a load in a
-  // branch is waited for where the branch ends, before the label rows' requests.)
+  // Requests that do not wait on each other, ahead of any use: the group's q
+  // for all 128 channels (so that no sum waits for the channel table), the
+  // channel table and the first pass's label rows; the label channels' sums
+  // are picked after the barrier.  The loads are unconditional and only the
+  // stores are not: a load in a branch is waited for where the branch ends.
   const TE* qg = q + row * G * kHeadDim;
   float qv8[8];
   q_load8(qg, G, tid & (kHeadDim - 1), qv8);
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(kNT) void partition_onepass_kernel(
     }
   };
   load_pass(0);
-  const double qsum = q_add8<true>(qv8, qg, G, tid & (kHeadDim - 1));
+  const double qsum = q_score_sum(qv8, qg, G, tid & (kHeadDim - 1));
   if (tid < kHeadDim) qall[tid] = qsum;
   if (tid < r) ch_l[tid] = cj;
   for (int i = tid; i < kHistBins; i += kNT) hist1[i] = 0u;
