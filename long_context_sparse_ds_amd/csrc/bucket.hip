@@ -75,12 +75,9 @@ struct BucketSmem {
   uint32_t map[1024];            // the row's kept tokens, one bit each (32768 tokens)
   uint32_t eq[1024];             // ties at the threshold: map of the tied candidates
   uint32_t eqpre[1024];          // ties: tied candidates before each map word
-  uint32_t rhi[kNT];             // R[2047 - 2t] of thread t (thread t - 1 needs it)
   uint32_t wsum[kNW];
   uint32_t info[4];              // a digit, the count above it, its count
-  uint32_t t_above[kMaxTiles], t_in[kMaxTiles], t_ci0[kMaxTiles];
-  __align__(16) uint32_t pre_cr[kMaxTiles + 4];      // tile offsets of the tokens above d0 past the window
-  __align__(16) uint32_t pre_ci[kMaxTiles + 4];      // and of the candidates past the window
+  uint32_t seam_lo[kNW], seam_hi[kNW];   // R[b_lo] of each wavefront's lane 63, R[b_hi] of its lane 0
   union {
     uint32_t pw[kMaxTiles][1024];   // the tiles' prefix words, until the tiles' slices are known
     struct {
@@ -200,7 +197,6 @@ __global__ __launch_bounds__(kNT) void bucket_attn_kernel(
   for (int i = 0; i < 2; ++i) sm.h1[i * kNT + tid] = 0u;
   sm.h2[tid] = 0u;
   sm.map[tid] = 0u;
-  if (tid == 0) sm.info[0] = sm.info[1] = sm.info[2] = 0u;
   uint32_t R_hi = 0u, R_lo = 0u;   // the row's tokens whose top digit exceeds b_hi, b_lo
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
@@ -209,54 +205,80 @@ __global__ __launch_bounds__(kNT) void bucket_attn_kernel(
     R_lo += in ? w0[t] & 0xFFFFu : 0u;
     if (in) sm.u.pw[t][kNT - 1 - tid] = w0[t];
   }
-  sm.rhi[tid] = R_hi;
-  __syncthreads();
-  DS_STAMP(bucket, 2);   // prefix words and list heads in
-
-  // B. d0: R[d0] < k <= R[d0 - 1] (R[-1] = every unit); R[b_lo - 1] is the next thread's R[b_hi].
+  // B. d0: R[d0] < k <= R[d0 - 1] (R[-1] = every unit).  Exactly one digit
+  // qualifies (R[2047] = 0 < k <= n_units).  Thread t tests b_hi, and b_lo
+  // with the next lane's R[b_hi] (DPP wave_shl:1), before the first barrier;
+  // the digit between two wavefronts (lane 63's b_lo) is tested after it by
+  // every wavefront, from the two counts its edge lanes leave in LDS.
   {
-    const uint32_t R_lm1 = tid == kNT - 1 ? uint32_t(n_units) : sm.rhi[tid + 1];
+    constexpr int kDppWaveShl1 = 0x130;
+    const uint32_t R_next = uint32_t(__builtin_amdgcn_update_dpp(0, int(R_hi), kDppWaveShl1, 0xF, 0xF, false));
+    const uint32_t R_lm1 = tid == kNT - 1 ? uint32_t(n_units) : R_next;
     const uint32_t b_hi = 2047u - 2u * uint32_t(tid);
     if (R_hi < k && R_lo >= k) {
       sm.info[0] = b_hi;
       sm.info[1] = R_hi;
       sm.info[2] = R_lo - R_hi;
-    } else if (R_lo < k && R_lm1 >= k) {
+    } else if ((lane < 63 || tid == kNT - 1) && R_lo < k && R_lm1 >= k) {
       sm.info[0] = b_hi - 1u;
       sm.info[1] = R_lo;
       sm.info[2] = R_lm1 - R_lo;
     }
+    if (lane == 63) sm.seam_lo[wave] = R_lo;
+    if (lane == 0) sm.seam_hi[wave] = R_hi;
   }
   __syncthreads();
+  DS_STAMP(bucket, 2);   // prefix words and list heads in
+  uint32_t d0, A, cnt0;
+  {
+    // Seam w: b_lo of thread 64 w + 63 (digit 1920 - 128 w), whose R[b_lo - 1]
+    // is thread 64 (w + 1)'s R[b_hi].  Otherwise a thread's own test wrote info.
+    const bool lv = lane < kNW - 1;
+    const uint32_t slo = lv ? sm.seam_lo[lane] : 0u, shi = lv ? sm.seam_hi[lane + 1] : 0u;
+    const uint64_t hit = __ballot(lv && slo < k && shi >= k);
+    if (hit != 0u) {
+      const int w = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+      const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(slo), w));
+      const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(shi), w));
+      d0 = 1920u - 128u * uint32_t(w);
+      A = lo;
+      cnt0 = hi - lo;
+    } else {
+      d0 = sm.info[0];
+      A = sm.info[1];
+      cnt0 = sm.info[2];
+    }
+  }
   DS_STAMP(bucket, 3);   // d0
-  // (Counts are bounded by the row's units, so that lists inconsistent with
-  // their prefixes cannot send a loop or an access out of range.)
-  const uint32_t d0 = sm.info[0], A = min(sm.info[1], k), cnt0 = min(sm.info[2], uint32_t(n_units));
-  if (wave == 0) {   // each tile's slices above and in d0, and their offsets
-    uint32_t above = 0u, in = 0u;
-    if (lane < tiles) {
-      const auto P = [&](int b) -> uint32_t {
-        return b < 0 ? tile_count(lane) : (sm.u.pw[lane][b >> 1] >> ((b & 1) * 16)) & 0xFFFFu;
-      };
-      above = min(P(int(d0)), tile_count(lane));
-      in = min(P(int(d0) - 1) - above, tile_count(lane) - above);
-    }
-    // Past the window (rare): tokens above d0 at [W, above), candidates at [ci0, above + in).
-    const uint32_t cr = above > uint32_t(W) ? above - uint32_t(W) : 0u;
-    const uint32_t ci0 = max(above, uint32_t(W));
-    const uint32_t ci = above + in > ci0 ? above + in - ci0 : 0u;
-    const uint32_t ir = wave_inclusive_scan(cr), ic = wave_inclusive_scan(ci);
-    if (lane <= MT) {   // lanes past the tiles hold the totals
-      sm.pre_cr[lane] = ir - cr;
-      sm.pre_ci[lane] = ic - ci;
-    }
-    if (lane < MT) {
-      sm.t_above[lane] = above;
-      sm.t_in[lane] = in;
-      sm.t_ci0[lane] = ci0;
-    }
+  // (Counts are bounded by the row's units, and d0 by the digit range, so that
+  // lists inconsistent with their prefixes cannot send a loop or an access out
+  // of range.)
+  d0 &= 2047u;
+  A = min(A, k);
+  cnt0 = min(cnt0, uint32_t(n_units));
+  // Tokens of tile t above d0 (the head of its list), from its prefix words.
+  const auto above_of = [&](int t) -> uint32_t {
+    return min((sm.u.pw[t][d0 >> 1] >> ((d0 & 1u) * 16)) & 0xFFFFu, tile_count(t));
+  };
+  // Every wavefront forms the tiles' slices itself (lane i: tile i), so no
+  // barrier is needed before the classification.
+  uint32_t above = 0u, in = 0u;
+  if (lane < tiles) {
+    above = above_of(lane);
+    const uint32_t pm1 = d0 == 0u ? tile_count(lane) : (sm.u.pw[lane][(d0 - 1u) >> 1] >> (((d0 - 1u) & 1u) * 16)) & 0xFFFFu;
+    in = min(pm1 - min(pm1, above), tile_count(lane) - above);
   }
-  __syncthreads();
+  // Past the window (rare): tokens above d0 at [W, above), candidates at [ci0, above + in).
+  const uint32_t cr = above > uint32_t(W) ? above - uint32_t(W) : 0u;
+  const uint32_t ci0_l = max(above, uint32_t(W));
+  const uint32_t ci = above + in > ci0_l ? above + in - ci0_l : 0u;
+  const uint32_t ir = wave_inclusive_scan(cr), ic = wave_inclusive_scan(ci);
+  uint32_t pr[MT + 1], pc[MT + 1];   // exclusive offsets; lanes past the tiles hold the totals
+#pragma unroll
+  for (int i = 0; i <= MT; ++i) {
+    pr[i] = uint32_t(__builtin_amdgcn_readlane(int(ir - cr), i));
+    pc[i] = uint32_t(__builtin_amdgcn_readlane(int(ic - ci), i));
+  }
   DS_STAMP(bucket, 4);   // the tiles' slices
   // A tile-local id read from a list, as a token of tile t (masked into the tile).
   const auto token_of = [&](int t, uint32_t id) -> int { return t * kTileU + int(min(id, tile_count(t) - 1u)); };
@@ -264,32 +286,31 @@ __global__ __launch_bounds__(kNT) void bucket_attn_kernel(
 
   // C. The prefetched entries: tokens above d0 into the map, candidates (in d0)
   // kept in registers with their key, counted into the first pass's histogram.
+  // An entry's tile is the same for the whole wavefront (W >= 64).
   uint32_t ck[2];
   int ct[2];
   bool cv[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int e = tid + j * kNT, t = min(e / W, tiles - 1);
-    const uint32_t pos = uint32_t(e % W), ab = sm.t_above[t], in = sm.t_in[t];
+    const int e = tid + j * kNT;
+    const int t = __builtin_amdgcn_readfirstlane(min((wave * 64 + j * kNT) / W, tiles - 1));
+    const uint32_t pos = uint32_t(e % W);
+    const uint32_t ab = uint32_t(__builtin_amdgcn_readlane(int(above), t));
+    const uint32_t in_t = uint32_t(__builtin_amdgcn_readlane(int(in), t));
     const int tok = token_of(t, pf[j] & 2047u);
     ck[j] = (d0 << 21) | (pf[j] >> 11);
     ct[j] = tok;
-    cv[j] = pf_ok[j] && pos >= ab && pos < ab + in;
+    cv[j] = pf_ok[j] && pos >= ab && pos < ab + in_t;
     if (pf_ok[j] && pos < ab) mark(sm.map, tok);
     if (cv[j]) atomicAdd(&sm.h1[(ck[j] >> 10) & 2047u], 1u);
   }
   // Entries past the window, if any (rare): loops with no iteration otherwise.
-  uint32_t pr[MT + 1], pc[MT + 1];
-#pragma unroll
-  for (int i = 0; i <= MT; ++i) {
-    pr[i] = uint32_t(__builtin_amdgcn_readfirstlane(int(sm.pre_cr[i])));
-    pc[i] = uint32_t(__builtin_amdgcn_readfirstlane(int(sm.pre_ci[i])));
-  }
   const uint32_t n_cr = pr[MT] , n_ci = pc[MT];   // (entries MT hold the totals)
   const auto cand_load = [&](uint32_t c, uint32_t& key, int& tok) {
     uint32_t off;
     const int t = tile_of<MT>(pc, tiles, c, off);
-    const uint32_t e = slist_[lrow + int64_t(t) * kTileU + min(sm.t_ci0[t] + (c - off), tile_count(t) - 1u)];
+    const uint32_t ci0 = max(above_of(t), uint32_t(W));
+    const uint32_t e = slist_[lrow + int64_t(t) * kTileU + min(ci0 + (c - off), tile_count(t) - 1u)];
     key = (d0 << 21) | (e >> 11);
     tok = token_of(t, e & 2047u);
   };
@@ -502,30 +523,8 @@ __global__ __launch_bounds__(kNT) void bucket_attn_kernel(
   // output channel sums the weighted wavefront states (independent LDS reads);
   // the same arithmetic as the fused kernel's, so both give equal outputs.
   static_assert(kNW == 16, "one 16-lane row per head");
-  if (wave < (HC + 3) / 4) {
-    const int hh = wave * 4 + lane / 16, w = lane % 16;
-    const bool in = hh < HC;
-    const int h = in ? hh : 0;
-    const float mw = in ? sm.wm[w][h] : -INFINITY;
-    const float M = row16_max(mw);
-    const float f = M == -INFINITY ? 0.f : __expf(mw - M);   // empty wavefronts: 0
-    const float Ls = row16_sum(in ? sm.wl[w][h] * f : 0.f);
-    if (in) {
-      sm.wf[h][w] = f;
-      if (w == 0) {
-        sm.hm[h] = M;
-        sm.hl[h] = Ls;
-      }
-    }
-  }
-  __syncthreads();
-  DS_STAMP(bucket, 11);   // combine weights
-  for (int i = tid; i < HC * kHeadDim; i += kNT) {
-    const int h = i / kHeadDim, c = i % kHeadDim;
-    float Acc = 0.f;
-#pragma unroll
-    for (int w = 0; w < kNW; ++w) Acc = fmaf(sm.u.a.wacc[w][h][c], sm.wf[h][w], Acc);
-    const float M = sm.hm[h], Ls = sm.hl[h];
+  // The state (Acc, M, Ls) of output channel c of head h, and where it goes.
+  const auto emit = [&](int h, int c, float Acc, float M, float Ls) {
     const int64_t bh = bh0 + h;
     if (n_split == 1) {
       out_[bh * kHeadDim + c] = Acc / Ls;
@@ -537,6 +536,61 @@ __global__ __launch_bounds__(kNT) void bucket_attn_kernel(
         __hip_atomic_store(&part_ml_[(bh * n_split + split) * 2 + 1], Ls, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
       }
+    }
+  };
+  if constexpr (HC == 1) {
+    // One head: each of the 128 output threads forms the wavefronts' weights
+    // exp(m_w - M) and the combined denominator itself (broadcast LDS reads),
+    // with no barrier between the weights and the sums.
+    if (tid < kHeadDim) {
+      float mw[kNW], f[kNW];
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kNW; ++w) {
+        mw[w] = sm.wm[w][0];
+        M = fmaxf(M, mw[w]);
+      }
+      float Ls = 0.f;
+#pragma unroll
+      for (int w = 0; w < kNW; ++w) {
+        f[w] = M == -INFINITY ? 0.f : __expf(mw[w] - M);   // empty wavefronts: 0
+        Ls = fmaf(sm.wl[w][0], f[w], Ls);
+      }
+      float Acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < kNW; ++w) Acc = fmaf(sm.u.a.wacc[w][0][tid], f[w], Acc);
+      DS_STAMP(bucket, 11);   // combine weights
+      emit(0, tid, Acc, M, Ls);
+    }
+  } else {
+    // Each wavefront's weight in the combined state, once per head: lane
+    // 16 (h % 4) + w of wavefront h / 4 (one 16-lane row per head).  Then every
+    // output channel sums the weighted wavefront states (independent LDS reads);
+    // the same arithmetic as the fused kernel's, so both give equal outputs.
+    if (wave < (HC + 3) / 4) {
+      const int hh = wave * 4 + lane / 16, w = lane % 16;
+      const bool in = hh < HC;
+      const int h = in ? hh : 0;
+      const float mw = in ? sm.wm[w][h] : -INFINITY;
+      const float M = row16_max(mw);
+      const float f = M == -INFINITY ? 0.f : __expf(mw - M);   // empty wavefronts: 0
+      const float Ls = row16_sum(in ? sm.wl[w][h] * f : 0.f);
+      if (in) {
+        sm.wf[h][w] = f;
+        if (w == 0) {
+          sm.hm[h] = M;
+          sm.hl[h] = Ls;
+        }
+      }
+    }
+    __syncthreads();
+    DS_STAMP(bucket, 11);   // combine weights
+    for (int i = tid; i < HC * kHeadDim; i += kNT) {
+      const int h = i / kHeadDim, c = i % kHeadDim;
+      float Acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < kNW; ++w) Acc = fmaf(sm.u.a.wacc[w][h][c], sm.wf[h][w], Acc);
+      emit(h, c, Acc, sm.hm[h], sm.hl[h]);
     }
   }
   DS_STAMP(bucket, 12);   // output or split state stored

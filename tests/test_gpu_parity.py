@@ -79,6 +79,13 @@ SMALL = [
              fixed_outliers=True),
     Workload("gqa8_block16", "bf16", B=1, Hq=16, Hkv=2, d=128, T=4000, r=16, block=16, k_units=25, seed_base=19700),
     Workload("gqa16_rows8", "bf16", B=4, Hq=32, Hkv=2, d=128, T=3000, r=8, block=1, k_units=150, seed_base=19800),
+    # One head per row, 8 rows (the XCD-grouped grid) and 8 splits per row: a padded cache, a kept count that
+    # leaves the last split one token (449 = 7 * 64 + 1), 10 tiles (the 16-tile selection), every token kept.
+    Workload("mha_cs_rows8", "bf16", B=2, Hq=4, Hkv=4, d=128, T=6000, r=16, block=1, k_units=512, seed_base=19900,
+             T_cap=6100),
+    Workload("mha_cs_k449_tiles10", "bf16", B=1, Hq=8, Hkv=8, d=128, T=20000, r=8, block=1, k_units=449,
+             seed_base=19910),
+    Workload("mha_cs_dense", "bf16", B=1, Hq=8, Hkv=8, d=128, T=500, r=16, block=1, k_units=500, seed_base=19920),
     # 256 rows: one workgroup per row, which builds the row's top-digit histogram itself
     Workload("rows256_one_split", "bf16", B=32, Hq=8, Hkv=8, d=128, T=2500, r=16, block=1, k_units=100,
              seed_base=19950),
