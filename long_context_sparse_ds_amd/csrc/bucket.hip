@@ -412,16 +412,19 @@ __global__ __launch_bounds__(kNT) void bucket_attn_kernel(
   const int n_sel = p0 < p1 ? int(p1 - p0) : 0;
   DS_STAMP(bucket, 7);   // position scan
   if (pos < p1 && pos + cnt > p0) {
-    int32_t* ridx = indices_ + int64_t(row) * k_units_;
     for (uint32_t w = word; w != 0u; w &= w - 1u, ++pos) {
       if (pos < p0 || pos >= p1) continue;
-      const int tok = tid * 32 + __builtin_ctz(w);
-      sm.u.a.sel[pos - p0] = tok;
-      if (hchunk == 0) ridx[pos] = tok;
+      sm.u.a.sel[pos - p0] = tid * 32 + __builtin_ctz(w);
     }
   }
   __syncthreads();
-  DS_STAMP(bucket, 8);   // the split's indices written
+  DS_STAMP(bucket, 8);   // the split's kept list in LDS
+  // The split's slice of the indices, from the list (coalesced), after the
+  // barrier: a barrier waits for the workgroup's outstanding global stores.
+  if (hchunk == 0) {
+    int32_t* ridx = indices_ + int64_t(row) * k_units_ + p0;
+    for (int i = tid; i < n_sel; i += kNT) ridx[i] = sm.u.a.sel[i];
+  }
 
   // E. Attention over the split's kept rows.
   const TE* __restrict__ K = static_cast<const TE*>(K_);

@@ -34,7 +34,7 @@ PHASES = {
     "select": {2: "partition scored", 3: "partition threshold", 4: "candidates' histogram stored",
                5: "candidates emitted"},
     "bucket": {2: "prefix words, list heads in", 3: "d0", 4: "tiles' slices", 5: "candidates classified",
-               6: "radix passes, join", 7: "position scan", 8: "split's indices written",
+               6: "radix passes, join", 7: "position scan", 8: "split's kept list in LDS",
                9: "wavefront 0: gather, lane-group merge", 10: "all states in LDS", 11: "combine weights",
                12: "state stored", 13: "stores completed", 14: "ticket", 15: "splits merged"},
     "selattn": {16: "one pass: label rows scored", 2: "scores, top-digit counts in", 3: "d0",
