@@ -90,6 +90,15 @@ __device__ __forceinline__ float append_row(const TE* __restrict__ Krow, TE* __r
   return float(a);
 }
 
+// append_row's score alone (same arithmetic), for a caller that stores the
+// label row later.
+template <typename TE>
+__device__ __forceinline__ float append_score(const TE* __restrict__ Krow, const int* sch, const double* qs, int r) {
+  double a = 0.0;
+  for (int j = 0; j < r; ++j) a = fma(qs[j], double(elem_to_f32(Krow[sch[j]])), a);
+  return float(a);
+}
+
 // append_row for a label width R known at compile time: every channel is
 // requested before any is used (one round trip), with the same arithmetic.
 template <int R, typename TE>

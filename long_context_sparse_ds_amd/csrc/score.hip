@@ -212,8 +212,10 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TE) == 2 && R == 16 && !RAGGED && !POS
 
   // An appended token's label row and score, from the staged K row when
   // there is one (separate calls keep the LDS reads LDS reads).
+  // A staged row's label row is stored at the end of the kernel: a barrier
+  // waits for the workgroup's outstanding global stores.
   const auto append = [&](int t, TE* Lrow) -> float {
-    if (t - a_lo < kPreRows) return append_row(reinterpret_cast<const TE*>(krow[t - a_lo]), Lrow, sch, qs, r);
+    if (t - a_lo < kPreRows) return append_score(reinterpret_cast<const TE*>(krow[t - a_lo]), sch, qs, r);
     return append_row(Kc + (int64_t(row) * T_cap + t) * kHeadDim, Lrow, sch, qs, r);
   };
   float u[kTPT];
@@ -308,7 +310,6 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TE) == 2 && R == 16 && !RAGGED && !POS
       const int t = t0 + i * kThreads;
       uv[i] = u[i];
       has[i] = t < Ti;
-      if (!SORT && t < T) out[t] = u[i];   // -inf past this sequence's length
     }
   } else {
     // 64 consecutive tokens per wavefront, 64-aligned: blocks of `block` lanes.
@@ -320,9 +321,19 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TE) == 2 && R == 16 && !RAGGED && !POS
       const int t = t0 + i * kThreads;
       uv[i] = v;
       has[i] = t < Ti && (t & (block - 1)) == 0;
-      if (t < T && (t & (block - 1)) == 0) out[t >> lb] = v;   // -inf past this sequence's length
     }
   }
+  // The unit scores (-inf past this sequence's length), stored after the
+  // histogram's barrier: a barrier waits for the workgroup's outstanding
+  // global stores.
+  const auto store_scores = [&]() {
+    const int lb = __builtin_ctz(unsigned(block));
+#pragma unroll
+    for (int i = 0; i < kTPT; ++i) {
+      const int t = t0 + i * kThreads;
+      if (t < T && (t & (block - 1)) == 0) out[t >> lb] = uv[i];
+    }
+  };
   constexpr int per = kHistBins / kThreads;   // 4 bins per thread: one 8-byte store
   static_assert(per == 4, "one uint2 of packed 16-bit counts per thread");
   if constexpr (SORT) {
@@ -357,10 +368,8 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TE) == 2 && R == 16 && !RAGGED && !POS
       h[hb - j] = p;
       p += c[j];
     }
-    uint16_t* dst = tile_hist + (int64_t(row) * n_tiles + tile) * kHistBins + (hb - (per - 1));
-    *reinterpret_cast<uint2*>(dst) = make_uint2(P[3] | (P[2] << 16), P[1] | (P[0] << 16));
     __syncthreads();
-    DS_STAMP(score, 6);   // descending prefix stored
+    DS_STAMP(score, 6);   // bin starts in LDS
     __shared__ __align__(16) uint32_t sent[SORT ? kTile : 1];
 #pragma unroll
     for (int i = 0; i < kTPT; ++i)
@@ -376,6 +385,9 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TE) == 2 && R == 16 && !RAGGED && !POS
     } else {
       for (int e = threadIdx.x; e < n_tile; e += kThreads) sl[e] = sent[e];
     }
+    // The tile's descending prefix, after the last barrier.
+    uint16_t* dst = tile_hist + (int64_t(row) * n_tiles + tile) * kHistBins + (hb - (per - 1));
+    *reinterpret_cast<uint2*>(dst) = make_uint2(P[3] | (P[2] << 16), P[1] | (P[0] << 16));
   } else if (tile_hist != nullptr) {
     // Dense histogram of the top 11 key bits of this tile's units (cleared
     // above, before the barriers), every bin written, so the buffer needs no
@@ -387,6 +399,21 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TE) == 2 && R == 16 && !RAGGED && !POS
     const int b0 = threadIdx.x * per;
     uint16_t* dst = tile_hist + (int64_t(row) * n_tiles + tile) * kHistBins + b0;
     *reinterpret_cast<uint2*>(dst) = make_uint2(h[b0] | (h[b0 + 1] << 16), h[b0 + 2] | (h[b0 + 3] << 16));
+    store_scores();
+  } else {
+    store_scores();
+  }
+  // The label rows of the staged appended tokens (their scores are above).
+  if (!POS && a_lo < a_hi) {
+#pragma unroll
+    for (int i = 0; i < kTPT; ++i) {
+      const int t = t0 + i * kThreads;
+      if (t >= a_lo && t < a_hi && t - a_lo < kPreRows) {
+        const TE* kr = reinterpret_cast<const TE*>(krow[t - a_lo]);
+        TE* Lrow = L + int64_t(t) * r;
+        for (int j = 0; j < r; ++j) Lrow[j] = kr[sch[j]];
+      }
+    }
   }
   // The row's merge tickets for the fused kernel that follows start at zero.
   if (tickets != nullptr && tile == 0)

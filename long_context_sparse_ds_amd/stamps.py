@@ -30,7 +30,7 @@ from .build import LIB_STAMPS
 # Stamp slots of each stamped source file, in the order a workgroup passes them.
 PHASES = {
     "score": {2: "q and channel table in", 3: "wavefront 0: label rows in, scored", 4: "tile histogram",
-              5: "bin starts", 6: "descending prefix stored", 7: "tile sorted in LDS", 8: "list stores issued"},
+              5: "bin starts", 6: "bin starts in LDS", 7: "tile sorted in LDS", 8: "list stores issued"},
     "select": {2: "partition scored", 3: "partition threshold", 4: "candidates' histogram stored",
                5: "candidates emitted"},
     "bucket": {2: "prefix words, list heads in", 3: "d0", 4: "tiles' slices", 5: "candidates classified",
