@@ -779,3 +779,62 @@ def test_decode_bucketed_adversarial_scores(kind):
             ref = O.attend(qg, Kg, Vg, want, O.default_scale(128))
             err = float(np.max(np.abs(out[0, g * G:(g + 1) * G] - ref)))
             assert err <= OUT_TOL["bf16"], (w.name, g, err)
+
+
+def _bf16_patterns_with_digit(digit, lo, hi):
+    """bf16 bit patterns (uint16) whose float value x lies in [lo, hi) and whose float32 sort key
+    (sign flipped for x >= 0, every bit flipped for x < 0) has top 11 bits equal to digit."""
+    pats = np.arange(1 << 16, dtype=np.uint32)
+    bits = pats << 16
+    x = bits.view(np.float32)
+    key = np.where(bits >> 31 == 0, bits | 0x80000000, ~bits & 0xFFFFFFFF).astype(np.uint32)
+    ok = np.isfinite(x) & (x >= lo) & (x < hi) & ((key >> 21) == digit)
+    return pats[ok].astype(np.uint16)
+
+
+def test_bucket_top_digit_at_wavefront_seams():
+    """Rows split over 8 workgroups (the sorted-list selection) whose k-th largest score sits in
+    a digit between two wavefronts of the selection's digit scan (digit 1920 - 128 w, tested
+    from the edge lanes' counts), with many exact ties at the threshold: q is one-hot on the
+    first label channel, so a token's score is its K value there.  Seam w = 3 holds [2, 2.5),
+    seam w = 11 holds (-2, -1.75].  The kept set must equal the oracle's exactly (ties go to
+    the lowest token ids on both sides), and each output must match the oracle's attention."""
+    B, H, T, r, k, d = 1, 8, 6000, 16, 512, 128
+    rng = np.random.default_rng(20251)
+    ch = np.stack([np.sort(rng.choice(d, r, replace=False)) for _ in range(H)]).astype(np.int32)
+    f32 = lambda a: np.asarray(a, dtype=np.float32)
+    bf = lambda a: (f32(a).view(np.uint32) >> 16).astype(np.uint16)   # truncation to bf16 patterns
+    K = bf(rng.normal(0.0, 0.1, (B, H, T, d)))
+    V = bf(rng.normal(0.0, 1.0, (B, H, T, d)))
+    q = np.zeros((B, H, d), dtype=np.uint16)
+    one = bf([1.0])[0]
+    seams = {3: ((2.5, 16.0), (2.0, 2.5), (-2.0, 2.0)), 11: ((-1.74, 4.0), (-2.0, -1.74), (-8.0, -2.0))}
+    for g in range(H):
+        w = 3 if g % 2 == 0 else 11
+        (a_lo, a_hi), (s_lo, s_hi), (b_lo, b_hi) = seams[w]
+        c0 = ch[g, 0]
+        q[0, g, c0] = one
+        inside = _bf16_patterns_with_digit(1920 - 128 * w, s_lo, s_hi)
+        assert len(inside) >= 8, (w, len(inside))
+        n_above, n_in = 300 + 7 * g, 400
+        perm = rng.permutation(T)
+        col = bf(rng.uniform(b_lo, b_hi, T))
+        col[perm[:n_above]] = bf(rng.uniform(a_lo, a_hi, n_above))
+        col[perm[n_above:n_above + n_in]] = rng.choice(inside, n_in)
+        K[0, g, :, c0] = col
+    qd, Kd, Vd = to_device(q, "bf16"), to_device(K, "bf16"), to_device(V, "bf16")
+    chd = torch.from_numpy(ch).cuda()
+    label = L.ds_build_label_cache(Kd, chd)
+    out, idx = L.ds_decode_sparse_attn(qd, Kd, Vd, label, chd, T, k)
+    torch.cuda.synchronize()
+    out, idx = out.cpu().numpy(), idx.cpu().numpy()
+    for g in range(H):
+        qg = dsgen.to_f64(q[0, g:g + 1], "bf16")
+        Kf, Vf = dsgen.to_f64(K[0, g], "bf16"), dsgen.to_f64(V[0, g], "bf16")
+        u = Kf[:, ch[g, 0]]
+        theta = np.sort(u)[::-1][k - 1]
+        key_digit = (np.float32(theta).view(np.uint32) ^ (0x80000000 if theta >= 0 else 0xFFFFFFFF)) >> 21
+        assert key_digit in (1920 - 128 * 3, 1920 - 128 * 11), (g, theta, key_digit)
+        assert np.sum(u == theta) > 1, (g, "the threshold should be tied")
+        np.testing.assert_array_equal(idx[0, g], O.select_topk(u, k), err_msg=f"head {g}")
+        check_row(qg, Kf, Vf, ch[g], k, 1, T, out[0, g:g + 1], idx[0, g], "bf16", f"head {g}")
