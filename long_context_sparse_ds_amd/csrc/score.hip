@@ -379,15 +379,21 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TE) == 2 && R == 16 && !RAGGED && !POS
     DS_STAMP(score, 7);   // the tile sorted in LDS
     const int n_tile = min(kTile, Ti - tile0);
     uint32_t* sl = reinterpret_cast<uint32_t*>(out) + tile0;
+    // Non-temporal stores: the selection kernel reads these from other XCDs
+    // anyway, and lines left dirty in the L2 are written back at the kernel's
+    // end, before the next kernel starts.
     if (n_tile == kTile) {
       const int e = int(threadIdx.x) * kTPT;
-      *reinterpret_cast<uint4*>(sl + e) = *reinterpret_cast<const uint4*>(&sent[e]);
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(&sent[e]), reinterpret_cast<u32x4*>(sl + e));
     } else {
-      for (int e = threadIdx.x; e < n_tile; e += kThreads) sl[e] = sent[e];
+      for (int e = threadIdx.x; e < n_tile; e += kThreads) __builtin_nontemporal_store(sent[e], sl + e);
     }
     // The tile's descending prefix, after the last barrier.
     uint16_t* dst = tile_hist + (int64_t(row) * n_tiles + tile) * kHistBins + (hb - (per - 1));
-    *reinterpret_cast<uint2*>(dst) = make_uint2(P[3] | (P[2] << 16), P[1] | (P[0] << 16));
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 pw2 = {P[3] | (P[2] << 16), P[1] | (P[0] << 16)};
+    __builtin_nontemporal_store(pw2, reinterpret_cast<u32x2*>(dst));
   } else if (tile_hist != nullptr) {
     // Dense histogram of the top 11 key bits of this tile's units (cleared
     // above, before the barriers), every bin written, so the buffer needs no
