@@ -172,14 +172,17 @@ __device__ __forceinline__ void partition_finish(const uint32_t (&key)[ITEMS], c
       }
     });
     __syncthreads();
+    // Non-temporal: the second stage reads a row's candidates from other XCDs'
+    // writes anyway, and lines left dirty in the L2 are written back at the
+    // kernel's end, before the next kernel may start.
     for (int64_t i = threadIdx.x; i < w1 - w0; i += kNT) {
-      cs[w0 + i] = key_to_float(sm.cand[i]);
-      ci[w0 + i] = int32_t(base + kept_id[i]);
+      __builtin_nontemporal_store(key_to_float(sm.cand[i]), cs + w0 + i);
+      __builtin_nontemporal_store(int32_t(base + kept_id[i]), ci + w0 + i);
     }
   }
   for (int64_t i = k_p + threadIdx.x; i < k; i += kNT) {
-    cs[i] = -INFINITY;
-    ci[i] = -1;
+    __builtin_nontemporal_store(-INFINITY, cs + i);
+    __builtin_nontemporal_store(int32_t(-1), ci + i);
   }
   DS_STAMP(select, 5);   // candidates emitted (stores issued)
   DS_STAMP_END(select);
