@@ -183,7 +183,17 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TE) == 2 && R == 16 && !RAGGED && !POS
       const int t = t0 + i * kThreads;
       const uint4* p = reinterpret_cast<const uint4*>(L + int64_t(t < Ti ? t : 0) * R);   // token 0 exists
 #pragma unroll
-      for (int v = 0; v < NV; ++v) raw[i][v] = p[v];
+      for (int v = 0; v < NV; ++v) {
+        if constexpr (SORT) {
+          // Sorted form: the label rows are read once and the next kernel
+          // reads this kernel's lists, so the stream is kept out of the caches.
+          typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+          const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + v));
+          raw[i][v] = make_uint4(x.x, x.y, x.z, x.w);
+        } else {
+          raw[i][v] = p[v];
+        }
+      }
     }
   }
   if (tile_hist != nullptr)
