@@ -392,18 +392,26 @@ __attribute__((amdgpu_waves_per_eu(sizeof(TE) == 2 && R == 16 && !RAGGED && !POS
     // Non-temporal stores: the selection kernel reads these from other XCDs
     // anyway, and lines left dirty in the L2 are written back at the kernel's
     // end, before the next kernel starts.
+    // The head of the list (the selection kernel's first round of loads reads
+    // the first 2048 / tiles-padded-to-8-or-16 entries) and the prefix go out
+    // as ordinary stores; the rest of the list, rarely read, non-temporally.
+    const int head = 2 * 1024 / (n_tiles <= 8 ? 8 : 16);
     if (n_tile == kTile) {
       const int e = int(threadIdx.x) * kTPT;
       typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(&sent[e]), reinterpret_cast<u32x4*>(sl + e));
+      if (e < head)
+        *reinterpret_cast<uint4*>(sl + e) = *reinterpret_cast<const uint4*>(&sent[e]);
+      else
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(&sent[e]), reinterpret_cast<u32x4*>(sl + e));
     } else {
-      for (int e = threadIdx.x; e < n_tile; e += kThreads) __builtin_nontemporal_store(sent[e], sl + e);
+      for (int e = threadIdx.x; e < n_tile; e += kThreads) {
+        if (e < head) sl[e] = sent[e];
+        else __builtin_nontemporal_store(sent[e], sl + e);
+      }
     }
     // The tile's descending prefix, after the last barrier.
     uint16_t* dst = tile_hist + (int64_t(row) * n_tiles + tile) * kHistBins + (hb - (per - 1));
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    const u32x2 pw2 = {P[3] | (P[2] << 16), P[1] | (P[0] << 16)};
-    __builtin_nontemporal_store(pw2, reinterpret_cast<u32x2*>(dst));
+    *reinterpret_cast<uint2*>(dst) = make_uint2(P[3] | (P[2] << 16), P[1] | (P[0] << 16));
   } else if (tile_hist != nullptr) {
     // Dense histogram of the top 11 key bits of this tile's units (cleared
     // above, before the barriers), every bin written, so the buffer needs no
